@@ -1,0 +1,299 @@
+"""Plain, slow CPU oracle of the FlashMap draft-step attention path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check and the
+CPU-baseline leg of the benchmark may import or call this module.  The HIP path
+never routes through it, and it shares no code, table or helper with the HIP
+path: every formula below is written out again from the pages that define the
+method.
+
+Sources (the flashmap 0.1.0 wheel pages and the TokenSpeed DFlash page):
+  * modeling_flashmap.py: ``rope_tables`` / ``apply_rope`` (interleaved-pair
+    RoPE in float32), ``FlashMapRMSNorm``, ``FlashMapAttention.project_kv`` /
+    ``forward`` (scaled dot-product attention, default scale), ``FlashMapCache``
+    (dense per-layer context; the anchor's entry at position ``length``),
+    ``draft`` (context ``0..anchor``, slots at ``anchor+1..anchor+K``).
+  * sglang/model.py: ``rope_freqs``, ``_paged_cross_attention`` (page table,
+    ``cache_seqlens``), ``write_target_hidden_kv`` / ``_kv_write`` (one GEMM over
+    all layers' context K/V weights, k-norm, RoPE, write that skips the
+    uncommitted verify columns), ``load_weights`` (the all-layer weight is the
+    concatenation ``[k_0; v_0; k_1; v_1; ...]``), ``forward`` (the anchor is
+    written at its own position; ``cache_seqlens = seq_lens + 1``).
+  * vllm/model.py: ``paged_cross_attention`` (cu_seqlens_q, seqused_k,
+    block_table, softmax_scale = head_dim ** -0.5, non-causal), ``_prologue``
+    (``seqused_k`` is 0 for empty rows), ``cache_layout`` (page, head, slot
+    strides), ``_dit`` (slot positions = positions + 1).
+
+Precision: every value is carried in float64, with two exceptions the pages
+fix.  (1) The rotary angle is a float32 product of a float32 position and a
+float32 inverse frequency (``rope_tables``: ``positions.float() * inv_freq``).
+The inverse frequency itself is read as the float32 value nearest to
+``theta ** (-2i / head_dim)``.  (2) A value stored into the KV pool takes the
+pool's storage type (bf16 or fp32), because the pool is the interface between
+the write and the attention.  Everything else, the GEMM, the norms, the
+rotation, the softmax and the weighted sums, is exact up to float64 rounding.
+
+Readings of points the pages leave open are listed in the design notes of the
+repository; the ones that change arithmetic are repeated at the function that
+takes them.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_inv_freq",
+    "rope_angles",
+    "apply_rope",
+    "rms_norm",
+    "round_to_bfloat16",
+    "round_to_storage",
+    "attention",
+    "context_slot",
+    "live_rows",
+    "project_context_rows",
+    "write_context_kv",
+    "scatter_into_pool",
+    "paged_cross_attention",
+    "block_self_attention",
+]
+
+
+# --------------------------------------------------------------------- RoPE
+
+
+def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
+    """Inverse frequencies ``theta ** (-2i / head_dim)`` for ``i < head_dim / 2``.
+
+    ``rope_tables`` computes ``1 / theta ** (arange(0, head_dim, 2) / head_dim)``
+    in float32.  The reading taken here: the float32 value nearest to the exact
+    power (computed in float64, rounded once), so any implementation can
+    reproduce the same bits."""
+    if head_dim % 2:
+        raise ValueError("RoPE needs an even head_dim")
+    # Python's float power is the C library's double pow, evaluated per element.
+    exact = [float(theta) ** (-(2.0 * i) / head_dim) for i in range(head_dim // 2)]
+    return np.array(exact, dtype=np.float64).astype(np.float32)
+
+
+def rope_angles(positions, inv_freq: np.ndarray) -> np.ndarray:
+    """float32 angles ``float32(position) * inv_freq`` (one float32 multiply),
+    shape ``positions.shape + (head_dim / 2,)``, as ``rope_tables`` forms them."""
+    pos = np.asarray(positions).astype(np.float32)
+    return pos[..., None] * inv_freq.astype(np.float32)
+
+
+def apply_rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
+    """Rotate the interleaved channel pairs ``(x[2i], x[2i+1])`` of ``x (..., D)``
+    by the angles of ``positions`` (shape ``x.shape[:-1]``), ``apply_rope``:
+    ``(x1 cos - x2 sin, x2 cos + x1 sin)``.  cos/sin are taken in float64 of the
+    float32 angle."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    ang = rope_angles(positions, rope_inv_freq(d, theta)).astype(np.float64)
+    c, s = np.cos(ang), np.sin(ang)
+    x1 = x[..., 0::2]
+    x2 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x1 * c - x2 * s
+    out[..., 1::2] = x2 * c + x1 * s
+    return out
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """``x * weight / sqrt(mean(x^2) + eps)`` over the last axis
+    (``FlashMapRMSNorm``; the scale is kept exact rather than rounded to the
+    input's dtype, the plain definition of the norm)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x * np.asarray(weight, dtype=np.float64) / np.sqrt(ms + float(eps))
+
+
+# ------------------------------------------------------------ storage types
+
+
+def round_to_bfloat16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (8 significant bits, nearest, ties to
+    even), returned as float64.  Zeros stay zero; inputs are finite."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)  # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The value a pool of storage type ``dtype`` ("bf16" or "f32") holds."""
+    if dtype == "bf16":
+        return round_to_bfloat16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown storage type {dtype!r}")
+
+
+# ---------------------------------------------------------------- attention
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Non-causal softmax attention ``softmax(scale * q k^T) v`` for
+    ``q (n, D)``, ``k, v (T, D)`` (``FlashMapAttention.forward``).  An empty
+    context (``T == 0``) gives zeros (``_prologue``: no keys to read)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.zeros((q.shape[0], v.shape[1]), dtype=np.float64)
+    s = float(scale) * (q @ k.T)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v) / p.sum(axis=1, keepdims=True)
+
+
+# ------------------------------------------------------------------- paging
+
+
+def context_slot(page_table_row: np.ndarray, pos: int, page_size: int) -> int:
+    """Pool slot of logical position ``pos``: entry ``pos // page_size`` of the
+    request's page table names the page, ``pos % page_size`` the slot in it
+    (vLLM ``block_table`` semantics; a page of size 1 is sglang's
+    ``req_to_token``)."""
+    page = int(page_table_row[pos // page_size])
+    return page * page_size + pos % page_size
+
+
+def live_rows(n_rows: int, row_pos, commit_lens=None, window: int = 0) -> np.ndarray:
+    """Which rows the write stores.  A row with a negative position is skipped.
+    With ``commit_lens``, the first ``len(commit_lens) * window`` rows are verify
+    windows, request-major: column ``j`` of request ``b``'s window is written
+    only if ``j < commit_lens[b]`` (``write_target_hidden_kv``: only the
+    committed columns are written).  Later rows (the anchors) are written."""
+    row_pos = np.asarray(row_pos)
+    live = row_pos >= 0
+    if commit_lens is not None:
+        commit_lens = np.asarray(commit_lens)
+        for r in range(min(n_rows, len(commit_lens) * window)):
+            b, j = divmod(r, window)
+            if j >= commit_lens[b]:
+                live[r] = False
+    return live
+
+
+def project_context_rows(x: np.ndarray, w_kv: np.ndarray, L: int, H: int, D: int) -> np.ndarray:
+    """One GEMM over every layer's context K/V weight: ``x (n, d_in) @ w_kv^T``
+    with ``w_kv`` rows ordered (layer, {k, v}, head, dim), viewed as
+    ``(n, L, 2, H, D)`` (``load_weights`` concatenation; vLLM ``_write`` view)."""
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w_kv, dtype=np.float64).T
+    return y.reshape(y.shape[0], L, 2, H, D)
+
+
+def write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, page_size,
+                     L, H, D, eps, theta, commit_lens=None, window=0):
+    """The context/anchor K/V write of every layer.
+
+    For each live row: ``y = W_kv x``; per layer ``l`` and head ``h``, the key
+    is RMS-normed with ``k_norm_w[l]`` and rotated at the row's position, the
+    value is left as projected (``project_kv``: no norm and no RoPE on v).
+
+    Returns ``(slots, keys, values)``: ``slots (n_rows)`` int64, -1 for a
+    skipped row; ``keys, values (n_rows, L, H, D)`` float64 (rows that are
+    skipped hold zeros)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    row_req = np.asarray(row_req)
+    row_pos = np.asarray(row_pos)
+    live = live_rows(n, row_pos, commit_lens, window)
+    slots = np.full(n, -1, dtype=np.int64)
+    keys = np.zeros((n, L, H, D))
+    values = np.zeros((n, L, H, D))
+    idx = np.nonzero(live)[0]
+    if idx.size == 0:
+        return slots, keys, values
+    y = project_context_rows(x[idx], w_kv, L, H, D)
+    k_norm_w = np.asarray(k_norm_w, dtype=np.float64).reshape(L, D)
+    for n_i, r in enumerate(idx):
+        pos = int(row_pos[r])
+        slots[r] = context_slot(page_table[int(row_req[r])], pos, page_size)
+        for l in range(L):
+            k = rms_norm(y[n_i, l, 0], k_norm_w[l], eps)          # (H, D)
+            keys[r, l] = apply_rope(k, np.full(H, pos), theta)
+            values[r, l] = y[n_i, l, 1]
+    return slots, keys, values
+
+
+def scatter_into_pool(pools_k, pools_v, slots, keys, values, page_size, dtype):
+    """Store each written row into every layer's pool at its slot, rounded to
+    the pool's storage type.  ``pools_k[l], pools_v[l]`` are logical float64
+    arrays ``(pages, page_size, H, D)`` updated in place.  Live rows must name
+    distinct slots (a precondition: the pages never write one slot twice in a
+    call)."""
+    live = np.nonzero(np.asarray(slots) >= 0)[0]
+    taken = set()
+    for r in live:
+        s = int(slots[r])
+        if s in taken:
+            raise ValueError(f"slot {s} written twice")
+        taken.add(s)
+        page, off = divmod(s, page_size)
+        for l in range(len(pools_k)):
+            pools_k[l][page, off] = round_to_storage(keys[r, l], dtype)
+            pools_v[l][page, off] = round_to_storage(values[r, l], dtype)
+
+
+def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
+                          cu_seqlens_q, page_size, scale, theta, eps,
+                          requests=None, heads=None):
+    """Cross-attention of each request's draft rows onto its paged context.
+
+    Row ``r`` of request ``b`` (``cu_seqlens_q[b] <= r < cu_seqlens_q[b+1]``)
+    is query slot ``k = r - cu_seqlens_q[b]`` at position ``ctx_lens[b] + k``
+    (slots sit at ``anchor + 1 + k`` and ``ctx_len = anchor + 1``).  Its query
+    is RMS-normed with ``q_norm_w`` and rotated there (``rms_norm_rope``), then
+    attends, non-causally, to the keys/values at logical positions
+    ``0 .. ctx_lens[b] - 1`` read through the page table.
+
+    ``pool_k, pool_v``: logical ``(pages, page_size, H, D)`` arrays.  Returns
+    float64 ``(total_q, H, D)``; rows of requests not in ``requests`` and heads
+    not in ``heads`` (when given) are left as NaN."""
+    q = np.asarray(q, dtype=np.float64)
+    total_q, H, D = q.shape
+    bs = len(ctx_lens)
+    out = np.full((total_q, H, D), np.nan)
+    reqs = range(bs) if requests is None else requests
+    hs = list(range(H)) if heads is None else list(heads)
+    for b in reqs:
+        r0, r1 = int(cu_seqlens_q[b]), int(cu_seqlens_q[b + 1])
+        if r1 == r0:
+            continue
+        ctx = int(ctx_lens[b])
+        positions = ctx + np.arange(r1 - r0)
+        # Dense context of request b, in logical order.
+        n_pages = -(-ctx // page_size)
+        pages = np.asarray(page_table[b][:n_pages], dtype=np.int64)
+        k_b = pool_k[pages].reshape(-1, H, D)[:ctx]
+        v_b = pool_v[pages].reshape(-1, H, D)[:ctx]
+        for h in hs:
+            qh = rms_norm(q[r0:r1, h], q_norm_w, eps)
+            qh = apply_rope(qh, positions, theta)
+            out[r0:r1, h] = attention(qh, k_b[:, h], v_b[:, h], scale)
+    return out
+
+
+def block_self_attention(qkv, q_norm_w, k_norm_w, ctx_lens, scale, theta, eps):
+    """Bidirectional attention within each draft block.
+
+    ``qkv (n_blocks, K, 3, H, D)``: slot ``i`` of block ``b`` sits at position
+    ``ctx_lens[b] + i``; its query and key are RMS-normed (``q_norm_w``,
+    ``k_norm_w``) and rotated there, its value is used as given; every slot
+    attends to all ``K`` slots of its own block (no mask).  Returns float64
+    ``(n_blocks, K, H, D)``."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    n_blocks, K, _, H, D = qkv.shape
+    out = np.zeros((n_blocks, K, H, D))
+    for b in range(n_blocks):
+        positions = int(ctx_lens[b]) + np.arange(K)
+        for h in range(H):
+            qh = apply_rope(rms_norm(qkv[b, :, 0, h], q_norm_w, eps), positions, theta)
+            kh = apply_rope(rms_norm(qkv[b, :, 1, h], k_norm_w, eps), positions, theta)
+            out[b, :, h] = attention(qh, kh, qkv[b, :, 2, h], scale)
+    return out

@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle to facts the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each compares the oracle with a
+closed form, a textbook or library routine (complex multiplication, torch's
+scaled_dot_product_attention, torch's bfloat16 conversion), an invariant, or
+brute force on tiny inputs, so that a dropped term, a wrong sign, a wrong index
+or a transposed operand in the oracle fails at least one of them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+
+
+# ------------------------------------------------------------------- RoPE
+
+
+def test_inv_freq_closed_form():
+    # theta ** (-2i/D) = 10 ** (-i) when theta = 10 ** (D/2): D = 8 with 1e4,
+    # D = 12 with 1e6.
+    for d, theta in ((8, 1e4), (12, 1e6)):
+        f = O.rope_inv_freq(d, theta)
+        assert f.dtype == np.float32
+        expect = np.array([10.0 ** (-i) for i in range(d // 2)]).astype(np.float32)
+        np.testing.assert_array_equal(f, expect)
+    f = O.rope_inv_freq(128, 1e6)
+    assert f[0] == 1.0 and f.shape == (64,)
+    assert np.all(np.diff(f) < 0)
+
+
+def test_rope_is_complex_rotation_of_interleaved_pairs(rng):
+    # Pair (x[2i], x[2i+1]) rotates like the complex number x[2i] + 1j*x[2i+1]
+    # multiplied by exp(1j * angle_i): the interleaved convention, counter-clockwise.
+    d, theta = 16, 1e4
+    x = rng.standard_normal((5, d))
+    pos = np.array([0, 1, 7, 100, 4095])
+    ang = O.rope_angles(pos, O.rope_inv_freq(d, theta)).astype(np.float64)
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * ang)
+    y = O.apply_rope(x, pos, theta)
+    np.testing.assert_allclose(y[:, 0::2], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[:, 1::2], z.imag, rtol=0, atol=1e-13)
+
+
+def test_rope_worked_rotation():
+    # head_dim 2: inv_freq = 1, so position p rotates by p radians:
+    # (1, 0) -> (cos p, sin p) and (0, 1) -> (-sin p, cos p).
+    p = 3
+    y = O.apply_rope(np.array([[1.0, 0.0], [0.0, 1.0]]), np.array([p, p]), 1e4)
+    np.testing.assert_allclose(y, [[math.cos(3), math.sin(3)], [-math.sin(3), math.cos(3)]], atol=1e-15)
+
+
+def test_rope_identity_norm_and_pair_locality(rng):
+    d, theta = 64, 1e6
+    x = rng.standard_normal((4, d))
+    np.testing.assert_array_equal(O.apply_rope(x, np.zeros(4, dtype=int), theta), x)
+    pos = np.array([5, 123, 9999, 131087])
+    y = O.apply_rope(x, pos, theta)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    for i in (0, 5, 31):
+        xp = x.copy()
+        xp[:, 2 * i] += 1.0
+        changed = np.any(O.apply_rope(xp, pos, theta) != y, axis=0)
+        assert set(np.nonzero(changed)[0]) == {2 * i, 2 * i + 1}
+
+
+def test_rope_relative_position(rng):
+    # <R_m q, R_n k> depends only on m - n (up to the float32 rounding of angles).
+    d, theta = 64, 1e6
+    q = rng.standard_normal(d)
+    k = rng.standard_normal(d)
+    for m, n in ((10, 3), (1000, 1500), (40, 40)):
+        base = O.apply_rope(q[None], [m], theta)[0] @ O.apply_rope(k[None], [n], theta)[0]
+        for shift in (1, 17, 1000):
+            got = O.apply_rope(q[None], [m + shift], theta)[0] @ O.apply_rope(k[None], [n + shift], theta)[0]
+            assert abs(got - base) <= 2e-3 * np.linalg.norm(q) * np.linalg.norm(k)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+
+def test_rms_norm_closed_forms(rng):
+    eps = 1e-6
+    x = rng.standard_normal((6, 128)) * rng.uniform(0.01, 10, (6, 1))
+    ms = np.mean(x * x, axis=1)
+    y = O.rms_norm(x, np.ones(128), eps)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-12)
+    # (3, 4): mean square 12.5
+    np.testing.assert_allclose(O.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0), [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=1e-15)
+    # scale invariance (eps = 0) and channel-wise weight
+    np.testing.assert_allclose(O.rms_norm(7.5 * x, np.ones(128), 0.0), O.rms_norm(x, np.ones(128), 0.0), rtol=1e-12)
+    w = rng.uniform(0.5, 1.5, 128)
+    np.testing.assert_allclose(O.rms_norm(x, w, eps), O.rms_norm(x, np.ones(128), eps) * w, rtol=1e-14)
+
+
+# ------------------------------------------------------------ bf16 storage
+
+
+def test_round_to_bfloat16_matches_torch(rng):
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-8, 8, 20000))).astype(np.float32)
+    # exact ties: bf16 grid midpoints (low 16 bits = 0x8000) with both parities
+    bits = rng.integers(0x3000, 0x4800, 2000).astype(np.uint32) << 16 | 0x8000
+    ties = bits.view(np.float32)
+    for v in (x32, ties, -ties):
+        ours = O.round_to_bfloat16(v.astype(np.float64))
+        ref = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(ours, ref)
+    assert O.round_to_bfloat16(np.array([0.0]))[0] == 0.0
+
+
+# -------------------------------------------------------------- attention
+
+
+def test_attention_matches_sdpa(rng):
+    for n, t, d in ((16, 1, 64), (16, 37, 128), (3, 500, 64)):
+        q, k, v = rng.standard_normal((n, d)), rng.standard_normal((t, d)), rng.standard_normal((t, d))
+        scale = d ** -0.5
+        ref = F.scaled_dot_product_attention(*(torch.from_numpy(a)[None, None] for a in (q, k, v)), scale=scale)[0, 0]
+        np.testing.assert_allclose(O.attention(q, k, v, scale), ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases(rng):
+    d = 64
+    q = rng.standard_normal((16, d))
+    v = rng.standard_normal((9, d))
+    k = rng.standard_normal((9, d))
+    np.testing.assert_array_equal(O.attention(q, k[:1], v[:1], 0.125), np.repeat(v[:1], 16, 0))
+    same = np.repeat(k[:1], 9, 0)
+    np.testing.assert_allclose(O.attention(q, same, v, 0.125), np.repeat(v.mean(0, keepdims=True), 16, 0), atol=1e-14)
+    np.testing.assert_allclose(O.attention(q, k, v, 0.0), np.repeat(v.mean(0, keepdims=True), 16, 0), atol=1e-14)
+    peaky = k.copy()
+    peaky[4] = q[0] * 100.0
+    out = O.attention(q[:1], peaky, v, 1.0)
+    np.testing.assert_allclose(out[0], v[4], atol=1e-12)
+    assert np.all(O.attention(q, k[:0], v[:0], 0.125) == 0)
+
+
+# ---------------------------------------------------------- paged context
+
+
+def _place_dense(dense_k, dense_v, ctx, page_table, ps, n_pages, H, D):
+    """Test-side placement: logical position t of request b -> page
+    page_table[b][t // ps], slot t % ps (written independently of the oracle)."""
+    pk = np.zeros((n_pages, ps, H, D))
+    pv = np.zeros((n_pages, ps, H, D))
+    for b, n in enumerate(ctx):
+        for t in range(n):
+            pk[page_table[b][t // ps], t % ps] = dense_k[b][t]
+            pv[page_table[b][t // ps], t % ps] = dense_v[b][t]
+    return pk, pv
+
+
+def _paged_case(rng, ctx, nq, H=2, D=64, ps=16):
+    bs = len(ctx)
+    pages_per = [-(-c // ps) for c in ctx]
+    n_pages = sum(pages_per) + 3
+    perm = rng.permutation(n_pages)
+    width = max(max(pages_per), 1)
+    pt = np.zeros((bs, width), dtype=np.int64)
+    at = 0
+    for b, n in enumerate(pages_per):
+        pt[b, :n] = perm[at:at + n]
+        at += n
+    dense_k = [rng.standard_normal((c, H, D)) for c in ctx]
+    dense_v = [rng.standard_normal((c, H, D)) for c in ctx]
+    pk, pv = _place_dense(dense_k, dense_v, ctx, pt, ps, n_pages, H, D)
+    cu = np.concatenate([[0], np.cumsum(nq)])
+    q = rng.standard_normal((cu[-1], H, D))
+    w = 1.0 + 0.1 * rng.standard_normal(D)
+    return dict(ctx=ctx, pt=pt, pk=pk, pv=pv, dense_k=dense_k, dense_v=dense_v, cu=cu, q=q, w=w, ps=ps, H=H, D=D)
+
+
+def test_paged_cross_attention_equals_dense(rng):
+    # The draft step (modeling_flashmap.py ``draft``): anchor = cache length,
+    # context = positions 0..anchor, query slot k at anchor + 1 + k.
+    c = _paged_case(rng, ctx=[64, 1, 37, 0, 200], nq=[16, 16, 3, 16, 5])
+    theta, eps, scale = 1e6, 1e-6, c["D"] ** -0.5
+    out = O.paged_cross_attention(c["q"], c["w"], c["pk"], c["pv"], c["pt"], c["ctx"], c["cu"],
+                                  c["ps"], scale, theta, eps)
+    for b, n in enumerate(c["ctx"]):
+        r0, r1 = c["cu"][b], c["cu"][b + 1]
+        anchor = n - 1
+        pos = anchor + 1 + np.arange(r1 - r0)
+        for h in range(c["H"]):
+            qh = O.apply_rope(O.rms_norm(c["q"][r0:r1, h], c["w"], eps), pos, theta)
+            if n == 0:
+                np.testing.assert_array_equal(out[r0:r1, h], 0.0)
+                continue
+            kt = torch.from_numpy(c["dense_k"][b][:, h])
+            vt = torch.from_numpy(c["dense_v"][b][:, h])
+            ref = F.scaled_dot_product_attention(torch.from_numpy(qh)[None], kt[None], vt[None], scale=scale)[0]
+            np.testing.assert_allclose(out[r0:r1, h], ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_paged_cross_attention_page_permutation_invariant(rng):
+    c = _paged_case(rng, ctx=[100, 33, 16], nq=[16, 16, 16])
+    args = (c["cu"], c["ps"], 0.125, 1e6, 1e-6)
+    base = O.paged_cross_attention(c["q"], c["w"], c["pk"], c["pv"], c["pt"], c["ctx"], *args)
+    relabel = rng.permutation(c["pk"].shape[0])          # new id of each old page
+    pk2 = np.empty_like(c["pk"])
+    pv2 = np.empty_like(c["pv"])
+    pk2[relabel] = c["pk"]
+    pv2[relabel] = c["pv"]
+    pt2 = relabel[c["pt"]]
+    moved = O.paged_cross_attention(c["q"], c["w"], pk2, pv2, pt2, c["ctx"], *args)
+    np.testing.assert_array_equal(moved, base)
+
+
+# ------------------------------------------------------- self-attention
+
+
+def test_block_self_attention_matches_sdpa_and_k1(rng):
+    nb, K, H, D = 3, 16, 2, 64
+    qkv = rng.standard_normal((nb, K, 3, H, D))
+    wq, wk = 1 + 0.1 * rng.standard_normal(D), 1 + 0.1 * rng.standard_normal(D)
+    ctx = np.array([5, 1000, 0])
+    theta, eps, scale = 1e6, 1e-6, D ** -0.5
+    out = O.block_self_attention(qkv, wq, wk, ctx, scale, theta, eps)
+    for b in range(nb):
+        pos = ctx[b] + np.arange(K)
+        for h in range(H):
+            q = O.apply_rope(O.rms_norm(qkv[b, :, 0, h], wq, eps), pos, theta)
+            k = O.apply_rope(O.rms_norm(qkv[b, :, 1, h], wk, eps), pos, theta)
+            ref = F.scaled_dot_product_attention(*(torch.from_numpy(a)[None] for a in (q, k, qkv[b, :, 2, h])), scale=scale)[0]
+            np.testing.assert_allclose(out[b, :, h], ref.numpy(), rtol=1e-11, atol=1e-12)
+    one = O.block_self_attention(qkv[:, :1], wq, wk, ctx, scale, theta, eps)
+    np.testing.assert_allclose(one[:, 0], qkv[:, 0, 2], rtol=0, atol=1e-15)
+
+
+def test_block_self_attention_shift_invariant(rng):
+    # q and k of a block rotate at the same positions, so shifting the block's
+    # base position changes no score (RoPE's relative property).
+    qkv = rng.standard_normal((1, 16, 3, 2, 64))
+    w = np.ones(64)
+    a = O.block_self_attention(qkv, w, w, [40], 0.125, 1e6, 1e-6)
+    b = O.block_self_attention(qkv, w, w, [1040], 0.125, 1e6, 1e-6)
+    np.testing.assert_allclose(a, b, atol=2e-3)
+
+
+# ------------------------------------------------------------------ write
+
+
+def test_projection_concatenates_layers(rng):
+    # load_weights: the all-layer weight is cat over layers of [k_proj_l; v_proj_l].
+    L, H, D, din = 3, 2, 8, 24
+    wk = [rng.standard_normal((H * D, din)) for _ in range(L)]
+    wv = [rng.standard_normal((H * D, din)) for _ in range(L)]
+    w_kv = np.concatenate([m for l in range(L) for m in (wk[l], wv[l])])
+    x = rng.standard_normal((5, din))
+    y = O.project_context_rows(x, w_kv, L, H, D)
+    for l in range(L):
+        np.testing.assert_allclose(y[:, l, 0].reshape(5, -1), x @ wk[l].T, rtol=1e-13)
+        np.testing.assert_allclose(y[:, l, 1].reshape(5, -1), x @ wv[l].T, rtol=1e-13)
+    # brute-force dot products on a tiny case
+    for r in range(5):
+        for col in (0, 7, H * D * 2 * L - 1):
+            l, rest = divmod(col, 2 * H * D)
+            kv, rest = divmod(rest, H * D)
+            h, d = divmod(rest, D)
+            assert abs(y[r, l, kv, h, d] - sum(x[r, i] * w_kv[col, i] for i in range(din))) < 1e-12
+
+
+def _write_case(rng, L=2, H=2, D=16, ps=4):
+    bs, window = 3, 5
+    commit = np.array([2, 5, 1])
+    anchor = np.array([9, 17, 4])                 # anchor positions p_b
+    # window column j of request b sits at p_b - c_b + j; the anchor row at p_b
+    row_req = np.concatenate([np.repeat(np.arange(bs), window), np.arange(bs)])
+    row_pos = np.concatenate([anchor[b] - commit[b] + np.arange(window) for b in range(bs)] + [anchor])
+    width = -(-(anchor.max() + window + 1) // ps)
+    n_pages = bs * width
+    pt = rng.permutation(n_pages).reshape(bs, width)
+    din = 2 * H * D
+    x = rng.standard_normal((len(row_pos), din))
+    return dict(L=L, H=H, D=D, ps=ps, bs=bs, window=window, commit=commit, anchor=anchor,
+                row_req=row_req, row_pos=row_pos, pt=pt, n_pages=n_pages, x=x)
+
+
+def test_write_identity_weight_passthrough_and_commit_rule(rng):
+    c = _write_case(rng, L=1)
+    H, D = c["H"], c["D"]
+    w_kv = np.eye(2 * H * D)                     # x = concat(k, v) passes through
+    knw = 1 + 0.1 * rng.standard_normal((1, D))
+    slots, keys, values = O.write_context_kv(c["x"], w_kv, knw, c["row_req"], c["row_pos"], c["pt"], c["ps"],
+                                             1, H, D, 1e-6, 1e6, commit_lens=c["commit"], window=c["window"])
+    for r in range(len(c["row_pos"])):
+        if r < c["bs"] * c["window"]:
+            b, j = divmod(r, c["window"])
+            live = j < c["commit"][b]
+        else:
+            b, live = r - c["bs"] * c["window"], True
+        if not live:
+            assert slots[r] == -1
+            continue
+        pos = c["row_pos"][r]
+        # brute-force slot: enumerate the request's pages in logical order
+        logical = [(page, off) for page in c["pt"][b] for off in range(c["ps"])]
+        page, off = logical[pos]
+        assert slots[r] == page * c["ps"] + off
+        k = c["x"][r, : H * D].reshape(H, D)
+        v = c["x"][r, H * D:].reshape(H, D)
+        np.testing.assert_array_equal(values[r, 0], v)
+        np.testing.assert_allclose(keys[r, 0], O.apply_rope(O.rms_norm(k, knw[0], 1e-6), np.full(H, pos), 1e6), rtol=1e-14)
+    # anchors always live, uncommitted columns never
+    assert np.all(slots[c["bs"] * c["window"]:] >= 0)
+    assert (slots >= 0).sum() == c["commit"].sum() + c["bs"]
+
+
+def test_scatter_touches_only_written_slots(rng):
+    c = _write_case(rng)
+    L, H, D, ps = c["L"], c["H"], c["D"], c["ps"]
+    w_kv = rng.standard_normal((L * 2 * H * D, c["x"].shape[1])) * 0.2
+    slots, keys, values = O.write_context_kv(c["x"], w_kv, np.ones((L, D)), c["row_req"], c["row_pos"], c["pt"], ps,
+                                             L, H, D, 1e-6, 1e6, commit_lens=c["commit"], window=c["window"])
+    sentinel = -12345.0
+    pk = [np.full((c["n_pages"], ps, H, D), sentinel) for _ in range(L)]
+    pv = [np.full((c["n_pages"], ps, H, D), sentinel) for _ in range(L)]
+    O.scatter_into_pool(pk, pv, slots, keys, values, ps, "bf16")
+    for l in range(L):
+        changed = np.nonzero(np.any(pk[l] != sentinel, axis=(2, 3)).reshape(-1))[0]
+        assert set(changed) == set(int(s) for s in slots if s >= 0)
+        for r in np.nonzero(slots >= 0)[0]:
+            page, off = divmod(int(slots[r]), ps)
+            np.testing.assert_array_equal(pk[l][page, off], O.round_to_bfloat16(keys[r, l]))
+            np.testing.assert_array_equal(pv[l][page, off], O.round_to_bfloat16(values[r, l]))
+    with pytest.raises(ValueError):
+        dup = slots.copy()
+        dup[np.nonzero(slots >= 0)[0][:2]] = slots[slots >= 0][0]
+        O.scatter_into_pool(pk, pv, dup, keys, values, ps, "bf16")
+
+
+def test_written_context_is_read_back_by_paged_attention(rng):
+    # Write a whole context 0..p (committed rows + the anchor at p), then the
+    # paged attention over ctx_len = p + 1 equals dense attention over the rows
+    # just written: ties the write's slot rule to the read's.
+    L, H, D, ps = 1, 2, 16, 4
+    p = 13
+    pt = rng.permutation(6)[None, :]
+    x = rng.standard_normal((p + 1, 2 * H * D))
+    w_kv = rng.standard_normal((2 * H * D, 2 * H * D)) * 0.3
+    slots, keys, values = O.write_context_kv(x, w_kv, np.ones((1, D)), np.zeros(p + 1, int), np.arange(p + 1),
+                                             pt, ps, L, H, D, 1e-6, 1e6)
+    pk = [np.zeros((6, ps, H, D))]
+    pv = [np.zeros((6, ps, H, D))]
+    O.scatter_into_pool(pk, pv, slots, keys, values, ps, "f32")
+    q = rng.standard_normal((16, H, D))
+    out = O.paged_cross_attention(q, np.ones(D), pk[0], pv[0], pt, [p + 1], [0, 16], ps, 0.25, 1e6, 1e-6)
+    for h in range(H):
+        qh = O.apply_rope(O.rms_norm(q[:, h], np.ones(D), 1e-6), p + 1 + np.arange(16), 1e6)
+        kk = O.round_to_storage(keys[:, 0, h], "f32")
+        vv = O.round_to_storage(values[:, 0, h], "f32")
+        np.testing.assert_allclose(out[:, h], O.attention(qh, kk, vv, 0.25), rtol=1e-12, atol=1e-13)
