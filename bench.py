@@ -1,0 +1,282 @@
+"""Benchmark of the FlashMap draft-step attention path on one MI355X.
+
+A step is one pass of the whole path over one batch: the context/anchor K/V
+write (one GEMM over every layer's weight, k-norm, RoPE, paged scatter that
+skips uncommitted columns), the cross-attention plan, and for every layer the
+block self-attention and the paged cross-attention.  The default workload is
+the full draft step: 64 requests, context lengths U[1024, 8192], block 16,
+5 layers, 32 heads x 128, page size 16, bf16 pool; each request commits
+U{1..17} verify columns plus its anchor through the write.
+
+Prints ONE JSON line (see the fields below).  Inputs are resident in HBM
+before timing starts; timing brackets exactly --steps steps with device
+synchronization on both sides.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft query rows/s over paged context + achieved KV-read HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="workload: 5 = full draft step (default); 3 = attention of 5 layers; 2, 4, 1")
+    ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"])
+    ap.add_argument("--min-split", type=int, default=0, help="minimum split of the cross-attention plan (tokens)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-requests", type=int, default=0,
+                    help="requests in the oracle's timed sample (0 = pick to take ~15 s)")
+    return ap.parse_args()
+
+
+def cross_bytes(w) -> int:
+    """Algorithmic bytes of one cross-attention call: every context key and
+    value read once, the queries read and the outputs written once, the page
+    ids, lengths, cu_seqlens and the norm weight."""
+    s = 2 if w.dtype.itemsize == 2 else 4
+    ctx = w.ctx_lens.cpu().tolist()
+    kv = sum(ctx) * w.H * w.Dh * 2 * s
+    qo = 2 * w.total_q * w.H * w.Dh * s
+    pages = 4 * sum(math.ceil(c / w.page_size) for c in ctx)
+    return kv + qo + pages + 4 * (2 * w.bs + 1) + 4 * w.Dh
+
+
+def cross_flops(w) -> int:
+    ctx = w.ctx_lens.cpu().tolist()
+    cu = w.cu_seqlens_q.cpu().tolist()
+    return sum(4 * (cu[b + 1] - cu[b]) * ctx[b] * w.H * w.Dh for b in range(w.bs))
+
+
+def write_flops_bytes(w):
+    import torch
+
+    wr = w.write
+    if wr is None:
+        return 0, 0
+    n_rows, d_in = wr.x.shape
+    pos = wr.row_pos.cpu()
+    live = pos >= 0
+    if wr.commit_lens is not None:
+        cl = wr.commit_lens.cpu()
+        r = torch.arange(n_rows)
+        win = r < w.bs * wr.window
+        col = r % wr.window
+        b = torch.clamp(r // wr.window, max=w.bs - 1)
+        live &= ~(win & (col >= cl[b]))
+    m = int(live.sum())
+    s = wr.x.element_size()
+    n = w.L * 2 * w.H * w.Dh
+    flops = 2 * m * d_in * n
+    nbytes = s * (n * d_in + m * d_in + m * n) + 4 * w.L * w.Dh + 12 * n_rows
+    return flops, nbytes
+
+
+def describe(w) -> dict:
+    ctx = w.ctx_lens.cpu().tolist()
+    d = {
+        "workload": {1: "tiny fp32 step (1 request, ctx 64, 4 x 64)",
+                     2: "one-layer bf16 step (8 requests, ctx U[512,2048])",
+                     3: "all-layers attention step (64 requests, ctx U[1024,8192], 5 layers)",
+                     4: "long skewed batch (256 lognormal + one 131072-token request)",
+                     5: "full draft step: context write + 5-layer attention (64 requests, ctx U[1024,8192])"}[
+            w.workload_id],
+        "requests": w.bs, "block_size": w.K, "layers": w.L, "heads": w.H, "head_dim": w.Dh,
+        "page_size": w.page_size, "total_context_tokens": int(sum(ctx)), "pool_layout": w.meta["layout"],
+    }
+    if w.write is not None:
+        d["write_rows"] = int(w.write.x.shape[0])
+        d["write_d_in"] = int(w.write.x.shape[1])
+    return d
+
+
+def cpu_baseline(w, n_req: int):
+    """Time the oracle (as it stands) on a bounded sample of the same step:
+    for ``n_req`` requests, their write rows, then for every layer their
+    self-attention block and their cross-attention rows."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle as O
+
+    def host(t):
+        return t.detach().to(torch.float64).cpu().numpy()
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    rng = np.random.default_rng(0)
+    reqs = sorted(rng.choice(w.bs, size=min(n_req, w.bs), replace=False).tolist())
+    ps = w.page_size
+    # host copies (not timed): pages of the sampled requests, their inputs
+    inputs = []
+    for l in range(w.L):
+        ids, rows, at = [], [], 0
+        for b in reqs:
+            n = math.ceil(int(w.ctx_lens[b]) / ps)
+            ids.append(w.page_table[b, :n].long())
+            rows.append(np.arange(at, at + n))
+            at += n
+        idx = torch.cat(ids)
+        inputs.append((host(w.pools[l].k[idx]), host(w.pools[l].v[idx]), rows))
+    cu = w.cu_seqlens_q.cpu().numpy()
+    ctx = w.ctx_lens.cpu().numpy()
+    wr_in = None
+    if w.write is not None:
+        wr = w.write
+        row_req = wr.row_req.cpu().numpy()
+        mask = np.isin(row_req, reqs)
+        sel = np.nonzero(mask)[0]
+        cl = None if wr.commit_lens is None else wr.commit_lens.cpu().numpy()
+        # keep the window structure: re-index the sampled requests' windows
+        wr_in = dict(x=host(wr.x[torch.as_tensor(sel, device=wr.x.device)]), w=host(wr.w_kv), kn=host(wr.k_norm_w),
+                     pos=wr.row_pos.cpu().numpy()[sel], req=row_req[sel], pt=w.page_table.cpu().numpy(),
+                     commit=cl, sel=sel)
+    q = [host(w.q[l]) for l in range(w.L)]
+    qkv = [host(w.qkv[l][torch.as_tensor(reqs, device=w.qkv[l].device)]) for l in range(w.L)]
+    with threadpool_limits(limits=cores):
+        blas = [i.get("num_threads") for i in threadpool_info()]
+        t0 = time.perf_counter()
+        if wr_in is not None:
+            # live rows of the sampled requests (commit rule applied the oracle's way)
+            live = O.live_rows(len(w.write.row_pos), w.write.row_pos.cpu().numpy(), wr_in["commit"],
+                               w.write.window)[wr_in["sel"]]
+            keep = np.nonzero(live)[0]
+            O.write_context_kv(wr_in["x"][keep], wr_in["w"], wr_in["kn"], wr_in["req"][keep], wr_in["pos"][keep],
+                               wr_in["pt"], ps, w.L, w.H, w.Dh, w.eps, w.theta)
+        for l in range(w.L):
+            O.block_self_attention(qkv[l], host(w.self_q_norm_w[l]), host(w.self_k_norm_w[l]), ctx[reqs],
+                                   w.softmax_scale, w.theta, w.eps)
+            pk, pv, rows = inputs[l]
+            for i, b in enumerate(reqs):
+                pt = rows[i][None, :]
+                O.paged_cross_attention(q[l][cu[b]:cu[b + 1]], host(w.q_norm_w[l]), pk, pv, pt, [ctx[b]],
+                                        [0, cu[b + 1] - cu[b]], ps, w.softmax_scale, w.theta, w.eps)
+        dt = time.perf_counter() - t0
+    rows = sum(int(cu[b + 1] - cu[b]) for b in reqs) * w.L
+    return {"value": rows / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{len(reqs)} of {w.bs} requests (ids {reqs}): their write rows and, for all {w.L} layers, "
+                       f"their self-attention blocks and cross-attention rows; {dt:.1f} s wall; numpy fp64, "
+                       f"BLAS threads {blas}"),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from block_diffusion_drafter_all_amd import step as S
+    from block_diffusion_drafter_all_amd.workloads import make_workload
+
+    torch.cuda.set_device(0)
+    w = make_workload(args.config, layout=args.layout)
+    buf = S.allocate(w)
+    torch.cuda.synchronize()
+
+    def one_step(events=None):
+        if w.write is not None:
+            if events is not None:
+                events["write"][0].record()
+            S.write_context(w, buf)
+            if events is not None:
+                events["write"][1].record()
+        S.plan(w, buf, args.min_split)
+        for l in range(w.L):
+            if events is not None:
+                events["self"][l][0].record()
+            from block_diffusion_drafter_all_amd import binding as B
+            B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.ctx_lens,
+                                      w.softmax_scale, w.theta, w.eps, out=buf.self_out[l])
+            if events is not None:
+                events["self"][l][1].record()
+                events["cross"][l][0].record()
+            B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens,
+                                       w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws,
+                                       out=buf.cross_out[l])
+            if events is not None:
+                events["cross"][l][1].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly --steps steps.  Events bracket each cross-attention
+    # call on the stream it is launched on (torch's current stream).
+    E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
+    per_step = [dict(write=E(), self=[E() for _ in range(w.L)], cross=[E() for _ in range(w.L)])
+                for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        one_step(per_step[s])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+
+    cross_ms = [ev[0].elapsed_time(ev[1]) for st in per_step for ev in st["cross"]]
+    self_ms = [ev[0].elapsed_time(ev[1]) for st in per_step for ev in st["self"]]
+    write_ms = [st["write"][0].elapsed_time(st["write"][1]) for st in per_step] if w.write is not None else []
+    avg_cross = sum(cross_ms) / len(cross_ms)
+    cb = cross_bytes(w)
+    achieved = cb / (avg_cross * 1e-3) / 1e9
+    rows = w.total_q * w.L
+    out = {
+        "metric": METRIC,
+        "value": rows / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded; shapes and distributions of the drafting workload)",
+        "config": describe(w),
+        "roofline": {"bound": "hbm", "kernel": "fm_paged_cross_attention", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": cb, "avg_launch_ms": avg_cross},
+        "kv_read_GBps": achieved,
+        "kv_read_pct_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "attention_rows_per_s": rows / (sum(cross_ms + self_ms) / args.steps * 1e-3),
+        "self_attention_avg_ms": sum(self_ms) / len(self_ms),
+        "wall_s_timed": t_wall,
+    }
+    if write_ms:
+        wf, wb = write_flops_bytes(w)
+        avg_w = sum(write_ms) / len(write_ms)
+        out["write"] = {"avg_ms": avg_w, "flops": wf, "tflops": wf / (avg_w * 1e-3) / 1e12,
+                        "mfma_frac_of_bf16_peak": wf / (avg_w * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                        "algorithmic_bytes": wb}
+    if not args.no_cpu_baseline:
+        n_req = args.cpu_sample_requests or max(1, min(w.bs, 4))
+        out["cpu_baseline"] = cpu_baseline(w, n_req)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+"""ctypes binding of libfm (include/fm.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, passes their
+device pointers, shapes and strides to the C ABI and enqueues the work on
+torch's current HIP stream.  Nothing here computes any part of the draft step;
+if libfm.so is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+FM_OK = 0
+FM_E_INVALID = -1
+FM_E_UNSUPPORTED = -2
+FM_E_WORKSPACE = -3
+FM_E_HIP = -4
+FM_F32 = 0
+FM_BF16 = 1
+
+SYMBOLS = (
+    "fm_last_error",
+    "fm_version",
+    "fm_write_context_kv_workspace_size",
+    "fm_write_context_kv",
+    "fm_cross_attention_workspace_size",
+    "fm_plan_cross_attention",
+    "fm_paged_cross_attention",
+    "fm_block_self_attention",
+)
+
+
+class FmError(RuntimeError):
+    """A negative fm_status, with fm_last_error()'s message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[fm status {status}] {message}")
+        self.status = status
+
+
+class fm_kv_pool(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("page_stride", ctypes.c_int64),
+        ("slot_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libfm.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with block_diffusion_drafter_all_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    c_i32, c_i64, c_sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    f32 = ctypes.c_float
+    lib.fm_last_error.restype = ctypes.c_char_p
+    lib.fm_version.restype = ctypes.c_char_p
+    lib.fm_write_context_kv_workspace_size.restype = c_sz
+    lib.fm_write_context_kv_workspace_size.argtypes = [c_i64]
+    lib.fm_write_context_kv.restype = ctypes.c_int
+    lib.fm_write_context_kv.argtypes = [
+        vp, c_i64, c_i32, ctypes.c_int, vp, vp, vp, vp, vp, c_i32, vp, c_i64, c_i32, c_i32,
+        ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, vp, vp, c_sz, vp,
+    ]
+    lib.fm_cross_attention_workspace_size.restype = c_sz
+    lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    lib.fm_plan_cross_attention.restype = ctypes.c_int
+    lib.fm_plan_cross_attention.argtypes = [vp, vp, c_i32, c_i32, c_i32, c_i32, c_i32, vp, c_sz, vp]
+    lib.fm_paged_cross_attention.restype = ctypes.c_int
+    lib.fm_paged_cross_attention.argtypes = [
+        vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
+        f32, f32, f32, vp, vp, c_sz, vp,
+    ]
+    lib.fm_block_self_attention.restype = ctypes.c_int
+    lib.fm_block_self_attention.argtypes = [
+        vp, ctypes.c_int, c_i32, c_i32, vp, vp, vp, c_i32, c_i32, f32, f32, f32, vp, vp,
+    ]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fm_last_error() -> str:
+    return load_library().fm_last_error().decode()
+
+
+def fm_version() -> str:
+    return load_library().fm_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != FM_OK:
+        raise FmError(status, fm_last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FM_BF16
+    if t.dtype == torch.float32:
+        return FM_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, contiguous=True) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class KVPool:
+    """One layer's paged pool: ``k`` and ``v`` viewed as ``(pages, page_size,
+    H, Dh)`` with any strides (head_dim contiguous), e.g. a head-major
+    ``(pages, H, page_size, Dh)`` tensor permuted to that view."""
+
+    k: torch.Tensor
+    v: torch.Tensor
+
+    def descriptor(self) -> fm_kv_pool:
+        k, v = self.k, self.v
+        if k.dim() != 4 or v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
+            raise ValueError("k and v must be (pages, page_size, H, Dh) views of one shape, stride and dtype")
+        if k.stride(3) != 1:
+            raise ValueError("head_dim must be contiguous")
+        return fm_kv_pool(k.data_ptr(), v.data_ptr(), k.shape[0], k.stride(0), k.stride(1), k.stride(2))
+
+    @property
+    def page_size(self) -> int:
+        return self.k.shape[1]
+
+
+def fm_write_context_kv_workspace_size(n_rows: int) -> int:
+    return load_library().fm_write_context_kv_workspace_size(n_rows)
+
+
+def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta,
+                        commit_lens=None, window=0, out_slots=None, ws=None):
+    """Project, k-norm, rotate and scatter every layer's context K/V rows into
+    ``pools`` (a list of KVPool, one per layer).  Returns ``out_slots`` if given."""
+    lib = load_library()
+    _need(x, "x")
+    _need(w_kv, "w_kv", x.dtype)
+    _need(k_norm_w, "k_norm_w", torch.float32)
+    for name, t in (("row_req", row_req), ("row_pos", row_pos), ("page_table", page_table)):
+        _need(t, name, torch.int32)
+    if commit_lens is not None:
+        _need(commit_lens, "commit_lens", torch.int32)
+    if out_slots is not None:
+        _need(out_slots, "out_slots", torch.int32)
+    L = len(pools)
+    H, Dh = pools[0].k.shape[2], pools[0].k.shape[3]
+    if row_req.shape[0] != x.shape[0] or row_pos.shape[0] != x.shape[0]:
+        raise ValueError("row_req and row_pos need one entry per row of x")
+    if commit_lens is not None and commit_lens.shape[0] != page_table.shape[0]:
+        raise ValueError("commit_lens needs one entry per request (page-table row)")
+    if k_norm_w.shape != (L, Dh) or w_kv.shape != (L * 2 * H * Dh, x.shape[1]):
+        raise ValueError("k_norm_w must be (L, Dh) and w_kv (L*2*H*Dh, d_in)")
+    if out_slots is not None and out_slots.shape[0] != x.shape[0]:
+        raise ValueError("out_slots needs one entry per row of x")
+    descs = (fm_kv_pool * L)(*[p.descriptor() for p in pools])
+    n_rows, d_in = x.shape
+    if ws is None:
+        ws = torch.empty(lib.fm_write_context_kv_workspace_size(n_rows), dtype=torch.uint8, device=x.device)
+    _check(lib.fm_write_context_kv(
+        _ptr(x), n_rows, d_in, _dtype_code(x), _ptr(w_kv), _ptr(k_norm_w), _ptr(row_req), _ptr(row_pos),
+        _ptr(commit_lens), window, _ptr(page_table), page_table.stride(0), pools[0].page_size,
+        page_table.shape[0], descs, L, H, Dh, eps, rope_theta, _ptr(out_slots), _ptr(ws), ws.numel(),
+        _stream()))
+    return out_slots
+
+
+def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16) -> int:
+    return load_library().fm_cross_attention_workspace_size(bs, H, Dh, max_q)
+
+
+def fm_plan_cross_attention(ctx_lens, cu_seqlens_q, H, Dh, ws, max_q=16, min_split_tokens=0):
+    """Build the per-step tile schedule into ``ws`` (every layer reuses it)."""
+    lib = load_library()
+    _need(ctx_lens, "ctx_lens", torch.int32)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _need(ws, "ws", torch.uint8)
+    _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), _ptr(cu_seqlens_q), ctx_lens.shape[0], H, Dh, max_q,
+                                       min_split_tokens, _ptr(ws), ws.numel(), _stream()))
+
+
+def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,
+                             rope_theta, eps, ws, out=None):
+    """Paged cross-attention of ``q (total_q, H, Dh)`` onto ``pool``; the plan
+    in ``ws`` must come from fm_plan_cross_attention with the same lengths."""
+    lib = load_library()
+    _need(q, "q")
+    _need(q_norm_w, "q_norm_w", torch.float32)
+    _need(page_table, "page_table", torch.int32, contiguous=False)
+    if page_table.stride(1) != 1:
+        raise ValueError("page_table rows must be contiguous")
+    _need(ctx_lens, "ctx_lens", torch.int32)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    total_q, H, Dh = q.shape
+    if page_table.shape[0] < ctx_lens.shape[0] or cu_seqlens_q.shape[0] != ctx_lens.shape[0] + 1:
+        raise ValueError("page_table needs a row per request and cu_seqlens_q bs + 1 entries")
+    desc = pool.descriptor()
+    _check(lib.fm_paged_cross_attention(
+        _ptr(q), _dtype_code(q), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
+        page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), ctx_lens.shape[0], H, Dh,
+        softmax_scale, rope_theta, eps, _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def fm_block_self_attention(qkv, q_norm_w, k_norm_w, ctx_lens, softmax_scale, rope_theta, eps, out=None):
+    """Bidirectional attention within each block of ``qkv (n_blocks, K, 3, H, Dh)``."""
+    lib = load_library()
+    _need(qkv, "qkv")
+    _need(q_norm_w, "q_norm_w", torch.float32)
+    _need(k_norm_w, "k_norm_w", torch.float32)
+    _need(ctx_lens, "ctx_lens", torch.int32)
+    n_blocks, K, three, H, Dh = qkv.shape
+    if three != 3:
+        raise ValueError("qkv must be (n_blocks, K, 3, H, Dh)")
+    if out is None:
+        out = torch.empty((n_blocks, K, H, Dh), dtype=qkv.dtype, device=qkv.device)
+    _need(out, "out", qkv.dtype)
+    _check(lib.fm_block_self_attention(
+        _ptr(qkv), _dtype_code(qkv), n_blocks, K, _ptr(q_norm_w), _ptr(k_norm_w), _ptr(ctx_lens), H, Dh,
+        softmax_scale, rope_theta, eps, _ptr(out), _stream()))
+    return out

@@ -1,0 +1,274 @@
+// extern "C" entry points of libfm (declared in include/fm.h): host-side
+// argument validation, the RoPE frequency table, workspace layout, launches.
+// No entry point allocates, frees or synchronizes.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/fm.h"
+#include "fm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FM_OK;
+}
+
+int from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FM_E_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2_exact(int64_t x) {
+  int r = 0;
+  while ((int64_t(1) << r) < x) ++r;
+  return r;
+}
+
+size_t elem_size(fm_dtype dt) { return dt == FM_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Inverse RoPE frequencies: the float32 nearest to theta^(-2i/D), i < D/2,
+// evaluated in double precision and rounded once.
+fm::RopeFreqs rope_freqs(float theta, int Dh) {
+  fm::RopeFreqs r{};
+  for (int i = 0; i < Dh / 2; ++i) r.inv[i] = (float)std::pow((double)theta, -(2.0 * i) / (double)Dh);
+  return r;
+}
+
+int check_common(const char* fn, fm_dtype dt, int32_t H, int32_t Dh, float eps, float theta) {
+  if (dt != FM_F32 && dt != FM_BF16) return fail(FM_E_UNSUPPORTED, "%s: dtype %d is not FM_F32 or FM_BF16", fn, (int)dt);
+  if (H < 1) return fail(FM_E_INVALID, "%s: H = %d must be >= 1", fn, H);
+  if (Dh != 64 && Dh != 128) return fail(FM_E_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, Dh);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FM_E_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (!(theta > 0.f) || !std::isfinite(theta)) return fail(FM_E_INVALID, "%s: rope_theta must be finite and > 0", fn);
+  return FM_OK;
+}
+
+int check_pool(const char* fn, const fm_kv_pool& p, fm_dtype dt, int idx, int64_t* elems_per16) {
+  const int64_t q = (int64_t)(16 / elem_size(dt));
+  *elems_per16 = q;
+  if (p.k == nullptr || p.v == nullptr) return fail(FM_E_INVALID, "%s: pool %d has a null k or v pointer", fn, idx);
+  if (!aligned16(p.k) || !aligned16(p.v)) return fail(FM_E_INVALID, "%s: pool %d k/v not 16-byte aligned", fn, idx);
+  if (p.num_pages < 1) return fail(FM_E_INVALID, "%s: pool %d has num_pages %lld < 1", fn, idx, (long long)p.num_pages);
+  if (p.num_pages > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: pool %d has more than 2^31-1 pages", fn, idx);
+  if (p.page_stride < 0 || p.slot_stride < 0 || p.head_stride < 0)
+    return fail(FM_E_INVALID, "%s: pool %d has a negative stride", fn, idx);
+  if (p.page_stride % q || p.slot_stride % q || p.head_stride % q)
+    return fail(FM_E_INVALID, "%s: pool %d strides must be multiples of 16 bytes", fn, idx);
+  return FM_OK;
+}
+
+int check_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need) {
+  if (ws == nullptr) return fail(FM_E_WORKSPACE, "%s: workspace is null", fn);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(FM_E_WORKSPACE, "%s: workspace not 256-byte aligned", fn);
+  if (ws_bytes < need)
+    return fail(FM_E_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+  return FM_OK;
+}
+
+fm::PoolDesc to_desc(const fm_kv_pool& p) {
+  fm::PoolDesc d;
+  d.k = reinterpret_cast<uint64_t>(p.k);
+  d.v = reinterpret_cast<uint64_t>(p.v);
+  d.num_pages = p.num_pages;
+  d.page_stride = p.page_stride;
+  d.slot_stride = p.slot_stride;
+  d.head_stride = p.head_stride;
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fm_last_error(void) { return g_last_error.c_str(); }
+
+const char* fm_version(void) { return "fm 0.1.0 (gfx950)"; }
+
+size_t fm_write_context_kv_workspace_size(int64_t n_rows) { return fm::write_layout(n_rows).total; }
+
+int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt, const void* w_kv,
+                        const float* k_norm_w, const int32_t* row_req, const int32_t* row_pos,
+                        const int32_t* commit_lens, int32_t window, const int32_t* page_table, int64_t pt_stride,
+                        int32_t page_size, int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
+                        float eps, float rope_theta, int32_t* out_slots, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  const char* fn = "fm_write_context_kv";
+  if (n_rows < 0) return fail(FM_E_INVALID, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (n_rows == 0) return ok();
+  if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
+  if (!x || !w_kv || !k_norm_w || !row_req || !row_pos || !page_table || !pools)
+    return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
+  if (!aligned16(x) || !aligned16(w_kv)) return fail(FM_E_INVALID, "%s: x and w_kv must be 16-byte aligned", fn);
+  if (d_in < 64 || d_in % 64) return fail(FM_E_UNSUPPORTED, "%s: d_in %d must be a positive multiple of 64", fn, d_in);
+  if (L < 1 || L > fm::kMaxLayers) return fail(FM_E_UNSUPPORTED, "%s: L = %d not in [1, %d]", fn, L, fm::kMaxLayers);
+  if (!is_pow2(page_size) || page_size > 4096)
+    return fail(FM_E_UNSUPPORTED, "%s: page_size %d is not a power of two in [1, 4096]", fn, page_size);
+  if (pt_stride < 1) return fail(FM_E_INVALID, "%s: pt_stride %lld < 1", fn, (long long)pt_stride);
+  if (bs < 1) return fail(FM_E_INVALID, "%s: bs %d < 1", fn, bs);
+  if (commit_lens != nullptr && window < 1) return fail(FM_E_INVALID, "%s: commit_lens given with window %d", fn, window);
+  if (n_rows > 65535LL * 64) return fail(FM_E_UNSUPPORTED, "%s: n_rows %lld above %lld", fn, (long long)n_rows, 65535LL * 64);
+  if ((int64_t)L * 2 * H > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: L*2*H too large", fn);
+  int64_t min_pages = INT64_MAX;
+  for (int l = 0; l < L; ++l) {
+    int64_t q;
+    if (int s = check_pool(fn, pools[l], dt, l, &q)) return s;
+    min_pages = pools[l].num_pages < min_pages ? pools[l].num_pages : min_pages;
+  }
+  if (out_slots != nullptr && min_pages * (int64_t)page_size > INT32_MAX)
+    return fail(FM_E_UNSUPPORTED, "%s: slots do not fit out_slots' int32", fn);
+  if (int s = check_ws(fn, ws, ws_bytes, fm::write_layout(n_rows).total)) return s;
+
+  fm::WritePrepArgs p{};
+  p.row_req = row_req;
+  p.row_pos = row_pos;
+  p.commit_lens = commit_lens;
+  p.window = commit_lens ? window : 0;
+  p.bs = bs;
+  p.n_rows = n_rows;
+  p.page_table = page_table;
+  p.pt_stride = pt_stride;
+  p.log2ps = log2_exact(page_size);
+  p.min_pages = min_pages;
+  p.out_slots = out_slots;
+  p.ws = static_cast<uint8_t*>(ws);
+  p.lay = fm::write_layout(n_rows);
+
+  fm::WriteGemmArgs g{};
+  g.x = x;
+  g.w = w_kv;
+  g.k_norm_w = k_norm_w;
+  g.d_in = d_in;
+  g.L = L;
+  g.H = H;
+  g.eps = eps;
+  g.ws = p.ws;
+  g.lay = p.lay;
+  for (int l = 0; l < L; ++l) g.pools[l] = to_desc(pools[l]);
+  g.rope = rope_freqs(rope_theta, Dh);
+  return from_hip(fm::launch_write(p, g, dt == FM_BF16 ? 1 : 0, Dh, n_rows, stream), fn);
+}
+
+size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q) {
+  (void)max_q;
+  if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128)) return 0;
+  return fm::plan_layout(bs, H, Dh).total;
+}
+
+int fm_plan_cross_attention(const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t bs, int32_t H,
+                            int32_t Dh, int32_t max_q, int32_t min_split_tokens, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  const char* fn = "fm_plan_cross_attention";
+  if (bs < 0) return fail(FM_E_INVALID, "%s: bs %d < 0", fn, bs);
+  if (H < 1) return fail(FM_E_INVALID, "%s: H = %d must be >= 1", fn, H);
+  if (Dh != 64 && Dh != 128) return fail(FM_E_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, Dh);
+  if (max_q < 0) return fail(FM_E_INVALID, "%s: max_q %d < 0", fn, max_q);
+  if (max_q > fm::kQRows)
+    return fail(FM_E_UNSUPPORTED, "%s: max_q %d above %d query rows per request", fn, max_q, fm::kQRows);
+  if (min_split_tokens < 0) return fail(FM_E_INVALID, "%s: min_split_tokens %d < 0", fn, min_split_tokens);
+  if (bs > 0 && (!ctx_lens || !cu_seqlens_q)) return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
+  if ((int64_t)(bs + fm::plan_target_entries(H)) * H > INT32_MAX)
+    return fail(FM_E_UNSUPPORTED, "%s: bs * H too large", fn);
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh);
+  if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
+  fm::PlanArgs a{};
+  a.ctx_lens = ctx_lens;
+  a.cu_q = cu_seqlens_q;
+  a.bs = bs;
+  a.H = H;
+  a.min_split = min_split_tokens > 0 ? min_split_tokens : fm::kDefaultMinSplit;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.lay = lay;
+  return from_hip(fm::launch_plan(a, stream), fn);
+}
+
+int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
+                             const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                             const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t bs, int32_t H, int32_t Dh,
+                             float softmax_scale, float rope_theta, float eps, void* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  const char* fn = "fm_paged_cross_attention";
+  if (total_q < 0 || bs < 0) return fail(FM_E_INVALID, "%s: total_q and bs must be >= 0", fn);
+  if (total_q == 0 || bs == 0) return ok();
+  if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
+  if (!q || !q_norm_w || !pool || !page_table || !ctx_lens || !cu_seqlens_q || !out)
+    return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
+  if (!aligned16(q) || !aligned16(out)) return fail(FM_E_INVALID, "%s: q and out must be 16-byte aligned", fn);
+  if (!is_pow2(page_size) || page_size > 4096)
+    return fail(FM_E_UNSUPPORTED, "%s: page_size %d is not a power of two in [1, 4096]", fn, page_size);
+  if (pt_stride < 1) return fail(FM_E_INVALID, "%s: pt_stride %lld < 1", fn, (long long)pt_stride);
+  if (!std::isfinite(softmax_scale)) return fail(FM_E_INVALID, "%s: softmax_scale must be finite", fn);
+  if (total_q > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: total_q above 2^31-1", fn);
+  int64_t q16;
+  if (int s = check_pool(fn, *pool, dt, 0, &q16)) return s;
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh);
+  if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
+  fm::CrossArgs a{};
+  a.q = q;
+  a.out = out;
+  a.q_norm_w = q_norm_w;
+  a.pool = to_desc(*pool);
+  a.page_table = page_table;
+  a.pt_stride = pt_stride;
+  a.log2ps = log2_exact(page_size);
+  a.ctx_lens = ctx_lens;
+  a.cu_q = cu_seqlens_q;
+  a.bs = bs;
+  a.H = H;
+  a.total_q = (int32_t)total_q;
+  a.qscale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  a.eps = eps;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.lay = lay;
+  a.rope = rope_freqs(rope_theta, Dh);
+  return from_hip(fm::launch_cross_attention(a, dt == FM_BF16 ? 1 : 0, Dh, stream), fn);
+}
+
+int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int32_t K, const float* q_norm_w,
+                            const float* k_norm_w, const int32_t* ctx_lens, int32_t H, int32_t Dh,
+                            float softmax_scale, float rope_theta, float eps, void* out, hipStream_t stream) {
+  const char* fn = "fm_block_self_attention";
+  if (n_blocks < 0) return fail(FM_E_INVALID, "%s: n_blocks %d < 0", fn, n_blocks);
+  if (n_blocks == 0) return ok();
+  if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
+  if (K < 1 || K > 16) return fail(FM_E_UNSUPPORTED, "%s: block size %d not in [1, 16]", fn, K);
+  if (!qkv || !q_norm_w || !k_norm_w || !ctx_lens || !out)
+    return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
+  if (!aligned16(qkv) || !aligned16(out)) return fail(FM_E_INVALID, "%s: qkv and out must be 16-byte aligned", fn);
+  if (!std::isfinite(softmax_scale)) return fail(FM_E_INVALID, "%s: softmax_scale must be finite", fn);
+  if ((int64_t)n_blocks * H > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: n_blocks * H too large", fn);
+  fm::SelfArgs a{};
+  a.qkv = qkv;
+  a.out = out;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.ctx_lens = ctx_lens;
+  a.n_blocks = n_blocks;
+  a.K = K;
+  a.H = H;
+  a.qscale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  a.eps = eps;
+  a.rope = rope_freqs(rope_theta, Dh);
+  return from_hip(fm::launch_self_attention(a, dt == FM_BF16 ? 1 : 0, Dh, stream), fn);
+}
+
+}  // extern "C"

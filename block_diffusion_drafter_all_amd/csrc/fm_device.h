@@ -1,0 +1,283 @@
+// Device-side building blocks shared by the gfx950 kernels of the draft-step
+// attention path: register fragments in MFMA operand layout, the MFMA
+// contractions, RMSNorm + interleaved RoPE on a fragment, and conversions.
+//
+// Fragment layout.  A "row fragment" holds 16 rows of a [rows, D] matrix in one
+// wave: lane l owns row (l % 16) and, for each 16-byte chunk ch, the EPC
+// consecutive elements starting at column ch*4*EPC + (l / 16)*EPC, where EPC
+// is the number of elements per 16 bytes (8 for bf16, 4 for fp32).  This is at
+// once the A-operand layout (rows = M) and the B-operand layout (rows = N) of
+// the 16x16 MFMA family, with the contraction index permuted consistently, so
+// a product of two row fragments over their columns needs no data movement:
+//   acc[i] (lane l) = sum_d A[4*(l/16) + i][d] * B[l % 16][d].
+// The result lane l therefore holds column (l % 16) of B against rows
+// 4*(l/16) .. 4*(l/16)+3 of A (the "C layout").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+  typedef uint16_t storage;
+  static constexpr int EPC = 8;  // elements per 16-byte chunk
+};
+struct F32 {
+  typedef float storage;
+  static constexpr int EPC = 4;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float round_bf16(float f) {
+  return bf16_bits_to_f32(f32_to_bf16_bits(f));
+}
+
+template <class T>
+__device__ __forceinline__ float chunk_elem(const u32x4_t& v, int j);
+
+template <>
+__device__ __forceinline__ float chunk_elem<Bf16>(const u32x4_t& v, int j) {
+  uint32_t w = v[j >> 1];
+  return (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+}
+
+template <>
+__device__ __forceinline__ float chunk_elem<F32>(const u32x4_t& v, int j) {
+  return __uint_as_float(v[j]);
+}
+
+// Pack EPC floats into one 16-byte chunk of storage type T.
+template <class T>
+__device__ __forceinline__ u32x4_t pack_chunk(const float* x);
+
+template <>
+__device__ __forceinline__ u32x4_t pack_chunk<Bf16>(const float* x) {
+  u32x4_t r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r[w] = f32_to_bf16_bits(x[2 * w]) | (f32_to_bf16_bits(x[2 * w + 1]) << 16);
+  return r;
+}
+
+template <>
+__device__ __forceinline__ u32x4_t pack_chunk<F32>(const float* x) {
+  u32x4_t r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r[w] = __float_as_uint(x[w]);
+  return r;
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) { return *(const u32x4_t*)p; }
+
+// acc += A_chunk x B_chunk^T over one 16-byte chunk of each row fragment.
+template <class T>
+__device__ __forceinline__ void mma_chunk(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b);
+
+template <>
+__device__ __forceinline__ void mma_chunk<Bf16>(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_chunk<F32>(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(b[j]), acc, 0, 0, 0);
+}
+
+// Selection operands that move a row fragment into the C layout ("column
+// fragment"): for column tile dt (16 columns), transpose_tile returns, in lane
+// l, M[4*(l/16) + i][16*dt + l%16] for i < 4 -- four consecutive rows of one
+// column.  It is the MFMA product of the fragment with a 0/1 selection matrix,
+// exact for finite inputs.
+template <class T>
+struct Selector;
+
+template <>
+struct Selector<Bf16> {
+  u32x4_t sel[2];  // sel[h]: element j of lane (g, c) is 1 iff 8g + j == 16h + c
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = (8 * g + j == 16 * h + c) ? 1.0f : 0.0f;
+      sel[h] = pack_chunk<Bf16>(e);
+    }
+  }
+  template <int NCH>
+  __device__ __forceinline__ f32x4_t transpose_tile(const u32x4_t (&frag)[NCH], int dt) const {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    mma_chunk<Bf16>(acc, frag[dt >> 1], sel[dt & 1]);
+    return acc;
+  }
+};
+
+template <>
+struct Selector<F32> {
+  float sel[4];  // sel[j] of lane (g, c) is 1 iff 4g + j == c
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sel[j] = (4 * g + j == c) ? 1.0f : 0.0f;
+  }
+  template <int NCH>
+  __device__ __forceinline__ f32x4_t transpose_tile(const u32x4_t (&frag)[NCH], int dt) const {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(frag[dt][j]), sel[j], acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+// acc (C layout, lane (g, c) = out[4g+i][c]) += Vt x P, the weighted sum of
+// four keys: vt[i] (lane (g, c)) is column c of key 4g+i, p[i] the weight of
+// key 4g+i for query row c.  Afterwards lane (g, c) holds, for query row c,
+// output columns 4g .. 4g+3 of the tile.
+template <class T>
+__device__ __forceinline__ void mma_pv(f32x4_t& acc, const f32x4_t& vt, const f32x4_t& p);
+
+template <>
+__device__ __forceinline__ void mma_pv<Bf16>(f32x4_t& acc, const f32x4_t& vt, const f32x4_t& p) {
+  i16x4_t a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (short)f32_to_bf16_bits(vt[i]);
+    b[i] = (short)f32_to_bf16_bits(p[i]);
+  }
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mma_pv<F32>(f32x4_t& acc, const f32x4_t& vt, const f32x4_t& p) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vt[i], p[i], acc, 0, 0, 0);
+}
+
+// The probability a weight takes into the PV contraction: bf16 operands round it.
+template <class T>
+__device__ __forceinline__ float operand_value(float p);
+template <>
+__device__ __forceinline__ float operand_value<Bf16>(float p) { return round_bf16(p); }
+template <>
+__device__ __forceinline__ float operand_value<F32>(float p) { return p; }
+
+__device__ __forceinline__ float sel4(int g, float a0, float a1, float a2, float a3) {
+  return g == 0 ? a0 : (g == 1 ? a1 : (g == 2 ? a2 : a3));
+}
+
+__device__ __forceinline__ float wave_sum_groups(float x) {
+  // Sum over the four lane groups (lanes c, c+16, c+32, c+48).
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+// Inverse RoPE frequencies, float32, computed by the host (nearest float32 to
+// theta^(-2i/D)) and passed by value so every kernel sees identical bits.
+struct RopeFreqs {
+  float inv[64];
+};
+
+// RMSNorm with weight w, then the interleaved-pair rotation at position pos,
+// applied in place to the fp32 values x of a row fragment (row = lane % 16,
+// values x[ch*EPC + j] at column ch*4*EPC + g*EPC + j).
+template <class T, int D>
+__device__ __forceinline__ void norm_rope_row(float (&x)[D / 4], const float* __restrict__ w, float eps,
+                                              int pos, const RopeFreqs& rf, int g) {
+  constexpr int EPC = T::EPC;
+  constexpr int NCH = D / (4 * EPC);
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) ss += x[k] * x[k];
+  ss = wave_sum_groups(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+  const float fpos = (float)pos;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int j = 0; j < EPC; j += 2) {
+      const int col = ch * 4 * EPC + g * EPC + j;
+      // frequency index col / 2 = ch*2*EPC + g*EPC/2 + j/2, selected by lane group
+      const int f0 = ch * 2 * EPC + j / 2;
+      const float inv = sel4(g, rf.inv[f0], rf.inv[f0 + EPC / 2], rf.inv[f0 + EPC], rf.inv[f0 + 3 * EPC / 2]);
+      const float ang = fpos * inv;
+      float sn, cs;
+      sincosf(ang, &sn, &cs);
+      const float y0 = x[ch * EPC + j] * rs * w[col];
+      const float y1 = x[ch * EPC + j + 1] * rs * w[col + 1];
+      x[ch * EPC + j] = y0 * cs - y1 * sn;
+      x[ch * EPC + j + 1] = y1 * cs + y0 * sn;
+    }
+  }
+}
+
+template <class T>
+__device__ __forceinline__ void store4(typename T::storage* p, const f32x4_t& v, float scale);
+
+template <>
+__device__ __forceinline__ void store4<Bf16>(uint16_t* p, const f32x4_t& v, float scale) {
+  u32x2_t w;
+  w[0] = f32_to_bf16_bits(v[0] * scale) | (f32_to_bf16_bits(v[1] * scale) << 16);
+  w[1] = f32_to_bf16_bits(v[2] * scale) | (f32_to_bf16_bits(v[3] * scale) << 16);
+  *(u32x2_t*)p = w;
+}
+
+template <>
+__device__ __forceinline__ void store4<F32>(float* p, const f32x4_t& v, float scale) {
+  *(f32x4_t*)p = v * scale;
+}
+
+// Exclusive prefix sum over a 1024-thread block; returns the block total in *total.
+// Every thread of the block must call it (it synchronizes the block).
+__device__ inline int block_exclusive_scan(int x, int* total) {
+  __shared__ int wave_tot[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wave_tot[wv] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    int t = wave_tot[w];
+    if (w < wv) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - x;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+__device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+}  // namespace fm

@@ -1,0 +1,172 @@
+// Internal host/device interface of libfm: kernel argument blocks, workspace
+// layouts and the launchers the C ABI calls.  Not installed; include/fm.h is
+// the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fm_device.h"
+
+namespace fm {
+
+constexpr int kMaxLayers = 16;
+constexpr int kQRows = 16;          // query rows per request handled by one unit
+constexpr int32_t kPlanMagic = 0x464d504c;   // "FMPL"
+constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
+constexpr int kDefaultMinSplit = 256;        // tokens
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------ pool descriptor
+
+struct PoolDesc {
+  uint64_t k, v;            // device addresses
+  int64_t num_pages;
+  int64_t page_stride, slot_stride, head_stride;
+};
+
+// ------------------------------------------------------------------- plan --
+
+// Header at byte 0 of a cross-attention workspace.  error at byte 4 (see fm.h).
+struct PlanHeader {
+  int32_t magic;
+  int32_t error;
+  int32_t n_entries;
+  int32_t split_tokens;
+  int32_t bs;
+  int32_t H;
+  int32_t max_entries;
+  int32_t reserved;
+};
+
+// Target number of (request, split) entries for H heads: enough units
+// (entries x heads) to fill every wave slot several times over.
+__host__ __device__ inline int plan_target_entries(int H) {
+  int h = H > 0 ? H : 1;
+  int u = 8192 / h;
+  return u < 64 ? 64 : u;
+}
+
+struct PlanLayout {
+  size_t first_entry, n_splits, entries, partial_ml, partial_o, total;
+  int max_entries;
+};
+
+inline PlanLayout plan_layout(int bs, int H, int Dh) {
+  PlanLayout p;
+  p.max_entries = bs + plan_target_entries(H);
+  size_t off = 256;
+  p.first_entry = off; off = align256(off + (size_t)bs * 4);
+  p.n_splits = off;    off = align256(off + (size_t)bs * 4);
+  p.entries = off;     off = align256(off + (size_t)p.max_entries * 8);
+  p.partial_ml = off;  off = align256(off + (size_t)p.max_entries * H * kQRows * 2 * 4);
+  p.partial_o = off;   off = align256(off + (size_t)p.max_entries * H * kQRows * Dh * 4);
+  p.total = off;
+  return p;
+}
+
+struct PlanArgs {
+  const int32_t* ctx_lens;
+  const int32_t* cu_q;
+  int32_t bs, H, min_split;
+  uint8_t* ws;
+  PlanLayout lay;
+};
+
+struct CrossArgs {
+  const void* q;
+  void* out;
+  const float* q_norm_w;
+  PoolDesc pool;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  int32_t log2ps;
+  const int32_t* ctx_lens;
+  const int32_t* cu_q;
+  int32_t bs, H;
+  int32_t total_q;          // rows of q / out; rows at or past it are never touched
+  float qscale_log2;        // softmax_scale * log2(e)
+  float eps;
+  uint8_t* ws;
+  PlanLayout lay;
+  RopeFreqs rope;
+};
+
+struct SelfArgs {
+  const void* qkv;
+  void* out;
+  const float* q_norm_w;
+  const float* k_norm_w;
+  const int32_t* ctx_lens;
+  int32_t n_blocks, K, H;
+  float qscale_log2;
+  float eps;
+  RopeFreqs rope;
+};
+
+// ------------------------------------------------------------------ write --
+
+struct WriteHeader {
+  int32_t magic;
+  int32_t error;
+  int32_t live_count;
+  int32_t reserved[5];
+};
+
+struct WriteLayout {
+  size_t live_row, live_pos, live_page, live_off, total;
+};
+
+inline WriteLayout write_layout(int64_t n_rows) {
+  WriteLayout w;
+  size_t off = 256;
+  size_t n = (size_t)(n_rows > 0 ? n_rows : 0);
+  w.live_row = off;  off = align256(off + n * 4);
+  w.live_pos = off;  off = align256(off + n * 4);
+  w.live_page = off; off = align256(off + n * 4);
+  w.live_off = off;  off = align256(off + n * 4);
+  w.total = off;
+  return w;
+}
+
+struct WritePrepArgs {
+  const int32_t* row_req;
+  const int32_t* row_pos;
+  const int32_t* commit_lens;
+  int32_t window;
+  int32_t bs;
+  int64_t n_rows;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  int32_t log2ps;
+  int64_t min_pages;        // smallest num_pages over the layers' pools
+  int32_t* out_slots;
+  uint8_t* ws;
+  WriteLayout lay;
+};
+
+struct WriteGemmArgs {
+  const void* x;
+  const void* w;
+  const float* k_norm_w;
+  int32_t d_in;
+  int32_t L, H;
+  float eps;
+  uint8_t* ws;
+  WriteLayout lay;
+  PoolDesc pools[kMaxLayers];
+  RopeFreqs rope;
+};
+
+// -------------------------------------------------------------- launchers --
+// Each returns hipSuccess or the launch error.  dtype: 0 = fp32, 1 = bf16.
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStream_t s);
+hipError_t launch_self_attention(const SelfArgs& a, int dtype, int Dh, hipStream_t s);
+hipError_t launch_write(const WritePrepArgs& p, const WriteGemmArgs& g, int dtype, int Dh,
+                        int64_t n_rows, hipStream_t s);
+
+}  // namespace fm

@@ -1,0 +1,71 @@
+"""One draft step's attention-path calls, in the order the method makes them.
+
+For every DiT layer the draft step runs self-attention within the block, then
+cross-attention onto the paged context (sglang/model.py ``_denoise``;
+vllm/model.py ``_dit``).  Before the layers, the step writes the newly
+committed context rows and the anchors into every layer's pool with one GEMM
+(``write_target_hidden_kv`` / ``_prologue``) and builds the cross-attention
+plan that every layer shares (``_cross_attention_schedule``).
+
+This module only sequences calls into libfm; all arithmetic runs in its
+kernels.  Buffers are allocated once, before the first step.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as B
+from .workloads import Workload
+
+
+@dataclass
+class StepBuffers:
+    cross_ws: torch.Tensor
+    write_ws: torch.Tensor | None
+    cross_out: list
+    self_out: list
+    out_slots: torch.Tensor | None
+
+
+def allocate(w: Workload) -> StepBuffers:
+    dev = w.ctx_lens.device
+    cross_ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.K), dtype=torch.uint8, device=dev)
+    write_ws = out_slots = None
+    if w.write is not None:
+        n_rows = w.write.x.shape[0]
+        write_ws = torch.empty(B.fm_write_context_kv_workspace_size(n_rows), dtype=torch.uint8, device=dev)
+        out_slots = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    cross_out = [torch.empty_like(q) for q in w.q]
+    self_out = [torch.empty((w.bs, w.K, w.H, w.Dh), dtype=w.dtype, device=dev) for _ in range(w.L)]
+    return StepBuffers(cross_ws, write_ws, cross_out, self_out, out_slots)
+
+
+def write_context(w: Workload, buf: StepBuffers) -> None:
+    wr = w.write
+    B.fm_write_context_kv(wr.x, wr.w_kv, wr.k_norm_w, wr.row_req, wr.row_pos, w.page_table, w.pools, w.eps,
+                          w.theta, commit_lens=wr.commit_lens, window=wr.window, out_slots=buf.out_slots,
+                          ws=buf.write_ws)
+
+
+def plan(w: Workload, buf: StepBuffers, min_split_tokens: int = 0) -> None:
+    B.fm_plan_cross_attention(w.ctx_lens, w.cu_seqlens_q, w.H, w.Dh, buf.cross_ws, max_q=w.K,
+                              min_split_tokens=min_split_tokens)
+
+
+def layer(w: Workload, buf: StepBuffers, l: int) -> None:
+    B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.ctx_lens, w.softmax_scale,
+                              w.theta, w.eps, out=buf.self_out[l])
+    B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens, w.cu_seqlens_q,
+                               w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=buf.cross_out[l])
+
+
+def run_step(w: Workload, buf: StepBuffers, min_split_tokens: int = 0) -> None:
+    """Write (if the workload has one), plan, then every layer."""
+    if w.write is not None:
+        write_context(w, buf)
+    plan(w, buf, min_split_tokens)
+    for l in range(w.L):
+        layer(w, buf, l)

@@ -1,0 +1,207 @@
+/*
+ * fm.h - C ABI of the FlashMap draft-step attention path on MI355X (gfx950).
+ *
+ * The draft step of the FlashMap block drafter (flashmap 0.1.0 wheel:
+ * sglang/model.py ``forward`` / ``_denoise``, vllm/model.py ``forward`` /
+ * ``_dit``, modeling_flashmap.py ``draft``) runs, for every DiT layer:
+ *   1. the context/anchor K/V write: one GEMM over every layer's context K/V
+ *      weight, RMS k-norm, interleaved-pair RoPE and a paged scatter that skips
+ *      uncommitted verify columns            -> fm_write_context_kv
+ *   2. paged cross-attention of each request's draft rows onto its context
+ *      positions 0..p                         -> fm_plan_cross_attention (once
+ *      per step) + fm_paged_cross_attention (once per layer)
+ *   3. bidirectional self-attention within each draft block
+ *                                             -> fm_block_self_attention
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as DEVICE pointers are device memory owned by the caller;
+ *     the library never allocates, frees or keeps them.  Host pointers are read
+ *     during the call only.
+ *   - Every call is asynchronous on ``stream`` and never synchronizes with the
+ *     host: it validates its host-side arguments, enqueues its kernels and
+ *     returns.  Calls with all sizes zero enqueue nothing and return FM_OK.
+ *   - Failures return a negative fm_status and leave a message for
+ *     fm_last_error(); nothing is enqueued then.  FM_E_HIP means a launch
+ *     failed after validation.
+ *   - Element strides are in elements, not bytes.  Every head row (head_dim
+ *     values) is contiguous and 16-byte aligned.
+ *   - Device-side index checks: a page-table entry outside [0, num_pages), a
+ *     position whose page index is past the page-table row, or a request index
+ *     outside [0, bs) never produces an access outside the buffers; the row or
+ *     token it names is skipped and bit 0 of the workspace's error word (the
+ *     int32 at byte offset 4 of ``ws``) is set.  Such inputs are caller errors.
+ *   - Not thread-safe on one workspace: calls that share ``ws`` must be ordered
+ *     on one stream.
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fm_status {
+  FM_OK = 0,
+  FM_E_INVALID = -1,     /* a null required pointer, a negative size, inconsistent sizes */
+  FM_E_UNSUPPORTED = -2, /* a shape or type this build does not implement */
+  FM_E_WORKSPACE = -3,   /* workspace null, misaligned or smaller than required */
+  FM_E_HIP = -4          /* a HIP launch failed */
+} fm_status;
+
+/* Storage type of the activations and of the KV pool.  One type per call. */
+typedef enum fm_dtype { FM_F32 = 0, FM_BF16 = 1 } fm_dtype;
+
+/* One layer's paged KV pool (vllm/model.py ``cache_layout``: page, head and
+ * slot strides with head_dim contiguous; sglang's pool is page_size 1).
+ * Key of slot ``s`` of page ``p`` for head ``h``: k + p*page_stride +
+ * s*slot_stride + h*head_stride, head_dim contiguous elements; the value is at
+ * the same offset from v.  Storage type = the call's fm_dtype.
+ * All strides and the byte addresses of k and v must be multiples of 16 bytes. */
+typedef struct fm_kv_pool {
+  void* k;               /* DEVICE */
+  void* v;               /* DEVICE */
+  int64_t num_pages;     /* pages in this pool; page ids must lie in [0, num_pages) */
+  int64_t page_stride;
+  int64_t slot_stride;
+  int64_t head_stride;
+} fm_kv_pool;
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* fm_last_error(void);
+
+/* Library version string. */
+const char* fm_version(void);
+
+/* ---------------------------------------------------------------- write -- */
+
+/* Workspace bytes fm_write_context_kv needs for n_rows rows. */
+size_t fm_write_context_kv_workspace_size(int64_t n_rows);
+
+/*
+ * Context/anchor K/V write of every layer (sglang/model.py
+ * ``write_target_hidden_kv``, ``_write_context``, ``_kv_write``; vllm/model.py
+ * ``_prologue``, ``_write``; modeling_flashmap.py ``project_kv``).
+ *
+ *   y_r = W_kv x_r                    one GEMM over all layers, fp32 accumulate
+ *   for layer l, head h:
+ *     k = RoPE(RMSNorm(y_r[l,k,h,:]; k_norm_w[l], eps), pos_r)   interleaved pairs
+ *     v = y_r[l,v,h,:]                                           (no norm, no RoPE)
+ *     slot = page_table[req_r][pos_r / page_size]*page_size + pos_r % page_size
+ *     pools[l].k[slot, h, :] = k ;  pools[l].v[slot, h, :] = v  (rounded once)
+ *
+ * x          DEVICE [n_rows, d_in], row-major, dtype dt.
+ * w_kv       DEVICE [L*2*H*Dh, d_in] row-major: rows ordered (layer, {k, v},
+ *            head, dim), i.e. the concatenation [k_proj_0; v_proj_0; k_proj_1; ...].
+ * k_norm_w   DEVICE fp32 [L, Dh]: each layer's key RMSNorm weight.
+ * row_req    DEVICE int32 [n_rows]: request (page-table row) of each row.
+ * row_pos    DEVICE int32 [n_rows]: position of each row; a negative position
+ *            skips the row.
+ * commit_lens, window
+ *            Optional verify-window rule (``commit_lens`` DEVICE int32 [bs], or
+ *            NULL).  When given, rows [0, bs*window) are bs verify windows of
+ *            ``window`` columns, request-major, and column j of request b is
+ *            written only if j < commit_lens[b]; rows from bs*window on (the
+ *            anchors) follow row_pos alone.
+ * page_table DEVICE int32 [bs, pt_stride]: physical page of each logical page.
+ * page_size  a power of two in [1, 4096].
+ * pools      HOST array [L]; L <= 16.
+ * H, Dh      heads and head dim; Dh in {64, 128}.  d_in a multiple of 64.
+ * eps        RMSNorm epsilon;  rope_theta  RoPE base.
+ * out_slots  DEVICE int32 [n_rows] or NULL: slot written by each row, -1 if skipped.
+ * ws         DEVICE workspace of fm_write_context_kv_workspace_size(n_rows)
+ *            bytes, 256-byte aligned; its contents need no initialisation.
+ * Rows that are written must name distinct slots.  Skipped rows cost no GEMM
+ * work and touch no pool byte.
+ */
+int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt,
+                        const void* w_kv, const float* k_norm_w,
+                        const int32_t* row_req, const int32_t* row_pos,
+                        const int32_t* commit_lens, int32_t window,
+                        const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                        int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
+                        float eps, float rope_theta, int32_t* out_slots,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------ cross-attention -- */
+
+/* Workspace bytes for a cross-attention plan of bs requests, H heads, head dim
+ * Dh and at most max_q query rows per request (max_q <= 16). */
+size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q);
+
+/*
+ * Tile schedule of paged cross-attention, computed once per draft step on the
+ * device and reused by every layer's fm_paged_cross_attention (sglang/model.py
+ * ``_cross_attention_schedule``: it depends only on shapes and lengths).
+ *
+ * Splits each request's context 0..ctx_lens[b]-1 into ranges of a common
+ * length (a multiple of 16 tokens, at least min_split_tokens, 0 = default 256)
+ * chosen from the total context so the work spreads over the GPU.
+ * ctx_lens      DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
+ * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
+ *               [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most max_q of them.
+ * ws            DEVICE, fm_cross_attention_workspace_size(bs, H, Dh, max_q)
+ *               bytes, 256-byte aligned.
+ */
+int fm_plan_cross_attention(const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t bs,
+                            int32_t H, int32_t Dh, int32_t max_q, int32_t min_split_tokens,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Paged cross-attention (sglang/model.py ``_paged_cross_attention`` +
+ * ``rms_norm_rope``; vllm/model.py ``paged_cross_attention``; modeling_flashmap.py
+ * ``FlashMapAttention.forward`` with the ``draft`` positions).
+ *
+ * For request b, query row r in [cu_seqlens_q[b], cu_seqlens_q[b+1]) is draft
+ * slot k = r - cu_seqlens_q[b] at position ctx_lens[b] + k:
+ *   q^ = RoPE(RMSNorm(q[r,h,:]; q_norm_w, eps), ctx_lens[b] + k)
+ *   out[r,h,:] = sum_t softmax_t(softmax_scale * q^.K_t) V_t,  t = 0..ctx_lens[b]-1
+ * non-causal, one KV head per query head; keys/values are read through the
+ * page table from ``pool``.  ctx_lens[b] = 0 gives out = 0.
+ *
+ * q, out      DEVICE [total_q, H, Dh] contiguous, dtype dt.
+ * q_norm_w    DEVICE fp32 [Dh].
+ * pool        HOST pointer to this layer's pool descriptor.
+ * page_table  DEVICE int32 [bs, pt_stride].
+ * ctx_lens, cu_seqlens_q, bs, H  as given to fm_plan_cross_attention, whose
+ *             plan ``ws`` must hold (same stream, earlier).
+ * Dh in {64, 128}; page_size a power of two in [1, 4096].
+ */
+int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
+                             const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride,
+                             int32_t page_size, const int32_t* ctx_lens,
+                             const int32_t* cu_seqlens_q, int32_t bs, int32_t H, int32_t Dh,
+                             float softmax_scale, float rope_theta, float eps, void* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------- self-attention -- */
+
+/*
+ * Bidirectional self-attention within each draft block (sglang/model.py
+ * ``_denoise`` -> ``block_self_attention``; modeling_flashmap.py
+ * ``FlashMapLayer`` self-attention over the block's slots).
+ *
+ * Slot i of block b sits at position ctx_lens[b] + i:
+ *   q^_i = RoPE(RMSNorm(q_i; q_norm_w, eps)),  k^_i = RoPE(RMSNorm(k_i; k_norm_w, eps))
+ *   out[b,i,h,:] = sum_j softmax_j(softmax_scale * q^_i.k^_j) v_j,  j = 0..K-1
+ *
+ * qkv   DEVICE [n_blocks, K, 3, H, Dh] contiguous ([q; k; v] per slot), dtype dt.
+ * q_norm_w, k_norm_w  DEVICE fp32 [Dh].
+ * ctx_lens  DEVICE int32 [n_blocks].
+ * out   DEVICE [n_blocks, K, H, Dh] contiguous, dtype dt.
+ * 1 <= K <= 16; Dh in {64, 128}.
+ */
+int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int32_t K,
+                            const float* q_norm_w, const float* k_norm_w, const int32_t* ctx_lens,
+                            int32_t H, int32_t Dh, float softmax_scale, float rope_theta, float eps,
+                            void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_H */

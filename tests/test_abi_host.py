@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/fm.h declares, and rejects bad arguments before any GPU work (so these
+run on machines without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_all_amd import binding as B
+from block_diffusion_drafter_all_amd.build import LIB_PATH, REPO_DIR
+
+HEADER = os.path.join(REPO_DIR, "include", "fm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from block_diffusion_drafter_all_amd.build import build
+        build()
+    return B.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert set(declared) == set(B.SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_empty_error(lib):
+    assert "gfx950" in B.fm_version()
+    assert lib.fm_write_context_kv_workspace_size(10) > 0
+
+
+def test_workspace_sizes(lib):
+    small = lib.fm_cross_attention_workspace_size(1, 4, 64, 16)
+    big = lib.fm_cross_attention_workspace_size(64, 32, 128, 16)
+    assert 0 < small < big
+    assert small % 256 == 0 and big % 256 == 0
+    assert lib.fm_cross_attention_workspace_size(4, 0, 128, 16) == 0
+    assert lib.fm_cross_attention_workspace_size(4, 4, 96, 16) == 0
+    assert lib.fm_write_context_kv_workspace_size(1152) >= 256 + 4 * 4 * 1152
+
+
+FAKE = 1 << 20   # a non-null, 256-aligned host-side stand-in; never dereferenced
+
+
+def _pool(num_pages=4):
+    return B.fm_kv_pool(FAKE, FAKE, num_pages, 16 * 4 * 64, 4 * 64, 64)
+
+
+def _cross(lib, **over):
+    args = dict(q=FAKE, dt=B.FM_BF16, total_q=16, qn=FAKE, pool=_pool(), pt=FAKE, pt_stride=4, ps=16, ctx=FAKE,
+                cu=FAKE, bs=1, H=4, Dh=64, scale=0.125, theta=1e6, eps=1e-6, out=FAKE, ws=FAKE,
+                ws_bytes=1 << 30)
+    args.update(over)
+    pool = args["pool"]
+    return lib.fm_paged_cross_attention(args["q"], args["dt"], args["total_q"], args["qn"],
+                                        ctypes.byref(pool) if pool is not None else None,
+                                        args["pt"], args["pt_stride"], args["ps"], args["ctx"], args["cu"],
+                                        args["bs"], args["H"], args["Dh"], args["scale"], args["theta"],
+                                        args["eps"], args["out"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(q=None), B.FM_E_INVALID, "null"),
+    (dict(pool=None), B.FM_E_INVALID, "null"),
+    (dict(Dh=96), B.FM_E_UNSUPPORTED, "head_dim"),
+    (dict(dt=7), B.FM_E_UNSUPPORTED, "dtype"),
+    (dict(ps=12), B.FM_E_UNSUPPORTED, "page_size"),
+    (dict(H=0), B.FM_E_INVALID, "H"),
+    (dict(ws=None), B.FM_E_WORKSPACE, "workspace"),
+    (dict(ws_bytes=1000), B.FM_E_WORKSPACE, "needed"),
+    (dict(ws=FAKE + 64), B.FM_E_WORKSPACE, "aligned"),
+    (dict(pool=B.fm_kv_pool(FAKE, FAKE, 0, 4096, 256, 64)), B.FM_E_INVALID, "num_pages"),
+    (dict(pool=B.fm_kv_pool(FAKE, FAKE, 4, 4096, 250, 64)), B.FM_E_INVALID, "16 bytes"),
+    (dict(eps=-1.0), B.FM_E_INVALID, "eps"),
+    (dict(theta=0.0), B.FM_E_INVALID, "rope_theta"),
+    (dict(scale=float("inf")), B.FM_E_INVALID, "softmax_scale"),
+    (dict(pt_stride=0), B.FM_E_INVALID, "pt_stride"),
+])
+def test_cross_attention_rejects(lib, over, status, needle):
+    assert _cross(lib, **over) == status
+    assert needle in B.fm_last_error()
+
+
+def test_cross_attention_empty_is_noop(lib):
+    assert _cross(lib, total_q=0, q=None) == B.FM_OK
+    assert _cross(lib, bs=0) == B.FM_OK
+    assert _cross(lib, total_q=-1) == B.FM_E_INVALID
+
+
+def test_plan_rejects(lib):
+    assert lib.fm_plan_cross_attention(FAKE, FAKE, 4, 32, 128, 17, 0, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert "max_q" in B.fm_last_error()
+    assert lib.fm_plan_cross_attention(None, FAKE, 4, 32, 128, 16, 0, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert lib.fm_plan_cross_attention(FAKE, FAKE, 4, 32, 128, 16, -5, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert lib.fm_plan_cross_attention(FAKE, FAKE, 4, 32, 128, 16, 0, FAKE, 10, None) == B.FM_E_WORKSPACE
+
+
+def _write(lib, **over):
+    pools = (B.fm_kv_pool * 2)(_pool(), _pool())
+    a = dict(x=FAKE, n_rows=8, d_in=512, dt=B.FM_BF16, w=FAKE, kn=FAKE, rr=FAKE, rp=FAKE, cl=None, win=0, pt=FAKE,
+             pt_stride=4, ps=16, bs=1, pools=pools, L=2, H=4, Dh=64, eps=1e-6, theta=1e6, slots=None, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(over)
+    return lib.fm_write_context_kv(a["x"], a["n_rows"], a["d_in"], a["dt"], a["w"], a["kn"], a["rr"], a["rp"],
+                                   a["cl"], a["win"], a["pt"], a["pt_stride"], a["ps"], a["bs"], a["pools"], a["L"],
+                                   a["H"], a["Dh"], a["eps"], a["theta"], a["slots"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(x=None), B.FM_E_INVALID, "null"),
+    (dict(d_in=100), B.FM_E_UNSUPPORTED, "d_in"),
+    (dict(L=17), B.FM_E_UNSUPPORTED, "L ="),
+    (dict(cl=FAKE, win=0), B.FM_E_INVALID, "window"),
+    (dict(bs=0), B.FM_E_INVALID, "bs"),
+    (dict(ws_bytes=100), B.FM_E_WORKSPACE, "needed"),
+    (dict(ps=3), B.FM_E_UNSUPPORTED, "page_size"),
+    (dict(n_rows=-1), B.FM_E_INVALID, "n_rows"),
+])
+def test_write_rejects(lib, over, status, needle):
+    assert _write(lib, **over) == status
+    assert needle in B.fm_last_error()
+
+
+def test_write_zero_rows_is_noop(lib):
+    assert _write(lib, n_rows=0, x=None) == B.FM_OK
+
+
+def test_self_attention_rejects(lib):
+    f = lib.fm_block_self_attention
+    assert f(FAKE, B.FM_BF16, 4, 17, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
+    assert f(FAKE, B.FM_BF16, 4, 0, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
+    assert f(None, B.FM_BF16, 4, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_INVALID
+    assert f(None, B.FM_BF16, 0, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_OK

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Floating outputs: max-abs <= 2e-2 and mean-abs <= 2e-3;
+slots and placement: exact."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from harness import (compact_context, compare, log, oracle_cross, rows_of, storage_name, to_np,
+                     ws_error_word)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU machines
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from block_diffusion_drafter_all_amd import binding as B  # noqa: E402
+from block_diffusion_drafter_all_amd import step as S  # noqa: E402
+from block_diffusion_drafter_all_amd.workloads import make_workload  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _oracle_self(w, layer, blocks=None):
+    blocks = range(w.bs) if blocks is None else blocks
+    qkv = to_np(w.qkv[layer][list(blocks)])
+    return O.block_self_attention(qkv, to_np(w.self_q_norm_w[layer]), to_np(w.self_k_norm_w[layer]),
+                                  w.ctx_lens.cpu().numpy()[list(blocks)], w.softmax_scale, w.theta, w.eps)
+
+
+def _check_attention(w, buf, reqs, layers=None, self_blocks=None, pools=None):
+    layers = range(w.L) if layers is None else layers
+    for l in layers:
+        pk, pv, rows = compact_context(w, l, reqs, pools)
+        ref = oracle_cross(w, l, reqs, pk, pv, rows)
+        compare(rows_of(w, reqs, buf.cross_out[l]), np.concatenate([ref[b] for b in reqs]), f"cross L{l}")
+        sb = list(range(w.bs)) if self_blocks is None else list(self_blocks)
+        compare(buf.self_out[l][sb], _oracle_self(w, l, sb), f"self L{l}")
+    assert ws_error_word(buf.cross_ws) == 0
+
+
+def _write_oracle(w):
+    wr = w.write
+    return O.write_context_kv(to_np(wr.x), to_np(wr.w_kv), to_np(wr.k_norm_w), wr.row_req.cpu().numpy(),
+                              wr.row_pos.cpu().numpy(), w.page_table.cpu().numpy(), w.page_size, w.L, w.H, w.Dh,
+                              w.eps, w.theta,
+                              commit_lens=None if wr.commit_lens is None else wr.commit_lens.cpu().numpy(),
+                              window=wr.window)
+
+
+def _snapshot(w):
+    return [(p.k.clone(), p.v.clone()) for p in w.pools]
+
+
+def _check_write(w, buf, before, slots, keys, values):
+    """Slots exact; the set of changed slots exact; written values in tolerance."""
+    np.testing.assert_array_equal(buf.out_slots.cpu().numpy(), slots)
+    assert int(buf.write_ws[4:8].view(torch.int32).item()) == 0
+    live = np.nonzero(slots >= 0)[0]
+    ps = w.page_size
+    expect = set(int(s) for s in slots[live])
+    for l in range(w.L):
+        for t_before, t_after, name in ((before[l][0], w.pools[l].k, "k"), (before[l][1], w.pools[l].v, "v")):
+            itype = torch.int16 if w.dtype == torch.bfloat16 else torch.int32
+            diff = (t_before.view(itype) != t_after.view(itype)).any(dim=3).any(dim=2)   # (pages, ps)
+            changed = torch.nonzero(diff.reshape(-1)).flatten().cpu().numpy()
+            assert set(changed.tolist()) == expect, f"layer {l} {name}: changed slots differ"
+        sl = torch.as_tensor(slots[live], device=w.page_table.device, dtype=torch.long)
+        got_k = w.pools[l].k[sl // ps, sl % ps]
+        got_v = w.pools[l].v[sl // ps, sl % ps]
+        compare(got_k, keys[live, l], f"written K L{l}")
+        compare(got_v, values[live, l], f"written V L{l}")
+
+
+def test_config1_full_step():
+    log("config 1: tiny fp32 full step")
+    w = make_workload(1)
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    slots, keys, values = _write_oracle(w)
+    _check_write(w, buf, before, slots, keys, values)
+    # oracle pool = pre-write pages + the oracle's own write
+    pk = [to_np(before[0][0])]
+    pv = [to_np(before[0][1])]
+    O.scatter_into_pool(pk, pv, slots, keys, values, w.page_size, storage_name(w.dtype))
+    ref = O.paged_cross_attention(to_np(w.q[0]), to_np(w.q_norm_w[0]), pk[0], pv[0], w.page_table.cpu().numpy(),
+                                  w.ctx_lens.cpu().numpy(), w.cu_seqlens_q.cpu().numpy(), w.page_size,
+                                  w.softmax_scale, w.theta, w.eps)
+    mx, _ = compare(buf.cross_out[0], ref, "cross (fp32)")
+    assert mx < 1e-4  # fp32 storage and MFMA: far inside the bf16 bar
+    mx, _ = compare(buf.self_out[0], _oracle_self(w, 0), "self (fp32)")
+    assert mx < 1e-4
+
+
+@pytest.mark.parametrize("variant", ["default", "splits_token_major", "peaky"])
+def test_config2_all_rows(variant):
+    log(f"config 2: {variant}")
+    kw = {}
+    min_split = 0
+    if variant == "splits_token_major":
+        kw = dict(weights="random", layout="token_major")
+        min_split = 64            # forces several splits per request (merge path)
+    elif variant == "peaky":
+        kw = dict(weights="random", q_scale=8.0)
+    w = make_workload(2, **kw)
+    buf = S.allocate(w)
+    S.run_step(w, buf, min_split_tokens=min_split)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)))
+
+
+@pytest.mark.parametrize("ps", [1, 8, 32, 64])
+def test_page_sizes_and_ragged_lengths(ps):
+    log(f"page size {ps}")
+    ctx = [0, 1, 15, 16, 17, 100, 257, 1000]
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=2, H=4, ps=ps))
+    buf = S.allocate(w)
+    S.run_step(w, buf, min_split_tokens=48)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)))
+    for l in range(w.L):   # empty context -> exactly zero
+        assert torch.count_nonzero(buf.cross_out[l][:16]) == 0
+
+
+def test_head_dim_64_bf16_and_ragged_query_rows():
+    log("Dh 64 bf16, ragged cu_seqlens_q")
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=[40, 300, 7, 129], L=1, H=3, Dh=64))
+    dev = w.ctx_lens.device
+    nq = [16, 3, 0, 9]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(torch.bfloat16)
+    w.q[0], w.cu_seqlens_q = q, cu
+    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, cu, w.H, w.Dh, ws, min_split_tokens=32)
+    out = B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu,
+                                     w.softmax_scale, w.theta, w.eps, ws)
+    torch.cuda.synchronize()
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows, q=q)
+    compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross Dh64 ragged q")
+
+
+def test_self_attention_small_blocks_fp32_dh128():
+    log("self-attention K < 16, fp32, Dh 128")
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    for K, dtype in ((1, torch.float32), (5, torch.bfloat16), (16, torch.float32)):
+        qkv = torch.randn((7, K, 3, 2, 128), generator=gen, device=dev).to(dtype)
+        wq = 1 + 0.1 * torch.randn(128, generator=gen, device=dev)
+        wk = 1 + 0.1 * torch.randn(128, generator=gen, device=dev)
+        ctx = torch.randint(0, 5000, (7,), generator=gen, device=dev, dtype=torch.int32)
+        out = B.fm_block_self_attention(qkv, wq, wk, ctx, 128 ** -0.5, 1e6, 1e-6)
+        torch.cuda.synchronize()
+        ref = O.block_self_attention(to_np(qkv), to_np(wq), to_np(wk), ctx.cpu().numpy(), 128 ** -0.5, 1e6, 1e-6)
+        compare(out, ref, f"self K={K} {dtype}")
+
+
+def test_cross_attention_deterministic():
+    w = make_workload(2, weights="random")
+    buf = S.allocate(w)
+    S.run_step(w, buf, min_split_tokens=64)
+    first = buf.cross_out[0].clone()
+    S.run_step(w, buf, min_split_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), buf.cross_out[0].view(torch.int16))
+
+
+def test_write_commit_rule_and_placement_small():
+    log("write: commit rule and placement on a small full step")
+    w = make_workload(5, weights="random", scale_down=dict(bs=6, ctx=(20, 90), L=2, H=4, d_in=256))
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf, min_split_tokens=32)
+    torch.cuda.synchronize()
+    slots, keys, values = _write_oracle(w)
+    _check_write(w, buf, before, slots, keys, values)
+    _check_full_step_attention(w, buf, before, slots, keys, values, list(range(w.bs)))
+
+
+def _check_full_step_attention(w, buf, before, slots, keys, values, reqs):
+    """Cross-attention against the oracle's own pool: the pre-write pages plus
+    the oracle's write."""
+    ps = w.page_size
+    for l in range(w.L):
+        pk, pv, rows = compact_context(w, l, reqs, pools=[type(p)(b[0], b[1]) for p, b in zip(w.pools, before)])
+        # move the oracle's written rows of these requests into the compact pages
+        remap = {}
+        for i, b in enumerate(reqs):
+            for j, page in enumerate(w.page_table[b, :len(rows[i])].cpu().numpy()):
+                remap[int(page)] = int(rows[i][j])
+        sel = [r for r in np.nonzero(slots >= 0)[0] if int(slots[r]) // ps in remap]
+        cslots = np.full_like(slots, -1)
+        for r in sel:
+            cslots[r] = remap[int(slots[r]) // ps] * ps + int(slots[r]) % ps
+        pkl, pvl = [pk], [pv]
+        O.scatter_into_pool(pkl, pvl, cslots, keys[:, l:l + 1], values[:, l:l + 1], ps, storage_name(w.dtype))
+        ref = oracle_cross(w, l, reqs, pk, pv, rows)
+        compare(rows_of(w, reqs, buf.cross_out[l]), np.concatenate([ref[b] for b in reqs]), f"cross L{l}")
+        compare(buf.self_out[l], _oracle_self(w, l), f"self L{l}")
+    assert ws_error_word(buf.cross_ws) == 0
+
+
+# ------------------------------------------------------------ full sizes
+
+
+def _sample(w, n_extra, seed):
+    ctx = w.ctx_lens.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    picks = {int(np.argmax(ctx)), int(np.argmin(ctx))}
+    picks.update(int(b) for b in rng.choice(w.bs, size=min(n_extra, w.bs), replace=False))
+    return sorted(picks)
+
+
+def test_config3_full_size_sampled():
+    log("config 3: 64 requests, ctx U[1024, 8192], 5 layers (sampled requests)")
+    w = make_workload(3)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    reqs = _sample(w, 4, 3)
+    log(f"  sampled requests {reqs}")
+    _check_attention(w, buf, reqs, self_blocks=range(w.bs))
+
+
+def test_config4_full_size_sampled():
+    log("config 4: 256 lognormal requests + one of 131072 tokens (sampled requests)")
+    w = make_workload(4)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    reqs = _sample(w, 3, 4)
+    log(f"  sampled requests {reqs} ctx {[int(w.ctx_lens[b]) for b in reqs]}")
+    _check_attention(w, buf, reqs, self_blocks=range(w.bs))
+
+
+def test_config5_full_step_full_size():
+    log("config 5: full draft step, write of 64 x 17 windows + anchors, 5 layers")
+    w = make_workload(5)
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    log("  oracle write (one fp64 GEMM over the live rows)")
+    slots, keys, values = _write_oracle(w)
+    live = int((slots >= 0).sum())
+    log(f"  live rows {live} of {len(slots)}")
+    _check_write(w, buf, before, slots, keys, values)
+    reqs = _sample(w, 3, 5)
+    log(f"  sampled requests {reqs}")
+    _check_full_step_attention(w, buf, before, slots, keys, values, reqs)
