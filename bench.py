@@ -39,7 +39,6 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="workload: 5 = full draft step (default); 3 = attention of 5 layers; 2, 4, 1")
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"])
-    ap.add_argument("--min-split", type=int, default=0, help="minimum split of the cross-attention plan (tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = pick to take ~15 s)")
@@ -199,7 +198,7 @@ def main():
             S.write_context(w, buf)
             if events is not None:
                 events["write"][1].record()
-        S.plan(w, buf, args.min_split)
+        S.plan(w, buf)
         for l in range(w.L):
             if events is not None:
                 events["self"][l][0].record()

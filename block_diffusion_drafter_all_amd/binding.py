@@ -81,7 +81,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_cross_attention_workspace_size.restype = c_sz
     lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
     lib.fm_plan_cross_attention.restype = ctypes.c_int
-    lib.fm_plan_cross_attention.argtypes = [vp, vp, c_i32, c_i32, c_i32, c_i32, c_i32, vp, c_sz, vp]
+    lib.fm_plan_cross_attention.argtypes = [vp, c_i32, c_i32, c_i32, c_i32, vp, c_sz, vp]
     lib.fm_paged_cross_attention.restype = ctypes.c_int
     lib.fm_paged_cross_attention.argtypes = [
         vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
@@ -200,14 +200,13 @@ def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16)
     return load_library().fm_cross_attention_workspace_size(bs, H, Dh, max_q)
 
 
-def fm_plan_cross_attention(ctx_lens, cu_seqlens_q, H, Dh, ws, max_q=16, min_split_tokens=0):
+def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16):
     """Build the per-step tile schedule into ``ws`` (every layer reuses it)."""
     lib = load_library()
     _need(ctx_lens, "ctx_lens", torch.int32)
-    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     _need(ws, "ws", torch.uint8)
-    _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), _ptr(cu_seqlens_q), ctx_lens.shape[0], H, Dh, max_q,
-                                       min_split_tokens, _ptr(ws), ws.numel(), _stream()))
+    _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), ctx_lens.shape[0], H, Dh, max_q, _ptr(ws), ws.numel(),
+                                       _stream()))
 
 
 def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,

@@ -85,6 +85,27 @@ int check_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need) {
   return FM_OK;
 }
 
+// Resident cross-attention wavefronts: compute units of the current device
+// times the waves one CU keeps resident.  A device that cannot be queried
+// (no GPU) is taken to have 256 CUs, MI355X's count.
+int plan_waves() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256 * fm::kWavesPerCU;
+  }
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    cached[dev] = cus * fm::kWavesPerCU;
+  }
+  return cached[dev];
+}
+
 fm::PoolDesc to_desc(const fm_kv_pool& p) {
   fm::PoolDesc d;
   d.k = reinterpret_cast<uint64_t>(p.k);
@@ -169,14 +190,12 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 }
 
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q) {
-  (void)max_q;
-  if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128)) return 0;
-  return fm::plan_layout(bs, H, Dh).total;
+  if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || max_q < 0 || max_q > fm::kQRows) return 0;
+  return fm::plan_layout(bs, H, Dh, plan_waves()).total;
 }
 
-int fm_plan_cross_attention(const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t bs, int32_t H,
-                            int32_t Dh, int32_t max_q, int32_t min_split_tokens, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
+int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   const char* fn = "fm_plan_cross_attention";
   if (bs < 0) return fail(FM_E_INVALID, "%s: bs %d < 0", fn, bs);
   if (H < 1) return fail(FM_E_INVALID, "%s: H = %d must be >= 1", fn, H);
@@ -184,18 +203,14 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, const int32_t* cu_seqlens_q
   if (max_q < 0) return fail(FM_E_INVALID, "%s: max_q %d < 0", fn, max_q);
   if (max_q > fm::kQRows)
     return fail(FM_E_UNSUPPORTED, "%s: max_q %d above %d query rows per request", fn, max_q, fm::kQRows);
-  if (min_split_tokens < 0) return fail(FM_E_INVALID, "%s: min_split_tokens %d < 0", fn, min_split_tokens);
-  if (bs > 0 && (!ctx_lens || !cu_seqlens_q)) return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
-  if ((int64_t)(bs + fm::plan_target_entries(H)) * H > INT32_MAX)
-    return fail(FM_E_UNSUPPORTED, "%s: bs * H too large", fn);
-  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh);
+  if (bs > 0 && !ctx_lens) return fail(FM_E_INVALID, "%s: ctx_lens is null", fn);
+  if ((int64_t)bs * H > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: bs * H too large", fn);
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves());
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::PlanArgs a{};
   a.ctx_lens = ctx_lens;
-  a.cu_q = cu_seqlens_q;
   a.bs = bs;
   a.H = H;
-  a.min_split = min_split_tokens > 0 ? min_split_tokens : fm::kDefaultMinSplit;
   a.ws = static_cast<uint8_t*>(ws);
   a.lay = lay;
   return from_hip(fm::launch_plan(a, stream), fn);
@@ -220,7 +235,7 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   if (total_q > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: total_q above 2^31-1", fn);
   int64_t q16;
   if (int s = check_pool(fn, *pool, dt, 0, &q16)) return s;
-  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh);
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves());
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::CrossArgs a{};
   a.q = q;

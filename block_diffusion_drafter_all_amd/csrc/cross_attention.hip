@@ -1,0 +1,485 @@
+// Paged cross-attention for gfx950: the per-step plan, the streaming
+// attention kernel and the merge of pairs cut between waves.
+//
+// What is computed (flashmap 0.1.0 wheel: sglang/model.py ``forward``,
+// ``_paged_cross_attention``, ``rms_norm_rope``; vllm/model.py
+// ``paged_cross_attention``): each request's draft rows, RMS-normed and
+// rotated at positions ctx_len + k, attend non-causally to the keys/values at
+// positions 0..ctx_len-1 of the request's paged context.
+//
+// How.  The work is the stream of 16-token K/V tiles of every (request, head)
+// pair.  The plan cuts it into one equal contiguous range per resident
+// wavefront; each wave streams its range with DEPTH tiles in flight and never
+// restarts its load pipeline at a pair boundary: the loader walks on to the
+// next pair and carries that pair's query rows along with its first tile.
+//   - K/V tiles are read straight from the pages into MFMA operand layout
+//     (16-byte loads; page ids come from a per-wave LDS window, so waiting for
+//     one never waits for K/V loads in flight);
+//   - S^T = K Q^T leaves each lane one query row and four keys, which is the
+//     B-operand layout of O^T = V^T P^T, so the online softmax and its rescale
+//     stay in registers; V is moved to column layout by an MFMA against a 0/1
+//     selection matrix;
+//   - a pair that lies inside one wave's range is written final; a pair cut by
+//     range boundaries leaves (m, l, O) partials that the merge kernel adds up
+//     in wave order (deterministic).
+
+#include "fm_internal.h"
+
+namespace fm {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kWin = 512;  // page ids cached per wave
+
+#ifndef FM_CROSS_DEPTH_BF16
+#define FM_CROSS_DEPTH_BF16 2  // 16-token K/V tiles per wave in the load/compute ring (bf16)
+#endif
+#ifndef FM_CROSS_DEPTH_F32
+#define FM_CROSS_DEPTH_F32 2
+#endif
+
+// Slot flags.
+constexpr int kStart = 1;  // first tile of a segment: reset the softmax state, take the query rows
+constexpr int kEnd = 2;    // last tile of a segment: write the output or a partial
+constexpr int kWhole = 4;  // the segment is the whole (request, head) pair: final output
+constexpr int kPart1 = 8;  // partial goes to the wave's second partial slot
+
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t x, int d) {
+  const int lo = __shfl_up((int)(uint32_t)(uint64_t)x, d);
+  const int hi = __shfl_up((int)(uint32_t)((uint64_t)x >> 32), d);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Exclusive prefix sum of int64 over a 1024-thread block (all threads call it).
+__device__ int64_t block_exclusive_scan_i64(int64_t x, int64_t* total) {
+  __shared__ int64_t wave_tot[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int64_t inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = shfl_up_i64(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wave_tot[wv] = inc;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int64_t t = wave_tot[w];
+    if (w < wv) before += t;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - x;
+}
+
+__device__ __forceinline__ int tiles_of(int ctx) { return (max(ctx, 0) + 15) >> 4; }
+
+// ------------------------------------------------------------------- plan --
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
+  uint8_t* ws = a.ws;
+  PlanHeader* hdr = (PlanHeader*)ws;
+  int64_t* pair_off = (int64_t*)(ws + a.lay.pair_off);
+  int4* wave_start = (int4*)(ws + a.lay.wave_start);
+  const int tid = threadIdx.x;
+  int64_t carry = 0;
+  for (int base = 0; base < a.bs; base += 1024) {
+    const int b = base + tid;
+    const int64_t v = b < a.bs ? (int64_t)tiles_of(a.ctx_lens[b]) * a.H : 0;
+    int64_t tot;
+    const int64_t ex = block_exclusive_scan_i64(v, &tot);
+    if (b < a.bs) pair_off[b] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) pair_off[a.bs] = carry;
+  __syncthreads();
+  const int64_t G = carry;
+  const int NW = a.lay.n_waves;
+  for (int w = tid; w < NW; w += 1024) {
+    const int64_t g0 = (int64_t)w * G / NW;
+    const int64_t g1 = (int64_t)(w + 1) * G / NW;
+    int4 r = make_int4(0, 0, 0, 0);
+    if (g1 > g0) {
+      // the request whose pairs hold tile g0: the largest b with pair_off[b] <= g0
+      int lo = 0, hi = a.bs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pair_off[mid] <= g0) lo = mid;
+        else hi = mid - 1;
+      }
+      const int T = tiles_of(a.ctx_lens[lo]);
+      const int64_t rel = g0 - pair_off[lo];
+      r = make_int4(lo, (int)(rel / T), (int)(rel % T), (int)(g1 - g0));
+    }
+    wave_start[w] = r;
+  }
+  if (tid == 0) {
+    hdr->magic = kPlanMagic;
+    hdr->error = 0;
+    hdr->n_waves = NW;
+    hdr->bs = a.bs;
+    hdr->H = a.H;
+    hdr->total_tiles = G;
+  }
+}
+
+// ----------------------------------------------------------- query rows --
+
+// q^ = RoPE(RMSNorm(q; q_norm_w, eps)) at position ctx_len + k for query row k
+// of request b, stored as [b][k][h][:] in the call's storage type (rows past
+// the request's count are zero), ready to be loaded as an MFMA operand.  One
+// wavefront per (request, head).
+template <class T, int D>
+__global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
+  typedef typename T::storage st;
+  constexpr int EPC = T::EPC;
+  constexpr int NCH = D / (4 * EPC);
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  const int unit = blockIdx.x * 4 + wave_in_block();
+  const int b = unit / a.H;
+  const int h = unit - b * a.H;
+  if (b >= a.bs) return;
+  const int ctx0 = max(0, a.ctx_lens[b]);
+  const int r0 = max(0, a.cu_q[b]);
+  const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows));
+  float qf[D / 4];
+  const bool has = c < nq;
+  const st* qrow = (const st*)a.q + ((int64_t)(has ? r0 + c : 0) * a.H + h) * D;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const u32x4_t v = load16(qrow + ch * 4 * EPC + g * EPC);
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) qf[ch * EPC + j] = has ? chunk_elem<T>(v, j) : 0.f;
+  }
+  norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);
+  st* dst = (st*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows + c) * a.H + h) * D;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(dst + ch * 4 * EPC + g * EPC) = pack_chunk<T>(&qf[ch * EPC]);
+}
+
+// -------------------------------------------------------- cross-attention --
+
+template <class T, int D>
+struct StreamSlot {
+  u32x4_t k[D / (4 * T::EPC)];
+  u32x4_t v[D / (4 * T::EPC)];
+  u32x4_t q[D / (4 * T::EPC)];  // raw query rows, meaningful on a kStart tile
+  uint32_t mask;                // bit t: token t of the tile is a valid key
+  int b, h, r0, nq, flags;
+};
+
+template <class T, int D, int DEPTH>
+__global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
+  typedef typename T::storage st;
+  constexpr int EPC = T::EPC;
+  constexpr int NCH = D / (4 * EPC);
+  constexpr int NDT = D / 16;
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  const int wv = wave_in_block();
+  uint8_t* ws = a.ws;
+  PlanHeader* hdr = (PlanHeader*)ws;
+  if (hdr->magic != kPlanMagic || hdr->bs != a.bs || hdr->H != a.H || hdr->n_waves != a.lay.n_waves) return;
+  const int w = blockIdx.x * 4 + wv;
+  if (w >= a.lay.n_waves) return;
+  const int4 st0 = ((const int4*)(ws + a.lay.wave_start))[w];
+  const int n_tiles = st0.w;
+  if (n_tiles <= 0) return;
+
+  // Per-wave LDS window of page ids.
+  __shared__ int32_t win_all[4][kWin];
+  int32_t* win = win_all[wv];
+
+  Selector<T> sel;
+  sel.init(lane);
+  const int ps_mask = (1 << a.log2ps) - 1;
+  const st* kpool = (const st*)a.pool.k;
+  const st* vpool = (const st*)a.pool.v;
+
+  // ---- loader state (wave-uniform) ----
+  int lb = st0.x, lh = st0.y, lk = st0.z;
+  int lctx = 0, lT = 0, lr0 = 0, lnq = 0;
+  bool exhausted = false;  // set only if the lengths changed after the plan was made
+  auto pair_info = [&](int b) {
+    lctx = max(0, sload_i32(a.ctx_lens + b));
+    lT = tiles_of(lctx);
+    lr0 = max(0, sload_i32(a.cu_q + b));
+    lnq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - lr0, kQRows));
+  };
+  pair_info(lb);
+  bool seg_first = true, seg_from0 = (lk == 0);
+  int wreq = -1, wbase = 0;
+  auto fill_window = [&](int b, int base) {
+    wreq = b;
+    wbase = base;
+    const int32_t* row = a.page_table + (int64_t)b * a.pt_stride;
+#pragma unroll
+    for (int k = 0; k < kWin / 64; ++k) {
+      const int64_t idx = (int64_t)base + lane + 64 * k;
+      win[lane + 64 * k] = idx < a.pt_stride ? load_i32(row + idx) : -1;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  int64_t kv_last = 0;  // per-lane element offset of the last real tile (a safe re-read)
+  bool bad_page = false;
+
+  auto load_slot = [&](StreamSlot<T, D>& s, int j) {
+    int64_t off = kv_last;
+    bool ok = false, bad = false;
+    s.flags = 0;
+    if (j < n_tiles && lk >= lT && !exhausted) {  // the next (request, head) pair with tiles
+      ++lh;
+      lk = 0;
+      seg_first = false;
+      seg_from0 = true;
+      if (lh == a.H) {
+        lh = 0;
+        do {
+          if (lb + 1 >= a.bs) {
+            exhausted = true;
+            break;
+          }
+          ++lb;
+          pair_info(lb);
+        } while (lT == 0);
+      }
+      exhausted = exhausted || lT == 0;
+    }
+    if (j < n_tiles && !exhausted) {
+      const bool last_of_pair = lk == lT - 1;
+      int flags = (lk == 0 || j == 0) ? kStart : 0;
+      if (last_of_pair || j == n_tiles - 1)
+        flags |= kEnd | ((seg_from0 && last_of_pair) ? kWhole : 0) | (seg_first ? 0 : kPart1);
+      const int tb = lk << 4;
+      const int first_page = tb >> a.log2ps;
+      const int last_page = min(tb + 15, lctx - 1) >> a.log2ps;
+      if (wreq != lb || first_page < wbase || last_page - wbase >= kWin)
+        // the whole request's page row when it fits (every head's pair reuses it)
+        fill_window(lb, ((lctx - 1) >> a.log2ps) < kWin ? 0 : first_page);
+      const int tok = tb + c;
+      const int tok_c = min(tok, lctx - 1);
+      const int page = win[((tok_c >> a.log2ps) - wbase) & (kWin - 1)];
+      const bool page_ok = page >= 0 && (int64_t)page < a.pool.num_pages;
+      ok = tok < lctx && page_ok;
+      bad = tok < lctx && !page_ok;
+      off = (int64_t)lh * a.pool.head_stride +
+            (page_ok ? (int64_t)page * a.pool.page_stride + (int64_t)(tok_c & ps_mask) * a.pool.slot_stride : 0);
+      kv_last = off;
+      if (flags & kStart) {  // this pair's prepared query rows ride along with its first tile
+        const st* qrow = (const st*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) s.q[ch] = load16(qrow + ch * 4 * EPC + g * EPC);
+      }
+      s.b = lb;
+      s.h = lh;
+      s.r0 = lr0;
+      s.nq = lnq;
+      s.flags = flags;
+      ++lk;
+    }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      s.k[ch] = load16(kpool + off + ch * 4 * EPC + g * EPC);
+      s.v[ch] = load16(vpool + off + ch * 4 * EPC + g * EPC);
+    }
+    s.mask = (uint32_t)(__ballot(ok) & 0xffffull);
+    bad_page |= __ballot(bad) != 0;
+  };
+
+  // ---- compute state ----
+  u32x4_t qop[NCH];
+  f32x4_t o[NDT];
+  float m_run = kNegInf;  // running max of this lane's query row (log2 domain)
+  float l_lane = 0.f;     // this lane's share of the running denominator
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) qop[ch] = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  auto compute_slot = [&](const StreamSlot<T, D>& s) {
+    if (s.flags & kStart) {
+      m_run = kNegInf;
+      l_lane = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) qop[ch] = s.q[ch];
+    }
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) mma_chunk<T>(sc, s.k[ch], qop[ch]);
+    float sv[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = (s.mask >> (4 * g + i)) & 1u;
+      sv[i] = valid ? sc[i] * a.qscale_log2 : kNegInf;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = wave_max_groups(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    f32x4_t p;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = operand_value<T>(exp2f(sv[i] - m_use));
+      psum += p[i];
+    }
+    if (__ballot(m_new != m_run) != 0) {  // some row's running max moved
+      const float alpha = exp2f(m_run - m_use);
+      l_lane *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    l_lane += psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) mma_pv<T>(o[dt], sel.template transpose_tile<NCH>(s.v, dt), p);
+    if (s.flags & kEnd) {
+      const float l_row = wave_sum_groups(l_lane);
+      if (s.flags & kWhole) {
+        const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
+        if (c < s.nq) {
+          st* orow = (st*)a.out + ((int64_t)(s.r0 + c) * a.H + s.h) * D;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, o[dt], inv);
+        }
+      } else {
+        const int64_t prow = ((int64_t)w * 2 + ((s.flags & kPart1) ? 1 : 0)) * kQRows + c;
+        float* po = (float*)(ws + a.lay.partial_o) + prow * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) *(f32x4_t*)(po + 16 * dt + 4 * g) = o[dt];
+        if (g == 0) {
+          float* pml = (float*)(ws + a.lay.partial_ml) + prow * 2;
+          pml[0] = m_run;
+          pml[1] = l_row;
+        }
+      }
+    }
+  };
+
+  // Every slot index is loaded unconditionally (indices past the range
+  // re-read the last tile, a cache hit, and are fully masked with no flags),
+  // so the loop body is straight-line and DEPTH-1 tiles stay in flight.
+  StreamSlot<T, D> buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) load_slot(buf[d], d);
+  for (int it = 0; it < n_tiles; it += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load_slot(buf[(d + DEPTH - 1) % DEPTH], it + d + DEPTH - 1);
+      compute_slot(buf[d]);
+    }
+  }
+  if (bad_page && lane == 0) atomicOr(&hdr->error, 1);
+}
+
+// Merge of a pair cut between waves: O = sum_w 2^(m_w - M) O_w / sum_w
+// 2^(m_w - M) l_w in wave order; also writes the zero output of requests with
+// an empty context.  One wavefront per (request, head).
+template <class T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(CrossArgs a) {
+  typedef typename T::storage st;
+  constexpr int NPL = D / 4;  // columns per lane
+  const int lane = lane_id(), g = lane >> 4, row = lane & 15;
+  const uint8_t* ws = a.ws;
+  const PlanHeader* hdr = (const PlanHeader*)ws;
+  if (hdr->magic != kPlanMagic || hdr->bs != a.bs || hdr->H != a.H || hdr->n_waves != a.lay.n_waves) return;
+  const int unit = blockIdx.x * 4 + wave_in_block();
+  const int b = unit / a.H;
+  const int h = unit - b * a.H;
+  if (b >= a.bs) return;
+  const int nt = tiles_of(a.ctx_lens[b]);
+  const int r0 = max(0, a.cu_q[b]);
+  const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows));
+  st* orow = (st*)a.out + ((int64_t)(r0 + row) * a.H + h) * D + g * NPL;
+  if (nt == 0) {
+    if (row < nq) {
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < NPL; k += 4) store4<T>(orow + k, z, 1.0f);
+    }
+    return;
+  }
+  const int64_t G = hdr->total_tiles;
+  const int64_t NW = a.lay.n_waves;
+  const int64_t P = ((const int64_t*)(ws + a.lay.pair_off))[b] + (int64_t)h * nt;
+  auto wave_of = [&](int64_t x) -> int64_t { return ((x + 1) * NW + G - 1) / G - 1; };
+  auto start_of = [&](int64_t wv) -> int64_t { return wv * G / NW; };
+  const int64_t w0 = wave_of(P), w1 = wave_of(P + nt - 1);
+  if (w0 == w1) return;  // written whole by the attention kernel
+  const float* pml = (const float*)(ws + a.lay.partial_ml);
+  const float* po = (const float*)(ws + a.lay.partial_o);
+  auto prow_of = [&](int64_t wv) -> int64_t {
+    const int slot = (wv == w0 && start_of(w0) < P) ? 1 : 0;
+    return (wv * 2 + slot) * kQRows + row;
+  };
+  float M = kNegInf;
+  for (int64_t wv = w0; wv <= w1; ++wv)
+    if (start_of(wv + 1) > start_of(wv)) M = fmaxf(M, pml[prow_of(wv) * 2]);
+  float acc[NPL];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) acc[k] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+    for (int64_t wv = w0; wv <= w1; ++wv) {
+      if (start_of(wv + 1) == start_of(wv)) continue;
+      const int64_t pr = prow_of(wv);
+      const float wgt = exp2f(pml[pr * 2] - M);
+      L += wgt * pml[pr * 2 + 1];
+      const float* src = po + pr * D + g * NPL;
+#pragma unroll
+      for (int k = 0; k < NPL; k += 4) {
+        const f32x4_t v = *(const f32x4_t*)(src + k);
+        acc[k] += wgt * v[0];
+        acc[k + 1] += wgt * v[1];
+        acc[k + 2] += wgt * v[2];
+        acc[k + 3] += wgt * v[3];
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  if (row < nq) {
+#pragma unroll
+    for (int k = 0; k < NPL; k += 4) {
+      const f32x4_t v = {acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
+      store4<T>(orow + k, v, inv);
+    }
+  }
+}
+
+template <class T, int D, int DEPTH>
+hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
+  const int64_t pairs = (int64_t)a.bs * a.H;
+  hipLaunchKernelGGL((q_prologue_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
+  hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH>), dim3(grid), dim3(256), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStream_t s) {
+  if (dtype == 1)
+    return Dh == 128 ? launch_cross_typed<Bf16, 128, FM_CROSS_DEPTH_BF16>(a, s)
+                     : launch_cross_typed<Bf16, 64, FM_CROSS_DEPTH_BF16>(a, s);
+  // fp32 rows of 128 take twice the registers: one tile in the ring.
+  return Dh == 128 ? launch_cross_typed<F32, 128, 1>(a, s) : launch_cross_typed<F32, 64, FM_CROSS_DEPTH_F32>(a, s);
+}
+
+}  // namespace fm

@@ -82,7 +82,24 @@ __device__ __forceinline__ u32x4_t pack_chunk<F32>(const float* x) {
   return r;
 }
 
-__device__ __forceinline__ u32x4_t load16(const void* p) { return *(const u32x4_t*)p; }
+// 16-byte load from global memory (device allocations only): an explicit
+// global-address-space access, so the compiler emits global_load_dwordx4
+// (counted by vmcnt alone) rather than a flat load.
+typedef const __attribute__((address_space(1))) u32x4_t* gptr_u32x4;
+__device__ __forceinline__ u32x4_t load16(const void* p) { return *(gptr_u32x4)(p); }
+
+typedef const __attribute__((address_space(1))) int32_t* gptr_i32;
+__device__ __forceinline__ int32_t load_i32(const int32_t* p) { return *(gptr_i32)(p); }
+
+// Wave-uniform load through the scalar unit (constant address space): for
+// small read-only tables such as lengths, so that waiting for the value never
+// waits for vector loads in flight.  Reads only; the data must not change
+// while the kernel runs.
+typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
+__device__ __forceinline__ int32_t sload_i32(const int32_t* p) { return *(cptr_i32)(p); }
+
+typedef const __attribute__((address_space(1))) float* gptr_f32;
+__device__ __forceinline__ float load_f32(const float* p) { return *(gptr_f32)(p); }
 
 // acc += A_chunk x B_chunk^T over one 16-byte chunk of each row fragment.
 template <class T>

@@ -15,7 +15,7 @@ constexpr int kMaxLayers = 16;
 constexpr int kQRows = 16;          // query rows per request handled by one unit
 constexpr int32_t kPlanMagic = 0x464d504c;   // "FMPL"
 constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
-constexpr int kDefaultMinSplit = 256;        // tokens
+constexpr int kWavesPerCU = 8;               // resident cross-attention waves per CU
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -29,48 +29,52 @@ struct PoolDesc {
 
 // ------------------------------------------------------------------- plan --
 
+// Cross-attention schedule.  The work of one call is the stream of 16-token
+// K/V tiles of every (request, head) pair, pairs in (request, head) order and
+// tiles in position order.  The plan cuts that stream into n_waves equal
+// contiguous ranges, one per resident wavefront of the attention kernel, so
+// every wave streams the same number of tiles across pair boundaries with no
+// per-unit restart.  A pair cut by a range boundary leaves (m, l, O) partials
+// (at most two per wave: its first and its last segment) that the merge
+// kernel combines in wave order.
+
 // Header at byte 0 of a cross-attention workspace.  error at byte 4 (see fm.h).
 struct PlanHeader {
   int32_t magic;
   int32_t error;
-  int32_t n_entries;
-  int32_t split_tokens;
+  int32_t n_waves;
   int32_t bs;
   int32_t H;
-  int32_t max_entries;
   int32_t reserved;
+  int64_t total_tiles;
 };
-
-// Target number of (request, split) entries for H heads: enough units
-// (entries x heads) to fill every wave slot several times over.
-__host__ __device__ inline int plan_target_entries(int H) {
-  int h = H > 0 ? H : 1;
-  int u = 8192 / h;
-  return u < 64 ? 64 : u;
-}
 
 struct PlanLayout {
-  size_t first_entry, n_splits, entries, partial_ml, partial_o, total;
-  int max_entries;
+  size_t q_hat;       // [bs][16][H][Dh] of the call's type: normed, rotated queries (0 past a request's rows)
+  size_t pair_off;    // int64 [bs + 1]: first tile of request b's pairs in the stream
+  size_t wave_start;  // int4 [n_waves]: (request, head, tile in pair, tile count)
+  size_t partial_ml;  // float [n_waves][2][16][2]: running max (log2) and denominator
+  size_t partial_o;   // float [n_waves][2][16][Dh]: unnormalized outputs
+  size_t total;
+  int n_waves;
 };
 
-inline PlanLayout plan_layout(int bs, int H, int Dh) {
+inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves) {
   PlanLayout p;
-  p.max_entries = bs + plan_target_entries(H);
+  p.n_waves = n_waves;
   size_t off = 256;
-  p.first_entry = off; off = align256(off + (size_t)bs * 4);
-  p.n_splits = off;    off = align256(off + (size_t)bs * 4);
-  p.entries = off;     off = align256(off + (size_t)p.max_entries * 8);
-  p.partial_ml = off;  off = align256(off + (size_t)p.max_entries * H * kQRows * 2 * 4);
-  p.partial_o = off;   off = align256(off + (size_t)p.max_entries * H * kQRows * Dh * 4);
+  p.q_hat = off;      off = align256(off + (size_t)bs * kQRows * H * Dh * 4);
+  p.pair_off = off;   off = align256(off + (size_t)(bs + 1) * 8);
+  p.wave_start = off; off = align256(off + (size_t)n_waves * 16);
+  p.partial_ml = off; off = align256(off + (size_t)n_waves * 2 * kQRows * 2 * 4);
+  p.partial_o = off;  off = align256(off + (size_t)n_waves * 2 * kQRows * Dh * 4);
   p.total = off;
   return p;
 }
 
 struct PlanArgs {
   const int32_t* ctx_lens;
-  const int32_t* cu_q;
-  int32_t bs, H, min_split;
+  int32_t bs, H;
   uint8_t* ws;
   PlanLayout lay;
 };

@@ -1,0 +1,118 @@
+// Bidirectional self-attention within each draft block for gfx950 (flashmap
+// 0.1.0 wheel: sglang/model.py ``_denoise`` -> ``block_self_attention``;
+// vllm/model.py ``_dit``; modeling_flashmap.py ``FlashMapLayer``).
+//
+// One wavefront per (block, head) holds the whole block of up to 16 slots:
+// q and k are RMS-normed and rotated at the slots' positions in registers,
+// S^T = K Q^T leaves each lane one query row with four keys, the softmax over
+// the block's keys reduces across the four lane groups, and O^T = V^T P^T
+// takes P straight from the score layout (V moved to column layout by a
+// selection-matrix MFMA).
+
+#include "fm_internal.h"
+
+namespace fm {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// --------------------------------------------------------- self-attention --
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void self_attn_kernel(SelfArgs a) {
+  typedef typename T::storage st;
+  constexpr int EPC = T::EPC;
+  constexpr int NCH = D / (4 * EPC);
+  constexpr int NDT = D / 16;
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  const int unit = blockIdx.x * 4 + wave_in_block();
+  const int b = unit / a.H;
+  const int h = unit - b * a.H;
+  if (b >= a.n_blocks) return;
+  const int K = a.K;
+  const int ctx = max(0, a.ctx_lens[b]);
+  const bool has = c < K;
+  const int64_t slot_stride = (int64_t)3 * a.H * D;
+  const st* base = (const st*)a.qkv + ((int64_t)b * K + (has ? c : 0)) * slot_stride + (int64_t)h * D;
+
+  float qf[D / 4], kf[D / 4];
+  u32x4_t vr[NCH];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int col = ch * 4 * EPC + g * EPC;
+    u32x4_t vq = load16(base + col);
+    u32x4_t vk = load16(base + (int64_t)a.H * D + col);
+    vr[ch] = load16(base + (int64_t)2 * a.H * D + col);
+    if (!has) {
+      vq = (u32x4_t){0u, 0u, 0u, 0u};
+      vk = vq;
+      vr[ch] = vq;
+    }
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) {
+      qf[ch * EPC + j] = chunk_elem<T>(vq, j);
+      kf[ch * EPC + j] = chunk_elem<T>(vk, j);
+    }
+  }
+  norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx + c, a.rope, g);
+  norm_rope_row<T, D>(kf, a.k_norm_w, a.eps, ctx + c, a.rope, g);
+  u32x4_t qop[NCH], kop[NCH];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    qop[ch] = pack_chunk<T>(&qf[ch * EPC]);
+    kop[ch] = pack_chunk<T>(&kf[ch * EPC]);
+  }
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) mma_chunk<T>(s, kop[ch], qop[ch]);
+  // lane (g, c): query row c against keys 4g .. 4g+3
+  float sv[4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (4 * g + i < K) ? s[i] * a.qscale_log2 : kNegInf;
+    mx = fmaxf(mx, sv[i]);
+  }
+  mx = wave_max_groups(mx);
+  f32x4_t p;
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = operand_value<T>(exp2f(sv[i] - mx));
+    l += p[i];
+  }
+  l = wave_sum_groups(l);
+  Selector<T> sel;
+  sel.init(lane);
+  const float inv = 1.0f / l;
+  // MFMAs run with every lane active; only the stores are predicated.
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    o[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    mma_pv<T>(o[dt], sel.template transpose_tile<NCH>(vr, dt), p);
+  }
+  if (has) {
+    st* orow = (st*)a.out + (((int64_t)b * K + c) * a.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, o[dt], inv);
+  }
+}
+
+template <class T, int D>
+hipError_t launch_self_typed(const SelfArgs& a, hipStream_t s) {
+  const int64_t units = (int64_t)a.n_blocks * a.H;
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL((self_attn_kernel<T, D>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_self_attention(const SelfArgs& a, int dtype, int Dh, hipStream_t s) {
+  if (dtype == 1) return Dh == 128 ? launch_self_typed<Bf16, 128>(a, s) : launch_self_typed<Bf16, 64>(a, s);
+  return Dh == 128 ? launch_self_typed<F32, 128>(a, s) : launch_self_typed<F32, 64>(a, s);
+}
+
+}  // namespace fm

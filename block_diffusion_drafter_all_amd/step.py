@@ -50,9 +50,8 @@ def write_context(w: Workload, buf: StepBuffers) -> None:
                           ws=buf.write_ws)
 
 
-def plan(w: Workload, buf: StepBuffers, min_split_tokens: int = 0) -> None:
-    B.fm_plan_cross_attention(w.ctx_lens, w.cu_seqlens_q, w.H, w.Dh, buf.cross_ws, max_q=w.K,
-                              min_split_tokens=min_split_tokens)
+def plan(w: Workload, buf: StepBuffers) -> None:
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.K)
 
 
 def layer(w: Workload, buf: StepBuffers, l: int) -> None:
@@ -62,10 +61,10 @@ def layer(w: Workload, buf: StepBuffers, l: int) -> None:
                                w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=buf.cross_out[l])
 
 
-def run_step(w: Workload, buf: StepBuffers, min_split_tokens: int = 0) -> None:
+def run_step(w: Workload, buf: StepBuffers) -> None:
     """Write (if the workload has one), plan, then every layer."""
     if w.write is not None:
         write_context(w, buf)
-    plan(w, buf, min_split_tokens)
+    plan(w, buf)
     for l in range(w.L):
         layer(w, buf, l)

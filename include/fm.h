@@ -129,8 +129,10 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 
 /* ------------------------------------------------------ cross-attention -- */
 
-/* Workspace bytes for a cross-attention plan of bs requests, H heads, head dim
- * Dh and at most max_q query rows per request (max_q <= 16). */
+/* Workspace bytes for a cross-attention plan of bs requests with head dim Dh
+ * and at most max_q query rows per request (max_q <= 16) on the current
+ * device; 0 for an unsupported shape.  One workspace serves every layer's
+ * call of a step. */
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q);
 
 /*
@@ -138,17 +140,16 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
  * device and reused by every layer's fm_paged_cross_attention (sglang/model.py
  * ``_cross_attention_schedule``: it depends only on shapes and lengths).
  *
- * Splits each request's context 0..ctx_lens[b]-1 into ranges of a common
- * length (a multiple of 16 tokens, at least min_split_tokens, 0 = default 256)
- * chosen from the total context so the work spreads over the GPU.
- * ctx_lens      DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
- * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
- *               [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most max_q of them.
- * ws            DEVICE, fm_cross_attention_workspace_size(bs, H, Dh, max_q)
- *               bytes, 256-byte aligned.
+ * The work of a call is the stream of 16-key tiles of every (request, head)
+ * pair; the plan cuts it into equal contiguous ranges, one per resident
+ * wavefront of the attention kernel, so every wave moves the same number of
+ * K/V bytes whatever the mix of context lengths.
+ * ctx_lens  DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
+ * max_q     host bound on query rows per request (<= 16), checked here.
+ * ws        DEVICE, fm_cross_attention_workspace_size(bs, H, Dh, max_q) bytes,
+ *           256-byte aligned.
  */
-int fm_plan_cross_attention(const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t bs,
-                            int32_t H, int32_t Dh, int32_t max_q, int32_t min_split_tokens,
+int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -167,8 +168,10 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, const int32_t* cu_seqlens_q
  * q_norm_w    DEVICE fp32 [Dh].
  * pool        HOST pointer to this layer's pool descriptor.
  * page_table  DEVICE int32 [bs, pt_stride].
- * ctx_lens, cu_seqlens_q, bs, H  as given to fm_plan_cross_attention, whose
- *             plan ``ws`` must hold (same stream, earlier).
+ * ctx_lens, bs, H  as given to fm_plan_cross_attention, whose plan ``ws``
+ *             must hold (same stream, earlier; lengths unchanged since).
+ * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
+ *             [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most 16 of them.
  * Dh in {64, 128}; page_size a power of two in [1, 4096].
  */
 int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,

@@ -47,6 +47,7 @@ def test_workspace_sizes(lib):
     assert small % 256 == 0 and big % 256 == 0
     assert lib.fm_cross_attention_workspace_size(4, 0, 128, 16) == 0
     assert lib.fm_cross_attention_workspace_size(4, 4, 96, 16) == 0
+    assert lib.fm_cross_attention_workspace_size(4, 4, 128, 17) == 0
     assert lib.fm_write_context_kv_workspace_size(1152) >= 256 + 4 * 4 * 1152
 
 
@@ -99,11 +100,12 @@ def test_cross_attention_empty_is_noop(lib):
 
 
 def test_plan_rejects(lib):
-    assert lib.fm_plan_cross_attention(FAKE, FAKE, 4, 32, 128, 17, 0, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 17, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
     assert "max_q" in B.fm_last_error()
-    assert lib.fm_plan_cross_attention(None, FAKE, 4, 32, 128, 16, 0, FAKE, 1 << 30, None) == B.FM_E_INVALID
-    assert lib.fm_plan_cross_attention(FAKE, FAKE, 4, 32, 128, 16, -5, FAKE, 1 << 30, None) == B.FM_E_INVALID
-    assert lib.fm_plan_cross_attention(FAKE, FAKE, 4, 32, 128, 16, 0, FAKE, 10, None) == B.FM_E_WORKSPACE
+    assert lib.fm_plan_cross_attention(None, 4, 32, 128, 16, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert lib.fm_plan_cross_attention(FAKE, -1, 32, 128, 16, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 16, FAKE, 10, None) == B.FM_E_WORKSPACE
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 96, 16, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
 
 
 def _write(lib, **over):
