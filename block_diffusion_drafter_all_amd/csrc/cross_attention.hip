@@ -227,42 +227,65 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   int64_t kv_last = 0;  // per-lane element offset of the last real tile (a safe re-read)
   bool bad_page = false;
 
+  // Move to the next (request, head) pair with tiles once the current one is done.
+  auto advance_if_done = [&]() {
+    if (lk < lT || exhausted) return;
+    ++lh;
+    lk = 0;
+    seg_first = false;
+    seg_from0 = true;
+    if (lh == a.H) {
+      lh = 0;
+      do {
+        if (lb + 1 >= a.bs) {
+          exhausted = true;
+          break;
+        }
+        ++lb;
+        pair_info(lb);
+      } while (lT == 0);
+    }
+    exhausted = exhausted || lT == 0;
+  };
+  auto window_covers = [&](int tb) -> bool {
+    const int first_page = tb >> a.log2ps;
+    const int last_page = min(tb + 15, lctx - 1) >> a.log2ps;
+    return wreq == lb && first_page >= wbase && last_page - wbase < kWin;
+  };
+  // Page id of the next tile, read from the window one tile ahead so the read
+  // has completed by the time that tile's loads are issued.
+  int pg_next = 0;
+  bool pg_have = false;
+  auto prefetch_page = [&]() {
+    pg_have = false;
+    if (exhausted || lk >= lT) return;
+    const int tb = lk << 4;
+    if (!window_covers(tb)) return;
+    pg_next = win[((min(tb + c, lctx - 1) >> a.log2ps) - wbase) & (kWin - 1)];
+    pg_have = true;
+  };
+
   auto load_slot = [&](StreamSlot<T, D>& s, int j) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
     s.flags = 0;
-    if (j < n_tiles && lk >= lT && !exhausted) {  // the next (request, head) pair with tiles
-      ++lh;
-      lk = 0;
-      seg_first = false;
-      seg_from0 = true;
-      if (lh == a.H) {
-        lh = 0;
-        do {
-          if (lb + 1 >= a.bs) {
-            exhausted = true;
-            break;
-          }
-          ++lb;
-          pair_info(lb);
-        } while (lT == 0);
-      }
-      exhausted = exhausted || lT == 0;
-    }
     if (j < n_tiles && !exhausted) {
       const bool last_of_pair = lk == lT - 1;
       int flags = (lk == 0 || j == 0) ? kStart : 0;
       if (last_of_pair || j == n_tiles - 1)
         flags |= kEnd | ((seg_from0 && last_of_pair) ? kWhole : 0) | (seg_first ? 0 : kPart1);
       const int tb = lk << 4;
-      const int first_page = tb >> a.log2ps;
-      const int last_page = min(tb + 15, lctx - 1) >> a.log2ps;
-      if (wreq != lb || first_page < wbase || last_page - wbase >= kWin)
-        // the whole request's page row when it fits (every head's pair reuses it)
-        fill_window(lb, ((lctx - 1) >> a.log2ps) < kWin ? 0 : first_page);
       const int tok = tb + c;
       const int tok_c = min(tok, lctx - 1);
-      const int page = win[((tok_c >> a.log2ps) - wbase) & (kWin - 1)];
+      int page;
+      if (pg_have) {
+        page = pg_next;
+      } else {
+        if (!window_covers(tb))
+          // the whole request's page row when it fits (every head's pair reuses it)
+          fill_window(lb, ((lctx - 1) >> a.log2ps) < kWin ? 0 : (tb >> a.log2ps));
+        page = win[((tok_c >> a.log2ps) - wbase) & (kWin - 1)];
+      }
       const bool page_ok = page >= 0 && (int64_t)page < a.pool.num_pages;
       ok = tok < lctx && page_ok;
       bad = tok < lctx && !page_ok;
@@ -280,11 +303,15 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
       s.nq = lnq;
       s.flags = flags;
       ++lk;
+      if (j + 1 < n_tiles) {
+        advance_if_done();
+        prefetch_page();
+      }
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      s.k[ch] = load16(kpool + off + ch * 4 * EPC + g * EPC);
-      s.v[ch] = load16(vpool + off + ch * 4 * EPC + g * EPC);
+      s.k[ch] = load16_stream(kpool + off + ch * 4 * EPC + g * EPC);
+      s.v[ch] = load16_stream(vpool + off + ch * 4 * EPC + g * EPC);
     }
     s.mask = (uint32_t)(__ballot(ok) & 0xffffull);
     bad_page |= __ballot(bad) != 0;

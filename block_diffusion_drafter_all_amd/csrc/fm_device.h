@@ -88,6 +88,15 @@ __device__ __forceinline__ u32x4_t pack_chunk<F32>(const float* x) {
 typedef const __attribute__((address_space(1))) u32x4_t* gptr_u32x4;
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *(gptr_u32x4)(p); }
 
+// Streaming 16-byte load (K/V tiles are read once): nontemporal hint.
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+#ifdef FM_KV_NT
+  return __builtin_nontemporal_load((gptr_u32x4)(p));
+#else
+  return *(gptr_u32x4)(p);
+#endif
+}
+
 typedef const __attribute__((address_space(1))) int32_t* gptr_i32;
 __device__ __forceinline__ int32_t load_i32(const int32_t* p) { return *(gptr_i32)(p); }
 
