@@ -41,8 +41,13 @@ def parse():
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
-                    help="requests in the oracle's timed sample (0 = pick to take ~15 s)")
+                    help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
     return ap.parse_args()
+
+
+def kv_bytes_per_row(L: int, H: int, Dh: int, elem_bytes: int) -> int:
+    """Bytes one context row's keys and values take in every layer's pool."""
+    return L * 2 * H * Dh * elem_bytes
 
 
 def cross_bytes(w) -> int:
@@ -83,7 +88,7 @@ def write_flops_bytes(w):
     s = wr.x.element_size()
     n = w.L * 2 * w.H * w.Dh
     flops = 2 * m * d_in * n
-    nbytes = s * (n * d_in + m * d_in + m * n) + 4 * w.L * w.Dh + 12 * n_rows
+    nbytes = s * (n * d_in + m * d_in) + m * kv_bytes_per_row(w.L, w.H, w.Dh, s) + 4 * w.L * w.Dh + 12 * n_rows
     return flops, nbytes
 
 
@@ -272,7 +277,7 @@ def main():
                         "mfma_frac_of_bf16_peak": wf / (avg_w * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                         "algorithmic_bytes": wb}
     if not args.no_cpu_baseline:
-        n_req = args.cpu_sample_requests or max(1, min(w.bs, 4))
+        n_req = args.cpu_sample_requests or max(1, min(w.bs, 24))
         out["cpu_baseline"] = cpu_baseline(w, n_req)
     print(json.dumps(out), flush=True)
 
