@@ -170,7 +170,10 @@ struct StreamSlot {
   int b, h, r0, nq, flags;
 };
 
-template <class T, int D, int DEPTH>
+// UNIFORM_PAGE: page_size >= 16, so the 16 keys of a tile share one page and
+// the tile's base address is wave-uniform (scalar), with a per-lane offset that
+// never changes.
+template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
 __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   typedef typename T::storage st;
   constexpr int EPC = T::EPC;
@@ -225,6 +228,9 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   };
 
   int64_t kv_last = 0;  // per-lane element offset of the last real tile (a safe re-read)
+  int64_t tile_base = 0;  // UNIFORM_PAGE: wave-uniform element offset of the tile (kept for re-reads)
+  // UNIFORM_PAGE: this lane's constant offset inside a tile (slot c, column group g)
+  const uint32_t lane_off_b = (uint32_t)(((int64_t)c * a.pool.slot_stride + g * EPC) * (int64_t)sizeof(st));
   bool bad_page = false;
 
   // Move to the next (request, head) pair with tiles once the current one is done.
@@ -286,12 +292,22 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
           fill_window(lb, ((lctx - 1) >> a.log2ps) < kWin ? 0 : (tb >> a.log2ps));
         page = win[((tok_c >> a.log2ps) - wbase) & (kWin - 1)];
       }
-      const bool page_ok = page >= 0 && (int64_t)page < a.pool.num_pages;
-      ok = tok < lctx && page_ok;
-      bad = tok < lctx && !page_ok;
-      off = (int64_t)lh * a.pool.head_stride +
-            (page_ok ? (int64_t)page * a.pool.page_stride + (int64_t)(tok_c & ps_mask) * a.pool.slot_stride : 0);
-      kv_last = off;
+      if (UNIFORM_PAGE) {
+        // one page per tile: scalar tile base; the lanes' slots c are in the page
+        const int pu = __builtin_amdgcn_readfirstlane(page);
+        const bool page_ok = pu >= 0 && (int64_t)pu < a.pool.num_pages;
+        ok = tok < lctx && page_ok;
+        bad = tok < lctx && !page_ok;
+        tile_base = (int64_t)lh * a.pool.head_stride +
+                    (page_ok ? (int64_t)pu * a.pool.page_stride + (int64_t)(tb & ps_mask) * a.pool.slot_stride : 0);
+      } else {
+        const bool page_ok = page >= 0 && (int64_t)page < a.pool.num_pages;
+        ok = tok < lctx && page_ok;
+        bad = tok < lctx && !page_ok;
+        off = (int64_t)lh * a.pool.head_stride +
+              (page_ok ? (int64_t)page * a.pool.page_stride + (int64_t)(tok_c & ps_mask) * a.pool.slot_stride : 0);
+        kv_last = off;
+      }
       if (flags & kStart) {  // this pair's prepared query rows ride along with its first tile
         const st* qrow = (const st*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
 #pragma unroll
@@ -308,10 +324,21 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
         prefetch_page();
       }
     }
+    if (UNIFORM_PAGE) {
+      // scalar tile base + 32-bit per-lane byte offset (the SGPR-base addressing form)
+      const char* kt = (const char*)(kpool + tile_base);
+      const char* vt = (const char*)(vpool + tile_base);
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      s.k[ch] = load16_stream(kpool + off + ch * 4 * EPC + g * EPC);
-      s.v[ch] = load16_stream(vpool + off + ch * 4 * EPC + g * EPC);
+      for (int ch = 0; ch < NCH; ++ch) {
+        s.k[ch] = load16_stream(kt + (lane_off_b + ch * 64u));
+        s.v[ch] = load16_stream(vt + (lane_off_b + ch * 64u));
+      }
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        s.k[ch] = load16_stream(kpool + off + ch * 4 * EPC + g * EPC);
+        s.v[ch] = load16_stream(vpool + off + ch * 4 * EPC + g * EPC);
+      }
     }
     s.mask = (uint32_t)(__ballot(ok) & 0xffffull);
     bad_page |= __ballot(bad) != 0;
@@ -480,18 +507,25 @@ __global__ __launch_bounds__(256) void merge_kernel(CrossArgs a) {
   }
 }
 
-template <class T, int D, int DEPTH>
-hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
+template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
+hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.bs * a.H;
   hipLaunchKernelGGL((q_prologue_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
-  hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH, UNIFORM_PAGE>), dim3(grid), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <class T, int D, int DEPTH>
+hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
+  // page_size >= 16 keeps each 16-key tile inside one page
+  if (a.log2ps >= 4) return launch_cross_paged<T, D, DEPTH, true>(a, s);
+  return launch_cross_paged<T, D, DEPTH, false>(a, s);
 }
 
 }  // namespace
