@@ -76,13 +76,30 @@ __device__ int64_t block_exclusive_scan_i64(int64_t x, int64_t* total) {
 
 __device__ __forceinline__ int tiles_of(int ctx) { return (max(ctx, 0) + 15) >> 4; }
 
+// Partials cross waves on different XCDs, whose L2s are not coherent with one
+// another.  They are written and read with the device-scope cache bit (sc1),
+// which writes through and reads past the non-coherent cache levels, so no
+// cache-wide write-back or invalidate is needed; the counter increment is
+// ordered after a wave's partial stores by waiting for all of them to be
+// acknowledged.  Buffer instructions also drop anything outside the partials.
+constexpr int kDeviceScope = 16;         // sc1 in the buffer instructions' cache-policy operand
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer on gfx9-family targets
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partials_rsrc(const CrossArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.ws + a.lay.partial_ml, 0, (int)(a.lay.total - a.lay.partial_ml),
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ void wait_stores_acknowledged() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ------------------------------------------------------------------- plan --
 
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   uint8_t* ws = a.ws;
   PlanHeader* hdr = (PlanHeader*)ws;
   int64_t* pair_off = (int64_t*)(ws + a.lay.pair_off);
-  int4* wave_start = (int4*)(ws + a.lay.wave_start);
+  WaveRec* rec = (WaveRec*)(ws + a.lay.wave_rec);
+  int32_t* cnt = (int32_t*)(ws + a.lay.merge_cnt);
   const int tid = threadIdx.x;
   int64_t carry = 0;
   for (int base = 0; base < a.bs; base += 1024) {
@@ -100,7 +117,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   for (int w = tid; w < NW; w += 1024) {
     const int64_t g0 = (int64_t)w * G / NW;
     const int64_t g1 = (int64_t)(w + 1) * G / NW;
-    int4 r = make_int4(0, 0, 0, 0);
+    WaveRec r{};
     if (g1 > g0) {
       // the request whose pairs hold tile g0: the largest b with pair_off[b] <= g0
       int lo = 0, hi = a.bs - 1;
@@ -109,11 +126,17 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
         if (pair_off[mid] <= g0) lo = mid;
         else hi = mid - 1;
       }
-      const int T = tiles_of(a.ctx_lens[lo]);
+      const int ctx = max(0, a.ctx_lens[lo]);
+      const int T = tiles_of(ctx);
       const int64_t rel = g0 - pair_off[lo];
-      r = make_int4(lo, (int)(rel / T), (int)(rel % T), (int)(g1 - g0));
+      r.b = lo;
+      r.h = (int)(rel / T);
+      r.k = (int)(rel % T);
+      r.count = (int)(g1 - g0);
+      r.ctx = ctx;
     }
-    wave_start[w] = r;
+    rec[w] = r;
+    cnt[w] = 0;
   }
   if (tid == 0) {
     hdr->magic = kPlanMagic;
@@ -129,7 +152,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 
 // q^ = RoPE(RMSNorm(q; q_norm_w, eps)) at position ctx_len + k for query row k
 // of request b, stored as [b][k][h][:] in the call's storage type (rows past
-// the request's count are zero), ready to be loaded as an MFMA operand.  One
+// the request's count are zero), ready to be loaded as an MFMA operand.  A
+// request with an empty context gets its zero output rows here instead.  One
 // wavefront per (request, head).
 template <class T, int D>
 __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
@@ -144,6 +168,14 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   const int ctx0 = max(0, a.ctx_lens[b]);
   const int r0 = max(0, a.cu_q[b]);
   const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows));
+  if (ctx0 == 0) {  // empty context: the output rows are zero
+    if (c < nq) {
+      st* orow = (st*)a.out + ((int64_t)(r0 + c) * a.H + h) * D;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(orow + ch * 4 * EPC + g * EPC) = (u32x4_t){0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   float qf[D / 4];
   const bool has = c < nq;
   const st* qrow = (const st*)a.q + ((int64_t)(has ? r0 + c : 0) * a.H + h) * D;
@@ -170,6 +202,80 @@ struct StreamSlot {
   int b, h, r0, nq, flags;
 };
 
+// Counts one partial of the cut pair (b, h) in; if it was the pair's last
+// outstanding partial, combines the pair's partials in wave order,
+//   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,   M = max_w m_w,
+// (accumulated online, two parts per round of loads), writes the output rows
+// and re-arms the pair's counter for the next call.  Lanes hold the same
+// fragment of the rows as in the attention loop.
+template <class T, int D>
+__device__ __forceinline__ void merge_if_last(const CrossArgs& a, int b, int h, int64_t G) {
+  typedef typename T::storage st;
+  constexpr int NDT = D / 16;
+  const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+  uint8_t* ws = a.ws;
+  const int64_t NW = a.lay.n_waves;
+  const int nt = tiles_of(sload_i32(a.ctx_lens + b));
+  const int64_t P = ((const int64_t*)(ws + a.lay.pair_off))[b] + (int64_t)h * nt;
+  auto wave_of = [&](int64_t x) -> int64_t { return ((x + 1) * NW + G - 1) / G - 1; };
+  auto start_of = [&](int64_t wv) -> int64_t { return wv * G / NW; };
+  const int64_t w0 = wave_of(P), w1 = wave_of(P + nt - 1);
+  // waves holding a part: all of w0..w1 when every wave has tiles, else one tile each
+  const int parts = G >= NW ? (int)(w1 - w0 + 1) : nt;
+  int32_t* cnt = (int32_t*)(ws + a.lay.merge_cnt) + w0;
+  wait_stores_acknowledged();  // this wave's partial before its count
+  int before = 0;
+  if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __shfl(before, 0);
+  if (before != parts - 1) return;
+  // Every other part was acknowledged before it was counted: read them all.
+  const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
+  const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
+  auto part_of = [&](int64_t wv) -> uint32_t {  // the wave's partial slot holding this pair
+    return (uint32_t)(wv * 2 + ((wv == w0 && start_of(w0) < P) ? 1 : 0));
+  };
+  float m_acc = kNegInf, l_acc = 0.f;
+  f32x4_t acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  auto combine = [&](bool ok, u32x2_t ml, const u32x4_t* ow) {
+    const float m_w = __uint_as_float(ml[0]), l_w = __uint_as_float(ml[1]);
+    const float m_new = fmaxf(m_acc, m_w);
+    const bool live = ok && m_new != kNegInf;
+    const float sa = (live && m_acc != kNegInf) ? exp2f(m_acc - m_new) : (live ? 0.f : 1.f);
+    const float sw = (live && m_w != kNegInf) ? exp2f(m_w - m_new) : 0.f;
+    l_acc = l_acc * sa + l_w * sw;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * sa + __builtin_bit_cast(f32x4_t, ow[dt]) * sw;
+    m_acc = live ? m_new : m_acc;
+  };
+  for (int64_t wv = w0; wv <= w1; wv += 2) {
+    const int64_t wb = min(wv + 1, w1);
+    const bool ok_a = start_of(wv + 1) > start_of(wv);
+    const bool ok_b = wv + 1 <= w1 && start_of(wb + 1) > start_of(wb);
+    const uint32_t pa = part_of(wv), pb = part_of(wb);
+    u32x4_t oa[NDT], ob[NDT];
+    const u32x2_t mla = __builtin_amdgcn_raw_buffer_load_b64(prs, (pa * 64 + lane) * 8, 0, kDeviceScope);
+    const u32x2_t mlb = __builtin_amdgcn_raw_buffer_load_b64(prs, (pb * 64 + lane) * 8, 0, kDeviceScope);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      oa[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pa * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+      ob[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pb * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+    }
+    combine(ok_a, mla, oa);
+    combine(ok_b, mlb, ob);
+  }
+  const int r0 = max(0, sload_i32(a.cu_q + b));
+  const int nq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - r0, kQRows));
+  const float inv = l_acc > 0.f ? 1.0f / l_acc : 0.f;
+  if (c < nq) {
+    st* orow = (st*)a.out + ((int64_t)(r0 + c) * a.H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, acc[dt], inv);
+  }
+  if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // UNIFORM_PAGE: page_size >= 16, so the 16 keys of a tile share one page and
 // the tile's base address is wave-uniform (scalar), with a per-lane offset that
 // never changes.
@@ -183,11 +289,16 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   const int wv = wave_in_block();
   uint8_t* ws = a.ws;
   PlanHeader* hdr = (PlanHeader*)ws;
-  if (hdr->magic != kPlanMagic || hdr->bs != a.bs || hdr->H != a.H || hdr->n_waves != a.lay.n_waves) return;
   const int w = blockIdx.x * 4 + wv;
   if (w >= a.lay.n_waves) return;
-  const int4 st0 = ((const int4*)(ws + a.lay.wave_start))[w];
-  const int n_tiles = st0.w;
+  // The plan header and this wave's record, read together.
+  // (No branch on the header before the record is read: the two loads issue
+  // together and a mismatched plan simply leaves the wave no tiles.)
+  const PlanHeader ph = *(const PlanHeader*)hdr;
+  const WaveRec rec = ((const WaveRec*)(ws + a.lay.wave_rec))[w];
+  const bool plan_ok =
+      (ph.magic == kPlanMagic) & (ph.bs == a.bs) & (ph.H == a.H) & (ph.n_waves == a.lay.n_waves);
+  const int n_tiles = plan_ok ? rec.count : 0;
   if (n_tiles <= 0) return;
 
   // Per-wave LDS window of page ids.
@@ -201,27 +312,26 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   const st* vpool = (const st*)a.pool.v;
 
   // ---- loader state (wave-uniform) ----
-  int lb = st0.x, lh = st0.y, lk = st0.z;
-  int lctx = 0, lT = 0, lr0 = 0, lnq = 0;
-  bool exhausted = false;  // set only if the lengths changed after the plan was made
-  auto pair_info = [&](int b) {
-    lctx = max(0, sload_i32(a.ctx_lens + b));
-    lT = tiles_of(lctx);
+  int lb = rec.b, lh = rec.h, lk = rec.k;
+  int lctx = rec.ctx, lT = tiles_of(rec.ctx), lr0 = 0, lnq = 0;
+  auto query_rows = [&](int b) {
     lr0 = max(0, sload_i32(a.cu_q + b));
     lnq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - lr0, kQRows));
   };
-  pair_info(lb);
+  query_rows(lb);
+  bool exhausted = false;  // set only if the lengths changed after the plan was made
   bool seg_first = true, seg_from0 = (lk == 0);
   int wreq = -1, wbase = 0;
   auto fill_window = [&](int b, int base) {
     wreq = b;
     wbase = base;
     const int32_t* row = a.page_table + (int64_t)b * a.pt_stride;
+    // every load issued before the first wait (clamped indices, masked after)
+    int32_t v[kWin / 64];
 #pragma unroll
-    for (int k = 0; k < kWin / 64; ++k) {
-      const int64_t idx = (int64_t)base + lane + 64 * k;
-      win[lane + 64 * k] = idx < a.pt_stride ? load_i32(row + idx) : -1;
-    }
+    for (int k = 0; k < kWin / 64; ++k) v[k] = load_i32(row + min((int64_t)base + lane + 64 * k, a.pt_stride - 1));
+#pragma unroll
+    for (int k = 0; k < kWin / 64; ++k) win[lane + 64 * k] = (int64_t)base + lane + 64 * k < a.pt_stride ? v[k] : -1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -248,8 +358,10 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
           break;
         }
         ++lb;
-        pair_info(lb);
+        lctx = max(0, sload_i32(a.ctx_lens + lb));
+        lT = tiles_of(lctx);
       } while (lT == 0);
+      if (!exhausted) query_rows(lb);
     }
     exhausted = exhausted || lT == 0;
   };
@@ -349,6 +461,7 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   f32x4_t o[NDT];
   float m_run = kNegInf;  // running max of this lane's query row (log2 domain)
   float l_lane = 0.f;     // this lane's share of the running denominator
+  int cut_b[2] = {-1, -1}, cut_h[2] = {0, 0};  // pairs this wave left partials of
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) qop[ch] = (u32x4_t){0u, 0u, 0u, 0u};
 #pragma unroll
@@ -404,15 +517,18 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
           for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, o[dt], inv);
         }
       } else {
-        const int64_t prow = ((int64_t)w * 2 + ((s.flags & kPart1) ? 1 : 0)) * kQRows + c;
-        float* po = (float*)(ws + a.lay.partial_o) + prow * D;
+        const int slot = (s.flags & kPart1) ? 1 : 0;
+        const uint32_t part = (uint32_t)(w * 2 + slot);
+        const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
+        const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
+        const u32x2_t ml = {__float_as_uint(m_run), __float_as_uint(l_row)};
+        __builtin_amdgcn_raw_buffer_store_b64(ml, prs, (part * 64 + lane) * 8, 0, kDeviceScope);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) *(f32x4_t*)(po + 16 * dt + 4 * g) = o[dt];
-        if (g == 0) {
-          float* pml = (float*)(ws + a.lay.partial_ml) + prow * 2;
-          pml[0] = m_run;
-          pml[1] = l_row;
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[dt]), prs,
+                                                 o_base + ((part * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+        cut_b[slot] = s.b;
+        cut_h[slot] = s.h;
       }
     }
   };
@@ -430,81 +546,12 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
       compute_slot(buf[d]);
     }
   }
-  if (bad_page && lane == 0) atomicOr(&hdr->error, 1);
-}
-
-// Merge of a pair cut between waves: O = sum_w 2^(m_w - M) O_w / sum_w
-// 2^(m_w - M) l_w in wave order; also writes the zero output of requests with
-// an empty context.  One wavefront per (request, head).
-template <class T, int D>
-__global__ __launch_bounds__(256) void merge_kernel(CrossArgs a) {
-  typedef typename T::storage st;
-  constexpr int NPL = D / 4;  // columns per lane
-  const int lane = lane_id(), g = lane >> 4, row = lane & 15;
-  const uint8_t* ws = a.ws;
-  const PlanHeader* hdr = (const PlanHeader*)ws;
-  if (hdr->magic != kPlanMagic || hdr->bs != a.bs || hdr->H != a.H || hdr->n_waves != a.lay.n_waves) return;
-  const int unit = blockIdx.x * 4 + wave_in_block();
-  const int b = unit / a.H;
-  const int h = unit - b * a.H;
-  if (b >= a.bs) return;
-  const int nt = tiles_of(a.ctx_lens[b]);
-  const int r0 = max(0, a.cu_q[b]);
-  const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows));
-  st* orow = (st*)a.out + ((int64_t)(r0 + row) * a.H + h) * D + g * NPL;
-  if (nt == 0) {
-    if (row < nq) {
-      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  const int err = (bad_page ? 1 : 0) | (exhausted ? 2 : 0);
+  if (err && lane == 0) atomicOr(&hdr->error, err);
+  // The pairs this wave cut: the last of each pair's waves to get here merges it.
 #pragma unroll
-      for (int k = 0; k < NPL; k += 4) store4<T>(orow + k, z, 1.0f);
-    }
-    return;
-  }
-  const int64_t G = hdr->total_tiles;
-  const int64_t NW = a.lay.n_waves;
-  const int64_t P = ((const int64_t*)(ws + a.lay.pair_off))[b] + (int64_t)h * nt;
-  auto wave_of = [&](int64_t x) -> int64_t { return ((x + 1) * NW + G - 1) / G - 1; };
-  auto start_of = [&](int64_t wv) -> int64_t { return wv * G / NW; };
-  const int64_t w0 = wave_of(P), w1 = wave_of(P + nt - 1);
-  if (w0 == w1) return;  // written whole by the attention kernel
-  const float* pml = (const float*)(ws + a.lay.partial_ml);
-  const float* po = (const float*)(ws + a.lay.partial_o);
-  auto prow_of = [&](int64_t wv) -> int64_t {
-    const int slot = (wv == w0 && start_of(w0) < P) ? 1 : 0;
-    return (wv * 2 + slot) * kQRows + row;
-  };
-  float M = kNegInf;
-  for (int64_t wv = w0; wv <= w1; ++wv)
-    if (start_of(wv + 1) > start_of(wv)) M = fmaxf(M, pml[prow_of(wv) * 2]);
-  float acc[NPL];
-#pragma unroll
-  for (int k = 0; k < NPL; ++k) acc[k] = 0.f;
-  float L = 0.f;
-  if (M != kNegInf) {
-    for (int64_t wv = w0; wv <= w1; ++wv) {
-      if (start_of(wv + 1) == start_of(wv)) continue;
-      const int64_t pr = prow_of(wv);
-      const float wgt = exp2f(pml[pr * 2] - M);
-      L += wgt * pml[pr * 2 + 1];
-      const float* src = po + pr * D + g * NPL;
-#pragma unroll
-      for (int k = 0; k < NPL; k += 4) {
-        const f32x4_t v = *(const f32x4_t*)(src + k);
-        acc[k] += wgt * v[0];
-        acc[k + 1] += wgt * v[1];
-        acc[k + 2] += wgt * v[2];
-        acc[k + 3] += wgt * v[3];
-      }
-    }
-  }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  if (row < nq) {
-#pragma unroll
-    for (int k = 0; k < NPL; k += 4) {
-      const f32x4_t v = {acc[k], acc[k + 1], acc[k + 2], acc[k + 3]};
-      store4<T>(orow + k, v, inv);
-    }
-  }
+  for (int k = 0; k < 2; ++k)
+    if (cut_b[k] >= 0) merge_if_last<T, D>(a, cut_b[k], cut_h[k], ph.total_tiles);
 }
 
 template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
@@ -515,9 +562,6 @@ hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
   hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH, UNIFORM_PAGE>), dim3(grid), dim3(256), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -35,8 +35,8 @@ struct PoolDesc {
 // contiguous ranges, one per resident wavefront of the attention kernel, so
 // every wave streams the same number of tiles across pair boundaries with no
 // per-unit restart.  A pair cut by a range boundary leaves (m, l, O) partials
-// (at most two per wave: its first and its last segment) that the merge
-// kernel combines in wave order.
+// (at most two per wave: its first and its last segment); the last of the
+// pair's waves to finish combines them in wave order.
 
 // Header at byte 0 of a cross-attention workspace.  error at byte 4 (see fm.h).
 struct PlanHeader {
@@ -49,12 +49,20 @@ struct PlanHeader {
   int64_t total_tiles;
 };
 
+// One wave's range: it starts at tile ``k`` of pair (b, h) and covers
+// ``count`` tiles; ``ctx`` is request b's context length.
+struct WaveRec {
+  int32_t b, h, k, count;
+  int32_t ctx, pad[3];
+};
+
 struct PlanLayout {
   size_t q_hat;       // [bs][16][H][Dh] of the call's type: normed, rotated queries (0 past a request's rows)
   size_t pair_off;    // int64 [bs + 1]: first tile of request b's pairs in the stream
-  size_t wave_start;  // int4 [n_waves]: (request, head, tile in pair, tile count)
-  size_t partial_ml;  // float [n_waves][2][16][2]: running max (log2) and denominator
-  size_t partial_o;   // float [n_waves][2][16][Dh]: unnormalized outputs
+  size_t wave_rec;    // WaveRec [n_waves]
+  size_t merge_cnt;   // int32 [n_waves]: partials counted in for the cut pair whose first wave is w
+  size_t partial_ml;  // float2 [n_waves][2][64 lanes]: running max (log2) and denominator of the lane's row
+  size_t partial_o;   // f32x4 [n_waves][2][Dh/16][64 lanes]: unnormalized outputs in MFMA fragment order
   size_t total;
   int n_waves;
 };
@@ -65,8 +73,9 @@ inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves) {
   size_t off = 256;
   p.q_hat = off;      off = align256(off + (size_t)bs * kQRows * H * Dh * 4);
   p.pair_off = off;   off = align256(off + (size_t)(bs + 1) * 8);
-  p.wave_start = off; off = align256(off + (size_t)n_waves * 16);
-  p.partial_ml = off; off = align256(off + (size_t)n_waves * 2 * kQRows * 2 * 4);
+  p.wave_rec = off;   off = align256(off + (size_t)n_waves * sizeof(WaveRec));
+  p.merge_cnt = off;  off = align256(off + (size_t)n_waves * 4);
+  p.partial_ml = off; off = align256(off + (size_t)n_waves * 2 * 64 * 8);
   p.partial_o = off;  off = align256(off + (size_t)n_waves * 2 * kQRows * Dh * 4);
   p.total = off;
   return p;
