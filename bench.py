@@ -11,11 +11,23 @@ U{1..17} verify columns plus its anchor through the write.
 Prints ONE JSON line (see the fields below).  Inputs are resident in HBM
 before timing starts; timing brackets exactly --steps steps with device
 synchronization on both sides.
+
+Two helper modes feed the ``roofline.traffic`` field (HBM bytes per
+cross-attention launch from rocprofv3's FETCH_SIZE / WRITE_SIZE counters):
+  --copy-calibration      one plain 1 GiB device-to-device copy, the known-size
+                          kernel the counters are scaled by;
+  --write-traffic DIRS    (CPU only) turns four counter-collection outputs
+                          into profiles/cross_attention_traffic.json, keyed by
+                          a hash of the kernel sources: the bench reports the
+                          traffic only while the sources still match.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -29,6 +41,12 @@ if ROOT not in sys.path:
 METRIC = "draft query rows/s over paged context + achieved KV-read HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cross_attention_traffic.json")
+# Sources whose code the cross-attention launch runs; a change in any of them
+# invalidates counters taken before it.
+KERNEL_SOURCES = ("cross_attention.hip", "fm_device.h", "fm_internal.h", "abi.cpp")
+CROSS_KERNELS = ("cross_attn_kernel", "q_prologue_kernel")
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -42,7 +60,91 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("CROSS_FETCH", "CROSS_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output directories: write the traffic record and exit (no GPU)")
+    ap.add_argument("--traffic-command", default="", help="the commands that produced --write-traffic's inputs")
     return ap.parse_args()
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_diffusion_drafter_all_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _kib_per_dispatch(rows, match):
+    """Mean counter value (KiB) per dispatch of kernels whose name contains ``match``, and the count."""
+    per = {}
+    for r in rows:
+        if match in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return (sum(per.values()) / len(per), len(per)) if per else (0.0, 0)
+
+
+def write_traffic(dirs, command: str) -> None:
+    cross_fetch, cross_write, copy_fetch, copy_write = (_counter_rows(d) for d in dirs)
+    # the calibration copy: the largest copy dispatch of the run
+    def largest(rows):
+        best = {}
+        for r in rows:
+            if "copy" in r["Kernel_Name"].lower():
+                best[r["Dispatch_Id"]] = best.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return max(best.values())
+    fetch_scale = COPY_BYTES / (largest(copy_fetch) * 1024.0)
+    write_scale = COPY_BYTES / (largest(copy_write) * 1024.0)
+    rec = {"sources_sha256": kernel_sources_hash(), "kernels": {}, "fetch_scale": fetch_scale,
+           "write_scale": write_scale, "calibration": f"plain {COPY_BYTES} B device copy (bench.py --copy-calibration)",
+           "command": command}
+    fetch = write = 0.0
+    for k in CROSS_KERNELS:
+        fk, n = _kib_per_dispatch(cross_fetch, k)
+        wk, _ = _kib_per_dispatch(cross_write, k)
+        rec["kernels"][k] = {"dispatches": n, "FETCH_SIZE_KiB": fk, "WRITE_SIZE_KiB": wk}
+        fetch += fk * 1024.0 * fetch_scale
+        write += wk * 1024.0 * write_scale
+    rec["fetch_bytes_per_launch"] = fetch
+    rec["write_bytes_per_launch"] = write
+    rec["traffic_bytes_per_launch"] = fetch + write
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def measured_traffic():
+    """HBM bytes per cross-attention launch from the committed counter record,
+    or None when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration() -> None:
+    import torch
+
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "ok": bool(dst[-1].item() == 7)}), flush=True)
 
 
 def kv_bytes_per_row(L: int, H: int, Dh: int, elem_bytes: int) -> int:
@@ -182,6 +284,9 @@ def cpu_baseline(w, n_req: int):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.traffic_command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "requested_gpus": args.gpus}))
@@ -192,6 +297,9 @@ def main():
     from block_diffusion_drafter_all_amd.workloads import make_workload
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = make_workload(args.config, layout=args.layout)
     buf = S.allocate(w)
     torch.cuda.synchronize()
@@ -261,9 +369,10 @@ def main():
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
         "data": "synthetic (seeded; shapes and distributions of the drafting workload)",
         "config": describe(w),
-        "roofline": {"bound": "hbm", "kernel": "fm_paged_cross_attention", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": cb, "avg_launch_ms": avg_cross},
+        "roofline": {"bound": "hbm",
+                     "kernel": "fm_paged_cross_attention (q_prologue_kernel + cross_attn_kernel, one launch)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(), "bytes_per_launch": cb, "avg_launch_ms": avg_cross},
         "kv_read_GBps": achieved,
         "kv_read_pct_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "attention_rows_per_s": rows / (sum(cross_ms + self_ms) / args.steps * 1e-3),
