@@ -169,7 +169,11 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  * pool        HOST pointer to this layer's pool descriptor.
  * page_table  DEVICE int32 [bs, pt_stride].
  * ctx_lens, bs, H  as given to fm_plan_cross_attention, whose plan ``ws``
- *             must hold (same stream, earlier; lengths unchanged since).
+ *             must hold (same stream, earlier; lengths unchanged since).  A
+ *             plan made for other shapes leaves ``out`` untouched.  If the
+ *             lengths changed after the plan, the outputs are unspecified, no
+ *             access leaves the buffers, and bit 1 of the error word is set
+ *             when a wave's share runs past the last tile; plan again.
  * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
  *             [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most 16 of them.
  * Dh in {64, 128}; page_size a power of two in [1, 4096].
