@@ -33,7 +33,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kWin = 512;  // page ids cached per wave
 
 #ifndef FM_CROSS_DEPTH_BF16
-#define FM_CROSS_DEPTH_BF16 2  // 16-token K/V tiles per wave in the load/compute ring (bf16)
+#define FM_CROSS_DEPTH_BF16 3  // 16-token K/V tiles per wave in the load/compute ring (bf16)
 #endif
 #ifndef FM_CROSS_DEPTH_F32
 #define FM_CROSS_DEPTH_F32 2
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
 #pragma unroll
     for (int j = 0; j < EPC; ++j) qf[ch * EPC + j] = has ? chunk_elem<T>(v, j) : 0.f;
   }
-  norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);
+  norm_rope_row<T, D, true>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);
   st* dst = (st*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows + c) * a.H + h) * D;
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(dst + ch * 4 * EPC + g * EPC) = pack_chunk<T>(&qf[ch * EPC]);
@@ -202,33 +202,52 @@ struct StreamSlot {
   int b, h, r0, nq, flags;
 };
 
-// Counts one partial of the cut pair (b, h) in; if it was the pair's last
-// outstanding partial, combines the pair's partials in wave order,
+// Where the cut pair (b, h) lies in the tile stream: its first tile P, the
+// waves w0..w1 holding its tiles, how many of them hold a part, and its counter.
+struct CutPair {
+  int64_t P, w0, w1;
+  int parts;
+  int32_t* cnt;
+};
+
+__device__ __forceinline__ CutPair cut_pair(const CrossArgs& a, int b, int h, int64_t G) {
+  const int64_t NW = a.lay.n_waves;
+  const int nt = tiles_of(sload_i32(a.ctx_lens + b));
+  CutPair p;
+  p.P = ((const int64_t*)(a.ws + a.lay.pair_off))[b] + (int64_t)h * nt;
+  p.w0 = ((p.P + 1) * NW + G - 1) / G - 1;       // the wave holding tile P
+  p.w1 = ((p.P + nt) * NW + G - 1) / G - 1;      // the wave holding tile P + nt - 1
+  // every wave has tiles when G >= NW; otherwise each holds at most one
+  p.parts = G >= NW ? (int)(p.w1 - p.w0 + 1) : nt;
+  p.cnt = (int32_t*)(a.ws + a.lay.merge_cnt) + p.w0;
+  return p;
+}
+
+// Counts this wave's partial of the cut pair (b, h) in (its stores must be
+// acknowledged already) and tells whether it was the pair's last part.
+__device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h, int64_t G) {
+  const CutPair p = cut_pair(a, b, h, G);
+  int before = 0;
+  if (lane_id() == 0) before = __hip_atomic_fetch_add(p.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __shfl(before, 0) == p.parts - 1;
+}
+
+// Combines the partials of the cut pair (b, h) in wave order,
 //   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,   M = max_w m_w,
 // (accumulated online, two parts per round of loads), writes the output rows
-// and re-arms the pair's counter for the next call.  Lanes hold the same
-// fragment of the rows as in the attention loop.
+// and re-arms the pair's counter for the next call.  Called by the wave that
+// counted the last part in: every other part was acknowledged before it was
+// counted.  Lanes hold the same fragment of the rows as in the attention loop.
 template <class T, int D>
-__device__ __forceinline__ void merge_if_last(const CrossArgs& a, int b, int h, int64_t G) {
+__device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, int64_t G) {
   typedef typename T::storage st;
   constexpr int NDT = D / 16;
   const int lane = lane_id(), g = lane >> 4, c = lane & 15;
-  uint8_t* ws = a.ws;
   const int64_t NW = a.lay.n_waves;
-  const int nt = tiles_of(sload_i32(a.ctx_lens + b));
-  const int64_t P = ((const int64_t*)(ws + a.lay.pair_off))[b] + (int64_t)h * nt;
-  auto wave_of = [&](int64_t x) -> int64_t { return ((x + 1) * NW + G - 1) / G - 1; };
+  const CutPair cp = cut_pair(a, b, h, G);
+  const int64_t P = cp.P, w0 = cp.w0, w1 = cp.w1;
+  int32_t* cnt = cp.cnt;
   auto start_of = [&](int64_t wv) -> int64_t { return wv * G / NW; };
-  const int64_t w0 = wave_of(P), w1 = wave_of(P + nt - 1);
-  // waves holding a part: all of w0..w1 when every wave has tiles, else one tile each
-  const int parts = G >= NW ? (int)(w1 - w0 + 1) : nt;
-  int32_t* cnt = (int32_t*)(ws + a.lay.merge_cnt) + w0;
-  wait_stores_acknowledged();  // this wave's partial before its count
-  int before = 0;
-  if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  before = __shfl(before, 0);
-  if (before != parts - 1) return;
-  // Every other part was acknowledged before it was counted: read them all.
   const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
   const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
   auto part_of = [&](int64_t wv) -> uint32_t {  // the wave's partial slot holding this pair
@@ -280,7 +299,7 @@ __device__ __forceinline__ void merge_if_last(const CrossArgs& a, int b, int h, 
 // the tile's base address is wave-uniform (scalar), with a per-lane offset that
 // never changes.
 template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
-__global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
+__global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kernel(CrossArgs a) {
   typedef typename T::storage st;
   constexpr int EPC = T::EPC;
   constexpr int NCH = D / (4 * EPC);
@@ -549,9 +568,16 @@ __global__ __launch_bounds__(256, 2) void cross_attn_kernel(CrossArgs a) {
   const int err = (bad_page ? 1 : 0) | (exhausted ? 2 : 0);
   if (err && lane == 0) atomicOr(&hdr->error, err);
   // The pairs this wave cut: the last of each pair's waves to get here merges it.
+  if (cut_b[0] >= 0 || cut_b[1] >= 0) {
+    wait_stores_acknowledged();  // this wave's partials before their counts
+    int last[2] = {0, 0};
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (cut_b[k] >= 0) merge_if_last<T, D>(a, cut_b[k], cut_h[k], ph.total_tiles);
+    for (int k = 0; k < 2; ++k)
+      if (cut_b[k] >= 0) last[k] = count_in(a, cut_b[k], cut_h[k], ph.total_tiles);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (last[k]) merge_pair<T, D>(a, cut_b[k], cut_h[k], ph.total_tiles);
+  }
 }
 
 template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
@@ -583,8 +609,8 @@ hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStre
   if (dtype == 1)
     return Dh == 128 ? launch_cross_typed<Bf16, 128, FM_CROSS_DEPTH_BF16>(a, s)
                      : launch_cross_typed<Bf16, 64, FM_CROSS_DEPTH_BF16>(a, s);
-  // fp32 rows of 128 take twice the registers: one tile in the ring.
-  return Dh == 128 ? launch_cross_typed<F32, 128, 1>(a, s) : launch_cross_typed<F32, 64, FM_CROSS_DEPTH_F32>(a, s);
+  return Dh == 128 ? launch_cross_typed<F32, 128, FM_CROSS_DEPTH_F32>(a, s)
+                   : launch_cross_typed<F32, 64, FM_CROSS_DEPTH_F32>(a, s);
 }
 
 }  // namespace fm

@@ -15,7 +15,10 @@ constexpr int kMaxLayers = 16;
 constexpr int kQRows = 16;          // query rows per request handled by one unit
 constexpr int32_t kPlanMagic = 0x464d504c;   // "FMPL"
 constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
-constexpr int kWavesPerCU = 8;               // resident cross-attention waves per CU
+#ifndef FM_CROSS_WAVES_PER_SIMD
+#define FM_CROSS_WAVES_PER_SIMD 1
+#endif
+constexpr int kWavesPerCU = 4 * FM_CROSS_WAVES_PER_SIMD;  // resident cross-attention waves per CU
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
