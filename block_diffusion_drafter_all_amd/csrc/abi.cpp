@@ -2,6 +2,7 @@
 // argument validation, the RoPE frequency table, workspace layout, launches.
 // No entry point allocates, frees or synchronizes.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -101,7 +102,7 @@ int plan_waves() {
       (void)hipGetLastError();
       cus = 256;
     }
-    cached[dev] = cus * fm::kWavesPerCU;
+    cached[dev] = std::min(cus * fm::kWavesPerCU, fm::kMaxPlanWaves);
   }
   return cached[dev];
 }

@@ -99,7 +99,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   PlanHeader* hdr = (PlanHeader*)ws;
   int64_t* pair_off = (int64_t*)(ws + a.lay.pair_off);
   WaveRec* rec = (WaveRec*)(ws + a.lay.wave_rec);
+  PairRec* prec = (PairRec*)(ws + a.lay.pair_rec);
   int32_t* cnt = (int32_t*)(ws + a.lay.merge_cnt);
+  __shared__ int64_t starts[kMaxPlanWaves + 1];
   const int tid = threadIdx.x;
   int64_t carry = 0;
   for (int base = 0; base < a.bs; base += 1024) {
@@ -111,13 +113,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     carry += tot;
   }
   if (tid == 0) pair_off[a.bs] = carry;
-  __syncthreads();
   const int64_t G = carry;
   const int NW = a.lay.n_waves;
+  for (int w = tid; w <= NW; w += 1024) starts[w] = G * w / NW;  // equal shares
+  __syncthreads();
   for (int w = tid; w < NW; w += 1024) {
-    const int64_t g0 = (int64_t)w * G / NW;
-    const int64_t g1 = (int64_t)(w + 1) * G / NW;
+    const int64_t g0 = starts[w], g1 = starts[w + 1];
     WaveRec r{};
+    r.start = g0;
     if (g1 > g0) {
       // the request whose pairs hold tile g0: the largest b with pair_off[b] <= g0
       int lo = 0, hi = a.bs - 1;
@@ -137,6 +140,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     }
     rec[w] = r;
     cnt[w] = 0;
+  }
+  // Each pair's first and last wave (the last wave whose range starts at or
+  // before its first and last tile), and how many waves hold a part of it.
+  auto wave_of = [&](int64_t x) -> int {
+    int lo = 0, hi = NW - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (starts[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  const int64_t pairs = (int64_t)a.bs * a.H;
+  for (int64_t i = tid; i < pairs; i += 1024) {
+    const int b = (int)(i / a.H), h = (int)(i % a.H);
+    const int T = tiles_of(a.ctx_lens[b]);
+    PairRec pr{};
+    if (T > 0) {
+      const int64_t P = pair_off[b] + (int64_t)h * T;
+      pr.w0 = wave_of(P);
+      pr.w1 = wave_of(P + T - 1);
+      for (int u = pr.w0; u <= pr.w1; ++u) pr.parts += starts[u + 1] > starts[u] ? 1 : 0;
+    }
+    prec[i] = pr;
   }
   if (tid == 0) {
     hdr->magic = kPlanMagic;
@@ -205,28 +232,27 @@ struct StreamSlot {
 // Where the cut pair (b, h) lies in the tile stream: its first tile P, the
 // waves w0..w1 holding its tiles, how many of them hold a part, and its counter.
 struct CutPair {
-  int64_t P, w0, w1;
-  int parts;
+  int64_t P;
+  int w0, w1, parts;
   int32_t* cnt;
 };
 
-__device__ __forceinline__ CutPair cut_pair(const CrossArgs& a, int b, int h, int64_t G) {
-  const int64_t NW = a.lay.n_waves;
+__device__ __forceinline__ CutPair cut_pair(const CrossArgs& a, int b, int h) {
   const int nt = tiles_of(sload_i32(a.ctx_lens + b));
+  const PairRec pr = ((const PairRec*)(a.ws + a.lay.pair_rec))[(int64_t)b * a.H + h];
   CutPair p;
   p.P = ((const int64_t*)(a.ws + a.lay.pair_off))[b] + (int64_t)h * nt;
-  p.w0 = ((p.P + 1) * NW + G - 1) / G - 1;       // the wave holding tile P
-  p.w1 = ((p.P + nt) * NW + G - 1) / G - 1;      // the wave holding tile P + nt - 1
-  // every wave has tiles when G >= NW; otherwise each holds at most one
-  p.parts = G >= NW ? (int)(p.w1 - p.w0 + 1) : nt;
+  p.w0 = pr.w0;
+  p.w1 = pr.w1;
+  p.parts = pr.parts;
   p.cnt = (int32_t*)(a.ws + a.lay.merge_cnt) + p.w0;
   return p;
 }
 
 // Counts this wave's partial of the cut pair (b, h) in (its stores must be
 // acknowledged already) and tells whether it was the pair's last part.
-__device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h, int64_t G) {
-  const CutPair p = cut_pair(a, b, h, G);
+__device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h) {
+  const CutPair p = cut_pair(a, b, h);
   int before = 0;
   if (lane_id() == 0) before = __hip_atomic_fetch_add(p.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return __shfl(before, 0) == p.parts - 1;
@@ -239,19 +265,19 @@ __device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h, int64
 // counted the last part in: every other part was acknowledged before it was
 // counted.  Lanes hold the same fragment of the rows as in the attention loop.
 template <class T, int D>
-__device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, int64_t G) {
+__device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
   typedef typename T::storage st;
   constexpr int NDT = D / 16;
   const int lane = lane_id(), g = lane >> 4, c = lane & 15;
-  const int64_t NW = a.lay.n_waves;
-  const CutPair cp = cut_pair(a, b, h, G);
-  const int64_t P = cp.P, w0 = cp.w0, w1 = cp.w1;
+  const CutPair cp = cut_pair(a, b, h);
+  const int64_t P = cp.P;
+  const int w0 = cp.w0, w1 = cp.w1;
   int32_t* cnt = cp.cnt;
-  auto start_of = [&](int64_t wv) -> int64_t { return wv * G / NW; };
+  const WaveRec* rec = (const WaveRec*)(a.ws + a.lay.wave_rec);
   const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
   const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
-  auto part_of = [&](int64_t wv) -> uint32_t {  // the wave's partial slot holding this pair
-    return (uint32_t)(wv * 2 + ((wv == w0 && start_of(w0) < P) ? 1 : 0));
+  auto part_of = [&](int wv) -> uint32_t {  // the wave's partial slot holding this pair
+    return (uint32_t)(wv * 2 + ((wv == w0 && rec[w0].start < P) ? 1 : 0));
   };
   float m_acc = kNegInf, l_acc = 0.f;
   f32x4_t acc[NDT];
@@ -268,10 +294,10 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, int
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * sa + __builtin_bit_cast(f32x4_t, ow[dt]) * sw;
     m_acc = live ? m_new : m_acc;
   };
-  for (int64_t wv = w0; wv <= w1; wv += 2) {
-    const int64_t wb = min(wv + 1, w1);
-    const bool ok_a = start_of(wv + 1) > start_of(wv);
-    const bool ok_b = wv + 1 <= w1 && start_of(wb + 1) > start_of(wb);
+  for (int wv = w0; wv <= w1; wv += 2) {
+    const int wb = min(wv + 1, w1);
+    const bool ok_a = rec[wv].count > 0;
+    const bool ok_b = wv + 1 <= w1 && rec[wb].count > 0;
     const uint32_t pa = part_of(wv), pb = part_of(wb);
     u32x4_t oa[NDT], ob[NDT];
     const u32x2_t mla = __builtin_amdgcn_raw_buffer_load_b64(prs, (pa * 64 + lane) * 8, 0, kDeviceScope);
@@ -573,10 +599,10 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     int last[2] = {0, 0};
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (cut_b[k] >= 0) last[k] = count_in(a, cut_b[k], cut_h[k], ph.total_tiles);
+      if (cut_b[k] >= 0) last[k] = count_in(a, cut_b[k], cut_h[k]);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (last[k]) merge_pair<T, D>(a, cut_b[k], cut_h[k], ph.total_tiles);
+      if (last[k]) merge_pair<T, D>(a, cut_b[k], cut_h[k]);
   }
 }
 

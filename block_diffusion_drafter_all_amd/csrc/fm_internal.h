@@ -19,6 +19,7 @@ constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
 #define FM_CROSS_WAVES_PER_SIMD 1
 #endif
 constexpr int kWavesPerCU = 4 * FM_CROSS_WAVES_PER_SIMD;  // resident cross-attention waves per CU
+constexpr int kMaxPlanWaves = 4096;  // most attention waves one plan describes
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -52,17 +53,26 @@ struct PlanHeader {
   int64_t total_tiles;
 };
 
-// One wave's range: it starts at tile ``k`` of pair (b, h) and covers
-// ``count`` tiles; ``ctx`` is request b's context length.
+// One wave's range: it starts at tile ``k`` of pair (b, h), which is tile
+// ``start`` of the stream, and covers ``count`` tiles; ``ctx`` is request b's
+// context length.
 struct WaveRec {
   int32_t b, h, k, count;
-  int32_t ctx, pad[3];
+  int32_t ctx, pad;
+  int64_t start;
+};
+
+// Where a pair's tiles lie among the wave ranges: the first and last wave
+// holding them and how many waves hold a part (1: the pair is whole).
+struct PairRec {
+  int32_t w0, w1, parts, pad;
 };
 
 struct PlanLayout {
   size_t q_hat;       // [bs][16][H][Dh] of the call's type: normed, rotated queries (0 past a request's rows)
   size_t pair_off;    // int64 [bs + 1]: first tile of request b's pairs in the stream
   size_t wave_rec;    // WaveRec [n_waves]
+  size_t pair_rec;    // PairRec [bs * H]
   size_t merge_cnt;   // int32 [n_waves]: partials counted in for the cut pair whose first wave is w
   size_t partial_ml;  // float2 [n_waves][2][64 lanes]: running max (log2) and denominator of the lane's row
   size_t partial_o;   // f32x4 [n_waves][2][Dh/16][64 lanes]: unnormalized outputs in MFMA fragment order
@@ -77,6 +87,7 @@ inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves) {
   p.q_hat = off;      off = align256(off + (size_t)bs * kQRows * H * Dh * 4);
   p.pair_off = off;   off = align256(off + (size_t)(bs + 1) * 8);
   p.wave_rec = off;   off = align256(off + (size_t)n_waves * sizeof(WaveRec));
+  p.pair_rec = off;   off = align256(off + (size_t)bs * H * sizeof(PairRec));
   p.merge_cnt = off;  off = align256(off + (size_t)n_waves * 4);
   p.partial_ml = off; off = align256(off + (size_t)n_waves * 2 * 64 * 8);
   p.partial_o = off;  off = align256(off + (size_t)n_waves * 2 * kQRows * Dh * 4);
