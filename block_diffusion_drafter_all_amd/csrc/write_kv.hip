@@ -152,27 +152,44 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
   }
 }
 
-// bf16 pools with head_dim 128: the MFMA-tiled GEMM.  One workgroup (4 waves
-// in a 2 x 2 arrangement) computes a 128-row x 128-column tile of
-// Y^T = W X^T, i.e. one (layer, {k|v}, head) for 128 compacted rows, with
-// v_mfma_f32_32x32x16_bf16 (each wave a 64 x 64 quarter).  Both operands are
-// staged through double-buffered LDS in 64-wide slices of d_in; rows are
-// padded to 144 bytes so the fragment reads do not collide in LDS banks.
-// Tiles are ordered so the row tiles that share one W tile run back to back
-// on the same XCD (workgroups go round-robin over the 8 XCDs), so W streams
-// from HBM once and the other row tiles find it in that XCD's L2.
+// bf16 pools with head_dim 128: the MFMA-tiled GEMM.  One workgroup (8 waves
+// in a 4 x 2 arrangement) computes a 256 x 256 tile of Y^T = W X^T: two
+// (layer, {k|v}, head) blocks of W (256 rows) against 256 compacted rows, each
+// wave one whole head for 64 rows with v_mfma_f32_32x32x16_bf16 (4 x 2
+// accumulator blocks of 32 x 32, held in AGPRs); two waves share each SIMD.
+// Operands stream through a ring of kStages LDS buffers, each a 32-wide slice
+// of d_in, filled by direct global->LDS loads that hold no registers while in
+// flight.  Each 1 KB load writes one MFMA operand fragment (32 rows x 16 k) in
+// lane order, so every fragment read is one contiguous, conflict-free 16-byte
+// LDS read.  Per slice: wait until the slice kStages-1 steps back has landed,
+// one barrier (after it every wave is also done with the buffer consumed last
+// step), refill that buffer, then 16 MFMAs per wave.  Tiles are ordered so the
+// row tiles that share one W tile run back to back on the same XCD
+// (workgroups go round-robin over the 8 XCDs), so W streams from HBM once and
+// the other row tiles find it in that XCD's L2.  A wave holds all 128 columns
+// of its head, so the k-norm's sum of squares needs one cross-lane exchange.
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kGM = 128, kGN = 128, kGK = 64;
-constexpr int kLdsRow = kGK * 2 + 16;  // bytes per staged row
+constexpr int kGM = 256, kGN = 256, kGK = 32;
+constexpr int kGemmWaves = 8;
+constexpr int kStages = 4;
+constexpr int kFrag = 1024;                     // bytes of one 32-row x 16-k fragment
+constexpr int kStageBytes = 2 * 16 * kFrag;     // 16 W fragments + 16 X fragments
+constexpr int kLoadsPerWave = 32 / kGemmWaves;  // fragments each wave loads per slice
 
-__global__ __launch_bounds__(256, 2) void write_gemm_bf16_kernel(WriteGemmArgs a, int n_tiles, int m_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_w[2][kGN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_x[2][kGM * kLdsRow];
-  __shared__ float ss_part[2][2][64];
-  const int tid = threadIdx.x, lane = tid & 63;
+// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kWaitLgkm0 = 0xC07F;              // lgkmcnt(0) only
+
+__global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(WriteGemmArgs a, int n_tiles,
+                                                                              int m_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring3[kStageBytes];
+  const int lane = lane_id();
   const int wv = wave_in_block();
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 1, wn = wv & 1;  // rows 64 wm .. +63 of the tile, head wn
   const int wg = blockIdx.x;
   const int n = ((wg >> 3) / m_tiles) * 8 + (wg & 7);
   const int mt = (wg >> 3) % m_tiles;
@@ -183,99 +200,108 @@ __global__ __launch_bounds__(256, 2) void write_gemm_bf16_kernel(WriteGemmArgs a
   const int live = hdr->live_count;
   const int m0 = mt * kGM;
   if (m0 >= live) return;
-  const int l = n / (2 * a.H);
-  const int kv = (n / a.H) & 1;
-  const int h = n - (n / a.H) * a.H;
+  const int hn = 2 * n + wn;  // this wave's (layer, k|v, head) block of W
+  const int l = hn / (2 * a.H);
+  const int kv = (hn / a.H) & 1;
+  const int h = hn - (hn / a.H) * a.H;
   const int32_t* live_row = (const int32_t*)(ws + a.lay.live_row);
+  const int frow = lane & 31, fchunk = lane >> 5;
 
-  // Global -> LDS staging: each operand slice is 128 rows x 8 chunks of 16 B.
-  // thread t moves rows (t >> 3) + 32 i, 16-byte segment t & 7, of each slice
-  const int srow = tid >> 3, seg = tid & 7;
-  const uint16_t* W = (const uint16_t*)a.w + ((int64_t)n * kGN + srow) * a.d_in + seg * 8;
-  const uint16_t* X = (const uint16_t*)a.x + seg * 8;
-  int32_t xrow[4];
+  // Fragment f of a slice (0..15 of W, 16..31 of X) covers rows 32 ((f & 15) >> 1)
+  // .. +31 and k chunk 2 (f & 1) + l/32; this wave loads fragments
+  // kLoadsPerWave * wv .. +kLoadsPerWave-1.
+  const uint16_t* src[kLoadsPerWave];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xrow[i] = live_row[min(m0 + srow + 32 * i, live - 1)];
-  const int64_t w_step = (int64_t)32 * a.d_in;
-  u32x4_t gw[4], gx[4];
-  auto gload = [&](int kc) {
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int f = kLoadsPerWave * wv + i, fl = f & 15;
+    const int row = 32 * (fl >> 1) + frow, ch = 2 * (fl & 1) + fchunk;
+    if (f < 16) {
+      src[i] = (const uint16_t*)a.w + ((int64_t)n * kGN + row) * a.d_in + ch * 8;
+    } else {
+      const int xr = live_row[min(m0 + row, live - 1)];
+      src[i] = (const uint16_t*)a.x + (int64_t)xr * a.d_in + ch * 8;
+    }
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto issue = [&](int kc, uint8_t* base) {  // slice kc into a ring buffer
     const int k0 = kc * kGK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gw[i] = load16(W + i * w_step + k0);
-      gx[i] = load16(X + (int64_t)xrow[i] * a.d_in + k0);
-    }
-  };
-  auto lstore = [&](int b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4_t*)(lds_w[b] + (srow + 32 * i) * kLdsRow + seg * 16) = gw[i];
-      *(u32x4_t*)(lds_x[b] + (srow + 32 * i) * kLdsRow + seg * 16) = gx[i];
-    }
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), (lds_ptr)(base + (kLoadsPerWave * wv + i) * kFrag),
+                                       16, 0, 0);
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int cg = 0; cg < 2; ++cg)
+  for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cg][rg][i] = 0.f;
 
-  // Fragment rows: lane l reads row (l % 32) of a 32-row group and the 16-byte
-  // chunk 2*kk + l/32 of the 64-wide slice (8 consecutive k per lane).
-  const int frow = lane & 31, fchunk = lane >> 5;
+  // One step of the ring: slice kc is read from ``cur``; slice kc + 3 goes
+  // into ``refill``, the buffer every wave finished reading last step.  (The
+  // buffers are named statically in each of the four unrolled steps so the
+  // compiler can tell the buffer being read from the ones being filled.)
   const int nk = a.d_in / kGK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    gload(min(kc + 1, nk - 1));
-    const uint8_t* bw = lds_w[kc & 1];
-    const uint8_t* bx = lds_x[kc & 1];
+  auto step = [&](int kc, const uint8_t* cur, uint8_t* refill) {
+    // slice kc landed (the two slices issued after it may still be in flight)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave * (kStages - 2)));
+    __builtin_amdgcn_s_barrier();
+    // past the end: a re-read of the last slice into a buffer nobody reads again
+    issue(min(kc + kStages - 1, nk - 1), refill);
+    const uint8_t* buf = cur + lane * 16;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int co = (2 * kk + fchunk) * 16;
-      const u32x4_t a0 = *(const u32x4_t*)(bw + (64 * wn + frow) * kLdsRow + co);
-      const u32x4_t a1 = *(const u32x4_t*)(bw + (64 * wn + 32 + frow) * kLdsRow + co);
-      const u32x4_t b0 = *(const u32x4_t*)(bx + (64 * wm + frow) * kLdsRow + co);
-      const u32x4_t b1 = *(const u32x4_t*)(bx + (64 * wm + 32 + frow) * kLdsRow + co);
-      const bf16x8_t A0 = __builtin_bit_cast(bf16x8_t, a0), A1 = __builtin_bit_cast(bf16x8_t, a1);
-      const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, b0), B1 = __builtin_bit_cast(bf16x8_t, b1);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1, acc[1][1], 0, 0, 0);
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t A[4], B[2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        A[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (2 * (4 * wn + q) + kk) * kFrag));
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        B[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (16 + 2 * (2 * wm + q) + kk) * kFrag));
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+          acc[cg][rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cg], B[rg], acc[cg][rg], 0, 0, 0);
     }
-    lstore((kc + 1) & 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's reads of the buffer are done
+  };
+  static_assert(kStages == 4, "the ring below is unrolled for four buffers");
+  issue(0, ring0);
+  issue(min(1, nk - 1), ring1);
+  issue(min(2, nk - 1), ring2);
+  // nk is even (d_in a multiple of 64); the tail handles nk % 4 == 2
+  int kc = 0;
+  for (; kc + 4 <= nk; kc += 4) {
+    step(kc, ring0, ring3);
+    step(kc + 1, ring1, ring0);
+    step(kc + 2, ring2, ring1);
+    step(kc + 3, ring3, ring2);
   }
+  if (kc < nk) {
+    step(kc, ring0, ring3);
+    step(kc + 1, ring1, ring0);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the ring's trailing loads
   // acc[cg][rg][i] (lane l) = Y[tile row 64 wm + 32 rg + l % 32]
-  //                            [head column 64 wn + 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]
+  //                            [head column 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]
 
-  float rs[2] = {1.f, 1.f};
-  if (kv == 0) {  // k-norm over the head's 128 columns: this wave's 64, then its partner's
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      float ss = 0.f;
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ss += acc[cg][rg][i] * acc[cg][rg][i];
-      ss += __shfl_xor(ss, 32);
-      if (lane < 32) ss_part[wm][wn][32 * rg + lane] = ss;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      const int r = 32 * rg + frow;
-      rs[rg] = 1.0f / sqrtf((ss_part[wm][0][r] + ss_part[wm][1][r]) / (float)kDhGemm + a.eps);
-    }
-  }
   const PoolDesc& P = a.pools[l];
   const float* kw = a.k_norm_w + (int64_t)l * kDhGemm;
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
+    float rs = 1.f;
+    if (kv == 0) {  // k-norm over the head's 128 columns: 64 in this lane, 64 in lane l ^ 32
+      float ss = 0.f;
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += acc[cg][rg][i] * acc[cg][rg][i];
+      ss += __shfl_xor(ss, 32);
+      rs = 1.0f / sqrtf(ss / (float)kDhGemm + a.eps);
+    }
     const int li = m0 + 64 * wm + 32 * rg + frow;
     const bool has = li < live;
     const int lic = has ? li : m0;
@@ -283,24 +309,24 @@ __global__ __launch_bounds__(256, 2) void write_gemm_bf16_kernel(WriteGemmArgs a
     const int off = ((const int32_t*)(ws + a.lay.live_off))[lic];
     const float fpos = (float)((const int32_t*)(ws + a.lay.live_pos))[lic];
     uint16_t* dst = (uint16_t*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
-                    (int64_t)h * P.head_stride + 64 * wn + 4 * fchunk;
+                    (int64_t)h * P.head_stride + 4 * fchunk;
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
+    for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // columns 64 wn + 32 cg + 8 q + 4 (l/32) + 0..3: two interleaved RoPE pairs
+        // columns 32 cg + 8 q + 4 (l/32) + 0..3: two interleaved RoPE pairs
         float v[4] = {acc[cg][rg][4 * q], acc[cg][rg][4 * q + 1], acc[cg][rg][4 * q + 2], acc[cg][rg][4 * q + 3]};
         if (kv == 0) {
 #pragma unroll
           for (int p2 = 0; p2 < 4; p2 += 2) {
-            const int col = 64 * wn + 32 * cg + 8 * q + 4 * fchunk + p2;
-            // frequency index col / 2 = 32 wn + 16 cg + 4 q + 2 (l/32) + p2/2
-            const int f0 = 32 * wn + 16 * cg + 4 * q + p2 / 2;
+            const int col = 32 * cg + 8 * q + 4 * fchunk + p2;
+            // frequency index col / 2 = 16 cg + 4 q + 2 (l/32) + p2/2
+            const int f0 = 16 * cg + 4 * q + p2 / 2;
             const float inv = fchunk ? a.rope.inv[f0 + 2] : a.rope.inv[f0];
             float sn, cs;
-            sincosf(fpos * inv, &sn, &cs);
-            const float y0 = v[p2] * rs[rg] * kw[col];
-            const float y1 = v[p2 + 1] * rs[rg] * kw[col + 1];
+            angle_sincos<true>(fpos * inv, &sn, &cs);
+            const float y0 = v[p2] * rs * kw[col];
+            const float y1 = v[p2 + 1] * rs * kw[col + 1];
             v[p2] = y0 * cs - y1 * sn;
             v[p2 + 1] = y1 * cs + y0 * sn;
           }
@@ -318,9 +344,9 @@ hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, in
   const int n_tiles = g.L * 2 * g.H;
   if (sizeof(typename T::storage) == 2 && D == kDhGemm) {
     const int m_tiles = (int)((n_rows + kGM - 1) / kGM);
-    const int64_t groups = (n_tiles + 7) / 8;
-    hipLaunchKernelGGL(write_gemm_bf16_kernel, dim3((unsigned)(groups * 8 * m_tiles)), dim3(256), 0, s, g, n_tiles,
-                       m_tiles);
+    const int64_t groups = (n_tiles / 2 + 7) / 8;  // 256-row tiles of W: two heads each
+    hipLaunchKernelGGL(write_gemm_bf16_kernel, dim3((unsigned)(groups * 8 * m_tiles)), dim3(64 * kGemmWaves), 0, s,
+                       g, n_tiles / 2, m_tiles);
     return hipGetLastError();
   }
   const unsigned m_tiles = (unsigned)((n_rows + 63) / 64);
