@@ -159,9 +159,11 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
 // accumulator blocks of 32 x 32, held in AGPRs); two waves share each SIMD.
 // Operands stream through a ring of kStages LDS buffers, each a 32-wide slice
 // of d_in, filled by direct global->LDS loads that hold no registers while in
-// flight.  Each 1 KB load writes one MFMA operand fragment (32 rows x 16 k) in
-// lane order, so every fragment read is one contiguous, conflict-free 16-byte
-// LDS read.  Per slice: wait until the slice kStages-1 steps back has landed,
+// flight.  A staged operand slice is 256 rows x 4 chunks of 16 bytes; each
+// 1 KB load moves 16 whole rows (64 contiguous bytes each: one L2 request per
+// row), and the chunk order within a row is swizzled by XOR with (row >> 2) & 3
+// so that the 16 lanes of each phase of an MFMA fragment read (16 rows, one
+// chunk) hit 64 distinct banks.  Per slice: wait until the slice kStages-1 steps back has landed,
 // one barrier (after it every wave is also done with the buffer consumed last
 // step), refill that buffer, then 16 MFMAs per wave.  Tiles are ordered so the
 // row tiles that share one W tile run back to back on the same XCD
@@ -207,14 +209,15 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
   const int32_t* live_row = (const int32_t*)(ws + a.lay.live_row);
   const int frow = lane & 31, fchunk = lane >> 5;
 
-  // Fragment f of a slice (0..15 of W, 16..31 of X) covers rows 32 ((f & 15) >> 1)
-  // .. +31 and k chunk 2 (f & 1) + l/32; this wave loads fragments
-  // kLoadsPerWave * wv .. +kLoadsPerWave-1.
+  // Load j of a slice (0..15 of W, 16..31 of X) fills LDS slots 64 (j & 15) ..
+  // +63 of its operand: lane l takes row 16 (j & 15) + l/4 and, in slot
+  // position l % 4, the chunk (l % 4) ^ ((row >> 2) & 3).  This wave issues
+  // loads kLoadsPerWave * wv .. +kLoadsPerWave-1.
   const uint16_t* src[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
     const int f = kLoadsPerWave * wv + i, fl = f & 15;
-    const int row = 32 * (fl >> 1) + frow, ch = 2 * (fl & 1) + fchunk;
+    const int row = 16 * fl + (lane >> 2), ch = (lane & 3) ^ ((row >> 2) & 3);
     if (f < 16) {
       src[i] = (const uint16_t*)a.w + ((int64_t)n * kGN + row) * a.d_in + ch * 8;
     } else {
@@ -239,6 +242,13 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cg][rg][i] = 0.f;
 
+  // Byte offset of this lane's fragment element in a staged operand, for k
+  // chunk pair kk: row l % 32 (plus 32 q rows = 2048 q bytes), chunk 2 kk + l/32
+  // at its swizzled position.
+  int frag_off[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) frag_off[kk] = frow * 64 + (((2 * kk + fchunk) ^ ((frow >> 2) & 3)) * 16);
+
   // One step of the ring: slice kc is read from ``cur``; slice kc + 3 goes
   // into ``refill``, the buffer every wave finished reading last step.  (The
   // buffers are named statically in each of the four unrolled steps so the
@@ -250,16 +260,17 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     __builtin_amdgcn_s_barrier();
     // past the end: a re-read of the last slice into a buffer nobody reads again
     issue(min(kc + kStages - 1, nk - 1), refill);
-    const uint8_t* buf = cur + lane * 16;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      // lane l reads row 32 q + l % 32 (rows of one fragment are 2 KB apart per 32) and chunk 2 kk + l/32
+      const uint8_t* buf = cur + frag_off[kk];
       bf16x8_t A[4], B[2];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        A[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (2 * (4 * wn + q) + kk) * kFrag));
+        A[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (4 * wn + q) * 2048));
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        B[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (16 + 2 * (2 * wm + q) + kk) * kFrag));
+        B[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + 16 * kFrag + (2 * wm + q) * 2048));
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
