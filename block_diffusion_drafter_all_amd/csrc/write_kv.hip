@@ -174,7 +174,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kGM = 256, kGN = 256, kGK = 32;
 constexpr int kGemmWaves = 8;
-constexpr int kStages = 4;
+#ifndef FM_GEMM_STAGES
+#define FM_GEMM_STAGES 5
+#endif
+constexpr int kStages = FM_GEMM_STAGES;  // LDS ring buffers of 32 KB (gfx950: 160 KB per workgroup)
 constexpr int kFrag = 1024;                     // bytes of one 32-row x 16-k fragment
 constexpr int kStageBytes = 2 * 16 * kFrag;     // 16 W fragments + 16 X fragments
 constexpr int kLoadsPerWave = 32 / kGemmWaves;  // fragments each wave loads per slice
@@ -189,6 +192,9 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring3[kStageBytes];
+#if FM_GEMM_STAGES == 5
+  __shared__ __attribute__((aligned(1024))) uint8_t ring4[kStageBytes];
+#endif
   const int lane = lane_id();
   const int wv = wave_in_block();
   const int wm = wv >> 1, wn = wv & 1;  // rows 64 wm .. +63 of the tile, head wn
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's reads of the buffer are done
   };
-  static_assert(kStages == 4, "the ring below is unrolled for four buffers");
+#if FM_GEMM_STAGES == 4
   issue(0, ring0);
   issue(min(1, nk - 1), ring1);
   issue(min(2, nk - 1), ring2);
@@ -295,6 +301,28 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     step(kc, ring0, ring3);
     step(kc + 1, ring1, ring0);
   }
+#elif FM_GEMM_STAGES == 5
+  issue(0, ring0);
+  issue(min(1, nk - 1), ring1);
+  issue(min(2, nk - 1), ring2);
+  issue(min(3, nk - 1), ring3);
+  int kc = 0;
+  for (; kc + 5 <= nk; kc += 5) {
+    step(kc, ring0, ring4);
+    step(kc + 1, ring1, ring0);
+    step(kc + 2, ring2, ring1);
+    step(kc + 3, ring3, ring2);
+    step(kc + 4, ring4, ring3);
+  }
+  // the last nk % 5 slices, in ring order (each step's buffers named statically)
+  const int rem = nk - kc;
+  if (rem > 0) step(kc, ring0, ring4);
+  if (rem > 1) step(kc + 1, ring1, ring0);
+  if (rem > 2) step(kc + 2, ring2, ring1);
+  if (rem > 3) step(kc + 3, ring3, ring2);
+#else
+#error "FM_GEMM_STAGES must be 4 or 5"
+#endif
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the ring's trailing loads
   // acc[cg][rg][i] (lane l) = Y[tile row 64 wm + 32 rg + l % 32]
   //                            [head column 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]
