@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
 #pragma unroll
     for (int j = 0; j < EPC; ++j) qf[ch * EPC + j] = has ? chunk_elem<T>(v, j) : 0.f;
   }
-  norm_rope_row<T, D, true>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);
+  norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);
   st* dst = (st*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows + c) * a.H + h) * D;
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(dst + ch * 4 * EPC + g * EPC) = pack_chunk<T>(&qf[ch * EPC]);

@@ -229,32 +229,27 @@ struct RopeFreqs {
   float inv[64];
 };
 
-// sin and cos of the fp32 angle ``ang``.  HW = false: sincosf.  HW = true: the
-// angle is reduced by a double-precision multiple of 2*pi (two-part constant)
-// to one revolution and passed to the hardware v_sin_f32 / v_cos_f32, which
-// take revolutions; absolute error against the exact values at the fp32 angle
-// is below 2e-7 for every RoPE angle up to position 2^17 (7e-8 for sincosf),
-// at a fraction of sincosf's cost for large angles.
-template <bool HW>
+// sin and cos of the fp32 RoPE angle ``ang``: the angle is reduced by a
+// double-precision multiple of 2*pi (two-part constant) to one revolution and
+// passed to the hardware v_sin_f32 / v_cos_f32, which take revolutions.
+// Absolute error against the exact values at the fp32 angle is below 2e-7 for
+// every RoPE angle up to position 2^17 (7e-8 for sincosf), at a fraction of
+// sincosf's cost and registers for large angles.
 __device__ __forceinline__ void angle_sincos(float ang, float* sn, float* cs) {
-  if (HW) {
-    constexpr double kInv2Pi = 0.15915494309189533577;
-    constexpr double k2PiHi = 6.283185307179586232;   // double nearest 2*pi
-    constexpr double k2PiLo = 2.4492935982947064e-16;  // 2*pi minus k2PiHi
-    const double a = (double)ang;
-    const double turns = rint(a * kInv2Pi);
-    const float rev = (float)((fma(-turns, k2PiHi, a) - turns * k2PiLo) * kInv2Pi);
-    *sn = __builtin_amdgcn_sinf(rev);
-    *cs = __builtin_amdgcn_cosf(rev);
-  } else {
-    sincosf(ang, sn, cs);
-  }
+  constexpr double kInv2Pi = 0.15915494309189533577;
+  constexpr double k2PiHi = 6.283185307179586232;   // double nearest 2*pi
+  constexpr double k2PiLo = 2.4492935982947064e-16;  // 2*pi minus k2PiHi
+  const double a = (double)ang;
+  const double turns = rint(a * kInv2Pi);
+  const float rev = (float)((fma(-turns, k2PiHi, a) - turns * k2PiLo) * kInv2Pi);
+  *sn = __builtin_amdgcn_sinf(rev);
+  *cs = __builtin_amdgcn_cosf(rev);
 }
 
 // RMSNorm with weight w, then the interleaved-pair rotation at position pos,
 // applied in place to the fp32 values x of a row fragment (row = lane % 16,
 // values x[ch*EPC + j] at column ch*4*EPC + g*EPC + j).
-template <class T, int D, bool HW_TRIG = false>
+template <class T, int D>
 __device__ __forceinline__ void norm_rope_row(float (&x)[D / 4], const float* __restrict__ w, float eps,
                                               int pos, const RopeFreqs& rf, int g) {
   constexpr int EPC = T::EPC;
@@ -275,7 +270,7 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[D / 4], const float* __
       const float inv = sel4(g, rf.inv[f0], rf.inv[f0 + EPC / 2], rf.inv[f0 + EPC], rf.inv[f0 + 3 * EPC / 2]);
       const float ang = fpos * inv;
       float sn, cs;
-      angle_sincos<HW_TRIG>(ang, &sn, &cs);
+      angle_sincos(ang, &sn, &cs);
       const float y0 = x[ch * EPC + j] * rs * w[col];
       const float y1 = x[ch * EPC + j + 1] * rs * w[col + 1];
       x[ch * EPC + j] = y0 * cs - y1 * sn;

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
         const int f0 = 8 * ct + i / 2;
         const float inv = sel4(g, a.rope.inv[f0], a.rope.inv[f0 + 2], a.rope.inv[f0 + 4], a.rope.inv[f0 + 6]);
         float sn, cs;
-        sincosf(fpos * inv, &sn, &cs);
+        angle_sincos(fpos * inv, &sn, &cs);
         const float y0 = acc[ct][i] * rs * kw[col];
         const float y1 = acc[ct][i + 1] * rs * kw[col + 1];
         acc[ct][i] = y0 * cs - y1 * sn;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
             const int f0 = 16 * cg + 4 * q + p2 / 2;
             const float inv = fchunk ? a.rope.inv[f0 + 2] : a.rope.inv[f0];
             float sn, cs;
-            angle_sincos<true>(fpos * inv, &sn, &cs);
+            angle_sincos(fpos * inv, &sn, &cs);
             const float y0 = v[p2] * rs * kw[col];
             const float y1 = v[p2 + 1] * rs * kw[col + 1];
             v[p2] = y0 * cs - y1 * sn;
