@@ -242,13 +242,17 @@ def scatter_into_pool(pools_k, pools_v, slots, keys, values, page_size, dtype):
 
 def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
                           cu_seqlens_q, page_size, scale, theta, eps,
-                          requests=None, heads=None):
+                          requests=None, heads=None, block_size=16):
     """Cross-attention of each request's draft rows onto its paged context.
 
     Row ``r`` of request ``b`` (``cu_seqlens_q[b] <= r < cu_seqlens_q[b+1]``)
-    is query slot ``k = r - cu_seqlens_q[b]`` at position ``ctx_lens[b] + k``
-    (slots sit at ``anchor + 1 + k`` and ``ctx_len = anchor + 1``).  Its query
-    is RMS-normed with ``q_norm_w`` and rotated there (``rms_norm_rope``), then
+    is query slot ``k = (r - cu_seqlens_q[b]) mod block_size`` of candidate
+    block ``(r - cu_seqlens_q[b]) // block_size``, at position
+    ``ctx_lens[b] + k`` (slots sit at ``anchor + 1 + k`` and
+    ``ctx_len = anchor + 1``; tree drafting puts a request's candidate blocks
+    side by side, candidate-major, so that its context is read once: the
+    sglang model's ``forward`` in the flashmap 0.1.0 wheel).  Its query is
+    RMS-normed with ``q_norm_w`` and rotated there (``rms_norm_rope``), then
     attends, non-causally, to the keys/values at logical positions
     ``0 .. ctx_lens[b] - 1`` read through the page table.
 
@@ -266,7 +270,7 @@ def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
         if r1 == r0:
             continue
         ctx = int(ctx_lens[b])
-        positions = ctx + np.arange(r1 - r0)
+        positions = ctx + np.arange(r1 - r0) % block_size
         # Dense context of request b, in logical order.
         n_pages = -(-ctx // page_size)
         pages = np.asarray(page_table[b][:n_pages], dtype=np.int64)

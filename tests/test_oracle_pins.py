@@ -210,6 +210,50 @@ def test_paged_cross_attention_page_permutation_invariant(rng):
     np.testing.assert_array_equal(moved, base)
 
 
+def test_candidate_blocks_read_one_context(rng):
+    # Tree drafting (sglang/model.py ``forward``): a request's n candidate
+    # blocks sit side by side on the query axis, candidate-major, and share its
+    # context; candidate c's slot j sits at the same position as slot j of a
+    # single block.  So a request with 3 blocks of 16 rows (the last ragged)
+    # must equal three one-block requests over the same pages, row for row,
+    # and against brute-force dense attention; identical candidates give
+    # identical rows.
+    ctx = [70, 16, 0]
+    c = _paged_case(rng, ctx=ctx, nq=[40, 32, 20])
+    theta, eps, scale = 1e6, 1e-6, c["D"] ** -0.5
+    joint = O.paged_cross_attention(c["q"], c["w"], c["pk"], c["pv"], c["pt"], c["ctx"], c["cu"], c["ps"], scale,
+                                    theta, eps)
+    # the same rows split into one-block requests that repeat their request's pages
+    split_ctx, split_pt, split_cu = [], [], [0]
+    for b, n in enumerate(ctx):
+        rows = c["cu"][b + 1] - c["cu"][b]
+        for c0 in range(0, rows, 16):
+            split_ctx.append(n)
+            split_pt.append(c["pt"][b])
+            split_cu.append(split_cu[-1] + min(16, rows - c0))
+    split = O.paged_cross_attention(c["q"], c["w"], c["pk"], c["pv"], np.array(split_pt), split_ctx,
+                                    np.array(split_cu), c["ps"], scale, theta, eps)
+    # (equal up to the matrix products' rounding order over different row counts)
+    np.testing.assert_allclose(joint, split, rtol=1e-12, atol=1e-14)
+    for b, n in enumerate(ctx):
+        r0, r1 = c["cu"][b], c["cu"][b + 1]
+        pos = n + np.arange(r1 - r0) % 16
+        for h in range(c["H"]):
+            qh = O.apply_rope(O.rms_norm(c["q"][r0:r1, h], c["w"], eps), pos, theta)
+            if n == 0:
+                np.testing.assert_array_equal(joint[r0:r1, h], 0.0)
+                continue
+            kt = torch.from_numpy(c["dense_k"][b][:, h])
+            vt = torch.from_numpy(c["dense_v"][b][:, h])
+            ref = F.scaled_dot_product_attention(torch.from_numpy(qh)[None], kt[None], vt[None], scale=scale)[0]
+            np.testing.assert_allclose(joint[r0:r1, h], ref.numpy(), rtol=1e-11, atol=1e-12)
+    q2 = c["q"].copy()
+    q2[16:32] = q2[0:16]                 # request 0: candidate 1 repeats candidate 0
+    twin = O.paged_cross_attention(q2, c["w"], c["pk"], c["pv"], c["pt"], c["ctx"], c["cu"], c["ps"], scale,
+                                   theta, eps)
+    np.testing.assert_allclose(twin[16:32], twin[0:16], rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------- self-attention
 
 
