@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="workload: 5 = full draft step (default); 3 = attention of 5 layers; 2, 4, 1")
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"])
+    ap.add_argument("--candidates", type=int, default=1, choices=[1, 2, 4],
+                    help="candidate blocks per request (tree drafting): 16 query rows each, one context read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
@@ -203,7 +205,8 @@ def describe(w) -> dict:
                      4: "long skewed batch (256 lognormal + one 131072-token request)",
                      5: "full draft step: context write + 5-layer attention (64 requests, ctx U[1024,8192])"}[
             w.workload_id],
-        "requests": w.bs, "block_size": w.K, "layers": w.L, "heads": w.H, "head_dim": w.Dh,
+        "requests": w.bs, "block_size": w.K, "candidate_blocks": w.n_cand, "layers": w.L, "heads": w.H,
+        "head_dim": w.Dh,
         "page_size": w.page_size, "total_context_tokens": int(sum(ctx)), "pool_layout": w.meta["layout"],
     }
     if w.write is not None:
@@ -254,7 +257,9 @@ def cpu_baseline(w, n_req: int):
                      pos=wr.row_pos.cpu().numpy()[sel], req=row_req[sel], pt=w.page_table.cpu().numpy(),
                      commit=cl, sel=sel)
     q = [host(w.q[l]) for l in range(w.L)]
-    qkv = [host(w.qkv[l][torch.as_tensor(reqs, device=w.qkv[l].device)]) for l in range(w.L)]
+    blocks = [b * w.n_cand + i for b in reqs for i in range(w.n_cand)]   # candidate blocks of the sample
+    qkv = [host(w.qkv[l][torch.as_tensor(blocks, device=w.qkv[l].device)]) for l in range(w.L)]
+    block_ctx = w.block_ctx_lens.cpu().numpy()[blocks]
     with threadpool_limits(limits=cores):
         blas = [i.get("num_threads") for i in threadpool_info()]
         t0 = time.perf_counter()
@@ -266,7 +271,7 @@ def cpu_baseline(w, n_req: int):
             O.write_context_kv(wr_in["x"][keep], wr_in["w"], wr_in["kn"], wr_in["req"][keep], wr_in["pos"][keep],
                                wr_in["pt"], ps, w.L, w.H, w.Dh, w.eps, w.theta)
         for l in range(w.L):
-            O.block_self_attention(qkv[l], host(w.self_q_norm_w[l]), host(w.self_k_norm_w[l]), ctx[reqs],
+            O.block_self_attention(qkv[l], host(w.self_q_norm_w[l]), host(w.self_k_norm_w[l]), block_ctx,
                                    w.softmax_scale, w.theta, w.eps)
             pk, pv, rows = inputs[l]
             for i, b in enumerate(reqs):
@@ -300,7 +305,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    w = make_workload(args.config, layout=args.layout)
+    w = make_workload(args.config, layout=args.layout, n_cand=args.candidates)
     buf = S.allocate(w)
     torch.cuda.synchronize()
 
@@ -316,14 +321,14 @@ def main():
             if events is not None:
                 events["self"][l][0].record()
             from block_diffusion_drafter_all_amd import binding as B
-            B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.ctx_lens,
+            B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.block_ctx_lens,
                                       w.softmax_scale, w.theta, w.eps, out=buf.self_out[l])
             if events is not None:
                 events["self"][l][1].record()
                 events["cross"][l][0].record()
             B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens,
                                        w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws,
-                                       out=buf.cross_out[l])
+                                       out=buf.cross_out[l], max_q=w.max_q)
             if events is not None:
                 events["cross"][l][1].record()
 

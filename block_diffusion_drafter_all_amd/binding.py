@@ -85,7 +85,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_paged_cross_attention.restype = ctypes.c_int
     lib.fm_paged_cross_attention.argtypes = [
         vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
-        f32, f32, f32, vp, vp, c_sz, vp,
+        c_i32, f32, f32, f32, vp, vp, c_sz, vp,
     ]
     lib.fm_block_self_attention.restype = ctypes.c_int
     lib.fm_block_self_attention.argtypes = [
@@ -210,9 +210,10 @@ def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16):
 
 
 def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,
-                             rope_theta, eps, ws, out=None):
+                             rope_theta, eps, ws, out=None, max_q=16):
     """Paged cross-attention of ``q (total_q, H, Dh)`` onto ``pool``; the plan
-    in ``ws`` must come from fm_plan_cross_attention with the same lengths."""
+    in ``ws`` must come from fm_plan_cross_attention with the same lengths and
+    ``max_q`` (query rows per request: 16 per draft block, up to 4 blocks)."""
     lib = load_library()
     _need(q, "q")
     _need(q_norm_w, "q_norm_w", torch.float32)
@@ -230,7 +231,7 @@ def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu
     desc = pool.descriptor()
     _check(lib.fm_paged_cross_attention(
         _ptr(q), _dtype_code(q), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
-        page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), ctx_lens.shape[0], H, Dh,
+        page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), max_q, ctx_lens.shape[0], H, Dh,
         softmax_scale, rope_theta, eps, _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 

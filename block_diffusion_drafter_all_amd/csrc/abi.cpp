@@ -191,8 +191,9 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 }
 
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q) {
-  if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || max_q < 0 || max_q > fm::kQRows) return 0;
-  return fm::plan_layout(bs, H, Dh, plan_waves()).total;
+  const int nqf = fm::q_frags(max_q);
+  if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || nqf == 0) return 0;
+  return fm::plan_layout(bs, H, Dh, plan_waves(), nqf).total;
 }
 
 int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q, void* ws,
@@ -202,11 +203,12 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
   if (H < 1) return fail(FM_E_INVALID, "%s: H = %d must be >= 1", fn, H);
   if (Dh != 64 && Dh != 128) return fail(FM_E_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, Dh);
   if (max_q < 0) return fail(FM_E_INVALID, "%s: max_q %d < 0", fn, max_q);
-  if (max_q > fm::kQRows)
-    return fail(FM_E_UNSUPPORTED, "%s: max_q %d above %d query rows per request", fn, max_q, fm::kQRows);
+  if (max_q > fm::kQRows * fm::kMaxQFrags)
+    return fail(FM_E_UNSUPPORTED, "%s: max_q %d above %d query rows per request", fn, max_q,
+                fm::kQRows * fm::kMaxQFrags);
   if (bs > 0 && !ctx_lens) return fail(FM_E_INVALID, "%s: ctx_lens is null", fn);
   if ((int64_t)bs * H > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: bs * H too large", fn);
-  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves());
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(), fm::q_frags(max_q));
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::PlanArgs a{};
   a.ctx_lens = ctx_lens;
@@ -219,9 +221,9 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
 
 int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
                              const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
-                             const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t bs, int32_t H, int32_t Dh,
-                             float softmax_scale, float rope_theta, float eps, void* out, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+                             const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs,
+                             int32_t H, int32_t Dh, float softmax_scale, float rope_theta, float eps, void* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "fm_paged_cross_attention";
   if (total_q < 0 || bs < 0) return fail(FM_E_INVALID, "%s: total_q and bs must be >= 0", fn);
   if (total_q == 0 || bs == 0) return ok();
@@ -236,7 +238,12 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   if (total_q > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: total_q above 2^31-1", fn);
   int64_t q16;
   if (int s = check_pool(fn, *pool, dt, 0, &q16)) return s;
-  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves());
+  if (max_q < 0) return fail(FM_E_INVALID, "%s: max_q %d < 0", fn, max_q);
+  const int nqf = fm::q_frags(max_q);
+  if (nqf == 0)
+    return fail(FM_E_UNSUPPORTED, "%s: max_q %d above %d query rows per request", fn, max_q,
+                fm::kQRows * fm::kMaxQFrags);
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(), nqf);
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::CrossArgs a{};
   a.q = q;

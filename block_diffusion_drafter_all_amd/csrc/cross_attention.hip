@@ -4,8 +4,11 @@
 // What is computed (flashmap 0.1.0 wheel: sglang/model.py ``forward``,
 // ``_paged_cross_attention``, ``rms_norm_rope``; vllm/model.py
 // ``paged_cross_attention``): each request's draft rows, RMS-normed and
-// rotated at positions ctx_len + k, attend non-causally to the keys/values at
-// positions 0..ctx_len-1 of the request's paged context.
+// rotated at positions ctx_len + (k mod 16), attend non-causally to the
+// keys/values at positions 0..ctx_len-1 of the request's paged context.  A
+// request holds one draft block of 16 rows or, in tree drafting, up to four
+// candidate blocks side by side, which share one read of its context: each
+// 16-row block is one MFMA fragment (NQF fragments per request).
 //
 // How.  The work is the stream of 16-token K/V tiles of every (request, head)
 // pair.  The plan cuts it into one equal contiguous range per resident
@@ -30,6 +33,7 @@ namespace fm {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;  // lazy online-softmax rescale: p stays <= 2^8 between rescales
 constexpr int kWin = 512;  // page ids cached per wave
 
 #ifndef FM_CROSS_DEPTH_BF16
@@ -171,18 +175,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     hdr->n_waves = NW;
     hdr->bs = a.bs;
     hdr->H = a.H;
+    hdr->nqf = a.lay.nqf;
     hdr->total_tiles = G;
   }
 }
 
 // ----------------------------------------------------------- query rows --
 
-// q^ = RoPE(RMSNorm(q; q_norm_w, eps)) at position ctx_len + k for query row k
-// of request b, stored as [b][k][h][:] in the call's storage type (rows past
-// the request's count are zero), ready to be loaded as an MFMA operand.  A
-// request with an empty context gets its zero output rows here instead.  One
-// wavefront per (request, head).
-template <class T, int D>
+// q^ = RoPE(RMSNorm(q; q_norm_w, eps)) at position ctx_len + (k mod 16) for
+// query row k of request b, stored as [b][k][h][:] for k < 16 NQF in the call's
+// storage type (rows past the request's count are zero), ready to be loaded
+// as MFMA operands.  A request with an empty context gets its zero output
+// rows here instead.  One wavefront per (request, head).
+template <class T, int D, int NQF>
 __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   typedef typename T::storage st;
   constexpr int EPC = T::EPC;
@@ -194,38 +199,45 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   if (b >= a.bs) return;
   const int ctx0 = max(0, a.ctx_lens[b]);
   const int r0 = max(0, a.cu_q[b]);
-  const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows));
-  if (ctx0 == 0) {  // empty context: the output rows are zero
-    if (c < nq) {
-      st* orow = (st*)a.out + ((int64_t)(r0 + c) * a.H + h) * D;
+  const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows * NQF));
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(orow + ch * 4 * EPC + g * EPC) = (u32x4_t){0u, 0u, 0u, 0u};
+  for (int f = 0; f < NQF; ++f) {
+    const int k = kQRows * f + c;  // this lane's row of fragment f
+    const bool has = k < nq;
+    if (ctx0 == 0) {  // empty context: the output rows are zero
+      if (has) {
+        st* orow = (st*)a.out + ((int64_t)(r0 + k) * a.H + h) * D;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(orow + ch * 4 * EPC + g * EPC) = (u32x4_t){0u, 0u, 0u, 0u};
+      }
+      continue;
     }
-    return;
+    float qf[D / 4];
+    const st* qrow = (const st*)a.q + ((int64_t)(has ? r0 + k : 0) * a.H + h) * D;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const u32x4_t v = load16(qrow + ch * 4 * EPC + g * EPC);
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) qf[ch * EPC + j] = has ? chunk_elem<T>(v, j) : 0.f;
+    }
+    norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);  // slot c of every candidate block
+    st* dst = (st*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows * NQF + k) * a.H + h) * D;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(dst + ch * 4 * EPC + g * EPC) = pack_chunk<T>(&qf[ch * EPC]);
   }
-  float qf[D / 4];
-  const bool has = c < nq;
-  const st* qrow = (const st*)a.q + ((int64_t)(has ? r0 + c : 0) * a.H + h) * D;
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    const u32x4_t v = load16(qrow + ch * 4 * EPC + g * EPC);
-#pragma unroll
-    for (int j = 0; j < EPC; ++j) qf[ch * EPC + j] = has ? chunk_elem<T>(v, j) : 0.f;
-  }
-  norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx0 + c, a.rope, g);
-  st* dst = (st*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows + c) * a.H + h) * D;
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(dst + ch * 4 * EPC + g * EPC) = pack_chunk<T>(&qf[ch * EPC]);
 }
 
 // -------------------------------------------------------- cross-attention --
 
-template <class T, int D>
+// One K/V tile in the load ring.  With one query fragment, the pair's
+// prepared query rows ride along with its first tile (q); with more, they are
+// read when that tile is computed (q unused).
+template <class T, int D, int NQF>
 struct StreamSlot {
   u32x4_t k[D / (4 * T::EPC)];
   u32x4_t v[D / (4 * T::EPC)];
-  u32x4_t q[D / (4 * T::EPC)];  // raw query rows, meaningful on a kStart tile
-  uint32_t mask;                // bit t: token t of the tile is a valid key
+  u32x4_t q[NQF == 1 ? D / (4 * T::EPC) : 1];
+  uint32_t mask;  // bit t: token t of the tile is a valid key
   int b, h, r0, nq, flags;
 };
 
@@ -258,13 +270,14 @@ __device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h) {
   return __shfl(before, 0) == p.parts - 1;
 }
 
-// Combines the partials of the cut pair (b, h) in wave order,
+// Combines the partials of the cut pair (b, h) in wave order, fragment by
+// fragment,
 //   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,   M = max_w m_w,
 // (accumulated online, two parts per round of loads), writes the output rows
 // and re-arms the pair's counter for the next call.  Called by the wave that
 // counted the last part in: every other part was acknowledged before it was
 // counted.  Lanes hold the same fragment of the rows as in the attention loop.
-template <class T, int D>
+template <class T, int D, int NQF>
 __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
   typedef typename T::storage st;
   constexpr int NDT = D / 16;
@@ -279,44 +292,47 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
   auto part_of = [&](int wv) -> uint32_t {  // the wave's partial slot holding this pair
     return (uint32_t)(wv * 2 + ((wv == w0 && rec[w0].start < P) ? 1 : 0));
   };
-  float m_acc = kNegInf, l_acc = 0.f;
-  f32x4_t acc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  auto combine = [&](bool ok, u32x2_t ml, const u32x4_t* ow) {
-    const float m_w = __uint_as_float(ml[0]), l_w = __uint_as_float(ml[1]);
-    const float m_new = fmaxf(m_acc, m_w);
-    const bool live = ok && m_new != kNegInf;
-    const float sa = (live && m_acc != kNegInf) ? exp2f(m_acc - m_new) : (live ? 0.f : 1.f);
-    const float sw = (live && m_w != kNegInf) ? exp2f(m_w - m_new) : 0.f;
-    l_acc = l_acc * sa + l_w * sw;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * sa + __builtin_bit_cast(f32x4_t, ow[dt]) * sw;
-    m_acc = live ? m_new : m_acc;
-  };
-  for (int wv = w0; wv <= w1; wv += 2) {
-    const int wb = min(wv + 1, w1);
-    const bool ok_a = rec[wv].count > 0;
-    const bool ok_b = wv + 1 <= w1 && rec[wb].count > 0;
-    const uint32_t pa = part_of(wv), pb = part_of(wb);
-    u32x4_t oa[NDT], ob[NDT];
-    const u32x2_t mla = __builtin_amdgcn_raw_buffer_load_b64(prs, (pa * 64 + lane) * 8, 0, kDeviceScope);
-    const u32x2_t mlb = __builtin_amdgcn_raw_buffer_load_b64(prs, (pb * 64 + lane) * 8, 0, kDeviceScope);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      oa[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pa * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
-      ob[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pb * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
-    }
-    combine(ok_a, mla, oa);
-    combine(ok_b, mlb, ob);
-  }
   const int r0 = max(0, sload_i32(a.cu_q + b));
-  const int nq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - r0, kQRows));
-  const float inv = l_acc > 0.f ? 1.0f / l_acc : 0.f;
-  if (c < nq) {
-    st* orow = (st*)a.out + ((int64_t)(r0 + c) * a.H + h) * D;
+  const int nq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - r0, kQRows * NQF));
+  for (int f = 0; f < NQF; ++f) {
+    float m_acc = kNegInf, l_acc = 0.f;
+    f32x4_t acc[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, acc[dt], inv);
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    auto combine = [&](bool ok, u32x2_t ml, const u32x4_t* ow) {
+      const float m_w = __uint_as_float(ml[0]), l_w = __uint_as_float(ml[1]);
+      const float m_new = fmaxf(m_acc, m_w);
+      const bool live = ok && m_new != kNegInf;
+      const float sa = (live && m_acc != kNegInf) ? exp2f(m_acc - m_new) : (live ? 0.f : 1.f);
+      const float sw = (live && m_w != kNegInf) ? exp2f(m_w - m_new) : 0.f;
+      l_acc = l_acc * sa + l_w * sw;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * sa + __builtin_bit_cast(f32x4_t, ow[dt]) * sw;
+      m_acc = live ? m_new : m_acc;
+    };
+    for (int wv = w0; wv <= w1; wv += 2) {
+      const int wb = min(wv + 1, w1);
+      const bool ok_a = rec[wv].count > 0;
+      const bool ok_b = wv + 1 <= w1 && rec[wb].count > 0;
+      const uint32_t pa = part_of(wv) * NQF + f, pb = part_of(wb) * NQF + f;
+      u32x4_t oa[NDT], ob[NDT];
+      const u32x2_t mla = __builtin_amdgcn_raw_buffer_load_b64(prs, (pa * 64 + lane) * 8, 0, kDeviceScope);
+      const u32x2_t mlb = __builtin_amdgcn_raw_buffer_load_b64(prs, (pb * 64 + lane) * 8, 0, kDeviceScope);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        oa[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pa * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+        ob[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pb * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+      }
+      combine(ok_a, mla, oa);
+      combine(ok_b, mlb, ob);
+    }
+    const float inv = l_acc > 0.f ? 1.0f / l_acc : 0.f;
+    const int k = kQRows * f + c;
+    if (k < nq) {
+      st* orow = (st*)a.out + ((int64_t)(r0 + k) * a.H + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, acc[dt], inv);
+    }
   }
   if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -324,7 +340,7 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
 // UNIFORM_PAGE: page_size >= 16, so the 16 keys of a tile share one page and
 // the tile's base address is wave-uniform (scalar), with a per-lane offset that
 // never changes.
-template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
+template <class T, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
 __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kernel(CrossArgs a) {
   typedef typename T::storage st;
   constexpr int EPC = T::EPC;
@@ -342,7 +358,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   const PlanHeader ph = *(const PlanHeader*)hdr;
   const WaveRec rec = ((const WaveRec*)(ws + a.lay.wave_rec))[w];
   const bool plan_ok =
-      (ph.magic == kPlanMagic) & (ph.bs == a.bs) & (ph.H == a.H) & (ph.n_waves == a.lay.n_waves);
+      (ph.magic == kPlanMagic) & (ph.bs == a.bs) & (ph.H == a.H) & (ph.n_waves == a.lay.n_waves) & (ph.nqf == NQF);
   const int n_tiles = plan_ok ? rec.count : 0;
   if (n_tiles <= 0) return;
 
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   int lctx = rec.ctx, lT = tiles_of(rec.ctx), lr0 = 0, lnq = 0;
   auto query_rows = [&](int b) {
     lr0 = max(0, sload_i32(a.cu_q + b));
-    lnq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - lr0, kQRows));
+    lnq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - lr0, kQRows * NQF));
   };
   query_rows(lb);
   bool exhausted = false;  // set only if the lengths changed after the plan was made
@@ -428,7 +444,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     pg_have = true;
   };
 
-  auto load_slot = [&](StreamSlot<T, D>& s, int j) {
+  auto load_slot = [&](StreamSlot<T, D, NQF>& s, int j) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
     s.flags = 0;
@@ -465,7 +481,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
               (page_ok ? (int64_t)page * a.pool.page_stride + (int64_t)(tok_c & ps_mask) * a.pool.slot_stride : 0);
         kv_last = off;
       }
-      if (flags & kStart) {  // this pair's prepared query rows ride along with its first tile
+      if (NQF == 1 && (flags & kStart)) {  // this pair's prepared query rows ride along with its first tile
         const st* qrow = (const st*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) s.q[ch] = load16(qrow + ch * 4 * EPC + g * EPC);
@@ -501,77 +517,135 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     bad_page |= __ballot(bad) != 0;
   };
 
-  // ---- compute state ----
-  u32x4_t qop[NCH];
-  f32x4_t o[NDT];
-  float m_run = kNegInf;  // running max of this lane's query row (log2 domain)
-  float l_lane = 0.f;     // this lane's share of the running denominator
+  // ---- compute state (per query fragment f) ----
+  u32x4_t qop[NQF][NCH];
+  f32x4_t o[NQF][NDT];
+  float m_run[NQF];   // running max of this lane's query row (log2 domain)
+  float l_lane[NQF];  // this lane's share of the running denominator
   int cut_b[2] = {-1, -1}, cut_h[2] = {0, 0};  // pairs this wave left partials of
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) qop[ch] = (u32x4_t){0u, 0u, 0u, 0u};
+  for (int f = 0; f < NQF; ++f) {
+    m_run[f] = kNegInf;
+    l_lane[f] = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < NCH; ++ch) qop[f][ch] = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
 
-  auto compute_slot = [&](const StreamSlot<T, D>& s) {
+  auto compute_slot = [&](const StreamSlot<T, D, NQF>& s) {
     if (s.flags & kStart) {
-      m_run = kNegInf;
-      l_lane = 0.f;
+      if (NQF == 1) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        for (int ch = 0; ch < NCH; ++ch) qop[0][ch] = s.q[ch];
+      } else {  // every fragment's prepared rows, read now
+        const st* qrow = (const st*)(ws + a.lay.q_hat) + (((int64_t)s.b * kQRows * NQF + c) * a.H + s.h) * D;
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) qop[ch] = s.q[ch];
+        for (int f = 0; f < NQF; ++f)
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch)
+            qop[f][ch] = load16(qrow + (int64_t)f * kQRows * a.H * D + ch * 4 * EPC + g * EPC);
+      }
+#pragma unroll
+      for (int f = 0; f < NQF; ++f) {
+        m_run[f] = kNegInf;
+        l_lane[f] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      }
     }
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t p[NQF];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) mma_chunk<T>(sc, s.k[ch], qop[ch]);
-    float sv[4];
-    float mx = kNegInf;
+    for (int f = 0; f < NQF; ++f) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = (s.mask >> (4 * g + i)) & 1u;
-      sv[i] = valid ? sc[i] * a.qscale_log2 : kNegInf;
-      mx = fmaxf(mx, sv[i]);
+      for (int ch = 0; ch < NCH; ++ch) mma_chunk<T>(sc, s.k[ch], qop[f][ch]);
+      float sv[4];
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = (s.mask >> (4 * g + i)) & 1u;
+        sv[i] = valid ? sc[i] * a.qscale_log2 : kNegInf;
+        mx = fmaxf(mx, sv[i]);
+      }
+      mx = wave_max_groups(mx);
+      float psum = 0.f;
+      if constexpr (NQF == 1) {
+        // the reference max follows the running max: rescale whenever a row's max moves
+        const float m_new = fmaxf(m_run[f], mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[f][i] = operand_value<T>(exp2f(sv[i] - m_use));
+          psum += p[f][i];
+        }
+        if (__ballot(m_new != m_run[f]) != 0) {
+          const float alpha = exp2f(m_run[f] - m_use);
+          l_lane[f] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[f][dt] *= alpha;
+        }
+        m_run[f] = m_new;
+      } else {
+        // Lazy rescale (several fragments' accumulators, mostly in AGPRs): the
+        // reference max moves only when a row's max exceeds it by more than
+        // kRescaleSlack (log2 units), or on its first keys, so p <= 2^slack
+        // and O, l rarely need rescaling; O / l is the same quotient.
+        const bool move = mx > m_run[f] + kRescaleSlack;  // false while both are -inf
+        if (__ballot(move) != 0) {
+          const float m_new = move ? mx : m_run[f];
+          const float alpha = (m_run[f] == kNegInf) ? 0.f : exp2f(m_run[f] - m_new);
+          if (move) {
+            l_lane[f] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[f][dt] *= alpha;
+            m_run[f] = m_new;
+          }
+        }
+        const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[f][i] = operand_value<T>(exp2f(sv[i] - m_use));
+          psum += p[f][i];
+        }
+      }
+      l_lane[f] += psum;
     }
-    mx = wave_max_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    f32x4_t p;
-    float psum = 0.f;
+    // V moved to column layout once per tile, shared by every fragment
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = operand_value<T>(exp2f(sv[i] - m_use));
-      psum += p[i];
+    for (int dt = 0; dt < NDT; ++dt) {
+      const auto vt = sel.template transpose_tile<NCH>(s.v, dt);
+#pragma unroll
+      for (int f = 0; f < NQF; ++f) mma_pv<T>(o[f][dt], vt, p[f]);
     }
-    if (__ballot(m_new != m_run) != 0) {  // some row's running max moved
-      const float alpha = exp2f(m_run - m_use);
-      l_lane *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    }
-    l_lane += psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) mma_pv<T>(o[dt], sel.template transpose_tile<NCH>(s.v, dt), p);
     if (s.flags & kEnd) {
-      const float l_row = wave_sum_groups(l_lane);
       if (s.flags & kWhole) {
-        const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
-        if (c < s.nq) {
-          st* orow = (st*)a.out + ((int64_t)(s.r0 + c) * a.H + s.h) * D;
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, o[dt], inv);
+        for (int f = 0; f < NQF; ++f) {
+          const float l_row = wave_sum_groups(l_lane[f]);
+          const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
+          const int k = kQRows * f + c;
+          if (k < s.nq) {
+            st* orow = (st*)a.out + ((int64_t)(s.r0 + k) * a.H + s.h) * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, o[f][dt], inv);
+          }
         }
       } else {
         const int slot = (s.flags & kPart1) ? 1 : 0;
-        const uint32_t part = (uint32_t)(w * 2 + slot);
         const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
         const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
-        const u32x2_t ml = {__float_as_uint(m_run), __float_as_uint(l_row)};
-        __builtin_amdgcn_raw_buffer_store_b64(ml, prs, (part * 64 + lane) * 8, 0, kDeviceScope);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[dt]), prs,
-                                                 o_base + ((part * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+        for (int f = 0; f < NQF; ++f) {
+          const float l_row = wave_sum_groups(l_lane[f]);
+          const uint32_t part = (uint32_t)((w * 2 + slot) * NQF + f);
+          const u32x2_t ml = {__float_as_uint(m_run[f]), __float_as_uint(l_row)};
+          __builtin_amdgcn_raw_buffer_store_b64(ml, prs, (part * 64 + lane) * 8, 0, kDeviceScope);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[f][dt]), prs,
+                                                   o_base + ((part * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+        }
         cut_b[slot] = s.b;
         cut_h[slot] = s.h;
       }
@@ -581,7 +655,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   // Every slot index is loaded unconditionally (indices past the range
   // re-read the last tile, a cache hit, and are fully masked with no flags),
   // so the loop body is straight-line and DEPTH-1 tiles stay in flight.
-  StreamSlot<T, D> buf[DEPTH];
+  StreamSlot<T, D, NQF> buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) load_slot(buf[d], d);
   for (int it = 0; it < n_tiles; it += DEPTH) {
@@ -602,26 +676,45 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
       if (cut_b[k] >= 0) last[k] = count_in(a, cut_b[k], cut_h[k]);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (last[k]) merge_pair<T, D>(a, cut_b[k], cut_h[k]);
+      if (last[k]) merge_pair<T, D, NQF>(a, cut_b[k], cut_h[k]);
   }
 }
 
-template <class T, int D, int DEPTH, bool UNIFORM_PAGE>
+template <class T, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
 hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.bs * a.H;
-  hipLaunchKernelGGL((q_prologue_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((q_prologue_kernel<T, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
-  hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH, UNIFORM_PAGE>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH, UNIFORM_PAGE, NQF>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <class T, int D, int DEPTH>
+template <class T, int D, int DEPTH, int NQF>
 hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
   // page_size >= 16 keeps each 16-key tile inside one page
-  if (a.log2ps >= 4) return launch_cross_paged<T, D, DEPTH, true>(a, s);
-  return launch_cross_paged<T, D, DEPTH, false>(a, s);
+  if (a.log2ps >= 4) return launch_cross_paged<T, D, DEPTH, true, NQF>(a, s);
+  return launch_cross_paged<T, D, DEPTH, false, NQF>(a, s);
+}
+
+#ifndef FM_CROSS_DEPTH_Q2
+#define FM_CROSS_DEPTH_Q2 3  // tiles in flight with two query fragments per request (bf16)
+#endif
+#ifndef FM_CROSS_DEPTH_Q4
+#define FM_CROSS_DEPTH_Q4 2  // ... with four (their accumulators fill the AGPRs)
+#endif
+
+template <class T, int D, int DEPTH>
+hipError_t launch_cross_frags(const CrossArgs& a, hipStream_t s) {
+  // Several candidate blocks per request hold more state per tile; fp32 rows,
+  // whose tiles take twice the registers, keep one tile in flight.
+  constexpr bool kF32 = sizeof(typename T::storage) == 4;
+  switch (a.lay.nqf) {
+    case 1: return launch_cross_typed<T, D, DEPTH, 1>(a, s);
+    case 2: return launch_cross_typed<T, D, kF32 ? 1 : FM_CROSS_DEPTH_Q2, 2>(a, s);
+    default: return launch_cross_typed<T, D, kF32 ? 1 : FM_CROSS_DEPTH_Q4, 4>(a, s);
+  }
 }
 
 }  // namespace
@@ -633,10 +726,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStream_t s) {
   if (dtype == 1)
-    return Dh == 128 ? launch_cross_typed<Bf16, 128, FM_CROSS_DEPTH_BF16>(a, s)
-                     : launch_cross_typed<Bf16, 64, FM_CROSS_DEPTH_BF16>(a, s);
-  return Dh == 128 ? launch_cross_typed<F32, 128, FM_CROSS_DEPTH_F32>(a, s)
-                   : launch_cross_typed<F32, 64, FM_CROSS_DEPTH_F32>(a, s);
+    return Dh == 128 ? launch_cross_frags<Bf16, 128, FM_CROSS_DEPTH_BF16>(a, s)
+                     : launch_cross_frags<Bf16, 64, FM_CROSS_DEPTH_BF16>(a, s);
+  return Dh == 128 ? launch_cross_frags<F32, 128, FM_CROSS_DEPTH_F32>(a, s)
+                   : launch_cross_frags<F32, 64, FM_CROSS_DEPTH_F32>(a, s);
 }
 
 }  // namespace fm

@@ -12,7 +12,16 @@
 namespace fm {
 
 constexpr int kMaxLayers = 16;
-constexpr int kQRows = 16;          // query rows per request handled by one unit
+constexpr int kQRows = 16;          // query rows of one MFMA fragment (one draft block)
+constexpr int kMaxQFrags = 4;       // fragments per request: up to 64 query rows (4 candidate blocks)
+
+// Fragments the plan and the kernel use for at most max_q query rows per request
+// (1, 2 or 4; 0 when max_q is out of range).
+inline int q_frags(int max_q) {
+  if (max_q < 0 || max_q > kQRows * kMaxQFrags) return 0;
+  const int f = (max_q + kQRows - 1) / kQRows;
+  return f <= 1 ? 1 : (f <= 2 ? 2 : 4);
+}
 constexpr int32_t kPlanMagic = 0x464d504c;   // "FMPL"
 constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
 #ifndef FM_CROSS_WAVES_PER_SIMD
@@ -49,7 +58,7 @@ struct PlanHeader {
   int32_t n_waves;
   int32_t bs;
   int32_t H;
-  int32_t reserved;
+  int32_t nqf;        // query fragments per request
   int64_t total_tiles;
 };
 
@@ -69,28 +78,30 @@ struct PairRec {
 };
 
 struct PlanLayout {
-  size_t q_hat;       // [bs][16][H][Dh] of the call's type: normed, rotated queries (0 past a request's rows)
+  size_t q_hat;       // [bs][16 nqf][H][Dh] of the call's type: normed, rotated queries (0 past a request's rows)
   size_t pair_off;    // int64 [bs + 1]: first tile of request b's pairs in the stream
   size_t wave_rec;    // WaveRec [n_waves]
   size_t pair_rec;    // PairRec [bs * H]
   size_t merge_cnt;   // int32 [n_waves]: partials counted in for the cut pair whose first wave is w
-  size_t partial_ml;  // float2 [n_waves][2][64 lanes]: running max (log2) and denominator of the lane's row
-  size_t partial_o;   // f32x4 [n_waves][2][Dh/16][64 lanes]: unnormalized outputs in MFMA fragment order
+  size_t partial_ml;  // float2 [n_waves][2][nqf][64 lanes]: running max (log2) and denominator of the lane's row
+  size_t partial_o;   // f32x4 [n_waves][2][nqf][Dh/16][64 lanes]: unnormalized outputs in MFMA fragment order
   size_t total;
   int n_waves;
+  int nqf;
 };
 
-inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves) {
+inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves, int nqf) {
   PlanLayout p;
   p.n_waves = n_waves;
+  p.nqf = nqf;
   size_t off = 256;
-  p.q_hat = off;      off = align256(off + (size_t)bs * kQRows * H * Dh * 4);
+  p.q_hat = off;      off = align256(off + (size_t)bs * kQRows * nqf * H * Dh * 4);
   p.pair_off = off;   off = align256(off + (size_t)(bs + 1) * 8);
   p.wave_rec = off;   off = align256(off + (size_t)n_waves * sizeof(WaveRec));
   p.pair_rec = off;   off = align256(off + (size_t)bs * H * sizeof(PairRec));
   p.merge_cnt = off;  off = align256(off + (size_t)n_waves * 4);
-  p.partial_ml = off; off = align256(off + (size_t)n_waves * 2 * 64 * 8);
-  p.partial_o = off;  off = align256(off + (size_t)n_waves * 2 * kQRows * Dh * 4);
+  p.partial_ml = off; off = align256(off + (size_t)n_waves * 2 * nqf * 64 * 8);
+  p.partial_o = off;  off = align256(off + (size_t)n_waves * 2 * nqf * kQRows * Dh * 4);
   p.total = off;
   return p;
 }

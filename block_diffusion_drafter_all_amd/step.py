@@ -32,14 +32,15 @@ class StepBuffers:
 
 def allocate(w: Workload) -> StepBuffers:
     dev = w.ctx_lens.device
-    cross_ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.K), dtype=torch.uint8, device=dev)
+    cross_ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.max_q), dtype=torch.uint8,
+                           device=dev)
     write_ws = out_slots = None
     if w.write is not None:
         n_rows = w.write.x.shape[0]
         write_ws = torch.empty(B.fm_write_context_kv_workspace_size(n_rows), dtype=torch.uint8, device=dev)
         out_slots = torch.empty(n_rows, dtype=torch.int32, device=dev)
     cross_out = [torch.empty_like(q) for q in w.q]
-    self_out = [torch.empty((w.bs, w.K, w.H, w.Dh), dtype=w.dtype, device=dev) for _ in range(w.L)]
+    self_out = [torch.empty((w.bs * w.n_cand, w.K, w.H, w.Dh), dtype=w.dtype, device=dev) for _ in range(w.L)]
     return StepBuffers(cross_ws, write_ws, cross_out, self_out, out_slots)
 
 
@@ -51,14 +52,14 @@ def write_context(w: Workload, buf: StepBuffers) -> None:
 
 
 def plan(w: Workload, buf: StepBuffers) -> None:
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.K)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.max_q)
 
 
 def layer(w: Workload, buf: StepBuffers, l: int) -> None:
-    B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.ctx_lens, w.softmax_scale,
+    B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.block_ctx_lens, w.softmax_scale,
                               w.theta, w.eps, out=buf.self_out[l])
     B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens, w.cu_seqlens_q,
-                               w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=buf.cross_out[l])
+                               w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=buf.cross_out[l], max_q=w.max_q)
 
 
 def run_step(w: Workload, buf: StepBuffers) -> None:

@@ -58,9 +58,21 @@ class Workload:
     self_q_norm_w: list                # L x (Dh,) fp32
     self_k_norm_w: list                # L x (Dh,) fp32
     write: WriteInputs | None = None
+    n_cand: int = 1                    # candidate blocks per request (tree drafting)
     eps: float = EPS
     theta: float = THETA
     meta: dict = field(default_factory=dict)
+
+    @property
+    def max_q(self) -> int:
+        """Query rows per request: K per candidate block."""
+        return self.K * self.n_cand
+
+    @property
+    def block_ctx_lens(self) -> torch.Tensor:
+        """Context length of each self-attention block (every candidate of a
+        request sits at the same positions)."""
+        return self.ctx_lens if self.n_cand == 1 else self.ctx_lens.repeat_interleave(self.n_cand)
 
     @property
     def softmax_scale(self) -> float:
@@ -119,7 +131,7 @@ def _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K, q_scale=1.0):
 
 
 def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_major", scale_down=None,
-                  q_scale=1.0, seed=None) -> Workload:
+                  q_scale=1.0, seed=None, n_cand=1) -> Workload:
     """The seeded inputs of one workload.
 
     1  tiny fp32 full step: 1 request, ctx 64, 1 layer, 4 x 64, page 16,
@@ -134,6 +146,9 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
 
     ``scale_down`` (dict) overrides bs / length bounds for small parity runs;
     ``q_scale`` multiplies the queries (a "peaky" softmax variant).
+    ``n_cand`` candidate blocks per request (tree drafting): each request's
+    cross-attention query holds ``n_cand * K`` rows, candidate-major, and the
+    self-attention runs over ``bs * n_cand`` blocks.
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + workload_id if seed is None else seed)
@@ -199,8 +214,8 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
         pt = _page_table(pages_needed, width, n_pages, gen, device)
 
     pools = [_pool_tensors(n_pages, ps, H, Dh, dtype, device, gen, layout) for _ in range(L)]
-    cu_q = torch.arange(0, (bs + 1) * K, K, dtype=torch.int32, device=device)
-    q, qkv = _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K, q_scale)
+    cu_q = torch.arange(0, (bs + 1) * K * n_cand, K * n_cand, dtype=torch.int32, device=device)
+    q, qkv = _attention_inputs(bs * n_cand, L, H, Dh, dtype, device, gen, cu_q, K, q_scale)
 
     if workload_id == 1:
         # the write fills the whole context 0..63: x = [k | v] with W = I
@@ -230,4 +245,4 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     return Workload(name=names[workload_id], workload_id=workload_id, bs=bs, K=K, L=L, H=H, Dh=Dh, page_size=ps,
                     dtype=dtype, ctx_lens=ctx.contiguous(), cu_seqlens_q=cu_q, page_table=pt, pools=pools, q=q,
                     qkv=qkv, q_norm_w=q_norm_w, self_q_norm_w=self_q, self_k_norm_w=self_k, write=write,
-                    meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale))
+                    n_cand=n_cand, meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale))

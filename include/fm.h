@@ -130,7 +130,7 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 /* ------------------------------------------------------ cross-attention -- */
 
 /* Workspace bytes for a cross-attention plan of bs requests with head dim Dh
- * and at most max_q query rows per request (max_q <= 16) on the current
+ * and at most max_q query rows per request (max_q <= 64) on the current
  * device; 0 for an unsupported shape.  One workspace serves every layer's
  * call of a step. */
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q);
@@ -145,7 +145,8 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
  * wavefront of the attention kernel, so every wave moves the same number of
  * K/V bytes whatever the mix of context lengths.
  * ctx_lens  DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
- * max_q     host bound on query rows per request (<= 16), checked here.
+ * max_q     host bound on query rows per request: one draft block (16) or up
+ *           to four candidate blocks side by side (<= 64), checked here.
  * ws        DEVICE, fm_cross_attention_workspace_size(bs, H, Dh, max_q) bytes,
  *           256-byte aligned.
  */
@@ -158,7 +159,10 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  * ``FlashMapAttention.forward`` with the ``draft`` positions).
  *
  * For request b, query row r in [cu_seqlens_q[b], cu_seqlens_q[b+1]) is draft
- * slot k = r - cu_seqlens_q[b] at position ctx_lens[b] + k:
+ * slot k = (r - cu_seqlens_q[b]) mod 16 at position ctx_lens[b] + k.  One
+ * draft block has 16 rows; tree drafting puts a request's candidate blocks
+ * side by side on the query axis, candidate-major, so that its context is
+ * read once for all of them (sglang/model.py ``forward``, ``n_cand``):
  *   q^ = RoPE(RMSNorm(q[r,h,:]; q_norm_w, eps), ctx_lens[b] + k)
  *   out[r,h,:] = sum_t softmax_t(softmax_scale * q^.K_t) V_t,  t = 0..ctx_lens[b]-1
  * non-causal, one KV head per query head; keys/values are read through the
@@ -175,13 +179,16 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  *             access leaves the buffers, and bit 1 of the error word is set
  *             when a wave's share runs past the last tile; plan again.
  * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
- *             [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most 16 of them.
+ *             [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most max_q of them.
+ * max_q       host bound on query rows per request (<= 64), the value the plan
+ *             in ``ws`` was made with (a plan made with another value leaves
+ *             ``out`` untouched); rows past it are not computed.
  * Dh in {64, 128}; page_size a power of two in [1, 4096].
  */
 int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
                              const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride,
                              int32_t page_size, const int32_t* ctx_lens,
-                             const int32_t* cu_seqlens_q, int32_t bs, int32_t H, int32_t Dh,
+                             const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs, int32_t H, int32_t Dh,
                              float softmax_scale, float rope_theta, float eps, void* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -47,7 +47,12 @@ def test_workspace_sizes(lib):
     assert small % 256 == 0 and big % 256 == 0
     assert lib.fm_cross_attention_workspace_size(4, 0, 128, 16) == 0
     assert lib.fm_cross_attention_workspace_size(4, 4, 96, 16) == 0
-    assert lib.fm_cross_attention_workspace_size(4, 4, 128, 17) == 0
+    assert lib.fm_cross_attention_workspace_size(4, 4, 128, 65) == 0
+    # candidate blocks: 1, 2 or 4 query fragments per request
+    one, two, four = (lib.fm_cross_attention_workspace_size(64, 32, 128, m) for m in (16, 32, 64))
+    assert big == one < two < four
+    assert lib.fm_cross_attention_workspace_size(64, 32, 128, 17) == two
+    assert lib.fm_cross_attention_workspace_size(64, 32, 128, 48) == four
     assert lib.fm_write_context_kv_workspace_size(1152) >= 256 + 4 * 4 * 1152
 
 
@@ -60,19 +65,21 @@ def _pool(num_pages=4):
 
 def _cross(lib, **over):
     args = dict(q=FAKE, dt=B.FM_BF16, total_q=16, qn=FAKE, pool=_pool(), pt=FAKE, pt_stride=4, ps=16, ctx=FAKE,
-                cu=FAKE, bs=1, H=4, Dh=64, scale=0.125, theta=1e6, eps=1e-6, out=FAKE, ws=FAKE,
+                cu=FAKE, max_q=16, bs=1, H=4, Dh=64, scale=0.125, theta=1e6, eps=1e-6, out=FAKE, ws=FAKE,
                 ws_bytes=1 << 30)
     args.update(over)
     pool = args["pool"]
     return lib.fm_paged_cross_attention(args["q"], args["dt"], args["total_q"], args["qn"],
                                         ctypes.byref(pool) if pool is not None else None,
                                         args["pt"], args["pt_stride"], args["ps"], args["ctx"], args["cu"],
-                                        args["bs"], args["H"], args["Dh"], args["scale"], args["theta"],
+                                        args["max_q"], args["bs"], args["H"], args["Dh"], args["scale"], args["theta"],
                                         args["eps"], args["out"], args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("over,status,needle", [
     (dict(q=None), B.FM_E_INVALID, "null"),
+    (dict(max_q=65), B.FM_E_UNSUPPORTED, "max_q"),
+    (dict(max_q=-1), B.FM_E_INVALID, "max_q"),
     (dict(pool=None), B.FM_E_INVALID, "null"),
     (dict(Dh=96), B.FM_E_UNSUPPORTED, "head_dim"),
     (dict(dt=7), B.FM_E_UNSUPPORTED, "dtype"),
@@ -100,7 +107,7 @@ def test_cross_attention_empty_is_noop(lib):
 
 
 def test_plan_rejects(lib):
-    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 17, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 65, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
     assert "max_q" in B.fm_last_error()
     assert lib.fm_plan_cross_attention(None, 4, 32, 128, 16, FAKE, 1 << 30, None) == B.FM_E_INVALID
     assert lib.fm_plan_cross_attention(FAKE, -1, 32, 128, 16, FAKE, 1 << 30, None) == B.FM_E_INVALID

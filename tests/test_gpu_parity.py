@@ -35,7 +35,7 @@ def _oracle_self(w, layer, blocks=None):
     blocks = range(w.bs) if blocks is None else blocks
     qkv = to_np(w.qkv[layer][list(blocks)])
     return O.block_self_attention(qkv, to_np(w.self_q_norm_w[layer]), to_np(w.self_k_norm_w[layer]),
-                                  w.ctx_lens.cpu().numpy()[list(blocks)], w.softmax_scale, w.theta, w.eps)
+                                  w.block_ctx_lens.cpu().numpy()[list(blocks)], w.softmax_scale, w.theta, w.eps)
 
 
 def _check_attention(w, buf, reqs, layers=None, self_blocks=None, pools=None):
@@ -121,6 +121,46 @@ def test_config2_all_rows(variant):
     _check_attention(w, buf, list(range(w.bs)))
 
 
+@pytest.mark.parametrize("n_cand", [2, 4])
+def test_candidate_blocks_share_one_context_read(n_cand):
+    # Tree drafting: each request's n_cand candidate blocks (16 rows each) sit
+    # side by side on the query axis and attend to one read of its context;
+    # config 2's shape, random norm weights, all rows against the oracle.
+    log(f"config 2 with {n_cand} candidate blocks per request")
+    w = make_workload(2, weights="random", n_cand=n_cand)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)), self_blocks=range(w.bs * n_cand))
+
+
+def test_candidate_blocks_ragged_rows_and_empty_context():
+    # max_q 64 (four fragments) with 0, 1, 16, 17, 40 and 64 rows per request,
+    # including an empty context and a context shorter than one tile.
+    log("candidate blocks: ragged rows, empty context")
+    ctx = [300, 0, 5, 1000, 77, 2100]
+    nq = [40, 17, 64, 1, 0, 16]
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=1, H=3), n_cand=4)
+    dev = w.ctx_lens.device
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(torch.bfloat16)
+    w.q[0], w.cu_seqlens_q = q, cu
+    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 64), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=64)
+    out = torch.full_like(q, float("nan"))
+    B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu, w.softmax_scale,
+                               w.theta, w.eps, ws, out=out, max_q=64)
+    torch.cuda.synchronize()
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows, q=q)
+    compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross 4 fragments ragged")
+    assert torch.all(out[cu[1]:cu[2]] == 0), "an empty context must give exactly zero"
+    assert ws_error_word(ws) == 0
+
+
 @pytest.mark.parametrize("ps", [1, 8, 32, 64])
 def test_page_sizes_and_ragged_lengths(ps):
     log(f"page size {ps}")
@@ -171,8 +211,9 @@ def test_self_attention_small_blocks_fp32_dh128():
         compare(out, ref, f"self K={K} {dtype}")
 
 
-def test_cross_attention_deterministic():
-    w = make_workload(2, weights="random")
+@pytest.mark.parametrize("n_cand", [1, 4])
+def test_cross_attention_deterministic(n_cand):
+    w = make_workload(2, weights="random", n_cand=n_cand)
     buf = S.allocate(w)
     S.run_step(w, buf)
     first = buf.cross_out[0].clone()
