@@ -17,7 +17,9 @@ Sources (the flashmap 0.1.0 wheel pages and the TokenSpeed DFlash page):
     all layers' context K/V weights, k-norm, RoPE, write that skips the
     uncommitted verify columns), ``load_weights`` (the all-layer weight is the
     concatenation ``[k_0; v_0; k_1; v_1; ...]``), ``forward`` (the anchor is
-    written at its own position; ``cache_seqlens = seq_lens + 1``).
+    written at its own position; ``cache_seqlens = seq_lens + 1``),
+    ``_paged_cross_attention_fp8`` and ``kv_norm_rope_write_fp8`` (the fp8 KV
+    pool).
   * vllm/model.py: ``paged_cross_attention`` (cu_seqlens_q, seqused_k,
     block_table, softmax_scale = head_dim ** -0.5, non-causal), ``_prologue``
     (``seqused_k`` is 0 for empty rows), ``cache_layout`` (page, head, slot
@@ -28,8 +30,10 @@ fix.  (1) The rotary angle is a float32 product of a float32 position and a
 float32 inverse frequency (``rope_tables``: ``positions.float() * inv_freq``).
 The inverse frequency itself is read as the float32 value nearest to
 ``theta ** (-2i / head_dim)``.  (2) A value stored into the KV pool takes the
-pool's storage type (bf16 or fp32), because the pool is the interface between
-the write and the attention.  Everything else, the GEMM, the norms, the
+pool's storage type (bf16, fp32 or e4m3 at scale 1), because the pool is the
+interface between the write and the attention.  (3) Over an e4m3 pool the
+query is itself cast to e4m3 under a per-(request, head) scale
+(``_paged_cross_attention_fp8``).  Everything else, the GEMM, the norms, the
 rotation, the softmax and the weighted sums, is exact up to float64 rounding.
 
 Readings of points the pages leave open are listed in the design notes of the
@@ -47,7 +51,9 @@ __all__ = [
     "apply_rope",
     "rms_norm",
     "round_to_bfloat16",
+    "round_to_e4m3",
     "round_to_storage",
+    "quantize_query_e4m3",
     "attention",
     "context_slot",
     "live_rows",
@@ -123,10 +129,39 @@ def round_to_bfloat16(x: np.ndarray) -> np.ndarray:
     return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the OCP float8 e4m3 ("e4m3fn") grid, returned as
+    float64: 3 mantissa bits, exponent bias 7, subnormals down to 2**-9, largest
+    finite 448.  Nearest, ties to even; magnitudes past 448 saturate to 448 (the
+    format has no infinity, and a pool entry must stay finite)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)                       # a in [2**(e-1), 2**e)
+    # spacing of the grid at a: 2**(e-1-3) for normals (e-1 >= -6), 2**-9 below
+    step = np.where(e - 1 >= -6, np.ldexp(1.0, e - 4), 2.0 ** -9)
+    r = np.minimum(np.rint(a / step) * step, 448.0)
+    return np.copysign(r, x)
+
+
+def quantize_query_e4m3(q_hat: np.ndarray):
+    """The fp8 pool's query: one scale per (request, head), the largest
+    magnitude over the request's rows and the head's channels divided by 448
+    (at least 1e-12 / 448), and the e4m3 query ``q_hat / scale`` (the sglang
+    model's ``_paged_cross_attention_fp8``: ``q_scale = amax / 448``,
+    ``query8 = query / q_scale``).  ``q_hat (rows, D)`` of one (request, head);
+    returns ``(q8, scale)`` with ``q8 * scale`` the query the attention uses."""
+    q_hat = np.asarray(q_hat, dtype=np.float64)
+    scale = max(float(np.max(np.abs(q_hat), initial=0.0)), 1e-12) / 448.0
+    return round_to_e4m3(q_hat / scale), scale
+
+
 def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
-    """The value a pool of storage type ``dtype`` ("bf16" or "f32") holds."""
+    """The value a pool of storage type ``dtype`` ("bf16", "f32" or "e4m3")
+    holds (an e4m3 pool is written with scale 1)."""
     if dtype == "bf16":
         return round_to_bfloat16(x)
+    if dtype == "e4m3":
+        return round_to_e4m3(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     raise ValueError(f"unknown storage type {dtype!r}")
@@ -242,7 +277,7 @@ def scatter_into_pool(pools_k, pools_v, slots, keys, values, page_size, dtype):
 
 def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
                           cu_seqlens_q, page_size, scale, theta, eps,
-                          requests=None, heads=None, block_size=16):
+                          requests=None, heads=None, block_size=16, kv_e4m3=False):
     """Cross-attention of each request's draft rows onto its paged context.
 
     Row ``r`` of request ``b`` (``cu_seqlens_q[b] <= r < cu_seqlens_q[b+1]``)
@@ -255,6 +290,10 @@ def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
     RMS-normed with ``q_norm_w`` and rotated there (``rms_norm_rope``), then
     attends, non-causally, to the keys/values at logical positions
     ``0 .. ctx_lens[b] - 1`` read through the page table.
+
+    ``kv_e4m3``: the pool holds e4m3 values (written with scale 1) and the
+    query is quantized to e4m3 per (request, head) first
+    (``quantize_query_e4m3``); the scores use the descaled query.
 
     ``pool_k, pool_v``: logical ``(pages, page_size, H, D)`` arrays.  Returns
     float64 ``(total_q, H, D)``; rows of requests not in ``requests`` and heads
@@ -279,6 +318,9 @@ def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
         for h in hs:
             qh = rms_norm(q[r0:r1, h], q_norm_w, eps)
             qh = apply_rope(qh, positions, theta)
+            if kv_e4m3:
+                q8, qs = quantize_query_e4m3(qh)
+                qh = q8 * qs
             out[r0:r1, h] = attention(qh, k_b[:, h], v_b[:, h], scale)
     return out
 

@@ -115,6 +115,37 @@ def test_round_to_bfloat16_matches_torch(rng):
 # -------------------------------------------------------------- attention
 
 
+def test_round_to_e4m3_matches_torch_and_saturates(rng):
+    # torch's float8_e4m3fn conversion is nearest-even on the same grid; it maps
+    # magnitudes past 464 to NaN, where the pool saturates to 448 instead.
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1.0, 30.0)])
+    x = np.concatenate([x[np.abs(x) <= 464.0], [0.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -6,
+                                                  448.0, 464.0, -464.0, 1.0625, 1.1875, -0.99]])
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_e4m3(x), ref)
+    np.testing.assert_array_equal(O.round_to_e4m3(np.array([470.0, -600.0, 1e9])), [448.0, -448.0, 448.0])
+    # all 256 codes: 253 distinct finite values (0x7F / 0xFF are NaN, +0 and -0 coincide), each a
+    # fixed point; a midpoint between neighbours goes to the code whose mantissa is even
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    grid = np.unique(codes[np.isfinite(codes)])
+    assert len(grid) == 253 and grid[0] == -448.0 and grid[-1] == 448.0
+    np.testing.assert_array_equal(O.round_to_e4m3(grid), grid)
+    pos = grid[grid >= 0]
+    mids = (pos[:-1] + pos[1:]) / 2
+    even = np.where(np.arange(len(mids)) % 2 == 0, pos[:-1], pos[1:])  # code index parity = mantissa parity
+    np.testing.assert_array_equal(O.round_to_e4m3(mids), even)
+
+
+def test_quantize_query_e4m3_scale_and_error(rng):
+    q = rng.standard_normal((16, 128)) * 3.0
+    q8, s = O.quantize_query_e4m3(q)
+    assert np.max(np.abs(q8)) == 448.0                  # the largest magnitude lands on 448 exactly
+    assert s == np.max(np.abs(q)) / 448.0
+    big = np.abs(q) >= 2.0 ** -6 * s                    # normal range: relative error <= 2^-4
+    assert np.all(np.abs(q8 * s - q)[big] <= 2.0 ** -4 * np.abs(q)[big] + 1e-15)
+    np.testing.assert_array_equal(O.quantize_query_e4m3(np.zeros((4, 8)))[0], 0.0)
+
+
 def test_attention_matches_sdpa(rng):
     for n, t, d in ((16, 1, 64), (16, 37, 128), (3, 500, 64)):
         q, k, v = rng.standard_normal((n, d)), rng.standard_normal((t, d)), rng.standard_normal((t, d))
@@ -194,6 +225,46 @@ def test_paged_cross_attention_equals_dense(rng):
             vt = torch.from_numpy(c["dense_v"][b][:, h])
             ref = F.scaled_dot_product_attention(torch.from_numpy(qh)[None], kt[None], vt[None], scale=scale)[0]
             np.testing.assert_allclose(out[r0:r1, h], ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_paged_cross_attention_e4m3_query_against_torch_fp8(rng):
+    # fp8 pool (sglang model ``_paged_cross_attention_fp8``): e4m3 keys/values,
+    # query scaled by amax/448 over the request's rows and the head's channels,
+    # cast to e4m3, then descaled in the scores.  The cast here is torch's.
+    c = _paged_case(rng, ctx=[40, 1, 0, 130], nq=[32, 16, 16, 7])
+    pk, pv = O.round_to_e4m3(c["pk"] * 4.0), O.round_to_e4m3(c["pv"] * 4.0)
+    theta, eps, scale = 1e6, 1e-6, c["D"] ** -0.5
+    args = (c["pt"], c["ctx"], c["cu"], c["ps"], scale, theta, eps)
+    out = O.paged_cross_attention(c["q"], c["w"], pk, pv, *args, kv_e4m3=True)
+    plain = O.paged_cross_attention(c["q"], c["w"], pk, pv, *args)
+    per_row_gap = 0.0
+    for b, n in enumerate(c["ctx"]):
+        r0, r1 = c["cu"][b], c["cu"][b + 1]
+        pos = n + np.arange(r1 - r0) % 16
+        for h in range(c["H"]):
+            if n == 0:
+                np.testing.assert_array_equal(out[r0:r1, h], 0.0)
+                continue
+            qh = torch.from_numpy(O.apply_rope(O.rms_norm(c["q"][r0:r1, h], c["w"], eps), pos, theta))
+            qs = qh.abs().max() / 448.0
+            q8 = (qh / qs).to(torch.float8_e4m3fn).to(torch.float64) * qs
+            dk = torch.from_numpy(O.round_to_e4m3(c["dense_k"][b][:, h] * 4.0))
+            dv = torch.from_numpy(O.round_to_e4m3(c["dense_v"][b][:, h] * 4.0))
+            ref = F.scaled_dot_product_attention(q8[None], dk[None], dv[None], scale=scale)[0]
+            np.testing.assert_allclose(out[r0:r1, h], ref.numpy(), rtol=1e-11, atol=1e-12)
+            # quantizing each row on its own scale gives other values
+            q8r = (qh / (qh.abs().amax(1, keepdim=True) / 448.0)).to(torch.float8_e4m3fn).to(torch.float64) \
+                * (qh.abs().amax(1, keepdim=True) / 448.0)
+            alt = F.scaled_dot_product_attention(q8r[None], dk[None], dv[None], scale=scale)[0]
+            per_row_gap = max(per_row_gap, float(np.abs(alt.numpy() - out[r0:r1, h]).max()))
+            # within the quantization bound of the unquantized query: |dq| <= 2^-4 |q| + 2^-10 qs
+            # per channel, |d score| <= M, and every output moves by at most (e^{2M} - 1) max|v|
+            dq = (2.0 ** -4) * qh.abs() + (2.0 ** -10) * qs
+            M = scale * float((dq @ dk.abs().T).max())
+            bound = (np.exp(2 * M) - 1) * float(dv.abs().max())
+            assert np.abs(out[r0:r1, h] - plain[r0:r1, h]).max() <= bound
+    assert per_row_gap > 1e-6
+    assert np.nanmax(np.abs(out - plain)) > 1e-6
 
 
 def test_paged_cross_attention_page_permutation_invariant(rng):
