@@ -6,7 +6,8 @@ skips uncommitted columns), the cross-attention plan, and for every layer the
 block self-attention and the paged cross-attention.  The default workload is
 the full draft step: 64 requests, context lengths U[1024, 8192], block 16,
 5 layers, 32 heads x 128, page size 16, bf16 pool; each request commits
-U{1..17} verify columns plus its anchor through the write.
+U{1..17} verify columns plus its anchor through the write.  ``--kv-fp8``
+runs the same step over an e4m3 pool (bf16 activations).
 
 Prints ONE JSON line (see the fields below).  Inputs are resident in HBM
 before timing starts; timing brackets exactly --steps steps with device
@@ -17,9 +18,11 @@ cross-attention launch from rocprofv3's FETCH_SIZE / WRITE_SIZE counters):
   --copy-calibration      one plain 1 GiB device-to-device copy, the known-size
                           kernel the counters are scaled by;
   --write-traffic DIRS    (CPU only) turns four counter-collection outputs
-                          into profiles/cross_attention_traffic.json, keyed by
-                          a hash of the kernel sources: the bench reports the
-                          traffic only while the sources still match.
+                          into an entry of profiles/cross_attention_traffic.json
+                          for the workload the other options name, keyed by a
+                          hash of the kernel sources: the bench reports the
+                          traffic only for that workload and only while the
+                          sources still match.
 """
 
 from __future__ import annotations
@@ -59,6 +62,8 @@ def parse():
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"])
     ap.add_argument("--candidates", type=int, default=1, choices=[1, 2, 4],
                     help="candidate blocks per request (tree drafting): 16 query rows each, one context read")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="e4m3 KV pool (written at scale 1; queries quantized per request and head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
@@ -95,7 +100,22 @@ def _kib_per_dispatch(rows, match):
     return (sum(per.values()) / len(per), len(per)) if per else (0.0, 0)
 
 
-def write_traffic(dirs, command: str) -> None:
+def workload_key(args) -> str:
+    """Names the workload a traffic record was measured on."""
+    return (f"config={args.config},layout={args.layout},candidates={args.candidates},"
+            f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}")
+
+
+def _traffic_records() -> dict:
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    return data.get("records", {}) if isinstance(data, dict) else {}
+
+
+def write_traffic(dirs, command: str, key: str) -> None:
     cross_fetch, cross_write, copy_fetch, copy_write = (_counter_rows(d) for d in dirs)
     # the calibration copy: the largest copy dispatch of the run
     def largest(rows):
@@ -106,7 +126,7 @@ def write_traffic(dirs, command: str) -> None:
         return max(best.values())
     fetch_scale = COPY_BYTES / (largest(copy_fetch) * 1024.0)
     write_scale = COPY_BYTES / (largest(copy_write) * 1024.0)
-    rec = {"sources_sha256": kernel_sources_hash(), "kernels": {}, "fetch_scale": fetch_scale,
+    rec = {"workload": key, "sources_sha256": kernel_sources_hash(), "kernels": {}, "fetch_scale": fetch_scale,
            "write_scale": write_scale, "calibration": f"plain {COPY_BYTES} B device copy (bench.py --copy-calibration)",
            "command": command}
     fetch = write = 0.0
@@ -119,21 +139,20 @@ def write_traffic(dirs, command: str) -> None:
     rec["fetch_bytes_per_launch"] = fetch
     rec["write_bytes_per_launch"] = write
     rec["traffic_bytes_per_launch"] = fetch + write
+    records = _traffic_records()
+    records[key] = rec
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump({"records": records}, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(rec))
 
 
-def measured_traffic():
-    """HBM bytes per cross-attention launch from the committed counter record,
-    or None when there is none or the kernel sources changed since it was taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("sources_sha256") != kernel_sources_hash():
+def measured_traffic(key: str):
+    """HBM bytes per cross-attention launch from the committed counter record
+    of workload ``key``, or None when there is none or the kernel sources
+    changed since it was taken."""
+    rec = _traffic_records().get(key)
+    if rec is None or rec.get("sources_sha256") != kernel_sources_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -158,9 +177,10 @@ def cross_bytes(w) -> int:
     """Algorithmic bytes of one cross-attention call: every context key and
     value read once, the queries read and the outputs written once, the page
     ids, lengths, cu_seqlens and the norm weight."""
-    s = 2 if w.dtype.itemsize == 2 else 4
+    s = w.dtype.itemsize          # queries and outputs
+    skv = w.pool_dtype.itemsize   # pool elements
     ctx = w.ctx_lens.cpu().tolist()
-    kv = sum(ctx) * w.H * w.Dh * 2 * s
+    kv = sum(ctx) * w.H * w.Dh * 2 * skv
     qo = 2 * w.total_q * w.H * w.Dh * s
     pages = 4 * sum(math.ceil(c / w.page_size) for c in ctx)
     return kv + qo + pages + 4 * (2 * w.bs + 1) + 4 * w.Dh
@@ -192,7 +212,8 @@ def write_flops_bytes(w):
     s = wr.x.element_size()
     n = w.L * 2 * w.H * w.Dh
     flops = 2 * m * d_in * n
-    nbytes = s * (n * d_in + m * d_in) + m * kv_bytes_per_row(w.L, w.H, w.Dh, s) + 4 * w.L * w.Dh + 12 * n_rows
+    nbytes = (s * (n * d_in + m * d_in) + m * kv_bytes_per_row(w.L, w.H, w.Dh, w.pool_dtype.itemsize)
+              + 4 * w.L * w.Dh + 12 * n_rows)
     return flops, nbytes
 
 
@@ -208,6 +229,7 @@ def describe(w) -> dict:
         "requests": w.bs, "block_size": w.K, "candidate_blocks": w.n_cand, "layers": w.L, "heads": w.H,
         "head_dim": w.Dh,
         "page_size": w.page_size, "total_context_tokens": int(sum(ctx)), "pool_layout": w.meta["layout"],
+        "kv_pool": {1: "e4m3", 2: "bf16", 4: "fp32"}[w.pool_dtype.itemsize],
     }
     if w.write is not None:
         d["write_rows"] = int(w.write.x.shape[0])
@@ -277,7 +299,8 @@ def cpu_baseline(w, n_req: int):
             for i, b in enumerate(reqs):
                 pt = rows[i][None, :]
                 O.paged_cross_attention(q[l][cu[b]:cu[b + 1]], host(w.q_norm_w[l]), pk, pv, pt, [ctx[b]],
-                                        [0, cu[b + 1] - cu[b]], ps, w.softmax_scale, w.theta, w.eps)
+                                        [0, cu[b + 1] - cu[b]], ps, w.softmax_scale, w.theta, w.eps,
+                                        kv_e4m3=w.pool_dtype.itemsize == 1)
         dt = time.perf_counter() - t0
     rows = sum(int(cu[b + 1] - cu[b]) for b in reqs) * w.L
     return {"value": rows / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
@@ -290,7 +313,7 @@ def cpu_baseline(w, n_req: int):
 def main():
     args = parse()
     if args.write_traffic:
-        write_traffic(args.write_traffic, args.traffic_command)
+        write_traffic(args.write_traffic, args.traffic_command, workload_key(args))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -305,7 +328,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    w = make_workload(args.config, layout=args.layout, n_cand=args.candidates)
+    w = make_workload(args.config, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8)
     buf = S.allocate(w)
     torch.cuda.synchronize()
 
@@ -371,13 +394,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        # activations; over an e4m3 pool QK^T runs on fp8 MFMA and PV on bf16
+        "dtype": ("bf16" if w.dtype == torch.bfloat16 else "f32") + ("+e4m3-kv" if args.kv_fp8 else ""),
         "data": "synthetic (seeded; shapes and distributions of the drafting workload)",
         "config": describe(w),
         "roofline": {"bound": "hbm",
                      "kernel": "fm_paged_cross_attention (q_prologue_kernel + cross_attn_kernel, one launch)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(), "bytes_per_launch": cb, "avg_launch_ms": avg_cross},
+                     "traffic": measured_traffic(workload_key(args)), "bytes_per_launch": cb,
+                     "avg_launch_ms": avg_cross},
         "kv_read_GBps": achieved,
         "kv_read_pct_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "attention_rows_per_s": rows / (sum(cross_ms + self_ms) / args.steps * 1e-3),

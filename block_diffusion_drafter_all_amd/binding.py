@@ -23,6 +23,7 @@ FM_E_WORKSPACE = -3
 FM_E_HIP = -4
 FM_F32 = 0
 FM_BF16 = 1
+FM_BF16_E4M3 = 2
 
 SYMBOLS = (
     "fm_last_error",
@@ -109,7 +110,14 @@ def _check(status: int) -> None:
         raise FmError(status, fm_last_error())
 
 
-def _dtype_code(t: torch.Tensor) -> int:
+def _dtype_code(t: torch.Tensor, pool_dtype=None) -> int:
+    """fm_dtype of activations ``t`` over a pool of ``pool_dtype`` (None: no pool)."""
+    if pool_dtype == torch.float8_e4m3fn:
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"an e4m3 pool takes bfloat16 activations, got {t.dtype}")
+        return FM_BF16_E4M3
+    if pool_dtype is not None and pool_dtype != t.dtype:
+        raise TypeError(f"pool dtype {pool_dtype} does not go with activations of {t.dtype}")
     if t.dtype == torch.bfloat16:
         return FM_BF16
     if t.dtype == torch.float32:
@@ -185,11 +193,14 @@ def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, 
     if out_slots is not None and out_slots.shape[0] != x.shape[0]:
         raise ValueError("out_slots needs one entry per row of x")
     descs = (fm_kv_pool * L)(*[p.descriptor() for p in pools])
+    if any(p.k.dtype != pools[0].k.dtype for p in pools):
+        raise TypeError("every layer's pool must have one dtype")
+    code = _dtype_code(x, pools[0].k.dtype)
     n_rows, d_in = x.shape
     if ws is None:
         ws = torch.empty(lib.fm_write_context_kv_workspace_size(n_rows), dtype=torch.uint8, device=x.device)
     _check(lib.fm_write_context_kv(
-        _ptr(x), n_rows, d_in, _dtype_code(x), _ptr(w_kv), _ptr(k_norm_w), _ptr(row_req), _ptr(row_pos),
+        _ptr(x), n_rows, d_in, code, _ptr(w_kv), _ptr(k_norm_w), _ptr(row_req), _ptr(row_pos),
         _ptr(commit_lens), window, _ptr(page_table), page_table.stride(0), pools[0].page_size,
         page_table.shape[0], descs, L, H, Dh, eps, rope_theta, _ptr(out_slots), _ptr(ws), ws.numel(),
         _stream()))
@@ -230,7 +241,7 @@ def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu
         raise ValueError("page_table needs a row per request and cu_seqlens_q bs + 1 entries")
     desc = pool.descriptor()
     _check(lib.fm_paged_cross_attention(
-        _ptr(q), _dtype_code(q), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
+        _ptr(q), _dtype_code(q, pool.k.dtype), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
         page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), max_q, ctx_lens.shape[0], H, Dh,
         softmax_scale, rope_theta, eps, _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out

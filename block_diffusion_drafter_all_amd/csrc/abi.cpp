@@ -43,7 +43,8 @@ int log2_exact(int64_t x) {
   return r;
 }
 
-size_t elem_size(fm_dtype dt) { return dt == FM_BF16 ? 2 : 4; }
+// Bytes of one pool element.
+size_t pool_elem_size(fm_dtype dt) { return dt == FM_F32 ? 4 : (dt == FM_BF16 ? 2 : 1); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -56,7 +57,8 @@ fm::RopeFreqs rope_freqs(float theta, int Dh) {
 }
 
 int check_common(const char* fn, fm_dtype dt, int32_t H, int32_t Dh, float eps, float theta) {
-  if (dt != FM_F32 && dt != FM_BF16) return fail(FM_E_UNSUPPORTED, "%s: dtype %d is not FM_F32 or FM_BF16", fn, (int)dt);
+  if (dt != FM_F32 && dt != FM_BF16 && dt != FM_BF16_E4M3)
+    return fail(FM_E_UNSUPPORTED, "%s: dtype %d is not FM_F32, FM_BF16 or FM_BF16_E4M3", fn, (int)dt);
   if (H < 1) return fail(FM_E_INVALID, "%s: H = %d must be >= 1", fn, H);
   if (Dh != 64 && Dh != 128) return fail(FM_E_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, Dh);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FM_E_INVALID, "%s: eps must be finite and >= 0", fn);
@@ -65,7 +67,7 @@ int check_common(const char* fn, fm_dtype dt, int32_t H, int32_t Dh, float eps, 
 }
 
 int check_pool(const char* fn, const fm_kv_pool& p, fm_dtype dt, int idx, int64_t* elems_per16) {
-  const int64_t q = (int64_t)(16 / elem_size(dt));
+  const int64_t q = (int64_t)(16 / pool_elem_size(dt));
   *elems_per16 = q;
   if (p.k == nullptr || p.v == nullptr) return fail(FM_E_INVALID, "%s: pool %d has a null k or v pointer", fn, idx);
   if (!aligned16(p.k) || !aligned16(p.v)) return fail(FM_E_INVALID, "%s: pool %d k/v not 16-byte aligned", fn, idx);
@@ -187,7 +189,7 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
   g.lay = p.lay;
   for (int l = 0; l < L; ++l) g.pools[l] = to_desc(pools[l]);
   g.rope = rope_freqs(rope_theta, Dh);
-  return from_hip(fm::launch_write(p, g, dt == FM_BF16 ? 1 : 0, Dh, n_rows, stream), fn);
+  return from_hip(fm::launch_write(p, g, (int)dt, Dh, n_rows, stream), fn);
 }
 
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q) {
@@ -263,7 +265,7 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   a.ws = static_cast<uint8_t*>(ws);
   a.lay = lay;
   a.rope = rope_freqs(rope_theta, Dh);
-  return from_hip(fm::launch_cross_attention(a, dt == FM_BF16 ? 1 : 0, Dh, stream), fn);
+  return from_hip(fm::launch_cross_attention(a, (int)dt, Dh, stream), fn);
 }
 
 int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int32_t K, const float* q_norm_w,
@@ -273,6 +275,8 @@ int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int3
   if (n_blocks < 0) return fail(FM_E_INVALID, "%s: n_blocks %d < 0", fn, n_blocks);
   if (n_blocks == 0) return ok();
   if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
+  if (dt == FM_BF16_E4M3)
+    return fail(FM_E_UNSUPPORTED, "%s: the block's own q, k, v are activations: use FM_BF16", fn);
   if (K < 1 || K > 16) return fail(FM_E_UNSUPPORTED, "%s: block size %d not in [1, 16]", fn, K);
   if (!qkv || !q_norm_w || !k_norm_w || !ctx_lens || !out)
     return fail(FM_E_INVALID, "%s: a required pointer is null", fn);

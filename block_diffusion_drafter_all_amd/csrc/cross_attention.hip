@@ -26,6 +26,8 @@
 //     range boundaries leaves (m, l, O) partials that the merge kernel adds up
 //     in wave order (deterministic).
 
+#include <type_traits>
+
 #include "fm_internal.h"
 
 namespace fm {
@@ -183,11 +185,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 // ----------------------------------------------------------- query rows --
 
 // q^ = RoPE(RMSNorm(q; q_norm_w, eps)) at position ctx_len + (k mod 16) for
-// query row k of request b, stored as [b][k][h][:] for k < 16 NQF in the call's
-// storage type (rows past the request's count are zero), ready to be loaded
-// as MFMA operands.  A request with an empty context gets its zero output
-// rows here instead.  One wavefront per (request, head).
-template <class T, int D, int NQF>
+// query row k of request b, stored as [b][k][h][:] for k < 16 NQF in the
+// pool's storage type (rows past the request's count are zero), ready to be
+// loaded as MFMA operands.  Over an e4m3 pool (sglang/model.py
+// ``_paged_cross_attention_fp8``) the rows of one (request, head) share one
+// scale, their largest magnitude / 448 (at least 1e-12 / 448), and the stored
+// e4m3 row is q^ / scale, rounded once from fp32; the scale goes to q_scale.
+// A request with an empty context gets its zero output rows here instead.
+// One wavefront per (request, head).
+template <class T, class PT, int D, int NQF>
 __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   typedef typename T::storage st;
   constexpr int EPC = T::EPC;
@@ -200,6 +206,55 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   const int ctx0 = max(0, a.ctx_lens[b]);
   const int r0 = max(0, a.cu_q[b]);
   const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows * NQF));
+  if constexpr (std::is_same<PT, E4m3>::value) {
+    if (ctx0 == 0) {  // empty context: the output rows are zero
+#pragma unroll
+      for (int f = 0; f < NQF; ++f) {
+        const int k = kQRows * f + c;
+        if (k < nq) {
+          st* orow = (st*)a.out + ((int64_t)(r0 + k) * a.H + h) * D;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) *(u32x4_t*)(orow + ch * 4 * EPC + g * EPC) = (u32x4_t){0u, 0u, 0u, 0u};
+        }
+      }
+      return;
+    }
+    float qf[NQF][D / 4];
+    float amax = 0.f;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) {
+      const int k = kQRows * f + c;
+      const bool has = k < nq;
+      const st* qrow = (const st*)a.q + ((int64_t)(has ? r0 + k : 0) * a.H + h) * D;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const u32x4_t v = load16(qrow + ch * 4 * EPC + g * EPC);
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) qf[f][ch * EPC + j] = has ? chunk_elem<T>(v, j) : 0.f;
+      }
+      norm_rope_row<T, D>(qf[f], a.q_norm_w, a.eps, ctx0 + c, a.rope, g);  // zero rows stay zero
+#pragma unroll
+      for (int j = 0; j < D / 4; ++j) amax = fmaxf(amax, fabsf(qf[f][j]));
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+    const float am = fmaxf(amax, 1e-12f);
+    const float r = 448.0f / am;
+    if (lane == 0) ((float*)(a.ws + a.lay.q_scale))[(int64_t)b * a.H + h] = am / 448.0f;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) {
+      const int k = kQRows * f + c;
+      uint8_t* dst = (uint8_t*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows * NQF + k) * a.H + h) * D;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {  // EPC (8) consecutive columns -> 8 codes
+        u32x2_t w = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) w[j >> 2] |= f32_to_e4m3_bits(qf[f][ch * EPC + j] * r) << (8 * (j & 3));
+        *(u32x2_t*)(dst + ch * 4 * EPC + g * EPC) = w;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int f = 0; f < NQF; ++f) {
     const int k = kQRows * f + c;  // this lane's row of fragment f
@@ -239,6 +294,18 @@ struct StreamSlot {
   u32x4_t q[NQF == 1 ? D / (4 * T::EPC) : 1];
   uint32_t mask;  // bit t: token t of the tile is a valid key
   int b, h, r0, nq, flags;
+  float qs;       // e4m3 pool: the pair's query scale (read with its first tile)
+};
+
+// The type of the PV contraction's operands: an e4m3 pool's values enter it
+// as bf16, which holds every e4m3 value exactly.
+template <class T>
+struct PvType {
+  typedef T type;
+};
+template <>
+struct PvType<E4m3> {
+  typedef Bf16 type;
 };
 
 // Where the cut pair (b, h) lies in the tile stream: its first tile P, the
@@ -277,7 +344,7 @@ __device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h) {
 // and re-arms the pair's counter for the next call.  Called by the wave that
 // counted the last part in: every other part was acknowledged before it was
 // counted.  Lanes hold the same fragment of the rows as in the attention loop.
-template <class T, int D, int NQF>
+template <class T, class PT, int D, int NQF>
 __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
   typedef typename T::storage st;
   constexpr int NDT = D / 16;
@@ -331,7 +398,7 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
     if (k < nq) {
       st* orow = (st*)a.out + ((int64_t)(r0 + k) * a.H + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, acc[dt], inv);
+      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), acc[dt], inv);
     }
   }
   if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -340,10 +407,14 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
 // UNIFORM_PAGE: page_size >= 16, so the 16 keys of a tile share one page and
 // the tile's base address is wave-uniform (scalar), with a per-lane offset that
 // never changes.
-template <class T, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
+// T: query/output rows; PT: the pool (T itself, or e4m3 under bf16 rows).
+template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
 __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kernel(CrossArgs a) {
   typedef typename T::storage st;
-  constexpr int EPC = T::EPC;
+  typedef typename PT::storage pst;
+  typedef typename PvType<PT>::type PV;
+  constexpr bool kFp8 = std::is_same<PT, E4m3>::value;
+  constexpr int EPC = PT::EPC;
   constexpr int NCH = D / (4 * EPC);
   constexpr int NDT = D / 16;
   const int lane = lane_id(), g = lane >> 4, c = lane & 15;
@@ -366,11 +437,11 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   __shared__ int32_t win_all[4][kWin];
   int32_t* win = win_all[wv];
 
-  Selector<T> sel;
+  Selector<PT> sel;
   sel.init(lane);
   const int ps_mask = (1 << a.log2ps) - 1;
-  const st* kpool = (const st*)a.pool.k;
-  const st* vpool = (const st*)a.pool.v;
+  const pst* kpool = (const pst*)a.pool.k;
+  const pst* vpool = (const pst*)a.pool.v;
 
   // ---- loader state (wave-uniform) ----
   int lb = rec.b, lh = rec.h, lk = rec.k;
@@ -401,7 +472,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   int64_t kv_last = 0;  // per-lane element offset of the last real tile (a safe re-read)
   int64_t tile_base = 0;  // UNIFORM_PAGE: wave-uniform element offset of the tile (kept for re-reads)
   // UNIFORM_PAGE: this lane's constant offset inside a tile (slot c, column group g)
-  const uint32_t lane_off_b = (uint32_t)(((int64_t)c * a.pool.slot_stride + g * EPC) * (int64_t)sizeof(st));
+  const uint32_t lane_off_b = (uint32_t)(((int64_t)c * a.pool.slot_stride + g * EPC) * (int64_t)sizeof(pst));
   bool bad_page = false;
 
   // Move to the next (request, head) pair with tiles once the current one is done.
@@ -444,7 +515,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     pg_have = true;
   };
 
-  auto load_slot = [&](StreamSlot<T, D, NQF>& s, int j) {
+  auto load_slot = [&](StreamSlot<PT, D, NQF>& s, int j) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
     s.flags = 0;
@@ -482,10 +553,11 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         kv_last = off;
       }
       if (NQF == 1 && (flags & kStart)) {  // this pair's prepared query rows ride along with its first tile
-        const st* qrow = (const st*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
+        const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) s.q[ch] = load16(qrow + ch * 4 * EPC + g * EPC);
       }
+      if (kFp8 && (flags & kStart)) s.qs = load_f32((const float*)(ws + a.lay.q_scale) + (int64_t)lb * a.H + lh);
       s.b = lb;
       s.h = lh;
       s.r0 = lr0;
@@ -523,6 +595,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   float m_run[NQF];   // running max of this lane's query row (log2 domain)
   float l_lane[NQF];  // this lane's share of the running denominator
   int cut_b[2] = {-1, -1}, cut_h[2] = {0, 0};  // pairs this wave left partials of
+  float score_scale = a.qscale_log2;  // softmax scale * log2(e), times the pair's query scale over e4m3
 #pragma unroll
   for (int f = 0; f < NQF; ++f) {
     m_run[f] = kNegInf;
@@ -533,13 +606,14 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_slot = [&](const StreamSlot<T, D, NQF>& s) {
+  auto compute_slot = [&](const StreamSlot<PT, D, NQF>& s) {
     if (s.flags & kStart) {
+      if (kFp8) score_scale = a.qscale_log2 * s.qs;
       if (NQF == 1) {
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) qop[0][ch] = s.q[ch];
       } else {  // every fragment's prepared rows, read now
-        const st* qrow = (const st*)(ws + a.lay.q_hat) + (((int64_t)s.b * kQRows * NQF + c) * a.H + s.h) * D;
+        const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)s.b * kQRows * NQF + c) * a.H + s.h) * D;
 #pragma unroll
         for (int f = 0; f < NQF; ++f)
 #pragma unroll
@@ -559,13 +633,13 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     for (int f = 0; f < NQF; ++f) {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) mma_chunk<T>(sc, s.k[ch], qop[f][ch]);
+      for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, s.k[ch], qop[f][ch]);
       float sv[4];
       float mx = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool valid = (s.mask >> (4 * g + i)) & 1u;
-        sv[i] = valid ? sc[i] * a.qscale_log2 : kNegInf;
+        sv[i] = valid ? sc[i] * score_scale : kNegInf;
         mx = fmaxf(mx, sv[i]);
       }
       mx = wave_max_groups(mx);
@@ -576,7 +650,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[f][i] = operand_value<T>(exp2f(sv[i] - m_use));
+          p[f][i] = operand_value<PV>(exp2f(sv[i] - m_use));
           psum += p[f][i];
         }
         if (__ballot(m_new != m_run[f]) != 0) {
@@ -605,7 +679,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[f][i] = operand_value<T>(exp2f(sv[i] - m_use));
+          p[f][i] = operand_value<PV>(exp2f(sv[i] - m_use));
           psum += p[f][i];
         }
       }
@@ -616,7 +690,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     for (int dt = 0; dt < NDT; ++dt) {
       const auto vt = sel.template transpose_tile<NCH>(s.v, dt);
 #pragma unroll
-      for (int f = 0; f < NQF; ++f) mma_pv<T>(o[f][dt], vt, p[f]);
+      for (int f = 0; f < NQF; ++f) mma_pv<PV>(o[f][dt], vt, p[f]);
     }
     if (s.flags & kEnd) {
       if (s.flags & kWhole) {
@@ -628,7 +702,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
           if (k < s.nq) {
             st* orow = (st*)a.out + ((int64_t)(s.r0 + k) * a.H + s.h) * D;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + 16 * dt + 4 * g, o[f][dt], inv);
+            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), o[f][dt], inv);
           }
         }
       } else {
@@ -655,7 +729,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   // Every slot index is loaded unconditionally (indices past the range
   // re-read the last tile, a cache hit, and are fully masked with no flags),
   // so the loop body is straight-line and DEPTH-1 tiles stay in flight.
-  StreamSlot<T, D, NQF> buf[DEPTH];
+  StreamSlot<PT, D, NQF> buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) load_slot(buf[d], d);
   for (int it = 0; it < n_tiles; it += DEPTH) {
@@ -676,26 +750,26 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
       if (cut_b[k] >= 0) last[k] = count_in(a, cut_b[k], cut_h[k]);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (last[k]) merge_pair<T, D, NQF>(a, cut_b[k], cut_h[k]);
+      if (last[k]) merge_pair<T, PT, D, NQF>(a, cut_b[k], cut_h[k]);
   }
 }
 
-template <class T, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
+template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
 hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.bs * a.H;
-  hipLaunchKernelGGL((q_prologue_kernel<T, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((q_prologue_kernel<T, PT, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
-  hipLaunchKernelGGL((cross_attn_kernel<T, D, DEPTH, UNIFORM_PAGE, NQF>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((cross_attn_kernel<T, PT, D, DEPTH, UNIFORM_PAGE, NQF>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <class T, int D, int DEPTH, int NQF>
+template <class T, class PT, int D, int DEPTH, int NQF>
 hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
   // page_size >= 16 keeps each 16-key tile inside one page
-  if (a.log2ps >= 4) return launch_cross_paged<T, D, DEPTH, true, NQF>(a, s);
-  return launch_cross_paged<T, D, DEPTH, false, NQF>(a, s);
+  if (a.log2ps >= 4) return launch_cross_paged<T, PT, D, DEPTH, true, NQF>(a, s);
+  return launch_cross_paged<T, PT, D, DEPTH, false, NQF>(a, s);
 }
 
 #ifndef FM_CROSS_DEPTH_Q2
@@ -704,17 +778,36 @@ hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
 #ifndef FM_CROSS_DEPTH_Q4
 #define FM_CROSS_DEPTH_Q4 2  // ... with four (their accumulators fill the AGPRs)
 #endif
+// An e4m3 tile is half the bytes of a bf16 one: twice the tiles keep the same
+// bytes in flight in the same registers.
+#ifndef FM_CROSS_DEPTH_FP8
+#define FM_CROSS_DEPTH_FP8 6
+#endif
+#ifndef FM_CROSS_DEPTH_FP8_Q2
+#define FM_CROSS_DEPTH_FP8_Q2 6
+#endif
+#ifndef FM_CROSS_DEPTH_FP8_Q4
+#define FM_CROSS_DEPTH_FP8_Q4 4
+#endif
 
-template <class T, int D, int DEPTH>
+// Tiles in flight for one, two and four query fragments per request.
+template <class T, class PT, int D, int DEPTH1, int DEPTH2, int DEPTH4>
 hipError_t launch_cross_frags(const CrossArgs& a, hipStream_t s) {
-  // Several candidate blocks per request hold more state per tile; fp32 rows,
-  // whose tiles take twice the registers, keep one tile in flight.
-  constexpr bool kF32 = sizeof(typename T::storage) == 4;
   switch (a.lay.nqf) {
-    case 1: return launch_cross_typed<T, D, DEPTH, 1>(a, s);
-    case 2: return launch_cross_typed<T, D, kF32 ? 1 : FM_CROSS_DEPTH_Q2, 2>(a, s);
-    default: return launch_cross_typed<T, D, kF32 ? 1 : FM_CROSS_DEPTH_Q4, 4>(a, s);
+    case 1: return launch_cross_typed<T, PT, D, DEPTH1, 1>(a, s);
+    case 2: return launch_cross_typed<T, PT, D, DEPTH2, 2>(a, s);
+    default: return launch_cross_typed<T, PT, D, DEPTH4, 4>(a, s);
   }
+}
+
+template <int D>
+hipError_t launch_cross_dh(const CrossArgs& a, int dtype, hipStream_t s) {
+  if (dtype == 1) return launch_cross_frags<Bf16, Bf16, D, FM_CROSS_DEPTH_BF16, FM_CROSS_DEPTH_Q2, FM_CROSS_DEPTH_Q4>(a, s);
+  if (dtype == 2)
+    return launch_cross_frags<Bf16, E4m3, D, FM_CROSS_DEPTH_FP8, FM_CROSS_DEPTH_FP8_Q2, FM_CROSS_DEPTH_FP8_Q4>(a, s);
+  // fp32 rows, whose tiles take twice the registers, keep one tile in flight
+  // with several candidate blocks
+  return launch_cross_frags<F32, F32, D, FM_CROSS_DEPTH_F32, 1, 1>(a, s);
 }
 
 }  // namespace
@@ -725,11 +818,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStream_t s) {
-  if (dtype == 1)
-    return Dh == 128 ? launch_cross_frags<Bf16, 128, FM_CROSS_DEPTH_BF16>(a, s)
-                     : launch_cross_frags<Bf16, 64, FM_CROSS_DEPTH_BF16>(a, s);
-  return Dh == 128 ? launch_cross_frags<F32, 128, FM_CROSS_DEPTH_F32>(a, s)
-                   : launch_cross_frags<F32, 64, FM_CROSS_DEPTH_F32>(a, s);
+  return Dh == 128 ? launch_cross_dh<128>(a, dtype, s) : launch_cross_dh<64>(a, dtype, s);
 }
 
 }  // namespace fm

@@ -33,6 +33,13 @@ struct F32 {
   typedef float storage;
   static constexpr int EPC = 4;
 };
+// OCP float8 e4m3 ("e4m3fn": bias 7, largest finite 448, no infinity): the
+// fp8 KV pool, written with scale 1.  Its row fragments hold 16 elements per
+// chunk, so a 16-byte load covers the same 16 rows x 64 bytes as for bf16.
+struct E4m3 {
+  typedef uint8_t storage;
+  static constexpr int EPC = 16;
+};
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
@@ -46,6 +53,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float round_bf16(float f) {
   return bf16_bits_to_f32(f32_to_bf16_bits(f));
+}
+
+// fp32 -> e4m3 code: nearest, ties to even, magnitudes past 448 saturating to
+// 448 (the pool must stay finite).  Normal results (>= 2^-6) round the fp32
+// significand to 3 bits in place and rebias the exponent (127 -> 7); below
+// 2^-6 the grid step is 2^-9, so the code is the rounded multiple of it (a
+// result of 8 is the code of 2^-6 as well).
+__device__ __forceinline__ uint32_t f32_to_e4m3_bits(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float a = fminf(fabsf(f), 448.0f);
+  uint32_t code;
+  if (a >= 0.015625f) {
+    const uint32_t u = __float_as_uint(a);
+    code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)rintf(a * 512.0f);
+  }
+  return sign | code;
 }
 
 template <class T>
@@ -127,6 +152,18 @@ __device__ __forceinline__ void mma_chunk<F32>(f32x4_t& acc, const u32x4_t& a, c
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(b[j]), acc, 0, 0, 0);
 }
 
+__device__ __forceinline__ long u64_of(uint32_t lo, uint32_t hi) {
+  return (long)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// e4m3 chunks: two 16x16x32 fp8 MFMAs, one per 8-byte half.  Every product of
+// two e4m3 values is exact in fp32.
+template <>
+__device__ __forceinline__ void mma_chunk<E4m3>(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(u64_of(a[0], a[1]), u64_of(b[0], b[1]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(u64_of(a[2], a[3]), u64_of(b[2], b[3]), acc, 0, 0, 0);
+}
+
 // Selection operands that move a row fragment into the C layout ("column
 // fragment"): for column tile dt (16 columns), transpose_tile returns, in lane
 // l, M[4*(l/16) + i][16*dt + l%16] for i < 4 -- four consecutive rows of one
@@ -173,6 +210,47 @@ struct Selector<F32> {
     return acc;
   }
 };
+
+// e4m3 fragments: each 8-byte half of a chunk is one fp8 MFMA operand, whose
+// element j in lane group g is "virtual column" 8g + j of that half; the
+// selection matrix (e4m3 1.0 = 0x38) is the bf16 one on 8-byte operands, and
+// the products are exact.  Tile dt = 4 ch + 2 half + hsel of chunk ch yields,
+// in lane (g, c), V[key 4g+i][virtual column 16 hsel + c] as fp32; the real
+// column of an output lane is given by out_col<E4m3>.
+template <>
+struct Selector<E4m3> {
+  long sel[2];  // sel[h]: byte j of lane (g, c) is 1.0 iff 8g + j == 16h + c
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (8 * g + j == 16 * h + c) v |= (uint64_t)0x38u << (8 * j);
+      sel[h] = (long)v;
+    }
+  }
+  template <int NCH>
+  __device__ __forceinline__ f32x4_t transpose_tile(const u32x4_t (&frag)[NCH], int dt) const {
+    const u32x4_t& ch = frag[dt >> 2];
+    const long a = ((dt >> 1) & 1) ? u64_of(ch[2], ch[3]) : u64_of(ch[0], ch[1]);
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, sel[dt & 1], (f32x4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+};
+
+// First of the four consecutive output columns lane group g holds after the
+// PV product of column tile dt (the tile order transpose_tile defines).
+template <class T>
+__device__ __forceinline__ int out_col(int dt, int g) {
+  return 16 * dt + 4 * g;
+}
+template <>
+__device__ __forceinline__ int out_col<E4m3>(int dt, int g) {
+  // virtual column 16 hsel + 4g + i of half ``half`` of chunk ch is real column
+  // 64 ch + 16 (2 hsel + g/2) + 8 half + 4 (g%2) + i
+  return 64 * (dt >> 2) + 32 * (dt & 1) + 16 * (g >> 1) + 8 * ((dt >> 1) & 1) + 4 * (g & 1);
+}
 
 // acc (C layout, lane (g, c) = out[4g+i][c]) += Vt x P, the weighted sum of
 // four keys: vt[i] (lane (g, c)) is column c of key 4g+i, p[i] the weight of
@@ -293,6 +371,12 @@ __device__ __forceinline__ void store4<Bf16>(uint16_t* p, const f32x4_t& v, floa
 template <>
 __device__ __forceinline__ void store4<F32>(float* p, const f32x4_t& v, float scale) {
   *(f32x4_t*)p = v * scale;
+}
+
+template <>
+__device__ __forceinline__ void store4<E4m3>(uint8_t* p, const f32x4_t& v, float scale) {
+  *(uint32_t*)p = f32_to_e4m3_bits(v[0] * scale) | (f32_to_e4m3_bits(v[1] * scale) << 8) |
+                  (f32_to_e4m3_bits(v[2] * scale) << 16) | (f32_to_e4m3_bits(v[3] * scale) << 24);
 }
 
 // Exclusive prefix sum over a 1024-thread block; returns the block total in *total.

@@ -78,7 +78,9 @@ struct PairRec {
 };
 
 struct PlanLayout {
-  size_t q_hat;       // [bs][16 nqf][H][Dh] of the call's type: normed, rotated queries (0 past a request's rows)
+  size_t q_hat;       // [bs][16 nqf][H][Dh] of the pool's type: normed, rotated queries (0 past a request's rows);
+                      // over an e4m3 pool, the queries divided by their (request, head) scale
+  size_t q_scale;     // float [bs][H]: e4m3 pool only, the query scale of each (request, head)
   size_t pair_off;    // int64 [bs + 1]: first tile of request b's pairs in the stream
   size_t wave_rec;    // WaveRec [n_waves]
   size_t pair_rec;    // PairRec [bs * H]
@@ -96,6 +98,7 @@ inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves, int nqf) {
   p.nqf = nqf;
   size_t off = 256;
   p.q_hat = off;      off = align256(off + (size_t)bs * kQRows * nqf * H * Dh * 4);
+  p.q_scale = off;    off = align256(off + (size_t)bs * H * 4);
   p.pair_off = off;   off = align256(off + (size_t)(bs + 1) * 8);
   p.wave_rec = off;   off = align256(off + (size_t)n_waves * sizeof(WaveRec));
   p.pair_rec = off;   off = align256(off + (size_t)bs * H * sizeof(PairRec));
@@ -199,7 +202,8 @@ struct WriteGemmArgs {
 };
 
 // -------------------------------------------------------------- launchers --
-// Each returns hipSuccess or the launch error.  dtype: 0 = fp32, 1 = bf16.
+// Each returns hipSuccess or the launch error.  dtype: 0 = fp32, 1 = bf16,
+// 2 = bf16 activations over an e4m3 pool (write and cross-attention only).
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStream_t s);

@@ -10,7 +10,9 @@
 //      tile = 64 rows x one (layer, {k|v}, head) of head_dim columns, so the
 //      tile holds whole heads: the epilogue RMS-norms and rotates keys in
 //      registers (fp32 from the MFMA accumulator) and stores every row's
-//      head straight to its page slot, rounded once to the pool's type.
+//      head straight to its page slot, rounded once to the pool's type (an
+//      e4m3 pool is written with scale 1: sglang/model.py ``_kv_write`` with
+//      ``kv_norm_rope_write_fp8``).
 
 #include "fm_internal.h"
 
@@ -73,9 +75,11 @@ __global__ __launch_bounds__(1024) void write_prep_kernel(WritePrepArgs a) {
   }
 }
 
-template <class T, int D>
+// T: x and W; PT: the pool (T itself, or e4m3 under bf16 operands).
+template <class T, class PT, int D>
 __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
   typedef typename T::storage st;
+  typedef typename PT::storage pst;
   constexpr int EPC = T::EPC;
   constexpr int KC = 4 * EPC;   // contraction elements per 16-byte chunk per lane group
   constexpr int NDT = D / 16;   // 16-column tiles of one head
@@ -145,10 +149,10 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
     const int page = ((const int32_t*)(ws + a.lay.live_page))[li];
     const int off = ((const int32_t*)(ws + a.lay.live_off))[li];
     const PoolDesc& P = a.pools[l];
-    st* dst = (st*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
-              (int64_t)h * P.head_stride + 4 * g;
+    pst* dst = (pst*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
+               (int64_t)h * P.head_stride + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < NDT; ++ct) store4<T>(dst + 16 * ct, acc[ct], 1.0f);
+    for (int ct = 0; ct < NDT; ++ct) store4<PT>(dst + 16 * ct, acc[ct], 1.0f);
   }
 }
 
@@ -186,8 +190,10 @@ constexpr int kLoadsPerWave = 32 / kGemmWaves;  // fragments each wave loads per
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr int kWaitLgkm0 = 0xC07F;              // lgkmcnt(0) only
 
+template <class PT>
 __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(WriteGemmArgs a, int n_tiles,
                                                                               int m_tiles) {
+  typedef typename PT::storage pst;
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
@@ -347,8 +353,8 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     const int page = ((const int32_t*)(ws + a.lay.live_page))[lic];
     const int off = ((const int32_t*)(ws + a.lay.live_off))[lic];
     const float fpos = (float)((const int32_t*)(ws + a.lay.live_pos))[lic];
-    uint16_t* dst = (uint16_t*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
-                    (int64_t)h * P.head_stride + 4 * fchunk;
+    pst* dst = (pst*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
+               (int64_t)h * P.head_stride + 4 * fchunk;
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
@@ -370,12 +376,12 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
             v[p2 + 1] = y1 * cs + y0 * sn;
           }
         }
-        if (has) store4<Bf16>(dst + 32 * cg + 8 * q, (f32x4_t){v[0], v[1], v[2], v[3]}, 1.0f);
+        if (has) store4<PT>(dst + 32 * cg + 8 * q, (f32x4_t){v[0], v[1], v[2], v[3]}, 1.0f);
       }
   }
 }
 
-template <class T, int D>
+template <class T, class PT, int D>
 hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, int64_t n_rows, hipStream_t s) {
   hipLaunchKernelGGL(write_prep_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t e = hipGetLastError();
@@ -384,12 +390,12 @@ hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, in
   if (sizeof(typename T::storage) == 2 && D == kDhGemm) {
     const int m_tiles = (int)((n_rows + kGM - 1) / kGM);
     const int64_t groups = (n_tiles / 2 + 7) / 8;  // 256-row tiles of W: two heads each
-    hipLaunchKernelGGL(write_gemm_bf16_kernel, dim3((unsigned)(groups * 8 * m_tiles)), dim3(64 * kGemmWaves), 0, s,
-                       g, n_tiles / 2, m_tiles);
+    hipLaunchKernelGGL(write_gemm_bf16_kernel<PT>, dim3((unsigned)(groups * 8 * m_tiles)), dim3(64 * kGemmWaves), 0,
+                       s, g, n_tiles / 2, m_tiles);
     return hipGetLastError();
   }
   const unsigned m_tiles = (unsigned)((n_rows + 63) / 64);
-  hipLaunchKernelGGL((write_gemm_kernel<T, D>), dim3((unsigned)n_tiles, m_tiles), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((write_gemm_kernel<T, PT, D>), dim3((unsigned)n_tiles, m_tiles), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -397,9 +403,12 @@ hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, in
 
 hipError_t launch_write(const WritePrepArgs& p, const WriteGemmArgs& g, int dtype, int Dh, int64_t n_rows,
                         hipStream_t s) {
-  if (dtype == 1) return Dh == 128 ? launch_write_typed<Bf16, 128>(p, g, n_rows, s)
-                                   : launch_write_typed<Bf16, 64>(p, g, n_rows, s);
-  return Dh == 128 ? launch_write_typed<F32, 128>(p, g, n_rows, s) : launch_write_typed<F32, 64>(p, g, n_rows, s);
+  if (dtype == 1) return Dh == 128 ? launch_write_typed<Bf16, Bf16, 128>(p, g, n_rows, s)
+                                   : launch_write_typed<Bf16, Bf16, 64>(p, g, n_rows, s);
+  if (dtype == 2) return Dh == 128 ? launch_write_typed<Bf16, E4m3, 128>(p, g, n_rows, s)
+                                   : launch_write_typed<Bf16, E4m3, 64>(p, g, n_rows, s);
+  return Dh == 128 ? launch_write_typed<F32, F32, 128>(p, g, n_rows, s)
+                   : launch_write_typed<F32, F32, 64>(p, g, n_rows, s);
 }
 
 }  // namespace fm

@@ -75,6 +75,11 @@ class Workload:
         return self.ctx_lens if self.n_cand == 1 else self.ctx_lens.repeat_interleave(self.n_cand)
 
     @property
+    def pool_dtype(self) -> torch.dtype:
+        """Element type of the KV pool: the activation type, or e4m3."""
+        return self.pools[0].k.dtype
+
+    @property
     def softmax_scale(self) -> float:
         return self.Dh ** -0.5
 
@@ -131,7 +136,7 @@ def _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K, q_scale=1.0):
 
 
 def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_major", scale_down=None,
-                  q_scale=1.0, seed=None, n_cand=1) -> Workload:
+                  q_scale=1.0, seed=None, n_cand=1, kv_fp8=False) -> Workload:
     """The seeded inputs of one workload.
 
     1  tiny fp32 full step: 1 request, ctx 64, 1 layer, 4 x 64, page 16,
@@ -149,6 +154,9 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     ``n_cand`` candidate blocks per request (tree drafting): each request's
     cross-attention query holds ``n_cand * K`` rows, candidate-major, and the
     self-attention runs over ``bs * n_cand`` blocks.
+    ``kv_fp8``: the pools hold e4m3 (the same N(0, 1) draws cast to e4m3;
+    bf16 workloads only); the write stores e4m3 at scale 1 and cross-attention
+    quantizes its queries (sglang/model.py ``_kv_fp8`` path).
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + workload_id if seed is None else seed)
@@ -213,7 +221,10 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     else:
         pt = _page_table(pages_needed, width, n_pages, gen, device)
 
-    pools = [_pool_tensors(n_pages, ps, H, Dh, dtype, device, gen, layout) for _ in range(L)]
+    if kv_fp8 and dtype != torch.bfloat16:
+        raise ValueError("an e4m3 pool goes with bf16 activations")
+    pool_dtype = torch.float8_e4m3fn if kv_fp8 else dtype
+    pools = [_pool_tensors(n_pages, ps, H, Dh, pool_dtype, device, gen, layout) for _ in range(L)]
     cu_q = torch.arange(0, (bs + 1) * K * n_cand, K * n_cand, dtype=torch.int32, device=device)
     q, qkv = _attention_inputs(bs * n_cand, L, H, Dh, dtype, device, gen, cu_q, K, q_scale)
 
@@ -245,4 +256,5 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     return Workload(name=names[workload_id], workload_id=workload_id, bs=bs, K=K, L=L, H=H, Dh=Dh, page_size=ps,
                     dtype=dtype, ctx_lens=ctx.contiguous(), cu_seqlens_q=cu_q, page_table=pt, pools=pools, q=q,
                     qkv=qkv, q_norm_w=q_norm_w, self_q_norm_w=self_q, self_k_norm_w=self_k, write=write,
-                    n_cand=n_cand, meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale))
+                    n_cand=n_cand, meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale,
+                                             kv_fp8=kv_fp8))

@@ -53,14 +53,21 @@ typedef enum fm_status {
   FM_E_HIP = -4          /* a HIP launch failed */
 } fm_status;
 
-/* Storage type of the activations and of the KV pool.  One type per call. */
-typedef enum fm_dtype { FM_F32 = 0, FM_BF16 = 1 } fm_dtype;
+/* Storage type of the activations and of the KV pool.  FM_F32 and FM_BF16:
+ * one type for both.  FM_BF16_E4M3: bf16 activations over an OCP float8 e4m3
+ * ("e4m3fn") pool written with scale 1 (sglang/model.py ``_kv_write`` with
+ * ``kv_norm_rope_write_fp8``, ``_paged_cross_attention_fp8``); the write
+ * rounds each key/value to nearest-even e4m3, saturating at +-448, and
+ * cross-attention quantizes the query per (request, head) as documented
+ * there.  Block self-attention reads no pool and takes FM_F32 or FM_BF16. */
+typedef enum fm_dtype { FM_F32 = 0, FM_BF16 = 1, FM_BF16_E4M3 = 2 } fm_dtype;
 
 /* One layer's paged KV pool (vllm/model.py ``cache_layout``: page, head and
  * slot strides with head_dim contiguous; sglang's pool is page_size 1).
  * Key of slot ``s`` of page ``p`` for head ``h``: k + p*page_stride +
  * s*slot_stride + h*head_stride, head_dim contiguous elements; the value is at
- * the same offset from v.  Storage type = the call's fm_dtype.
+ * the same offset from v.  Element type = the call's pool type (fp32, bf16 or
+ * e4m3 for FM_F32, FM_BF16, FM_BF16_E4M3); strides count elements.
  * All strides and the byte addresses of k and v must be multiples of 16 bytes. */
 typedef struct fm_kv_pool {
   void* k;               /* DEVICE */
@@ -94,7 +101,8 @@ size_t fm_write_context_kv_workspace_size(int64_t n_rows);
  *     slot = page_table[req_r][pos_r / page_size]*page_size + pos_r % page_size
  *     pools[l].k[slot, h, :] = k ;  pools[l].v[slot, h, :] = v  (rounded once)
  *
- * x          DEVICE [n_rows, d_in], row-major, dtype dt.
+ * x          DEVICE [n_rows, d_in], row-major, the activation type of dt
+ *            (bf16 for FM_BF16_E4M3; w_kv likewise).
  * w_kv       DEVICE [L*2*H*Dh, d_in] row-major: rows ordered (layer, {k, v},
  *            head, dim), i.e. the concatenation [k_proj_0; v_proj_0; k_proj_1; ...].
  * k_norm_w   DEVICE fp32 [L, Dh]: each layer's key RMSNorm weight.
@@ -167,8 +175,13 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  *   out[r,h,:] = sum_t softmax_t(softmax_scale * q^.K_t) V_t,  t = 0..ctx_lens[b]-1
  * non-causal, one KV head per query head; keys/values are read through the
  * page table from ``pool``.  ctx_lens[b] = 0 gives out = 0.
+ * Over an e4m3 pool (FM_BF16_E4M3; sglang/model.py ``_paged_cross_attention_fp8``)
+ * q^ is first quantized per (request, head): s = max(max |q^|, 1e-12) / 448
+ * over the request's rows and the head's channels, q8 = e4m3(q^ / s) (nearest,
+ * ties to even, from fp32), and the scores use s * q8 (the softmax weights
+ * stay bf16; the e4m3 values enter the products exactly).
  *
- * q, out      DEVICE [total_q, H, Dh] contiguous, dtype dt.
+ * q, out      DEVICE [total_q, H, Dh] contiguous, the activation type of dt.
  * q_norm_w    DEVICE fp32 [Dh].
  * pool        HOST pointer to this layer's pool descriptor.
  * page_table  DEVICE int32 [bs, pt_stride].

@@ -26,7 +26,36 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def storage_name(dtype: torch.dtype) -> str:
+    if dtype == torch.float8_e4m3fn:
+        return "e4m3"
     return "bf16" if dtype == torch.bfloat16 else "f32"
+
+
+def bits_view(t: torch.Tensor) -> torch.Tensor:
+    """The tensor's raw elements as integers of the same width."""
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()])
+
+
+def check_e4m3_rounding(got, exact, what: str, max_other=1e-3):
+    """Codes written from fp32 against the oracle's unrounded values: each is
+    the nearest-even e4m3 of the exact value, except that a value within fp32
+    noise of a midpoint may take the other neighbour (at most ``max_other`` of
+    them)."""
+    got = to_np(got) if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    assert got.shape == exact.shape, (what, got.shape, exact.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite codes"
+    want = O.round_to_e4m3(exact)
+    a = np.minimum(np.abs(exact), 448.0)
+    _, e = np.frexp(a)
+    half = np.where(e - 1 >= -6, np.ldexp(1.0, e - 4), 2.0 ** -9) / 2
+    other = got != want
+    err = np.abs(got - np.clip(exact, -448.0, 448.0))
+    bad = other & (err > half + np.maximum(1e-3 * half, 1e-6))
+    frac = float(other.mean()) if other.size else 0.0
+    log(f"  {what}: {int(other.sum())} of {other.size} codes at the other neighbour of a midpoint")
+    assert not bad.any(), f"{what}: {int(bad.sum())} codes are not a nearest e4m3 of the exact value"
+    assert frac <= max_other, f"{what}: {frac:.2e} of the codes off the nearest-even one"
 
 
 def compare(gpu, ref, what: str, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
@@ -83,7 +112,8 @@ def oracle_cross(w, layer: int, reqs, pk, pv, pt_rows, q=None):
         pt[0, :len(pt_rows[i])] = pt_rows[i]
         r0, r1 = cu[b], cu[b + 1]
         o = O.paged_cross_attention(q[r0:r1], to_np(w.q_norm_w[layer]), pk, pv, pt, [ctx[b]], [0, r1 - r0],
-                                    w.page_size, w.softmax_scale, w.theta, w.eps)
+                                    w.page_size, w.softmax_scale, w.theta, w.eps,
+                                    kv_e4m3=w.pools[layer].k.dtype == torch.float8_e4m3fn)
         out[b] = o
     return out
 

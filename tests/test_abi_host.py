@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from block_diffusion_drafter_all_amd import binding as B
 from block_diffusion_drafter_all_amd.build import LIB_PATH, REPO_DIR
@@ -83,6 +84,9 @@ def _cross(lib, **over):
     (dict(pool=None), B.FM_E_INVALID, "null"),
     (dict(Dh=96), B.FM_E_UNSUPPORTED, "head_dim"),
     (dict(dt=7), B.FM_E_UNSUPPORTED, "dtype"),
+    (dict(dt=3), B.FM_E_UNSUPPORTED, "dtype"),
+    # e4m3 elements are one byte: a stride of 72 elements is 144 bytes in bf16, 72 in e4m3
+    (dict(dt=B.FM_BF16_E4M3, pool=B.fm_kv_pool(FAKE, FAKE, 4, 4096, 72, 64)), B.FM_E_INVALID, "16 bytes"),
     (dict(ps=12), B.FM_E_UNSUPPORTED, "page_size"),
     (dict(H=0), B.FM_E_INVALID, "H"),
     (dict(ws=None), B.FM_E_WORKSPACE, "workspace"),
@@ -135,6 +139,8 @@ def _write(lib, **over):
     (dict(ws_bytes=100), B.FM_E_WORKSPACE, "needed"),
     (dict(ps=3), B.FM_E_UNSUPPORTED, "page_size"),
     (dict(n_rows=-1), B.FM_E_INVALID, "n_rows"),
+    (dict(dt=B.FM_BF16_E4M3, pools=(B.fm_kv_pool * 2)(_pool(), B.fm_kv_pool(FAKE, FAKE, 4, 4096, 256, 8))),
+     B.FM_E_INVALID, "16 bytes"),
 ])
 def test_write_rejects(lib, over, status, needle):
     assert _write(lib, **over) == status
@@ -151,3 +157,17 @@ def test_self_attention_rejects(lib):
     assert f(FAKE, B.FM_BF16, 4, 0, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
     assert f(None, B.FM_BF16, 4, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_INVALID
     assert f(None, B.FM_BF16, 0, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_OK
+    # the block's own q, k, v are activations: an e4m3 pool type means nothing here
+    assert f(FAKE, B.FM_BF16_E4M3, 4, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
+    assert "FM_BF16" in B.fm_last_error()
+
+
+def test_binding_dtype_pairs():
+    bf, f32 = torch.zeros(1, dtype=torch.bfloat16), torch.zeros(1)
+    assert B._dtype_code(bf) == B.FM_BF16 and B._dtype_code(f32) == B.FM_F32
+    assert B._dtype_code(bf, torch.bfloat16) == B.FM_BF16
+    assert B._dtype_code(bf, torch.float8_e4m3fn) == B.FM_BF16_E4M3
+    with pytest.raises(TypeError):
+        B._dtype_code(f32, torch.float8_e4m3fn)
+    with pytest.raises(TypeError):
+        B._dtype_code(bf, torch.float32)

@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import oracle as O
-from harness import (compact_context, compare, log, oracle_cross, rows_of, storage_name, to_np,
-                     ws_error_word)
+from harness import (bits_view, check_e4m3_rounding, compact_context, compare, log, oracle_cross, rows_of,
+                     storage_name, to_np, ws_error_word)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,15 +71,18 @@ def _check_write(w, buf, before, slots, keys, values):
     expect = set(int(s) for s in slots[live])
     for l in range(w.L):
         for t_before, t_after, name in ((before[l][0], w.pools[l].k, "k"), (before[l][1], w.pools[l].v, "v")):
-            itype = torch.int16 if w.dtype == torch.bfloat16 else torch.int32
-            diff = (t_before.view(itype) != t_after.view(itype)).any(dim=3).any(dim=2)   # (pages, ps)
+            diff = (bits_view(t_before) != bits_view(t_after)).any(dim=3).any(dim=2)   # (pages, ps)
             changed = torch.nonzero(diff.reshape(-1)).flatten().cpu().numpy()
             assert set(changed.tolist()) == expect, f"layer {l} {name}: changed slots differ"
         sl = torch.as_tensor(slots[live], device=w.page_table.device, dtype=torch.long)
         got_k = w.pools[l].k[sl // ps, sl % ps]
         got_v = w.pools[l].v[sl // ps, sl % ps]
-        compare(got_k, keys[live, l], f"written K L{l}")
-        compare(got_v, values[live, l], f"written V L{l}")
+        if w.pool_dtype == torch.float8_e4m3fn:
+            check_e4m3_rounding(got_k, keys[live, l], f"written K L{l} (e4m3)")
+            check_e4m3_rounding(got_v, values[live, l], f"written V L{l} (e4m3)")
+        else:
+            compare(got_k, keys[live, l], f"written K L{l}")
+            compare(got_v, values[live, l], f"written V L{l}")
 
 
 def test_config1_full_step():
@@ -94,7 +97,7 @@ def test_config1_full_step():
     # oracle pool = pre-write pages + the oracle's own write
     pk = [to_np(before[0][0])]
     pv = [to_np(before[0][1])]
-    O.scatter_into_pool(pk, pv, slots, keys, values, w.page_size, storage_name(w.dtype))
+    O.scatter_into_pool(pk, pv, slots, keys, values, w.page_size, storage_name(w.pool_dtype))
     ref = O.paged_cross_attention(to_np(w.q[0]), to_np(w.q_norm_w[0]), pk[0], pv[0], w.page_table.cpu().numpy(),
                                   w.ctx_lens.cpu().numpy(), w.cu_seqlens_q.cpu().numpy(), w.page_size,
                                   w.softmax_scale, w.theta, w.eps)
@@ -250,7 +253,7 @@ def _check_full_step_attention(w, buf, before, slots, keys, values, reqs):
         for r in sel:
             cslots[r] = remap[int(slots[r]) // ps] * ps + int(slots[r]) % ps
         pkl, pvl = [pk], [pv]
-        O.scatter_into_pool(pkl, pvl, cslots, keys[:, l:l + 1], values[:, l:l + 1], ps, storage_name(w.dtype))
+        O.scatter_into_pool(pkl, pvl, cslots, keys[:, l:l + 1], values[:, l:l + 1], ps, storage_name(w.pool_dtype))
         ref = oracle_cross(w, l, reqs, pk, pv, rows)
         compare(rows_of(w, reqs, buf.cross_out[l]), np.concatenate([ref[b] for b in reqs]), f"cross L{l}")
         compare(buf.self_out[l], _oracle_self(w, l), f"self L{l}")
@@ -303,5 +306,98 @@ def test_config5_full_step_full_size():
     log(f"  live rows {live} of {len(slots)}")
     _check_write(w, buf, before, slots, keys, values)
     reqs = _sample(w, 3, 5)
+    log(f"  sampled requests {reqs}")
+    _check_full_step_attention(w, buf, before, slots, keys, values, reqs)
+
+
+# ------------------------------------------------------------ e4m3 KV pool
+# sglang/model.py ``_kv_fp8``: the write stores e4m3 at scale 1, cross-attention
+# quantizes each (request, head)'s query with scale amax / 448.
+
+
+@pytest.mark.parametrize("variant", ["default", "peaky", "token_major"])
+def test_fp8_pool_config2_all_rows(variant):
+    log(f"e4m3 pool, config 2 shape: {variant}")
+    kw = dict(weights="random")
+    if variant == "peaky":
+        kw["q_scale"] = 8.0
+    elif variant == "token_major":
+        kw["layout"] = "token_major"
+    w = make_workload(2, kv_fp8=True, **kw)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)))
+
+
+@pytest.mark.parametrize("n_cand", [2, 4])
+def test_fp8_pool_candidate_blocks(n_cand):
+    log(f"e4m3 pool, {n_cand} candidate blocks per request")
+    w = make_workload(2, weights="random", n_cand=n_cand, kv_fp8=True)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)), self_blocks=range(w.bs * n_cand))
+
+
+@pytest.mark.parametrize("ps,Dh", [(1, 128), (32, 128), (16, 64), (4, 64)])
+def test_fp8_pool_page_sizes_ragged(ps, Dh):
+    # empty and sub-tile contexts, one query row, a request with no rows
+    log(f"e4m3 pool, page size {ps}, Dh {Dh}, ragged rows")
+    ctx = [0, 1, 15, 17, 300, 1000]
+    nq = [16, 1, 16, 0, 9, 16]
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=1, H=3, Dh=Dh, ps=ps), kv_fp8=True)
+    dev = w.ctx_lens.device
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(13)
+    q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(torch.bfloat16)
+    w.q[0], w.cu_seqlens_q = q, cu
+    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    out = torch.full_like(q, float("nan"))
+    B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu, w.softmax_scale,
+                               w.theta, w.eps, ws, out=out)
+    torch.cuda.synchronize()
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows, q=q)
+    compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), f"cross e4m3 ps{ps} Dh{Dh}")
+    assert torch.all(out[:16] == 0), "an empty context must give exactly zero"
+    assert ws_error_word(ws) == 0
+
+
+def test_fp8_pool_write_and_step_small():
+    log("e4m3 pool: write (commit rule, placement, rounding) and the step on it")
+    w = make_workload(5, weights="random", scale_down=dict(bs=6, ctx=(20, 90), L=2, H=4, d_in=256), kv_fp8=True)
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    slots, keys, values = _write_oracle(w)
+    _check_write(w, buf, before, slots, keys, values)
+    _check_full_step_attention(w, buf, before, slots, keys, values, list(range(w.bs)))
+
+
+def test_fp8_pool_deterministic():
+    w = make_workload(2, weights="random", kv_fp8=True)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    first = buf.cross_out[0].clone()
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), buf.cross_out[0].view(torch.int16))
+
+
+def test_fp8_pool_full_step_full_size():
+    log("e4m3 pool: full draft step at full size (sampled requests)")
+    w = make_workload(5, kv_fp8=True)
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    slots, keys, values = _write_oracle(w)
+    _check_write(w, buf, before, slots, keys, values)
+    reqs = _sample(w, 2, 6)
     log(f"  sampled requests {reqs}")
     _check_full_step_attention(w, buf, before, slots, keys, values, reqs)
