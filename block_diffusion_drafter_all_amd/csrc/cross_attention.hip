@@ -620,14 +620,12 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
           for (int ch = 0; ch < NCH; ++ch)
             qop[f][ch] = load16(qrow + (int64_t)f * kQRows * a.H * D + ch * 4 * EPC + g * EPC);
       }
+      // O and l restart through the rescale below: its factor is 0 while the
+      // running max is -inf
 #pragma unroll
-      for (int f = 0; f < NQF; ++f) {
-        m_run[f] = kNegInf;
-        l_lane[f] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      }
+      for (int f = 0; f < NQF; ++f) m_run[f] = kNegInf;
     }
+    const bool start = (s.flags & kStart) != 0;
     f32x4_t p[NQF];
 #pragma unroll
     for (int f = 0; f < NQF; ++f) {
@@ -635,13 +633,17 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, s.k[ch], qop[f][ch]);
       float sv[4];
-      float mx = kNegInf;
+      if (s.mask == 0xFFFFu) {  // a full tile (wave-uniform): no key to mask
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = (s.mask >> (4 * g + i)) & 1u;
-        sv[i] = valid ? sc[i] * score_scale : kNegInf;
-        mx = fmaxf(mx, sv[i]);
+        for (int i = 0; i < 4; ++i) sv[i] = sc[i] * score_scale;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = (s.mask >> (4 * g + i)) & 1u;
+          sv[i] = valid ? sc[i] * score_scale : kNegInf;
+        }
       }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = wave_max_groups(mx);
       float psum = 0.f;
       if constexpr (NQF == 1) {
@@ -650,11 +652,11 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[f][i] = operand_value<PV>(exp2f(sv[i] - m_use));
+          p[f][i] = operand_value<PV>(exp2_hw(sv[i] - m_use));
           psum += p[f][i];
         }
-        if (__ballot(m_new != m_run[f]) != 0) {
-          const float alpha = exp2f(m_run[f] - m_use);
+        if (start || __ballot(m_new != m_run[f]) != 0) {
+          const float alpha = exp2_hw(m_run[f] - m_use);  // 0 on a pair's first tile
           l_lane[f] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[f][dt] *= alpha;
@@ -665,10 +667,11 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         // reference max moves only when a row's max exceeds it by more than
         // kRescaleSlack (log2 units), or on its first keys, so p <= 2^slack
         // and O, l rarely need rescaling; O / l is the same quotient.
-        const bool move = mx > m_run[f] + kRescaleSlack;  // false while both are -inf
+        // (a pair's first tile always moves it, which also clears O and l)
+        const bool move = start || mx > m_run[f] + kRescaleSlack;
         if (__ballot(move) != 0) {
           const float m_new = move ? mx : m_run[f];
-          const float alpha = (m_run[f] == kNegInf) ? 0.f : exp2f(m_run[f] - m_new);
+          const float alpha = (m_run[f] == kNegInf) ? 0.f : exp2_hw(m_run[f] - m_new);
           if (move) {
             l_lane[f] *= alpha;
 #pragma unroll
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[f][i] = operand_value<PV>(exp2f(sv[i] - m_use));
+          p[f][i] = operand_value<PV>(exp2_hw(sv[i] - m_use));
           psum += p[f][i];
         }
       }

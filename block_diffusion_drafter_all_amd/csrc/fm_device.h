@@ -259,15 +259,21 @@ __device__ __forceinline__ int out_col<E4m3>(int dt, int g) {
 template <class T>
 __device__ __forceinline__ void mma_pv(f32x4_t& acc, const f32x4_t& vt, const f32x4_t& p);
 
+// bf16 bits of two fp32 values that bf16 holds exactly (their high halves),
+// packed lo | hi << 16 by one byte permute.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// bf16 operands: vt comes from transpose_tile of bf16 or e4m3 data and p from
+// operand_value<Bf16>, so every value is bf16-representable and packing its
+// high half is exact.
 template <>
 __device__ __forceinline__ void mma_pv<Bf16>(f32x4_t& acc, const f32x4_t& vt, const f32x4_t& p) {
-  i16x4_t a, b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = (short)f32_to_bf16_bits(vt[i]);
-    b[i] = (short)f32_to_bf16_bits(p[i]);
-  }
-  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+  const u32x2_t a = {pack_hi16(vt[0], vt[1]), pack_hi16(vt[2], vt[3])};
+  const u32x2_t b = {pack_hi16(p[0], p[1]), pack_hi16(p[2], p[3])};
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b),
+                                                  acc, 0, 0, 0);
 }
 
 template <>
@@ -288,18 +294,36 @@ __device__ __forceinline__ float sel4(int g, float a0, float a1, float a2, float
   return g == 0 ? a0 : (g == 1 ? a1 : (g == 2 ? a2 : a3));
 }
 
+// Reductions over the four lane groups (lanes c, c+16, c+32, c+48) with the
+// gfx950 row swaps: v_permlane16_swap of x with itself leaves x's and its
+// xor-16 partner's values in the two results (in some order), and
+// v_permlane32_swap does the same for xor 32; no LDS round trip.
+__device__ __forceinline__ u32x2_t swap16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (u32x2_t){r[0], r[1]};
+}
+__device__ __forceinline__ u32x2_t swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return (u32x2_t){r[0], r[1]};
+}
+
 __device__ __forceinline__ float wave_sum_groups(float x) {
-  // Sum over the four lane groups (lanes c, c+16, c+32, c+48).
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  u32x2_t r = swap16(x);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = swap32(x);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_max_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  u32x2_t r = swap16(x);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = swap32(x);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+
+// 2^x by the hardware v_exp_f32 (about 1 ulp; results below 2^-126 may flush
+// to zero, which a softmax weight that small can take).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Inverse RoPE frequencies, float32, computed by the host (nearest float32 to
 // theta^(-2i/D)) and passed by value so every kernel sees identical bits.
