@@ -143,14 +143,19 @@ def round_to_e4m3(x: np.ndarray) -> np.ndarray:
     return np.copysign(r, x)
 
 
-def quantize_query_e4m3(q_hat: np.ndarray):
+def quantize_query_e4m3(q_hat: np.ndarray, static_scale=None):
     """The fp8 pool's query: one scale per (request, head), the largest
     magnitude over the request's rows and the head's channels divided by 448
     (at least 1e-12 / 448), and the e4m3 query ``q_hat / scale`` (the sglang
     model's ``_paged_cross_attention_fp8``: ``q_scale = amax / 448``,
     ``query8 = query / q_scale``).  ``q_hat (rows, D)`` of one (request, head);
-    returns ``(q8, scale)`` with ``q8 * scale`` the query the attention uses."""
+    returns ``(q8, scale)`` with ``q8 * scale`` the query the attention uses.
+    ``static_scale``: a fixed per-tensor scale instead (the vLLM model's
+    ``q_scale``: ``query / q_scale`` cast to e4m3, saturating here)."""
     q_hat = np.asarray(q_hat, dtype=np.float64)
+    if static_scale is not None:
+        scale = float(static_scale)
+        return round_to_e4m3(q_hat / scale), scale
     scale = max(float(np.max(np.abs(q_hat), initial=0.0)), 1e-12) / 448.0
     return round_to_e4m3(q_hat / scale), scale
 
@@ -256,12 +261,14 @@ def write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, page_size,
     return slots, keys, values
 
 
-def scatter_into_pool(pools_k, pools_v, slots, keys, values, page_size, dtype):
+def scatter_into_pool(pools_k, pools_v, slots, keys, values, page_size, dtype, kv_scales=None):
     """Store each written row into every layer's pool at its slot, rounded to
     the pool's storage type.  ``pools_k[l], pools_v[l]`` are logical float64
     arrays ``(pages, page_size, H, D)`` updated in place.  Live rows must name
     distinct slots (a precondition: the pages never write one slot twice in a
-    call)."""
+    call).  ``kv_scales (L, 2)``: an e4m3 pool's per-layer key and value
+    scales; the pool holds ``k / k_scale`` and ``v / v_scale`` (vllm/model.py
+    ``write_context_kv`` with ``kv_scales``; 1 when not given, as in sglang)."""
     live = np.nonzero(np.asarray(slots) >= 0)[0]
     taken = set()
     for r in live:
@@ -271,13 +278,15 @@ def scatter_into_pool(pools_k, pools_v, slots, keys, values, page_size, dtype):
         taken.add(s)
         page, off = divmod(s, page_size)
         for l in range(len(pools_k)):
-            pools_k[l][page, off] = round_to_storage(keys[r, l], dtype)
-            pools_v[l][page, off] = round_to_storage(values[r, l], dtype)
+            ks, vs = (1.0, 1.0) if kv_scales is None else (float(kv_scales[l][0]), float(kv_scales[l][1]))
+            pools_k[l][page, off] = round_to_storage(keys[r, l] / ks, dtype)
+            pools_v[l][page, off] = round_to_storage(values[r, l] / vs, dtype)
 
 
 def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
                           cu_seqlens_q, page_size, scale, theta, eps,
-                          requests=None, heads=None, block_size=16, kv_e4m3=False):
+                          requests=None, heads=None, block_size=16, kv_e4m3=False, q_scale=None,
+                          k_scale=1.0, v_scale=1.0):
     """Cross-attention of each request's draft rows onto its paged context.
 
     Row ``r`` of request ``b`` (``cu_seqlens_q[b] <= r < cu_seqlens_q[b+1]``)
@@ -291,9 +300,11 @@ def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
     attends, non-causally, to the keys/values at logical positions
     ``0 .. ctx_lens[b] - 1`` read through the page table.
 
-    ``kv_e4m3``: the pool holds e4m3 values (written with scale 1) and the
-    query is quantized to e4m3 per (request, head) first
-    (``quantize_query_e4m3``); the scores use the descaled query.
+    ``kv_e4m3``: the pool holds e4m3 codes and the query is quantized to
+    e4m3 first (``quantize_query_e4m3``): per (request, head) with amax / 448
+    (sglang), or with the fixed ``q_scale`` when given (vLLM).  The keys and
+    values the attention sees are ``k_scale`` and ``v_scale`` times the codes
+    (the descales; 1 in sglang), the query the descaled one.
 
     ``pool_k, pool_v``: logical ``(pages, page_size, H, D)`` arrays.  Returns
     float64 ``(total_q, H, D)``; rows of requests not in ``requests`` and heads
@@ -318,10 +329,12 @@ def paged_cross_attention(q, q_norm_w, pool_k, pool_v, page_table, ctx_lens,
         for h in hs:
             qh = rms_norm(q[r0:r1, h], q_norm_w, eps)
             qh = apply_rope(qh, positions, theta)
+            kh, vh = k_b[:, h], v_b[:, h]
             if kv_e4m3:
-                q8, qs = quantize_query_e4m3(qh)
+                q8, qs = quantize_query_e4m3(qh, q_scale)
                 qh = q8 * qs
-            out[r0:r1, h] = attention(qh, k_b[:, h], v_b[:, h], scale)
+                kh, vh = kh * float(k_scale), vh * float(v_scale)
+            out[r0:r1, h] = attention(qh, kh, vh, scale)
     return out
 
 

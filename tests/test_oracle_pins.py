@@ -267,6 +267,49 @@ def test_paged_cross_attention_e4m3_query_against_torch_fp8(rng):
     assert np.nanmax(np.abs(out - plain)) > 1e-6
 
 
+def test_fp8_static_and_tensor_scales(rng):
+    # vLLM's fp8 cache: static per-tensor q scale, per-tensor k/v descales.
+    c = _paged_case(rng, ctx=[70], nq=[16], H=1)
+    pk, pv = O.round_to_e4m3(c["pk"] * 4.0), O.round_to_e4m3(c["pv"] * 4.0)
+    theta, eps, scale = 1e6, 1e-6, c["D"] ** -0.5
+    args = (c["pt"], c["ctx"], c["cu"], c["ps"], scale, theta, eps)
+    dyn = O.paged_cross_attention(c["q"], c["w"], pk, pv, *args, kv_e4m3=True)
+    # one (request, head): the static scale equal to its amax / 448 is the dynamic case
+    qh = O.apply_rope(O.rms_norm(c["q"][:, 0], c["w"], eps), 70 + np.arange(16), theta)
+    stat = O.paged_cross_attention(c["q"], c["w"], pk, pv, *args, kv_e4m3=True, q_scale=np.abs(qh).max() / 448.0)
+    np.testing.assert_array_equal(stat, dyn)
+    # the output is linear in the value descale
+    v2 = O.paged_cross_attention(c["q"], c["w"], pk, pv, *args, kv_e4m3=True, v_scale=2.5)
+    np.testing.assert_allclose(v2, 2.5 * dyn, rtol=1e-12, atol=1e-14)
+    # a key descale multiplies the logits: k_scale = s with softmax scale / s is the same attention
+    k2 = O.paged_cross_attention(c["q"], c["w"], pk, pv, c["pt"], c["ctx"], c["cu"], c["ps"], scale / 2.0, theta,
+                                 eps, kv_e4m3=True, k_scale=2.0)
+    np.testing.assert_allclose(k2, dyn, rtol=1e-12, atol=1e-13)
+    # a static scale quantizes q^ / s with torch's cast, no per-row or per-request amax
+    s_fix = 0.01
+    q8 = (torch.from_numpy(qh) / s_fix).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64) * s_fix
+    t8 = lambda x: torch.from_numpy(x * 4.0).to(torch.float8_e4m3fn).to(torch.float64)  # noqa: E731
+    dk = t8(c["dense_k"][0][:, 0]) * 1.5      # logical context, cast by torch
+    dv = t8(c["dense_v"][0][:, 0]) * 0.5
+    ref = F.scaled_dot_product_attention(q8[None], dk[None], dv[None], scale=scale)[0]
+    got = O.paged_cross_attention(c["q"], c["w"], pk, pv, *args, kv_e4m3=True, q_scale=s_fix, k_scale=1.5,
+                                  v_scale=0.5)
+    np.testing.assert_allclose(got[:, 0], ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_scatter_divides_by_the_layer_scales(rng):
+    keys = rng.standard_normal((3, 2, 1, 8)) * 3
+    values = rng.standard_normal((3, 2, 1, 8)) * 3
+    pk = [np.zeros((2, 4, 1, 8)) for _ in range(2)]
+    pv = [np.zeros((2, 4, 1, 8)) for _ in range(2)]
+    O.scatter_into_pool(pk, pv, np.array([5, -1, 0]), keys, values, 4, "e4m3", kv_scales=[[1.0, 1.0], [0.5, 4.0]])
+    t = lambda x: torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()  # noqa: E731
+    np.testing.assert_array_equal(pk[0][1, 1], t(keys[0, 0]))
+    np.testing.assert_array_equal(pk[1][1, 1], t(keys[0, 1] / 0.5))
+    np.testing.assert_array_equal(pv[1][0, 0], t(values[2, 1] / 4.0))
+    assert not pk[0][0, 1].any() and not pv[1][0, 2].any()
+
+
 def test_paged_cross_attention_page_permutation_invariant(rng):
     c = _paged_case(rng, ctx=[100, 33, 16], nq=[16, 16, 16])
     args = (c["cu"], c["ps"], 0.125, 1e6, 1e-6)
