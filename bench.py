@@ -351,7 +351,7 @@ def main():
                 events["cross"][l][0].record()
             B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens,
                                        w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws,
-                                       out=buf.cross_out[l], max_q=w.max_q)
+                                       out=buf.cross_out[l], max_q=w.max_q, fp8_scales=w.fp8_scales(l))
             if events is not None:
                 events["cross"][l][1].record()
 

@@ -77,7 +77,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_write_context_kv.restype = ctypes.c_int
     lib.fm_write_context_kv.argtypes = [
         vp, c_i64, c_i32, ctypes.c_int, vp, vp, vp, vp, vp, c_i32, vp, c_i64, c_i32, c_i32,
-        ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, vp, vp, c_sz, vp,
+        ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp,
     ]
     lib.fm_cross_attention_workspace_size.restype = c_sz
     lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
@@ -86,7 +86,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_paged_cross_attention.restype = ctypes.c_int
     lib.fm_paged_cross_attention.argtypes = [
         vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
-        c_i32, f32, f32, f32, vp, vp, c_sz, vp,
+        c_i32, f32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp,
     ]
     lib.fm_block_self_attention.restype = ctypes.c_int
     lib.fm_block_self_attention.argtypes = [
@@ -168,10 +168,20 @@ def fm_write_context_kv_workspace_size(n_rows: int) -> int:
     return load_library().fm_write_context_kv_workspace_size(n_rows)
 
 
+def _floats(values):
+    """A host float array for the C ABI, or None."""
+    if values is None:
+        return None
+    flat = [float(v) for row in values for v in (row if hasattr(row, "__len__") else [row])]
+    return (ctypes.c_float * len(flat))(*flat)
+
+
 def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta,
-                        commit_lens=None, window=0, out_slots=None, ws=None):
+                        commit_lens=None, window=0, out_slots=None, ws=None, kv_scales=None):
     """Project, k-norm, rotate and scatter every layer's context K/V rows into
-    ``pools`` (a list of KVPool, one per layer).  Returns ``out_slots`` if given."""
+    ``pools`` (a list of KVPool, one per layer).  Returns ``out_slots`` if given.
+    ``kv_scales``: e4m3 pools only, one (k_scale, v_scale) per layer (the pool
+    receives k / k_scale and v / v_scale); None = 1."""
     lib = load_library()
     _need(x, "x")
     _need(w_kv, "w_kv", x.dtype)
@@ -195,6 +205,8 @@ def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, 
     descs = (fm_kv_pool * L)(*[p.descriptor() for p in pools])
     if any(p.k.dtype != pools[0].k.dtype for p in pools):
         raise TypeError("every layer's pool must have one dtype")
+    if kv_scales is not None and len(kv_scales) != L:
+        raise ValueError("kv_scales needs one (k_scale, v_scale) pair per layer")
     code = _dtype_code(x, pools[0].k.dtype)
     n_rows, d_in = x.shape
     if ws is None:
@@ -202,8 +214,8 @@ def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, 
     _check(lib.fm_write_context_kv(
         _ptr(x), n_rows, d_in, code, _ptr(w_kv), _ptr(k_norm_w), _ptr(row_req), _ptr(row_pos),
         _ptr(commit_lens), window, _ptr(page_table), page_table.stride(0), pools[0].page_size,
-        page_table.shape[0], descs, L, H, Dh, eps, rope_theta, _ptr(out_slots), _ptr(ws), ws.numel(),
-        _stream()))
+        page_table.shape[0], descs, L, H, Dh, eps, rope_theta, _floats(kv_scales), _ptr(out_slots), _ptr(ws),
+        ws.numel(), _stream()))
     return out_slots
 
 
@@ -221,10 +233,12 @@ def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16):
 
 
 def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,
-                             rope_theta, eps, ws, out=None, max_q=16):
+                             rope_theta, eps, ws, out=None, max_q=16, fp8_scales=None):
     """Paged cross-attention of ``q (total_q, H, Dh)`` onto ``pool``; the plan
     in ``ws`` must come from fm_plan_cross_attention with the same lengths and
-    ``max_q`` (query rows per request: 16 per draft block, up to 4 blocks)."""
+    ``max_q`` (query rows per request: 16 per draft block, up to 4 blocks).
+    ``fp8_scales``: e4m3 pools only, (q_scale, k_scale, v_scale): a fixed
+    query scale (0 = per request and head) and the key/value descales."""
     lib = load_library()
     _need(q, "q")
     _need(q_norm_w, "q_norm_w", torch.float32)
@@ -243,7 +257,7 @@ def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu
     _check(lib.fm_paged_cross_attention(
         _ptr(q), _dtype_code(q, pool.k.dtype), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
         page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), max_q, ctx_lens.shape[0], H, Dh,
-        softmax_scale, rope_theta, eps, _ptr(out), _ptr(ws), ws.numel(), _stream()))
+        softmax_scale, rope_theta, eps, _floats(fp8_scales), _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
 
 

@@ -134,8 +134,8 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
                         const float* k_norm_w, const int32_t* row_req, const int32_t* row_pos,
                         const int32_t* commit_lens, int32_t window, const int32_t* page_table, int64_t pt_stride,
                         int32_t page_size, int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
-                        float eps, float rope_theta, int32_t* out_slots, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        float eps, float rope_theta, const float* kv_scales, int32_t* out_slots, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   const char* fn = "fm_write_context_kv";
   if (n_rows < 0) return fail(FM_E_INVALID, "%s: n_rows %lld < 0", fn, (long long)n_rows);
   if (n_rows == 0) return ok();
@@ -160,6 +160,12 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
   }
   if (out_slots != nullptr && min_pages * (int64_t)page_size > INT32_MAX)
     return fail(FM_E_UNSUPPORTED, "%s: slots do not fit out_slots' int32", fn);
+  if (kv_scales != nullptr) {
+    if (dt != FM_BF16_E4M3) return fail(FM_E_INVALID, "%s: kv_scales apply to an e4m3 pool only", fn);
+    for (int i = 0; i < 2 * L; ++i)
+      if (!(kv_scales[i] > 0.f) || !std::isfinite(kv_scales[i]) || !std::isfinite(1.0 / kv_scales[i]))
+        return fail(FM_E_INVALID, "%s: kv_scales[%d] must be finite and > 0", fn, i);
+  }
   if (int s = check_ws(fn, ws, ws_bytes, fm::write_layout(n_rows).total)) return s;
 
   fm::WritePrepArgs p{};
@@ -187,7 +193,10 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
   g.eps = eps;
   g.ws = p.ws;
   g.lay = p.lay;
-  for (int l = 0; l < L; ++l) g.pools[l] = to_desc(pools[l]);
+  for (int l = 0; l < L; ++l) {
+    g.pools[l] = to_desc(pools[l]);
+    for (int kv = 0; kv < 2; ++kv) g.inv_scale[l][kv] = kv_scales ? (float)(1.0 / kv_scales[2 * l + kv]) : 1.0f;
+  }
   g.rope = rope_freqs(rope_theta, Dh);
   return from_hip(fm::launch_write(p, g, (int)dt, Dh, n_rows, stream), fn);
 }
@@ -224,8 +233,8 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
 int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
                              const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
                              const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs,
-                             int32_t H, int32_t Dh, float softmax_scale, float rope_theta, float eps, void* out,
-                             void* ws, size_t ws_bytes, hipStream_t stream) {
+                             int32_t H, int32_t Dh, float softmax_scale, float rope_theta, float eps,
+                             const float* fp8_scales, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "fm_paged_cross_attention";
   if (total_q < 0 || bs < 0) return fail(FM_E_INVALID, "%s: total_q and bs must be >= 0", fn);
   if (total_q == 0 || bs == 0) return ok();
@@ -245,6 +254,17 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   if (nqf == 0)
     return fail(FM_E_UNSUPPORTED, "%s: max_q %d above %d query rows per request", fn, max_q,
                 fm::kQRows * fm::kMaxQFrags);
+  float q_static = 0.f, k_descale = 1.f, v_descale = 1.f;
+  if (fp8_scales != nullptr) {
+    if (dt != FM_BF16_E4M3) return fail(FM_E_INVALID, "%s: fp8_scales apply to an e4m3 pool only", fn);
+    q_static = fp8_scales[0];
+    k_descale = fp8_scales[1];
+    v_descale = fp8_scales[2];
+    if (!(q_static >= 0.f) || !std::isfinite(q_static) || (q_static > 0.f && !std::isfinite(1.0 / q_static)))
+      return fail(FM_E_INVALID, "%s: fp8_scales[0] (query scale) must be 0 or finite and > 0", fn);
+    if (!(k_descale > 0.f) || !std::isfinite(k_descale) || !(v_descale > 0.f) || !std::isfinite(v_descale))
+      return fail(FM_E_INVALID, "%s: fp8_scales[1..2] (key, value descales) must be finite and > 0", fn);
+  }
   const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(), nqf);
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::CrossArgs a{};
@@ -260,8 +280,11 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   a.bs = bs;
   a.H = H;
   a.total_q = (int32_t)total_q;
-  a.qscale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  a.qscale_log2 = (float)((double)softmax_scale * (double)k_descale * 1.4426950408889634074);
   a.eps = eps;
+  a.q_static = q_static;
+  a.q_static_inv = q_static > 0.f ? (float)(1.0 / q_static) : 0.f;
+  a.v_descale = v_descale;
   a.ws = static_cast<uint8_t*>(ws);
   a.lay = lay;
   a.rope = rope_freqs(rope_theta, Dh);

@@ -189,7 +189,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
 // pool's storage type (rows past the request's count are zero), ready to be
 // loaded as MFMA operands.  Over an e4m3 pool (sglang/model.py
 // ``_paged_cross_attention_fp8``) the rows of one (request, head) share one
-// scale, their largest magnitude / 448 (at least 1e-12 / 448), and the stored
+// scale, their largest magnitude / 448 (at least 1e-12 / 448), or the fixed
+// per-tensor scale when one is given (vllm/model.py ``_dit``), and the stored
 // e4m3 row is q^ / scale, rounded once from fp32; the scale goes to q_scale.
 // A request with an empty context gets its zero output rows here instead.
 // One wavefront per (request, head).
@@ -236,11 +237,18 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
 #pragma unroll
       for (int j = 0; j < D / 4; ++j) amax = fmaxf(amax, fabsf(qf[f][j]));
     }
+    float qs, r;
+    if (a.q_static > 0.f) {
+      qs = a.q_static;
+      r = a.q_static_inv;
+    } else {
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-    const float am = fmaxf(amax, 1e-12f);
-    const float r = 448.0f / am;
-    if (lane == 0) ((float*)(a.ws + a.lay.q_scale))[(int64_t)b * a.H + h] = am / 448.0f;
+      for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+      const float am = fmaxf(amax, 1e-12f);
+      qs = am / 448.0f;
+      r = 448.0f / am;
+    }
+    if (lane == 0) ((float*)(a.ws + a.lay.q_scale))[(int64_t)b * a.H + h] = qs;
 #pragma unroll
     for (int f = 0; f < NQF; ++f) {
       const int k = kQRows * f + c;
@@ -398,7 +406,7 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
     if (k < nq) {
       st* orow = (st*)a.out + ((int64_t)(r0 + k) * a.H + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), acc[dt], inv);
+      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), acc[dt], inv * a.v_descale);
     }
   }
   if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -705,7 +713,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
           if (k < s.nq) {
             st* orow = (st*)a.out + ((int64_t)(s.r0 + k) * a.H + s.h) * D;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), o[f][dt], inv);
+            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), o[f][dt], inv * a.v_descale);
           }
         }
       } else {

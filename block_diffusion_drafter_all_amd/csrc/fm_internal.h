@@ -128,8 +128,11 @@ struct CrossArgs {
   const int32_t* cu_q;
   int32_t bs, H;
   int32_t total_q;          // rows of q / out; rows at or past it are never touched
-  float qscale_log2;        // softmax_scale * log2(e)
+  float qscale_log2;        // softmax_scale * log2(e) (times the key descale over e4m3)
   float eps;
+  float q_static;           // e4m3 pool: a fixed query scale, or 0 for amax / 448 per (request, head)
+  float q_static_inv;       // 1 / q_static
+  float v_descale;          // e4m3 pool: the value descale (1 otherwise)
   uint8_t* ws;
   PlanLayout lay;
   RopeFreqs rope;
@@ -198,6 +201,7 @@ struct WriteGemmArgs {
   uint8_t* ws;
   WriteLayout lay;
   PoolDesc pools[kMaxLayers];
+  float inv_scale[kMaxLayers][2];  // e4m3 pool: 1 / (key, value) scale of each layer (1 otherwise)
   RopeFreqs rope;
 };
 

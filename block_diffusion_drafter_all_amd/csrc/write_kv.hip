@@ -151,8 +151,9 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
     const PoolDesc& P = a.pools[l];
     pst* dst = (pst*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
                (int64_t)h * P.head_stride + 4 * g;
+    const float sc = a.inv_scale[l][kv];
 #pragma unroll
-    for (int ct = 0; ct < NDT; ++ct) store4<PT>(dst + 16 * ct, acc[ct], 1.0f);
+    for (int ct = 0; ct < NDT; ++ct) store4<PT>(dst + 16 * ct, acc[ct], sc);
   }
 }
 
@@ -355,6 +356,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     const float fpos = (float)((const int32_t*)(ws + a.lay.live_pos))[lic];
     pst* dst = (pst*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
                (int64_t)h * P.head_stride + 4 * fchunk;
+    const float sc = a.inv_scale[l][kv];
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
             v[p2 + 1] = y1 * cs + y0 * sn;
           }
         }
-        if (has) store4<PT>(dst + 32 * cg + 8 * q, (f32x4_t){v[0], v[1], v[2], v[3]}, 1.0f);
+        if (has) store4<PT>(dst + 32 * cg + 8 * q, (f32x4_t){v[0], v[1], v[2], v[3]}, sc);
       }
   }
 }

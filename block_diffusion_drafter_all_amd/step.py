@@ -48,7 +48,7 @@ def write_context(w: Workload, buf: StepBuffers) -> None:
     wr = w.write
     B.fm_write_context_kv(wr.x, wr.w_kv, wr.k_norm_w, wr.row_req, wr.row_pos, w.page_table, w.pools, w.eps,
                           w.theta, commit_lens=wr.commit_lens, window=wr.window, out_slots=buf.out_slots,
-                          ws=buf.write_ws)
+                          ws=buf.write_ws, kv_scales=w.kv_scales)
 
 
 def plan(w: Workload, buf: StepBuffers) -> None:
@@ -59,7 +59,8 @@ def layer(w: Workload, buf: StepBuffers, l: int) -> None:
     B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.block_ctx_lens, w.softmax_scale,
                               w.theta, w.eps, out=buf.self_out[l])
     B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens, w.cu_seqlens_q,
-                               w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=buf.cross_out[l], max_q=w.max_q)
+                               w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=buf.cross_out[l], max_q=w.max_q,
+                               fp8_scales=w.fp8_scales(l))
 
 
 def run_step(w: Workload, buf: StepBuffers) -> None:

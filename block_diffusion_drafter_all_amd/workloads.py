@@ -59,6 +59,8 @@ class Workload:
     self_k_norm_w: list                # L x (Dh,) fp32
     write: WriteInputs | None = None
     n_cand: int = 1                    # candidate blocks per request (tree drafting)
+    kv_scales: list | None = None      # e4m3 pool: (k_scale, v_scale) per layer (None = 1)
+    q_scales: list | None = None       # e4m3 pool: fixed query scale per layer (None = per request and head)
     eps: float = EPS
     theta: float = THETA
     meta: dict = field(default_factory=dict)
@@ -78,6 +80,14 @@ class Workload:
     def pool_dtype(self) -> torch.dtype:
         """Element type of the KV pool: the activation type, or e4m3."""
         return self.pools[0].k.dtype
+
+    def fp8_scales(self, layer: int):
+        """(q_scale, k_scale, v_scale) of a layer's cross-attention, or None."""
+        if self.kv_scales is None and self.q_scales is None:
+            return None
+        q = 0.0 if self.q_scales is None else self.q_scales[layer]
+        k, v = (1.0, 1.0) if self.kv_scales is None else self.kv_scales[layer]
+        return (q, k, v)
 
     @property
     def softmax_scale(self) -> float:

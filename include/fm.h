@@ -120,6 +120,11 @@ size_t fm_write_context_kv_workspace_size(int64_t n_rows);
  * pools      HOST array [L]; L <= 16.
  * H, Dh      heads and head dim; Dh in {64, 128}.  d_in a multiple of 64.
  * eps        RMSNorm epsilon;  rope_theta  RoPE base.
+ * kv_scales  HOST float [L][2] (key scale, value scale of each layer) or NULL
+ *            (all 1).  e4m3 pools only (FM_E_INVALID otherwise): the pool
+ *            receives e4m3(k / k_scale) and e4m3(v / v_scale), as vLLM's
+ *            calibrated fp8 caches do (vllm/model.py ``write_context_kv`` with
+ *            ``kv_scales``); every scale finite and > 0.
  * out_slots  DEVICE int32 [n_rows] or NULL: slot written by each row, -1 if skipped.
  * ws         DEVICE workspace of fm_write_context_kv_workspace_size(n_rows)
  *            bytes, 256-byte aligned; its contents need no initialisation.
@@ -132,7 +137,7 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
                         const int32_t* commit_lens, int32_t window,
                         const int32_t* page_table, int64_t pt_stride, int32_t page_size,
                         int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
-                        float eps, float rope_theta, int32_t* out_slots,
+                        float eps, float rope_theta, const float* kv_scales, int32_t* out_slots,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------ cross-attention -- */
@@ -178,8 +183,14 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  * Over an e4m3 pool (FM_BF16_E4M3; sglang/model.py ``_paged_cross_attention_fp8``)
  * q^ is first quantized per (request, head): s = max(max |q^|, 1e-12) / 448
  * over the request's rows and the head's channels, q8 = e4m3(q^ / s) (nearest,
- * ties to even, from fp32), and the scores use s * q8 (the softmax weights
- * stay bf16; the e4m3 values enter the products exactly).
+ * ties to even, from fp32, saturating at +-448), and the scores use s * q8
+ * (the softmax weights stay bf16; the e4m3 values enter the products exactly).
+ * fp8_scales (HOST float[3] or NULL) = {q_scale, k_scale, v_scale} of vLLM's
+ * per-tensor fp8 caches (vllm/model.py ``_dit``, ``paged_cross_attention``
+ * descales): q_scale > 0 replaces s by that fixed scale (0 keeps the
+ * per-(request, head) one); keys and values enter as k_scale and v_scale
+ * times their codes.  NULL = {0, 1, 1}.  e4m3 pools only (FM_E_INVALID
+ * otherwise); scales finite, k_scale and v_scale > 0.
  *
  * q, out      DEVICE [total_q, H, Dh] contiguous, the activation type of dt.
  * q_norm_w    DEVICE fp32 [Dh].
@@ -202,8 +213,8 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
                              const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride,
                              int32_t page_size, const int32_t* ctx_lens,
                              const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs, int32_t H, int32_t Dh,
-                             float softmax_scale, float rope_theta, float eps, void* out,
-                             void* ws, size_t ws_bytes, hipStream_t stream);
+                             float softmax_scale, float rope_theta, float eps, const float* fp8_scales,
+                             void* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------- self-attention -- */
 

@@ -107,13 +107,15 @@ def oracle_cross(w, layer: int, reqs, pk, pv, pt_rows, q=None):
     ctx = w.ctx_lens.cpu().numpy()
     out = {}
     width = max([len(r) for r in pt_rows] + [1])
+    fp8 = w.fp8_scales(layer)
+    scales = {} if fp8 is None else dict(q_scale=fp8[0] or None, k_scale=fp8[1], v_scale=fp8[2])
     for i, b in enumerate(reqs):
         pt = np.zeros((1, width), dtype=np.int64)
         pt[0, :len(pt_rows[i])] = pt_rows[i]
         r0, r1 = cu[b], cu[b + 1]
         o = O.paged_cross_attention(q[r0:r1], to_np(w.q_norm_w[layer]), pk, pv, pt, [ctx[b]], [0, r1 - r0],
                                     w.page_size, w.softmax_scale, w.theta, w.eps,
-                                    kv_e4m3=w.pools[layer].k.dtype == torch.float8_e4m3fn)
+                                    kv_e4m3=w.pools[layer].k.dtype == torch.float8_e4m3fn, **scales)
         out[b] = o
     return out
 

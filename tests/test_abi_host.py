@@ -74,7 +74,7 @@ def _cross(lib, **over):
                                         ctypes.byref(pool) if pool is not None else None,
                                         args["pt"], args["pt_stride"], args["ps"], args["ctx"], args["cu"],
                                         args["max_q"], args["bs"], args["H"], args["Dh"], args["scale"], args["theta"],
-                                        args["eps"], args["out"], args["ws"], args["ws_bytes"], None)
+                                        args["eps"], args.get("fp8"), args["out"], args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("over,status,needle", [
@@ -87,6 +87,10 @@ def _cross(lib, **over):
     (dict(dt=3), B.FM_E_UNSUPPORTED, "dtype"),
     # e4m3 elements are one byte: a stride of 72 elements is 144 bytes in bf16, 72 in e4m3
     (dict(dt=B.FM_BF16_E4M3, pool=B.fm_kv_pool(FAKE, FAKE, 4, 4096, 72, 64)), B.FM_E_INVALID, "16 bytes"),
+    (dict(fp8=B._floats([0.0, 1.0, 1.0])), B.FM_E_INVALID, "e4m3 pool only"),
+    (dict(dt=B.FM_BF16_E4M3, fp8=B._floats([-1.0, 1.0, 1.0])), B.FM_E_INVALID, "query scale"),
+    (dict(dt=B.FM_BF16_E4M3, fp8=B._floats([0.0, 0.0, 1.0])), B.FM_E_INVALID, "descales"),
+    (dict(dt=B.FM_BF16_E4M3, fp8=B._floats([0.0, 1.0, float("nan")])), B.FM_E_INVALID, "descales"),
     (dict(ps=12), B.FM_E_UNSUPPORTED, "page_size"),
     (dict(H=0), B.FM_E_INVALID, "H"),
     (dict(ws=None), B.FM_E_WORKSPACE, "workspace"),
@@ -127,7 +131,8 @@ def _write(lib, **over):
     a.update(over)
     return lib.fm_write_context_kv(a["x"], a["n_rows"], a["d_in"], a["dt"], a["w"], a["kn"], a["rr"], a["rp"],
                                    a["cl"], a["win"], a["pt"], a["pt_stride"], a["ps"], a["bs"], a["pools"], a["L"],
-                                   a["H"], a["Dh"], a["eps"], a["theta"], a["slots"], a["ws"], a["ws_bytes"], None)
+                                   a["H"], a["Dh"], a["eps"], a["theta"], a.get("kvs"), a["slots"], a["ws"],
+                                   a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("over,status,needle", [
@@ -141,6 +146,9 @@ def _write(lib, **over):
     (dict(n_rows=-1), B.FM_E_INVALID, "n_rows"),
     (dict(dt=B.FM_BF16_E4M3, pools=(B.fm_kv_pool * 2)(_pool(), B.fm_kv_pool(FAKE, FAKE, 4, 4096, 256, 8))),
      B.FM_E_INVALID, "16 bytes"),
+    (dict(kvs=B._floats([1.0, 1.0, 1.0, 1.0])), B.FM_E_INVALID, "e4m3 pool only"),
+    (dict(dt=B.FM_BF16_E4M3, kvs=B._floats([1.0, 1.0, 0.0, 1.0])), B.FM_E_INVALID, "kv_scales[2]"),
+    (dict(dt=B.FM_BF16_E4M3, kvs=B._floats([1.0, float("inf"), 1.0, 1.0])), B.FM_E_INVALID, "kv_scales[1]"),
 ])
 def test_write_rejects(lib, over, status, needle):
     assert _write(lib, **over) == status

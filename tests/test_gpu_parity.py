@@ -78,8 +78,9 @@ def _check_write(w, buf, before, slots, keys, values):
         got_k = w.pools[l].k[sl // ps, sl % ps]
         got_v = w.pools[l].v[sl // ps, sl % ps]
         if w.pool_dtype == torch.float8_e4m3fn:
-            check_e4m3_rounding(got_k, keys[live, l], f"written K L{l} (e4m3)")
-            check_e4m3_rounding(got_v, values[live, l], f"written V L{l} (e4m3)")
+            ks, vs = (1.0, 1.0) if w.kv_scales is None else w.kv_scales[l]
+            check_e4m3_rounding(got_k, keys[live, l] / ks, f"written K L{l} (e4m3)")
+            check_e4m3_rounding(got_v, values[live, l] / vs, f"written V L{l} (e4m3)")
         else:
             compare(got_k, keys[live, l], f"written K L{l}")
             compare(got_v, values[live, l], f"written V L{l}")
@@ -97,7 +98,7 @@ def test_config1_full_step():
     # oracle pool = pre-write pages + the oracle's own write
     pk = [to_np(before[0][0])]
     pv = [to_np(before[0][1])]
-    O.scatter_into_pool(pk, pv, slots, keys, values, w.page_size, storage_name(w.pool_dtype))
+    O.scatter_into_pool(pk, pv, slots, keys, values, w.page_size, storage_name(w.pool_dtype), kv_scales=w.kv_scales)
     ref = O.paged_cross_attention(to_np(w.q[0]), to_np(w.q_norm_w[0]), pk[0], pv[0], w.page_table.cpu().numpy(),
                                   w.ctx_lens.cpu().numpy(), w.cu_seqlens_q.cpu().numpy(), w.page_size,
                                   w.softmax_scale, w.theta, w.eps)
@@ -253,7 +254,8 @@ def _check_full_step_attention(w, buf, before, slots, keys, values, reqs):
         for r in sel:
             cslots[r] = remap[int(slots[r]) // ps] * ps + int(slots[r]) % ps
         pkl, pvl = [pk], [pv]
-        O.scatter_into_pool(pkl, pvl, cslots, keys[:, l:l + 1], values[:, l:l + 1], ps, storage_name(w.pool_dtype))
+        O.scatter_into_pool(pkl, pvl, cslots, keys[:, l:l + 1], values[:, l:l + 1], ps, storage_name(w.pool_dtype),
+                            kv_scales=None if w.kv_scales is None else w.kv_scales[l:l + 1])
         ref = oracle_cross(w, l, reqs, pk, pv, rows)
         compare(rows_of(w, reqs, buf.cross_out[l]), np.concatenate([ref[b] for b in reqs]), f"cross L{l}")
         compare(buf.self_out[l], _oracle_self(w, l), f"self L{l}")
@@ -401,3 +403,33 @@ def test_fp8_pool_full_step_full_size():
     reqs = _sample(w, 2, 6)
     log(f"  sampled requests {reqs}")
     _check_full_step_attention(w, buf, before, slots, keys, values, reqs)
+
+
+@pytest.mark.parametrize("q_static", [True, False])
+def test_fp8_pool_per_tensor_scales_small_step(q_static):
+    # vLLM's calibrated fp8 cache: per-layer k/v scales in the write and as
+    # descales in the attention, a fixed per-layer query scale (or, with
+    # q_static False, sglang's per-(request, head) one with the k/v scales).
+    log(f"e4m3 pool with per-tensor scales, static q scale: {q_static}")
+    w = make_workload(5, weights="random", scale_down=dict(bs=6, ctx=(20, 90), L=2, H=4, d_in=256), kv_fp8=True)
+    w.kv_scales = [(0.25, 0.5), (2.0, 0.125)]
+    if q_static:
+        w.q_scales = [1.0 / 64, 1.0 / 128]
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    slots, keys, values = _write_oracle(w)
+    _check_write(w, buf, before, slots, keys, values)
+    _check_full_step_attention(w, buf, before, slots, keys, values, list(range(w.bs)))
+
+
+def test_fp8_pool_static_q_scale_saturates():
+    # a fixed query scale small enough that q^ / scale passes 448: codes saturate
+    log("e4m3 pool: static query scale with saturation")
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=[40, 300, 1000], L=1, H=2), kv_fp8=True)
+    w.q_scales = [1.0 / 512]
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)))
