@@ -80,9 +80,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp,
     ]
     lib.fm_cross_attention_workspace_size.restype = c_sz
-    lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]
     lib.fm_plan_cross_attention.restype = ctypes.c_int
-    lib.fm_plan_cross_attention.argtypes = [vp, c_i32, c_i32, c_i32, c_i32, vp, c_sz, vp]
+    lib.fm_plan_cross_attention.argtypes = [vp, c_i32, c_i32, c_i32, c_i32, ctypes.c_int, vp, c_sz, vp]
     lib.fm_paged_cross_attention.restype = ctypes.c_int
     lib.fm_paged_cross_attention.argtypes = [
         vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
@@ -219,17 +219,27 @@ def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, 
     return out_slots
 
 
-def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16) -> int:
-    return load_library().fm_cross_attention_workspace_size(bs, H, Dh, max_q)
+def _pool_code(pool_dtype) -> int:
+    """fm_dtype of the calls over a pool of ``pool_dtype``."""
+    codes = {torch.float32: FM_F32, torch.bfloat16: FM_BF16, torch.float8_e4m3fn: FM_BF16_E4M3}
+    if pool_dtype not in codes:
+        raise TypeError(f"unsupported pool dtype {pool_dtype}")
+    return codes[pool_dtype]
 
 
-def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16):
-    """Build the per-step tile schedule into ``ws`` (every layer reuses it)."""
+def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16,
+                                      pool_dtype=torch.bfloat16) -> int:
+    return load_library().fm_cross_attention_workspace_size(bs, H, Dh, max_q, _pool_code(pool_dtype))
+
+
+def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16, pool_dtype=torch.bfloat16):
+    """Build the per-step tile schedule into ``ws`` (every layer reuses it) for
+    calls over pools of ``pool_dtype``."""
     lib = load_library()
     _need(ctx_lens, "ctx_lens", torch.int32)
     _need(ws, "ws", torch.uint8)
-    _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), ctx_lens.shape[0], H, Dh, max_q, _ptr(ws), ws.numel(),
-                                       _stream()))
+    _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), ctx_lens.shape[0], H, Dh, max_q, _pool_code(pool_dtype),
+                                       _ptr(ws), ws.numel(), _stream()))
 
 
 def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,

@@ -88,15 +88,14 @@ int check_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need) {
   return FM_OK;
 }
 
-// Resident cross-attention wavefronts: compute units of the current device
-// times the waves one CU keeps resident.  A device that cannot be queried
-// (no GPU) is taken to have 256 CUs, MI355X's count.
-int plan_waves() {
+// Compute units of the current device; a device that cannot be queried (no
+// GPU) is taken to have 256 CUs, MI355X's count.
+int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
-    return 256 * fm::kWavesPerCU;
+    return 256;
   }
   if (cached[dev] == 0) {
     int cus = 0;
@@ -104,9 +103,15 @@ int plan_waves() {
       (void)hipGetLastError();
       cus = 256;
     }
-    cached[dev] = std::min(cus * fm::kWavesPerCU, fm::kMaxPlanWaves);
+    cached[dev] = cus;
   }
   return cached[dev];
+}
+
+// Resident cross-attention wavefronts for a pool type: CUs x 4 SIMDs x the
+// waves per SIMD that type's kernel keeps.
+int plan_waves(fm_dtype dt) {
+  return std::min(device_cus() * 4 * fm::cross_occupancy((int)dt), fm::kMaxPlanWaves);
 }
 
 fm::PoolDesc to_desc(const fm_kv_pool& p) {
@@ -201,15 +206,18 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
   return from_hip(fm::launch_write(p, g, (int)dt, Dh, n_rows, stream), fn);
 }
 
-size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q) {
+size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt) {
   const int nqf = fm::q_frags(max_q);
   if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || nqf == 0) return 0;
-  return fm::plan_layout(bs, H, Dh, plan_waves(), nqf).total;
+  if (dt != FM_F32 && dt != FM_BF16 && dt != FM_BF16_E4M3) return 0;
+  return fm::plan_layout(bs, H, Dh, plan_waves(dt), nqf).total;
 }
 
-int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "fm_plan_cross_attention";
+  if (dt != FM_F32 && dt != FM_BF16 && dt != FM_BF16_E4M3)
+    return fail(FM_E_UNSUPPORTED, "%s: dtype %d is not FM_F32, FM_BF16 or FM_BF16_E4M3", fn, (int)dt);
   if (bs < 0) return fail(FM_E_INVALID, "%s: bs %d < 0", fn, bs);
   if (H < 1) return fail(FM_E_INVALID, "%s: H = %d must be >= 1", fn, H);
   if (Dh != 64 && Dh != 128) return fail(FM_E_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", fn, Dh);
@@ -219,7 +227,7 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
                 fm::kQRows * fm::kMaxQFrags);
   if (bs > 0 && !ctx_lens) return fail(FM_E_INVALID, "%s: ctx_lens is null", fn);
   if ((int64_t)bs * H > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: bs * H too large", fn);
-  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(), fm::q_frags(max_q));
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(dt), fm::q_frags(max_q));
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::PlanArgs a{};
   a.ctx_lens = ctx_lens;
@@ -265,7 +273,7 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
     if (!(k_descale > 0.f) || !std::isfinite(k_descale) || !(v_descale > 0.f) || !std::isfinite(v_descale))
       return fail(FM_E_INVALID, "%s: fp8_scales[1..2] (key, value descales) must be finite and > 0", fn);
   }
-  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(), nqf);
+  const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(dt), nqf);
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
   fm::CrossArgs a{};
   a.q = q;

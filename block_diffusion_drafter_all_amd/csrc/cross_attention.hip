@@ -46,10 +46,12 @@ constexpr int kWin = 512;  // page ids cached per wave
 #endif
 
 // Slot flags.
-constexpr int kStart = 1;  // first tile of a segment: reset the softmax state, take the query rows
-constexpr int kEnd = 2;    // last tile of a segment: write the output or a partial
-constexpr int kWhole = 4;  // the segment is the whole (request, head) pair: final output
-constexpr int kPart1 = 8;  // partial goes to the wave's second partial slot
+// Tile flags, kept above the 16 key-mask bits of a stream slot's word.
+constexpr uint32_t kStart = 1u << 16;  // first tile of a segment: reset the softmax state, take the query rows
+constexpr uint32_t kEnd = 2u << 16;    // last tile of a segment: write the output or a partial
+constexpr uint32_t kWhole = 4u << 16;  // the segment is the whole (request, head) pair: final output
+constexpr uint32_t kPart1 = 8u << 16;  // partial goes to the wave's second partial slot
+constexpr uint32_t kKeyMask = 0xFFFFu;
 
 __device__ __forceinline__ int64_t shfl_up_i64(int64_t x, int d) {
   const int lo = __shfl_up((int)(uint32_t)(uint64_t)x, d);
@@ -294,15 +296,14 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
 
 // One K/V tile in the load ring.  With one query fragment, the pair's
 // prepared query rows ride along with its first tile (q); with more, they are
-// read when that tile is computed (q unused).
-template <class T, int D, int NQF>
+// read when that tile is computed (q unused).  Which pair a tile belongs to is
+// not stored: the compute side walks the same pair sequence as the loader.
+template <class T, int D, bool QIN>
 struct StreamSlot {
   u32x4_t k[D / (4 * T::EPC)];
   u32x4_t v[D / (4 * T::EPC)];
-  u32x4_t q[NQF == 1 ? D / (4 * T::EPC) : 1];
-  uint32_t mask;  // bit t: token t of the tile is a valid key
-  int b, h, r0, nq, flags;
-  float qs;       // e4m3 pool: the pair's query scale (read with its first tile)
+  u32x4_t q[QIN ? D / (4 * T::EPC) : 1];
+  uint32_t mf;  // bits 0-15: token t of the tile is a valid key; above: kStart, kEnd, kWhole, kPart1
 };
 
 // The type of the PV contraction's operands: an e4m3 pool's values enter it
@@ -416,12 +417,14 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
 // the tile's base address is wave-uniform (scalar), with a per-lane offset that
 // never changes.
 // T: query/output rows; PT: the pool (T itself, or e4m3 under bf16 rows).
-template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
-__global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kernel(CrossArgs a) {
+template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF, int OCC>
+__global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   typedef typename T::storage st;
   typedef typename PT::storage pst;
   typedef typename PvType<PT>::type PV;
   constexpr bool kFp8 = std::is_same<PT, E4m3>::value;
+  // the pair's query rows ride with its first tile (one fragment), else they are read when it is computed
+  constexpr bool kQIn = NQF == 1;
   constexpr int EPC = PT::EPC;
   constexpr int NCH = D / (4 * EPC);
   constexpr int NDT = D / 16;
@@ -453,12 +456,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
 
   // ---- loader state (wave-uniform) ----
   int lb = rec.b, lh = rec.h, lk = rec.k;
-  int lctx = rec.ctx, lT = tiles_of(rec.ctx), lr0 = 0, lnq = 0;
-  auto query_rows = [&](int b) {
-    lr0 = max(0, sload_i32(a.cu_q + b));
-    lnq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - lr0, kQRows * NQF));
-  };
-  query_rows(lb);
+  int lctx = rec.ctx, lT = tiles_of(rec.ctx);
   bool exhausted = false;  // set only if the lengths changed after the plan was made
   bool seg_first = true, seg_from0 = (lk == 0);
   int wreq = -1, wbase = 0;
@@ -501,7 +499,6 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         lctx = max(0, sload_i32(a.ctx_lens + lb));
         lT = tiles_of(lctx);
       } while (lT == 0);
-      if (!exhausted) query_rows(lb);
     }
     exhausted = exhausted || lT == 0;
   };
@@ -523,13 +520,13 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     pg_have = true;
   };
 
-  auto load_slot = [&](StreamSlot<PT, D, NQF>& s, int j) {
+  auto load_slot = [&](StreamSlot<PT, D, kQIn>& s, int j) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
-    s.flags = 0;
+    uint32_t flags = 0;
     if (j < n_tiles && !exhausted) {
       const bool last_of_pair = lk == lT - 1;
-      int flags = (lk == 0 || j == 0) ? kStart : 0;
+      flags = (lk == 0 || j == 0) ? kStart : 0;
       if (last_of_pair || j == n_tiles - 1)
         flags |= kEnd | ((seg_from0 && last_of_pair) ? kWhole : 0) | (seg_first ? 0 : kPart1);
       const int tb = lk << 4;
@@ -560,17 +557,11 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
               (page_ok ? (int64_t)page * a.pool.page_stride + (int64_t)(tok_c & ps_mask) * a.pool.slot_stride : 0);
         kv_last = off;
       }
-      if (NQF == 1 && (flags & kStart)) {  // this pair's prepared query rows ride along with its first tile
+      if (kQIn && (flags & kStart)) {  // this pair's prepared query rows ride along with its first tile
         const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) s.q[ch] = load16(qrow + ch * 4 * EPC + g * EPC);
       }
-      if (kFp8 && (flags & kStart)) s.qs = load_f32((const float*)(ws + a.lay.q_scale) + (int64_t)lb * a.H + lh);
-      s.b = lb;
-      s.h = lh;
-      s.r0 = lr0;
-      s.nq = lnq;
-      s.flags = flags;
       ++lk;
       if (j + 1 < n_tiles) {
         advance_if_done();
@@ -593,7 +584,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
         s.v[ch] = load16_stream(vpool + off + ch * 4 * EPC + g * EPC);
       }
     }
-    s.mask = (uint32_t)(__ballot(ok) & 0xffffull);
+    s.mf = flags | (uint32_t)(__ballot(ok) & 0xffffull);
     bad_page |= __ballot(bad) != 0;
   };
 
@@ -604,6 +595,24 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   float l_lane[NQF];  // this lane's share of the running denominator
   int cut_b[2] = {-1, -1}, cut_h[2] = {0, 0};  // pairs this wave left partials of
   float score_scale = a.qscale_log2;  // softmax scale * log2(e), times the pair's query scale over e4m3
+  // ---- compute-side pair cursor: the pair of the slot being computed ----
+  // The wave's first tile belongs to its record's pair; every later kStart
+  // is the next pair with tiles, in the order the loader takes them.
+  int cb = rec.b, chh = rec.h, cr0 = 0, cnq = 0;
+  bool c_fresh = true;
+  auto c_rows = [&]() {
+    cr0 = max(0, sload_i32(a.cu_q + cb));
+    cnq = max(0, min(min(sload_i32(a.cu_q + cb + 1), a.total_q) - cr0, kQRows * NQF));
+  };
+  c_rows();
+  auto c_next_pair = [&]() {
+    if (++chh < a.H) return;
+    chh = 0;
+    do {
+      ++cb;
+    } while (cb < a.bs - 1 && tiles_of(sload_i32(a.ctx_lens + cb)) == 0);
+    c_rows();
+  };
 #pragma unroll
   for (int f = 0; f < NQF; ++f) {
     m_run[f] = kNegInf;
@@ -614,14 +623,17 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
     for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_slot = [&](const StreamSlot<PT, D, NQF>& s) {
-    if (s.flags & kStart) {
-      if (kFp8) score_scale = a.qscale_log2 * s.qs;
-      if (NQF == 1) {
+  auto compute_slot = [&](const StreamSlot<PT, D, kQIn>& s) {
+    const uint32_t sflags = s.mf & ~kKeyMask;
+    if (sflags & kStart) {
+      if (!c_fresh) c_next_pair();
+      c_fresh = false;
+      if (kFp8) score_scale = a.qscale_log2 * sload_f32((const float*)(ws + a.lay.q_scale) + (int64_t)cb * a.H + chh);
+      if constexpr (kQIn) {
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) qop[0][ch] = s.q[ch];
       } else {  // every fragment's prepared rows, read now
-        const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)s.b * kQRows * NQF + c) * a.H + s.h) * D;
+        const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)cb * kQRows * NQF + c) * a.H + chh) * D;
 #pragma unroll
         for (int f = 0; f < NQF; ++f)
 #pragma unroll
@@ -633,7 +645,8 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
 #pragma unroll
       for (int f = 0; f < NQF; ++f) m_run[f] = kNegInf;
     }
-    const bool start = (s.flags & kStart) != 0;
+    const bool start = (sflags & kStart) != 0;
+    const uint32_t smask = s.mf & kKeyMask;
     f32x4_t p[NQF];
 #pragma unroll
     for (int f = 0; f < NQF; ++f) {
@@ -641,58 +654,40 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, s.k[ch], qop[f][ch]);
       float sv[4];
-      if (s.mask == 0xFFFFu) {  // a full tile (wave-uniform): no key to mask
+      if (smask == kKeyMask) {  // a full tile (wave-uniform): no key to mask
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[i] = sc[i] * score_scale;
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool valid = (s.mask >> (4 * g + i)) & 1u;
+          const bool valid = (smask >> (4 * g + i)) & 1u;
           sv[i] = valid ? sc[i] * score_scale : kNegInf;
         }
       }
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = wave_max_groups(mx);
       float psum = 0.f;
-      if constexpr (NQF == 1) {
-        // the reference max follows the running max: rescale whenever a row's max moves
-        const float m_new = fmaxf(m_run[f], mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[f][i] = operand_value<PV>(exp2_hw(sv[i] - m_use));
-          psum += p[f][i];
-        }
-        if (start || __ballot(m_new != m_run[f]) != 0) {
-          const float alpha = exp2_hw(m_run[f] - m_use);  // 0 on a pair's first tile
+      // Lazy rescale: the reference max moves only when a row's max exceeds
+      // it by more than kRescaleSlack (log2 units), so p <= 2^slack and O, l
+      // (in AGPRs) are rarely rescaled; O / l is the same quotient.  A pair's
+      // first tile always moves it, which also clears O and l (the factor is
+      // 0 while the reference max is -inf).
+      const bool move = start || mx > m_run[f] + kRescaleSlack;
+      if (__ballot(move) != 0) {
+        const float m_new = move ? mx : m_run[f];
+        const float alpha = (m_run[f] == kNegInf) ? 0.f : exp2_hw(m_run[f] - m_new);
+        if (move) {
           l_lane[f] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[f][dt] *= alpha;
+          m_run[f] = m_new;
         }
-        m_run[f] = m_new;
-      } else {
-        // Lazy rescale (several fragments' accumulators, mostly in AGPRs): the
-        // reference max moves only when a row's max exceeds it by more than
-        // kRescaleSlack (log2 units), or on its first keys, so p <= 2^slack
-        // and O, l rarely need rescaling; O / l is the same quotient.
-        // (a pair's first tile always moves it, which also clears O and l)
-        const bool move = start || mx > m_run[f] + kRescaleSlack;
-        if (__ballot(move) != 0) {
-          const float m_new = move ? mx : m_run[f];
-          const float alpha = (m_run[f] == kNegInf) ? 0.f : exp2_hw(m_run[f] - m_new);
-          if (move) {
-            l_lane[f] *= alpha;
+      }
+      const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) o[f][dt] *= alpha;
-            m_run[f] = m_new;
-          }
-        }
-        const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[f][i] = operand_value<PV>(exp2_hw(sv[i] - m_use));
-          psum += p[f][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        p[f][i] = operand_value<PV>(exp2_hw(sv[i] - m_use));
+        psum += p[f][i];
       }
       l_lane[f] += psum;
     }
@@ -703,21 +698,21 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
 #pragma unroll
       for (int f = 0; f < NQF; ++f) mma_pv<PV>(o[f][dt], vt, p[f]);
     }
-    if (s.flags & kEnd) {
-      if (s.flags & kWhole) {
+    if (sflags & kEnd) {
+      if (sflags & kWhole) {
 #pragma unroll
         for (int f = 0; f < NQF; ++f) {
           const float l_row = wave_sum_groups(l_lane[f]);
           const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
           const int k = kQRows * f + c;
-          if (k < s.nq) {
-            st* orow = (st*)a.out + ((int64_t)(s.r0 + k) * a.H + s.h) * D;
+          if (k < cnq) {
+            st* orow = (st*)a.out + ((int64_t)(cr0 + k) * a.H + chh) * D;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), o[f][dt], inv * a.v_descale);
           }
         }
       } else {
-        const int slot = (s.flags & kPart1) ? 1 : 0;
+        const int slot = (sflags & kPart1) ? 1 : 0;
         const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
         const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
 #pragma unroll
@@ -731,8 +726,8 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[f][dt]), prs,
                                                    o_base + ((part * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
         }
-        cut_b[slot] = s.b;
-        cut_h[slot] = s.h;
+        cut_b[slot] = cb;
+        cut_h[slot] = chh;
       }
     }
   };
@@ -740,7 +735,7 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   // Every slot index is loaded unconditionally (indices past the range
   // re-read the last tile, a cache hit, and are fully masked with no flags),
   // so the loop body is straight-line and DEPTH-1 tiles stay in flight.
-  StreamSlot<PT, D, NQF> buf[DEPTH];
+  StreamSlot<PT, D, kQIn> buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) load_slot(buf[d], d);
   for (int it = 0; it < n_tiles; it += DEPTH) {
@@ -765,22 +760,22 @@ __global__ __launch_bounds__(256, FM_CROSS_WAVES_PER_SIMD) void cross_attn_kerne
   }
 }
 
-template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF>
+template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF, int OCC>
 hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.bs * a.H;
   hipLaunchKernelGGL((q_prologue_kernel<T, PT, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
-  hipLaunchKernelGGL((cross_attn_kernel<T, PT, D, DEPTH, UNIFORM_PAGE, NQF>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((cross_attn_kernel<T, PT, D, DEPTH, UNIFORM_PAGE, NQF, OCC>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <class T, class PT, int D, int DEPTH, int NQF>
+template <class T, class PT, int D, int DEPTH, int NQF, int OCC>
 hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
   // page_size >= 16 keeps each 16-key tile inside one page
-  if (a.log2ps >= 4) return launch_cross_paged<T, PT, D, DEPTH, true, NQF>(a, s);
-  return launch_cross_paged<T, PT, D, DEPTH, false, NQF>(a, s);
+  if (a.log2ps >= 4) return launch_cross_paged<T, PT, D, DEPTH, true, NQF, OCC>(a, s);
+  return launch_cross_paged<T, PT, D, DEPTH, false, NQF, OCC>(a, s);
 }
 
 #ifndef FM_CROSS_DEPTH_Q2
@@ -789,36 +784,39 @@ hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
 #ifndef FM_CROSS_DEPTH_Q4
 #define FM_CROSS_DEPTH_Q4 2  // ... with four (their accumulators fill the AGPRs)
 #endif
-// An e4m3 tile is half the bytes of a bf16 one: twice the tiles keep the same
-// bytes in flight in the same registers.
+// e4m3 tiles: two waves per SIMD, each with two tiles in flight.
 #ifndef FM_CROSS_DEPTH_FP8
-#define FM_CROSS_DEPTH_FP8 6
+#define FM_CROSS_DEPTH_FP8 2
 #endif
 #ifndef FM_CROSS_DEPTH_FP8_Q2
-#define FM_CROSS_DEPTH_FP8_Q2 6
+#define FM_CROSS_DEPTH_FP8_Q2 2
 #endif
 #ifndef FM_CROSS_DEPTH_FP8_Q4
-#define FM_CROSS_DEPTH_FP8_Q4 4
+#define FM_CROSS_DEPTH_FP8_Q4 2
 #endif
 
-// Tiles in flight for one, two and four query fragments per request.
-template <class T, class PT, int D, int DEPTH1, int DEPTH2, int DEPTH4>
+// Tiles in flight for one, two and four query fragments per request; OCC
+// waves per SIMD.
+template <class T, class PT, int D, int DEPTH1, int DEPTH2, int DEPTH4, int OCC>
 hipError_t launch_cross_frags(const CrossArgs& a, hipStream_t s) {
   switch (a.lay.nqf) {
-    case 1: return launch_cross_typed<T, PT, D, DEPTH1, 1>(a, s);
-    case 2: return launch_cross_typed<T, PT, D, DEPTH2, 2>(a, s);
-    default: return launch_cross_typed<T, PT, D, DEPTH4, 4>(a, s);
+    case 1: return launch_cross_typed<T, PT, D, DEPTH1, 1, OCC>(a, s);
+    case 2: return launch_cross_typed<T, PT, D, DEPTH2, 2, OCC>(a, s);
+    default: return launch_cross_typed<T, PT, D, DEPTH4, 4, OCC>(a, s);
   }
 }
 
 template <int D>
 hipError_t launch_cross_dh(const CrossArgs& a, int dtype, hipStream_t s) {
-  if (dtype == 1) return launch_cross_frags<Bf16, Bf16, D, FM_CROSS_DEPTH_BF16, FM_CROSS_DEPTH_Q2, FM_CROSS_DEPTH_Q4>(a, s);
+  if (dtype == 1)
+    return launch_cross_frags<Bf16, Bf16, D, FM_CROSS_DEPTH_BF16, FM_CROSS_DEPTH_Q2, FM_CROSS_DEPTH_Q4,
+                              cross_occupancy(1)>(a, s);
   if (dtype == 2)
-    return launch_cross_frags<Bf16, E4m3, D, FM_CROSS_DEPTH_FP8, FM_CROSS_DEPTH_FP8_Q2, FM_CROSS_DEPTH_FP8_Q4>(a, s);
+    return launch_cross_frags<Bf16, E4m3, D, FM_CROSS_DEPTH_FP8, FM_CROSS_DEPTH_FP8_Q2, FM_CROSS_DEPTH_FP8_Q4,
+                              cross_occupancy(2)>(a, s);
   // fp32 rows, whose tiles take twice the registers, keep one tile in flight
   // with several candidate blocks
-  return launch_cross_frags<F32, F32, D, FM_CROSS_DEPTH_F32, 1, 1>(a, s);
+  return launch_cross_frags<F32, F32, D, FM_CROSS_DEPTH_F32, 1, 1, cross_occupancy(0)>(a, s);
 }
 
 }  // namespace

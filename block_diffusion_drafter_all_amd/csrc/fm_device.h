@@ -131,6 +131,8 @@ __device__ __forceinline__ int32_t load_i32(const int32_t* p) { return *(gptr_i3
 // while the kernel runs.
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
 __device__ __forceinline__ int32_t sload_i32(const int32_t* p) { return *(cptr_i32)(p); }
+typedef const __attribute__((address_space(4))) float* cptr_f32;
+__device__ __forceinline__ float sload_f32(const float* p) { return *(cptr_f32)(p); }
 
 typedef const __attribute__((address_space(1))) float* gptr_f32;
 __device__ __forceinline__ float load_f32(const float* p) { return *(gptr_f32)(p); }

@@ -24,10 +24,17 @@ inline int q_frags(int max_q) {
 }
 constexpr int32_t kPlanMagic = 0x464d504c;   // "FMPL"
 constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
-#ifndef FM_CROSS_WAVES_PER_SIMD
-#define FM_CROSS_WAVES_PER_SIMD 1
+// Resident cross-attention waves per SIMD, by pool type: a bf16 or fp32 tile
+// keeps one wave busy; e4m3 tiles (half the bytes for the same instructions)
+// run two waves per SIMD so that one issues while the other waits.  The plan
+// cuts the tile stream for exactly the waves the kernel keeps resident.
+#ifndef FM_CROSS_OCC_BF16
+#define FM_CROSS_OCC_BF16 1
 #endif
-constexpr int kWavesPerCU = 4 * FM_CROSS_WAVES_PER_SIMD;  // resident cross-attention waves per CU
+#ifndef FM_CROSS_OCC_FP8
+#define FM_CROSS_OCC_FP8 2
+#endif
+constexpr int cross_occupancy(int dtype) { return dtype == 2 ? FM_CROSS_OCC_FP8 : (dtype == 1 ? FM_CROSS_OCC_BF16 : 1); }
 constexpr int kMaxPlanWaves = 4096;  // most attention waves one plan describes
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -32,8 +32,8 @@ class StepBuffers:
 
 def allocate(w: Workload) -> StepBuffers:
     dev = w.ctx_lens.device
-    cross_ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.max_q), dtype=torch.uint8,
-                           device=dev)
+    cross_ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.max_q, w.pool_dtype),
+                           dtype=torch.uint8, device=dev)
     write_ws = out_slots = None
     if w.write is not None:
         n_rows = w.write.x.shape[0]
@@ -52,7 +52,7 @@ def write_context(w: Workload, buf: StepBuffers) -> None:
 
 
 def plan(w: Workload, buf: StepBuffers) -> None:
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.max_q)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.max_q, pool_dtype=w.pool_dtype)
 
 
 def layer(w: Workload, buf: StepBuffers, l: int) -> None:

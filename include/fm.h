@@ -142,11 +142,11 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 
 /* ------------------------------------------------------ cross-attention -- */
 
-/* Workspace bytes for a cross-attention plan of bs requests with head dim Dh
- * and at most max_q query rows per request (max_q <= 64) on the current
- * device; 0 for an unsupported shape.  One workspace serves every layer's
- * call of a step. */
-size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q);
+/* Workspace bytes for a cross-attention plan of bs requests with head dim Dh,
+ * at most max_q query rows per request (max_q <= 64) and pool type dt on the
+ * current device; 0 for an unsupported shape or type.  One workspace serves
+ * every layer's call of a step. */
+size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt);
 
 /*
  * Tile schedule of paged cross-attention, computed once per draft step on the
@@ -160,11 +160,14 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
  * ctx_lens  DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
  * max_q     host bound on query rows per request: one draft block (16) or up
  *           to four candidate blocks side by side (<= 64), checked here.
- * ws        DEVICE, fm_cross_attention_workspace_size(bs, H, Dh, max_q) bytes,
- *           256-byte aligned.
+ * dt        the pool type of the calls the plan serves: the number of
+ *           resident waves, and so the cut, depends on it (two per SIMD over
+ *           an e4m3 pool, one otherwise).
+ * ws        DEVICE, fm_cross_attention_workspace_size(bs, H, Dh, max_q, dt)
+ *           bytes, 256-byte aligned.
  */
 int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
-                            void* ws, size_t ws_bytes, hipStream_t stream);
+                            fm_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Paged cross-attention (sglang/model.py ``_paged_cross_attention`` +
@@ -198,7 +201,8 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  * page_table  DEVICE int32 [bs, pt_stride].
  * ctx_lens, bs, H  as given to fm_plan_cross_attention, whose plan ``ws``
  *             must hold (same stream, earlier; lengths unchanged since).  A
- *             plan made for other shapes leaves ``out`` untouched.  If the
+ *             plan made for other shapes or another pool type leaves ``out``
+ *             untouched.  If the
  *             lengths changed after the plan, the outputs are unspecified, no
  *             access leaves the buffers, and bit 1 of the error word is set
  *             when a wave's share runs past the last tile; plan again.

@@ -42,19 +42,22 @@ def test_version_and_empty_error(lib):
 
 
 def test_workspace_sizes(lib):
-    small = lib.fm_cross_attention_workspace_size(1, 4, 64, 16)
-    big = lib.fm_cross_attention_workspace_size(64, 32, 128, 16)
+    small = lib.fm_cross_attention_workspace_size(1, 4, 64, 16, B.FM_BF16)
+    big = lib.fm_cross_attention_workspace_size(64, 32, 128, 16, B.FM_BF16)
     assert 0 < small < big
     assert small % 256 == 0 and big % 256 == 0
-    assert lib.fm_cross_attention_workspace_size(4, 0, 128, 16) == 0
-    assert lib.fm_cross_attention_workspace_size(4, 4, 96, 16) == 0
-    assert lib.fm_cross_attention_workspace_size(4, 4, 128, 65) == 0
+    assert lib.fm_cross_attention_workspace_size(4, 0, 128, 16, B.FM_BF16) == 0
+    assert lib.fm_cross_attention_workspace_size(4, 4, 96, 16, B.FM_BF16) == 0
+    assert lib.fm_cross_attention_workspace_size(4, 4, 128, 65, B.FM_BF16) == 0
     # candidate blocks: 1, 2 or 4 query fragments per request
-    one, two, four = (lib.fm_cross_attention_workspace_size(64, 32, 128, m) for m in (16, 32, 64))
+    one, two, four = (lib.fm_cross_attention_workspace_size(64, 32, 128, m, B.FM_BF16) for m in (16, 32, 64))
     assert big == one < two < four
-    assert lib.fm_cross_attention_workspace_size(64, 32, 128, 17) == two
-    assert lib.fm_cross_attention_workspace_size(64, 32, 128, 48) == four
+    assert lib.fm_cross_attention_workspace_size(64, 32, 128, 17, B.FM_BF16) == two
+    assert lib.fm_cross_attention_workspace_size(64, 32, 128, 48, B.FM_BF16) == four
     assert lib.fm_write_context_kv_workspace_size(1152) >= 256 + 4 * 4 * 1152
+    # an e4m3 pool's plan cuts for twice the resident waves: more partial slots
+    e4 = lib.fm_cross_attention_workspace_size(64, 32, 128, 16, B.FM_BF16_E4M3)
+    assert e4 > one and lib.fm_cross_attention_workspace_size(64, 32, 128, 16, 7) == 0
 
 
 FAKE = 1 << 20   # a non-null, 256-aligned host-side stand-in; never dereferenced
@@ -115,12 +118,14 @@ def test_cross_attention_empty_is_noop(lib):
 
 
 def test_plan_rejects(lib):
-    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 65, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 65, B.FM_BF16, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
     assert "max_q" in B.fm_last_error()
-    assert lib.fm_plan_cross_attention(None, 4, 32, 128, 16, FAKE, 1 << 30, None) == B.FM_E_INVALID
-    assert lib.fm_plan_cross_attention(FAKE, -1, 32, 128, 16, FAKE, 1 << 30, None) == B.FM_E_INVALID
-    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 16, FAKE, 10, None) == B.FM_E_WORKSPACE
-    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 96, 16, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert lib.fm_plan_cross_attention(None, 4, 32, 128, 16, B.FM_BF16, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert lib.fm_plan_cross_attention(FAKE, -1, 32, 128, 16, B.FM_BF16, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 16, B.FM_BF16, FAKE, 10, None) == B.FM_E_WORKSPACE
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 96, 16, B.FM_BF16, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert lib.fm_plan_cross_attention(FAKE, 4, 32, 128, 16, 9, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert "dtype" in B.fm_last_error()
 
 
 def _write(lib, **over):

@@ -151,8 +151,9 @@ def test_candidate_blocks_ragged_rows_and_empty_context():
     gen.manual_seed(11)
     q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(torch.bfloat16)
     w.q[0], w.cu_seqlens_q = q, cu
-    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 64), dtype=torch.uint8, device=dev)
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=64)
+    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 64, w.pool_dtype), dtype=torch.uint8,
+                     device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=64, pool_dtype=w.pool_dtype)
     out = torch.full_like(q, float("nan"))
     B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu, w.softmax_scale,
                                w.theta, w.eps, ws, out=out, max_q=64)
@@ -188,8 +189,9 @@ def test_head_dim_64_bf16_and_ragged_query_rows():
     gen.manual_seed(7)
     q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(torch.bfloat16)
     w.q[0], w.cu_seqlens_q = q, cu
-    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16, w.pool_dtype), dtype=torch.uint8,
+                     device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, pool_dtype=w.pool_dtype)
     out = B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu,
                                      w.softmax_scale, w.theta, w.eps, ws)
     torch.cuda.synchronize()
@@ -355,8 +357,9 @@ def test_fp8_pool_page_sizes_ragged(ps, Dh):
     gen.manual_seed(13)
     q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(torch.bfloat16)
     w.q[0], w.cu_seqlens_q = q, cu
-    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    ws = torch.empty(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16, w.pool_dtype), dtype=torch.uint8,
+                     device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, pool_dtype=w.pool_dtype)
     out = torch.full_like(q, float("nan"))
     B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu, w.softmax_scale,
                                w.theta, w.eps, ws, out=out)
