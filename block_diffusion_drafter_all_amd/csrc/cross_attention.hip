@@ -639,6 +639,10 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch)
             qop[f][ch] = load16(qrow + (int64_t)f * kQRows * a.H * D + ch * 4 * EPC + g * EPC);
+        // Wait here, on the pair's first tile only: left to the compiler, the
+        // wait for these loads lands after the branch, on every tile, and
+        // drains the whole load ring each time.
+        wait_all_vector_loads();
       }
       // O and l restart through the rescale below: its factor is 0 while the
       // running max is -inf
@@ -795,28 +799,26 @@ hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
 #define FM_CROSS_DEPTH_FP8_Q4 2
 #endif
 
-// Tiles in flight for one, two and four query fragments per request; OCC
-// waves per SIMD.
-template <class T, class PT, int D, int DEPTH1, int DEPTH2, int DEPTH4, int OCC>
+// Tiles in flight for one, two and four query fragments per request, each
+// at the occupancy the plan was cut for.
+template <class T, class PT, int D, int DTYPE, int DEPTH1, int DEPTH2, int DEPTH4>
 hipError_t launch_cross_frags(const CrossArgs& a, hipStream_t s) {
   switch (a.lay.nqf) {
-    case 1: return launch_cross_typed<T, PT, D, DEPTH1, 1, OCC>(a, s);
-    case 2: return launch_cross_typed<T, PT, D, DEPTH2, 2, OCC>(a, s);
-    default: return launch_cross_typed<T, PT, D, DEPTH4, 4, OCC>(a, s);
+    case 1: return launch_cross_typed<T, PT, D, DEPTH1, 1, cross_occupancy(DTYPE)>(a, s);
+    case 2: return launch_cross_typed<T, PT, D, DEPTH2, 2, cross_occupancy(DTYPE)>(a, s);
+    default: return launch_cross_typed<T, PT, D, DEPTH4, 4, cross_occupancy(DTYPE)>(a, s);
   }
 }
 
 template <int D>
 hipError_t launch_cross_dh(const CrossArgs& a, int dtype, hipStream_t s) {
   if (dtype == 1)
-    return launch_cross_frags<Bf16, Bf16, D, FM_CROSS_DEPTH_BF16, FM_CROSS_DEPTH_Q2, FM_CROSS_DEPTH_Q4,
-                              cross_occupancy(1)>(a, s);
+    return launch_cross_frags<Bf16, Bf16, D, 1, FM_CROSS_DEPTH_BF16, FM_CROSS_DEPTH_Q2, FM_CROSS_DEPTH_Q4>(a, s);
   if (dtype == 2)
-    return launch_cross_frags<Bf16, E4m3, D, FM_CROSS_DEPTH_FP8, FM_CROSS_DEPTH_FP8_Q2, FM_CROSS_DEPTH_FP8_Q4,
-                              cross_occupancy(2)>(a, s);
+    return launch_cross_frags<Bf16, E4m3, D, 2, FM_CROSS_DEPTH_FP8, FM_CROSS_DEPTH_FP8_Q2, FM_CROSS_DEPTH_FP8_Q4>(a, s);
   // fp32 rows, whose tiles take twice the registers, keep one tile in flight
   // with several candidate blocks
-  return launch_cross_frags<F32, F32, D, FM_CROSS_DEPTH_F32, 1, 1, cross_occupancy(0)>(a, s);
+  return launch_cross_frags<F32, F32, D, 0, FM_CROSS_DEPTH_F32, 1, 1>(a, s);
 }
 
 }  // namespace

@@ -125,6 +125,10 @@ __device__ __forceinline__ u32x4_t load16_stream(const void* p) {
 typedef const __attribute__((address_space(1))) int32_t* gptr_i32;
 __device__ __forceinline__ int32_t load_i32(const int32_t* p) { return *(gptr_i32)(p); }
 
+// s_waitcnt vmcnt(0) through the builtin, so that the compiler's wait
+// bookkeeping knows every vector load has completed here.
+__device__ __forceinline__ void wait_all_vector_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Wave-uniform load through the scalar unit (constant address space): for
 // small read-only tables such as lengths, so that waiting for the value never
 // waits for vector loads in flight.  Reads only; the data must not change
