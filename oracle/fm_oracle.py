@@ -58,6 +58,8 @@ __all__ = [
     "context_slot",
     "live_rows",
     "project_context_rows",
+    "context_input_rows",
+    "anchor_input_rows",
     "write_context_kv",
     "scatter_into_pool",
     "paged_cross_attention",
@@ -225,6 +227,28 @@ def project_context_rows(x: np.ndarray, w_kv: np.ndarray, L: int, H: int, D: int
     ``(n, L, 2, H, D)`` (``load_weights`` concatenation; vLLM ``_write`` view)."""
     y = np.asarray(x, dtype=np.float64) @ np.asarray(w_kv, dtype=np.float64).T
     return y.reshape(y.shape[0], L, 2, H, D)
+
+
+def context_input_rows(target_hidden, w_fc, hidden_norm_w, eps):
+    """The rows the context K/V GEMM takes for committed target positions:
+    the concatenated hidden states of the target's chosen layers projected by
+    ``fc`` (no bias) and RMS-normed with ``hidden_norm`` (the sglang model's
+    ``_write_context``: ``rms_norm(fc(target_hidden), hidden_norm)``; vLLM
+    ``combine_hidden_states`` then ``hidden_norm``).  ``target_hidden (n,
+    n_aux * d_target)``, ``w_fc (dim, n_aux * d_target)``; returns ``(n, dim)``."""
+    y = np.asarray(target_hidden, dtype=np.float64) @ np.asarray(w_fc, dtype=np.float64).T
+    return rms_norm(y, hidden_norm_w, eps)
+
+
+def anchor_input_rows(anchor_ids, embedding, w_anchor_proj, b_anchor_proj, anchor_norm_w, eps):
+    """The rows the context K/V GEMM takes for anchors: the anchor token's
+    embedding through ``anchor_proj`` (with bias) and ``anchor_norm`` (the
+    sglang model's ``_anchor_kv_impl``; vLLM ``_prologue``).  ``embedding
+    (vocab, d_target)``, ``w_anchor_proj (dim, d_target)``, ``b_anchor_proj
+    (dim)``; returns ``(n, dim)``."""
+    e = np.asarray(embedding, dtype=np.float64)[np.asarray(anchor_ids, dtype=np.int64)]
+    y = e @ np.asarray(w_anchor_proj, dtype=np.float64).T + np.asarray(b_anchor_proj, dtype=np.float64)
+    return rms_norm(y, anchor_norm_w, eps)
 
 
 def write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, page_size,

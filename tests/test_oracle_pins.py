@@ -438,6 +438,40 @@ def _write_case(rng, L=2, H=2, D=16, ps=4):
                 row_req=row_req, row_pos=row_pos, pt=pt, n_pages=n_pages, x=x)
 
 
+def test_context_input_rows_against_torch_and_selector(rng):
+    # fc then hidden_norm (the sglang model's _write_context)
+    n, aux, dt, dim = 7, 3, 16, 12
+    x = rng.standard_normal((n, aux * dt))
+    w = rng.standard_normal((dim, aux * dt)) * 0.3
+    g = 1.0 + 0.1 * rng.standard_normal(dim)
+    got = O.context_input_rows(x, w, g, 1e-6)
+    ref = F.rms_norm(F.linear(torch.from_numpy(x), torch.from_numpy(w)), (dim,), torch.from_numpy(g), 1e-6)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # fc selecting the second aux block: the norm of that block alone
+    sel = np.zeros((dt, aux * dt))
+    sel[:, dt:2 * dt] = np.eye(dt)
+    np.testing.assert_allclose(O.context_input_rows(x, sel, np.ones(dt), 0.0),
+                               x[:, dt:2 * dt] / np.sqrt(np.mean(x[:, dt:2 * dt] ** 2, axis=1, keepdims=True)),
+                               rtol=1e-13, atol=0)
+
+
+def test_anchor_input_rows_against_torch_and_closed_forms(rng):
+    vocab, dt, dim = 50, 16, 12
+    emb = rng.standard_normal((vocab, dt))
+    w = rng.standard_normal((dim, dt)) * 0.3
+    b = rng.standard_normal(dim)
+    g = 1.0 + 0.1 * rng.standard_normal(dim)
+    ids = np.array([3, 49, 0, 3])
+    got = O.anchor_input_rows(ids, emb, w, b, g, 1e-6)
+    e = F.embedding(torch.from_numpy(ids), torch.from_numpy(emb))
+    ref = F.rms_norm(F.linear(e, torch.from_numpy(w), torch.from_numpy(b)), (dim,), torch.from_numpy(g), 1e-6)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(got[0], got[3])                  # repeated token, identical row
+    # a zero projection leaves rms_norm(bias) in every row
+    z = O.anchor_input_rows(ids, emb, np.zeros((dim, dt)), b, np.ones(dim), 0.0)
+    np.testing.assert_allclose(z, np.tile(b / np.sqrt(np.mean(b ** 2)), (4, 1)), rtol=1e-13, atol=0)
+
+
 def test_write_identity_weight_passthrough_and_commit_rule(rng):
     c = _write_case(rng, L=1)
     H, D = c["H"], c["D"]
