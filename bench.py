@@ -64,6 +64,9 @@ def parse():
                     help="candidate blocks per request (tree drafting): 16 query rows each, one context read")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="e4m3 KV pool (written at scale 1; queries quantized per request and head)")
+    ap.add_argument("--upstream", action="store_true",
+                    help="config 5: make the write's rows on the device from the target hidden states (fc + "
+                         "hidden_norm) and the anchor tokens (embedding + anchor_proj + anchor_norm) in the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
@@ -103,7 +106,7 @@ def _kib_per_dispatch(rows, match):
 def workload_key(args) -> str:
     """Names the workload a traffic record was measured on."""
     return (f"config={args.config},layout={args.layout},candidates={args.candidates},"
-            f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}")
+            f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}" + (",upstream" if args.upstream else ""))
 
 
 def _traffic_records() -> dict:
@@ -217,6 +220,17 @@ def write_flops_bytes(w):
     return flops, nbytes
 
 
+def context_rows_flops(w) -> int:
+    """MFMA flops of fm_context_rows: fc over the committed window rows and
+    anchor_proj over the anchors."""
+    up = w.upstream
+    if up is None:
+        return 0
+    live = int(w.write.commit_lens.sum().item())
+    dim = up.w_fc.shape[0]
+    return 2 * live * up.hidden.shape[1] * dim + 2 * up.anchor_ids.shape[0] * up.embedding.shape[1] * dim
+
+
 def describe(w) -> dict:
     ctx = w.ctx_lens.cpu().tolist()
     d = {
@@ -234,6 +248,9 @@ def describe(w) -> dict:
     if w.write is not None:
         d["write_rows"] = int(w.write.x.shape[0])
         d["write_d_in"] = int(w.write.x.shape[1])
+    if w.upstream is not None:
+        d["upstream"] = {"hidden_width": int(w.upstream.hidden.shape[1]), "vocab": int(w.upstream.embedding.shape[0]),
+                         "dim": int(w.upstream.w_fc.shape[0])}
     return d
 
 
@@ -328,15 +345,24 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    w = make_workload(args.config, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8)
+    if args.upstream and args.config != 5:
+        raise SystemExit("--upstream applies to config 5 (the full draft step)")
+    w = make_workload(args.config, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8,
+                      upstream=args.upstream)
     buf = S.allocate(w)
     torch.cuda.synchronize()
 
     def one_step(events=None):
+        if w.upstream is not None:
+            if events is not None:
+                events["rows"][0].record()
+            S.context_rows(w, buf)
+            if events is not None:
+                events["rows"][1].record()
         if w.write is not None:
             if events is not None:
                 events["write"][0].record()
-            S.write_context(w, buf)
+            S.write_kv(w, buf)
             if events is not None:
                 events["write"][1].record()
         S.plan(w, buf)
@@ -362,7 +388,7 @@ def main():
     # Timed region: exactly --steps steps.  Events bracket each cross-attention
     # call on the stream it is launched on (torch's current stream).
     E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
-    per_step = [dict(write=E(), self=[E() for _ in range(w.L)], cross=[E() for _ in range(w.L)])
+    per_step = [dict(rows=E(), write=E(), self=[E() for _ in range(w.L)], cross=[E() for _ in range(w.L)])
                 for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -379,6 +405,7 @@ def main():
     cross_ms = [ev[0].elapsed_time(ev[1]) for st in per_step for ev in st["cross"]]
     self_ms = [ev[0].elapsed_time(ev[1]) for st in per_step for ev in st["self"]]
     write_ms = [st["write"][0].elapsed_time(st["write"][1]) for st in per_step] if w.write is not None else []
+    rows_ms = [st["rows"][0].elapsed_time(st["rows"][1]) for st in per_step] if w.upstream is not None else []
     avg_cross = sum(cross_ms) / len(cross_ms)
     cb = cross_bytes(w)
     achieved = cb / (avg_cross * 1e-3) / 1e9
@@ -415,6 +442,11 @@ def main():
         out["write"] = {"avg_ms": avg_w, "flops": wf, "tflops": wf / (avg_w * 1e-3) / 1e12,
                         "mfma_frac_of_bf16_peak": wf / (avg_w * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                         "algorithmic_bytes": wb}
+    if rows_ms:
+        rf = context_rows_flops(w)
+        avg_r = sum(rows_ms) / len(rows_ms)
+        out["context_rows"] = {"avg_ms": avg_r, "flops": rf, "tflops": rf / (avg_r * 1e-3) / 1e12,
+                               "mfma_frac_of_bf16_peak": rf / (avg_r * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     if not args.no_cpu_baseline:
         n_req = args.cpu_sample_requests or max(1, min(w.bs, 24))
         out["cpu_baseline"] = cpu_baseline(w, n_req)

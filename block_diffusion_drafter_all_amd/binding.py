@@ -30,6 +30,8 @@ SYMBOLS = (
     "fm_version",
     "fm_write_context_kv_workspace_size",
     "fm_write_context_kv",
+    "fm_context_rows_workspace_size",
+    "fm_context_rows",
     "fm_cross_attention_workspace_size",
     "fm_plan_cross_attention",
     "fm_paged_cross_attention",
@@ -78,6 +80,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_write_context_kv.argtypes = [
         vp, c_i64, c_i32, ctypes.c_int, vp, vp, vp, vp, vp, c_i32, vp, c_i64, c_i32, c_i32,
         ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp,
+    ]
+    lib.fm_context_rows_workspace_size.restype = c_sz
+    lib.fm_context_rows_workspace_size.argtypes = [c_i64, c_i64, c_i32, c_i32, c_i32]
+    lib.fm_context_rows.restype = ctypes.c_int
+    lib.fm_context_rows.argtypes = [
+        vp, c_i64, c_i32, vp, vp, vp, c_i64, vp, c_i64, c_i32, vp, vp, vp, c_i32, vp, c_i32, c_i32, f32, vp, vp,
+        c_sz, vp,
     ]
     lib.fm_cross_attention_workspace_size.restype = c_sz
     lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]
@@ -225,6 +234,55 @@ def _pool_code(pool_dtype) -> int:
     if pool_dtype not in codes:
         raise TypeError(f"unsupported pool dtype {pool_dtype}")
     return codes[pool_dtype]
+
+
+def fm_context_rows_workspace_size(n_hidden: int, n_anchor: int, d_hidden: int, d_target: int, dim: int) -> int:
+    return load_library().fm_context_rows_workspace_size(n_hidden, n_anchor, d_hidden, d_target, dim)
+
+
+def fm_context_rows(hidden, w_fc, hidden_norm_w, anchor_ids, embedding, w_anchor_proj, b_anchor_proj, anchor_norm_w,
+                    eps, commit_lens=None, window=0, bs=None, rows=None, ws=None):
+    """The rows fm_write_context_kv projects: ``hidden_norm(fc(hidden))`` for
+    the committed hidden rows, then ``anchor_norm(anchor_proj(embedding[id]))``
+    for the anchors.  ``hidden`` or ``anchor_ids`` may be None.  Returns
+    ``rows (n_hidden + n_anchor, dim)`` bf16."""
+    lib = load_library()
+    n_hidden = 0 if hidden is None else hidden.shape[0]
+    n_anchor = 0 if anchor_ids is None else anchor_ids.shape[0]
+    dim = (w_fc if hidden is not None else w_anchor_proj).shape[0]
+    d_hidden = 0 if hidden is None else hidden.shape[1]
+    d_target = 0 if anchor_ids is None else embedding.shape[1]
+    if hidden is not None:
+        _need(hidden, "hidden", torch.bfloat16)
+        _need(w_fc, "w_fc", torch.bfloat16)
+        _need(hidden_norm_w, "hidden_norm_w", torch.float32)
+        if w_fc.shape != (dim, d_hidden) or hidden_norm_w.shape != (dim,):
+            raise ValueError("w_fc must be (dim, d_hidden) and hidden_norm_w (dim,)")
+    if anchor_ids is not None:
+        _need(anchor_ids, "anchor_ids", torch.int32)
+        for name, t in (("embedding", embedding), ("w_anchor_proj", w_anchor_proj), ("b_anchor_proj", b_anchor_proj)):
+            _need(t, name, torch.bfloat16)
+        _need(anchor_norm_w, "anchor_norm_w", torch.float32)
+        if w_anchor_proj.shape != (dim, d_target) or b_anchor_proj.shape != (dim,) or anchor_norm_w.shape != (dim,):
+            raise ValueError("w_anchor_proj must be (dim, d_target), b_anchor_proj and anchor_norm_w (dim,)")
+    if commit_lens is not None:
+        _need(commit_lens, "commit_lens", torch.int32)
+        bs = commit_lens.shape[0] if bs is None else bs
+    dev = (hidden if hidden is not None else anchor_ids).device
+    if rows is None:
+        rows = torch.empty((n_hidden + n_anchor, dim), dtype=torch.bfloat16, device=dev)
+    _need(rows, "rows", torch.bfloat16)
+    if rows.shape != (n_hidden + n_anchor, dim):
+        raise ValueError("rows must be (n_hidden + n_anchor, dim)")
+    if ws is None:
+        ws = torch.empty(lib.fm_context_rows_workspace_size(n_hidden, n_anchor, d_hidden, d_target, dim),
+                         dtype=torch.uint8, device=dev)
+    _check(lib.fm_context_rows(
+        _ptr(hidden), n_hidden, d_hidden, _ptr(w_fc), _ptr(hidden_norm_w), _ptr(anchor_ids), n_anchor,
+        _ptr(embedding), 0 if embedding is None else embedding.shape[0], d_target, _ptr(w_anchor_proj),
+        _ptr(b_anchor_proj), _ptr(anchor_norm_w), dim, _ptr(commit_lens), window, 0 if bs is None else bs, eps,
+        _ptr(rows), _ptr(ws), ws.numel(), _stream()))
+    return rows
 
 
 def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16,

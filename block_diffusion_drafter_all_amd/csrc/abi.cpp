@@ -206,6 +206,72 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
   return from_hip(fm::launch_write(p, g, (int)dt, Dh, n_rows, stream), fn);
 }
 
+size_t fm_context_rows_workspace_size(int64_t n_hidden, int64_t n_anchor, int32_t d_hidden, int32_t d_target,
+                                      int32_t dim) {
+  if (n_hidden < 0 || n_anchor < 0 || d_hidden < 1 || d_target < 1 || dim < 1) return 0;
+  return fm::ctx_rows_layout(n_hidden, n_anchor, d_hidden, d_target, dim).total;
+}
+
+int fm_context_rows(const void* hidden, int64_t n_hidden, int32_t d_hidden, const void* w_fc,
+                    const float* hidden_norm_w, const int32_t* anchor_ids, int64_t n_anchor, const void* embedding,
+                    int64_t vocab, int32_t d_target, const void* w_anchor_proj, const void* b_anchor_proj,
+                    const float* anchor_norm_w, int32_t dim, const int32_t* commit_lens, int32_t window, int32_t bs,
+                    float eps, void* rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "fm_context_rows";
+  if (n_hidden < 0 || n_anchor < 0) return fail(FM_E_INVALID, "%s: n_hidden and n_anchor must be >= 0", fn);
+  if (n_hidden == 0 && n_anchor == 0) return ok();
+  if (!rows) return fail(FM_E_INVALID, "%s: rows is null", fn);
+  if (dim < 1024 || dim % 1024 || dim > 8192)
+    return fail(FM_E_UNSUPPORTED, "%s: dim %d must be a multiple of 1024 in [1024, 8192]", fn, dim);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FM_E_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (!aligned16(rows)) return fail(FM_E_INVALID, "%s: rows must be 16-byte aligned", fn);
+  if (n_hidden > 0) {
+    if (!hidden || !w_fc || !hidden_norm_w) return fail(FM_E_INVALID, "%s: a hidden-row pointer is null", fn);
+    if (d_hidden < 32 || d_hidden % 32)
+      return fail(FM_E_UNSUPPORTED, "%s: d_hidden %d must be a positive multiple of 32", fn, d_hidden);
+    if (!aligned16(hidden) || !aligned16(w_fc) || !aligned16(hidden_norm_w))
+      return fail(FM_E_INVALID, "%s: hidden, w_fc and hidden_norm_w must be 16-byte aligned", fn);
+    if (commit_lens != nullptr && (window < 1 || bs < 1 || (int64_t)bs * window > n_hidden))
+      return fail(FM_E_INVALID, "%s: commit_lens needs window >= 1 and bs >= 1 with bs * window <= n_hidden", fn);
+  }
+  if (n_anchor > 0) {
+    if (!anchor_ids || !embedding || !w_anchor_proj || !b_anchor_proj || !anchor_norm_w)
+      return fail(FM_E_INVALID, "%s: an anchor-row pointer is null", fn);
+    if (d_target < 32 || d_target % 32)
+      return fail(FM_E_UNSUPPORTED, "%s: d_target %d must be a positive multiple of 32", fn, d_target);
+    if (vocab < 1) return fail(FM_E_INVALID, "%s: vocab %lld < 1", fn, (long long)vocab);
+    if (!aligned16(embedding) || !aligned16(w_anchor_proj) || !aligned16(b_anchor_proj) || !aligned16(anchor_norm_w))
+      return fail(FM_E_INVALID, "%s: embedding, w_anchor_proj, b_anchor_proj, anchor_norm_w must be 16-byte aligned",
+                  fn);
+  }
+  if (n_hidden + n_anchor > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: too many rows", fn);
+  const fm::CtxRowsLayout lay = fm::ctx_rows_layout(n_hidden, n_anchor, d_hidden, d_target, dim);
+  if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
+  fm::CtxRowsArgs a{};
+  a.hidden = hidden;
+  a.n_hidden = n_hidden;
+  a.d_hidden = d_hidden;
+  a.w_fc = w_fc;
+  a.hidden_norm_w = hidden_norm_w;
+  a.anchor_ids = anchor_ids;
+  a.n_anchor = n_anchor;
+  a.embedding = embedding;
+  a.vocab = vocab;
+  a.d_target = d_target;
+  a.w_anchor = w_anchor_proj;
+  a.b_anchor = b_anchor_proj;
+  a.anchor_norm_w = anchor_norm_w;
+  a.dim = dim;
+  a.commit_lens = commit_lens;
+  a.window = commit_lens ? window : 0;
+  a.bs = commit_lens ? bs : 0;
+  a.eps = eps;
+  a.rows = rows;
+  a.ws = static_cast<uint8_t*>(ws);
+  a.lay = lay;
+  return from_hip(fm::launch_context_rows(a, stream), fn);
+}
+
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt) {
   const int nqf = fm::q_frags(max_q);
   if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || nqf == 0) return 0;

@@ -24,6 +24,7 @@ inline int q_frags(int max_q) {
 }
 constexpr int32_t kPlanMagic = 0x464d504c;   // "FMPL"
 constexpr int32_t kWriteMagic = 0x464d5752;  // "FMWR"
+constexpr int32_t kCtxMagic = 0x464d4358;    // "FMCX"
 // Resident cross-attention waves per SIMD, by pool type: a bf16 or fp32 tile
 // keeps one wave busy; e4m3 tiles (half the bytes for the same instructions)
 // run two waves per SIMD so that one issues while the other waits.  The plan
@@ -212,6 +213,67 @@ struct WriteGemmArgs {
   RopeFreqs rope;
 };
 
+// ------------------------------------------------------------ context rows --
+
+struct CtxRowsHeader {
+  int32_t magic;
+  int32_t error;       // bit 0: an anchor id outside [0, vocab) (read as a clamped row)
+  int32_t live_count;  // committed hidden rows
+  int32_t reserved[5];
+};
+
+struct CtxRowsLayout {
+  size_t live_idx, part_fc, part_anchor, total;
+  int s_fc, s_anchor;  // contraction splits of the two projections
+};
+
+// Contraction splits of a projection with m_tiles x n_tiles output tiles and
+// a k-wide contraction: enough (1..8, a power of two dividing k / 32) to give
+// the chip about 256 workgroups.
+inline int proj_splits(int64_t m_tiles, int64_t n_tiles, int64_t k) {
+  const int64_t tiles = m_tiles * n_tiles > 0 ? m_tiles * n_tiles : 1;
+  int s = 1;
+  while (s < 8 && tiles * s < 256 && (k / 32) % (2 * s) == 0 && k / 32 / (2 * s) >= 4) s *= 2;
+  return s;
+}
+
+inline CtxRowsLayout ctx_rows_layout(int64_t n_hidden, int64_t n_anchor, int64_t d_hidden, int64_t d_target,
+                                     int64_t dim) {
+  CtxRowsLayout c;
+  const int64_t nt = dim / 256;
+  c.s_fc = proj_splits((n_hidden + 255) / 256, nt, d_hidden);
+  c.s_anchor = proj_splits((n_anchor + 255) / 256, nt, d_target);
+  size_t off = 256;
+  c.live_idx = off;    off = align256(off + (size_t)n_hidden * 4);
+  c.part_fc = off;     off = align256(off + (size_t)c.s_fc * n_hidden * dim * 4);
+  c.part_anchor = off; off = align256(off + (size_t)c.s_anchor * n_anchor * dim * 4);
+  c.total = off;
+  return c;
+}
+
+struct CtxRowsArgs {
+  const void* hidden;           // bf16 [n_hidden, d_hidden]
+  int64_t n_hidden;
+  int32_t d_hidden;
+  const void* w_fc;             // bf16 [dim, d_hidden]
+  const float* hidden_norm_w;   // [dim]
+  const int32_t* anchor_ids;    // [n_anchor]
+  int64_t n_anchor;
+  const void* embedding;        // bf16 [vocab, d_target]
+  int64_t vocab;
+  int32_t d_target;
+  const void* w_anchor;         // bf16 [dim, d_target]
+  const void* b_anchor;         // bf16 [dim]
+  const float* anchor_norm_w;   // [dim]
+  int32_t dim;
+  const int32_t* commit_lens;   // or null
+  int32_t window, bs;
+  float eps;
+  void* rows;                   // bf16 [n_hidden + n_anchor, dim]
+  uint8_t* ws;
+  CtxRowsLayout lay;
+};
+
 // -------------------------------------------------------------- launchers --
 // Each returns hipSuccess or the launch error.  dtype: 0 = fp32, 1 = bf16,
 // 2 = bf16 activations over an e4m3 pool (write and cross-attention only).
@@ -221,5 +283,6 @@ hipError_t launch_cross_attention(const CrossArgs& a, int dtype, int Dh, hipStre
 hipError_t launch_self_attention(const SelfArgs& a, int dtype, int Dh, hipStream_t s);
 hipError_t launch_write(const WritePrepArgs& p, const WriteGemmArgs& g, int dtype, int Dh,
                         int64_t n_rows, hipStream_t s);
+hipError_t launch_context_rows(const CtxRowsArgs& a, hipStream_t s);
 
 }  // namespace fm

@@ -14,7 +14,7 @@
 //      e4m3 pool is written with scale 1: sglang/model.py ``_kv_write`` with
 //      ``kv_norm_rope_write_fp8``).
 
-#include "fm_internal.h"
+#include "gemm_core.h"
 
 namespace fm {
 
@@ -157,51 +157,19 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
   }
 }
 
-// bf16 pools with head_dim 128: the MFMA-tiled GEMM.  One workgroup (8 waves
-// in a 4 x 2 arrangement) computes a 256 x 256 tile of Y^T = W X^T: two
-// (layer, {k|v}, head) blocks of W (256 rows) against 256 compacted rows, each
-// wave one whole head for 64 rows with v_mfma_f32_32x32x16_bf16 (4 x 2
-// accumulator blocks of 32 x 32, held in AGPRs); two waves share each SIMD.
-// Operands stream through a ring of kStages LDS buffers, each a 32-wide slice
-// of d_in, filled by direct global->LDS loads that hold no registers while in
-// flight.  A staged operand slice is 256 rows x 4 chunks of 16 bytes; each
-// 1 KB load moves 16 whole rows (64 contiguous bytes each: one L2 request per
-// row), and the chunk order within a row is swizzled by XOR with (row >> 2) & 3
-// so that the 16 lanes of each phase of an MFMA fragment read (16 rows, one
-// chunk) hit 64 distinct banks.  Per slice: wait until the slice kStages-1 steps back has landed,
-// one barrier (after it every wave is also done with the buffer consumed last
-// step), refill that buffer, then 16 MFMAs per wave.  Tiles are ordered so the
-// row tiles that share one W tile run back to back on the same XCD
-// (workgroups go round-robin over the 8 XCDs), so W streams from HBM once and
-// the other row tiles find it in that XCD's L2.  A wave holds all 128 columns
-// of its head, so the k-norm's sum of squares needs one cross-lane exchange.
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int kGM = 256, kGN = 256, kGK = 32;
-constexpr int kGemmWaves = 8;
-#ifndef FM_GEMM_STAGES
-#define FM_GEMM_STAGES 5
-#endif
-constexpr int kStages = FM_GEMM_STAGES;  // LDS ring buffers of 32 KB (gfx950: 160 KB per workgroup)
-constexpr int kFrag = 1024;                     // bytes of one 32-row x 16-k fragment
-constexpr int kStageBytes = 2 * 16 * kFrag;     // 16 W fragments + 16 X fragments
-constexpr int kLoadsPerWave = 32 / kGemmWaves;  // fragments each wave loads per slice
-
-// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
-constexpr int kWaitLgkm0 = 0xC07F;              // lgkmcnt(0) only
-
+// bf16 activations with head_dim 128: the MFMA-tiled GEMM (gemm_core.h), one
+// 256 x 256 tile of Y^T = W X^T per workgroup: two (layer, {k|v}, head) blocks
+// of W against 256 compacted rows, each wave one whole head for 64 rows.  Tiles
+// are ordered so the row tiles that share one W tile run back to back on the
+// same XCD (workgroups go round-robin over the 8 XCDs), so W streams from HBM
+// once and the other row tiles find it in that XCD's L2.  A wave holds all 128
+// columns of its head, so the k-norm's sum of squares needs one cross-lane
+// exchange.
 template <class PT>
 __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(WriteGemmArgs a, int n_tiles,
                                                                               int m_tiles) {
   typedef typename PT::storage pst;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring3[kStageBytes];
-#if FM_GEMM_STAGES == 5
-  __shared__ __attribute__((aligned(1024))) uint8_t ring4[kStageBytes];
-#endif
+  FM_GEMM_RING;
   const int lane = lane_id();
   const int wv = wave_in_block();
   const int wm = wv >> 1, wn = wv & 1;  // rows 64 wm .. +63 of the tile, head wn
@@ -222,31 +190,17 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
   const int32_t* live_row = (const int32_t*)(ws + a.lay.live_row);
   const int frow = lane & 31, fchunk = lane >> 5;
 
-  // Load j of a slice (0..15 of W, 16..31 of X) fills LDS slots 64 (j & 15) ..
-  // +63 of its operand: lane l takes row 16 (j & 15) + l/4 and, in slot
-  // position l % 4, the chunk (l % 4) ^ ((row >> 2) & 3).  This wave issues
-  // loads kLoadsPerWave * wv .. +kLoadsPerWave-1.
   const uint16_t* src[kLoadsPerWave];
 #pragma unroll
   for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int f = kLoadsPerWave * wv + i, fl = f & 15;
-    const int row = 16 * fl + (lane >> 2), ch = (lane & 3) ^ ((row >> 2) & 3);
-    if (f < 16) {
-      src[i] = (const uint16_t*)a.w + ((int64_t)n * kGN + row) * a.d_in + ch * 8;
+    const GemmLoad g = gemm_load_of(wv, lane, i);
+    if (g.is_w) {
+      src[i] = (const uint16_t*)a.w + ((int64_t)n * kGN + g.row) * a.d_in + g.chunk * 8;
     } else {
-      const int xr = live_row[min(m0 + row, live - 1)];
-      src[i] = (const uint16_t*)a.x + (int64_t)xr * a.d_in + ch * 8;
+      const int xr = live_row[min(m0 + g.row, live - 1)];
+      src[i] = (const uint16_t*)a.x + (int64_t)xr * a.d_in + g.chunk * 8;
     }
   }
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto issue = [&](int kc, uint8_t* base) {  // slice kc into a ring buffer
-    const int k0 = kc * kGK;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(src[i] + k0), (lds_ptr)(base + (kLoadsPerWave * wv + i) * kFrag),
-                                       16, 0, 0);
-  };
-
   f32x16_t acc[4][2];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg)
@@ -254,83 +208,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cg][rg][i] = 0.f;
-
-  // Byte offset of this lane's fragment element in a staged operand, for k
-  // chunk pair kk: row l % 32 (plus 32 q rows = 2048 q bytes), chunk 2 kk + l/32
-  // at its swizzled position.
-  int frag_off[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) frag_off[kk] = frow * 64 + (((2 * kk + fchunk) ^ ((frow >> 2) & 3)) * 16);
-
-  // One step of the ring: slice kc is read from ``cur``; slice kc + 3 goes
-  // into ``refill``, the buffer every wave finished reading last step.  (The
-  // buffers are named statically in each of the four unrolled steps so the
-  // compiler can tell the buffer being read from the ones being filled.)
-  const int nk = a.d_in / kGK;
-  auto step = [&](int kc, const uint8_t* cur, uint8_t* refill) {
-    // slice kc landed (the two slices issued after it may still be in flight)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerWave * (kStages - 2)));
-    __builtin_amdgcn_s_barrier();
-    // past the end: a re-read of the last slice into a buffer nobody reads again
-    issue(min(kc + kStages - 1, nk - 1), refill);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      // lane l reads row 32 q + l % 32 (rows of one fragment are 2 KB apart per 32) and chunk 2 kk + l/32
-      const uint8_t* buf = cur + frag_off[kk];
-      bf16x8_t A[4], B[2];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        A[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + (4 * wn + q) * 2048));
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        B[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(buf + 16 * kFrag + (2 * wm + q) * 2048));
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
-          acc[cg][rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[cg], B[rg], acc[cg][rg], 0, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's reads of the buffer are done
-  };
-#if FM_GEMM_STAGES == 4
-  issue(0, ring0);
-  issue(min(1, nk - 1), ring1);
-  issue(min(2, nk - 1), ring2);
-  // nk is even (d_in a multiple of 64); the tail handles nk % 4 == 2
-  int kc = 0;
-  for (; kc + 4 <= nk; kc += 4) {
-    step(kc, ring0, ring3);
-    step(kc + 1, ring1, ring0);
-    step(kc + 2, ring2, ring1);
-    step(kc + 3, ring3, ring2);
-  }
-  if (kc < nk) {
-    step(kc, ring0, ring3);
-    step(kc + 1, ring1, ring0);
-  }
-#elif FM_GEMM_STAGES == 5
-  issue(0, ring0);
-  issue(min(1, nk - 1), ring1);
-  issue(min(2, nk - 1), ring2);
-  issue(min(3, nk - 1), ring3);
-  int kc = 0;
-  for (; kc + 5 <= nk; kc += 5) {
-    step(kc, ring0, ring4);
-    step(kc + 1, ring1, ring0);
-    step(kc + 2, ring2, ring1);
-    step(kc + 3, ring3, ring2);
-    step(kc + 4, ring4, ring3);
-  }
-  // the last nk % 5 slices, in ring order (each step's buffers named statically)
-  const int rem = nk - kc;
-  if (rem > 0) step(kc, ring0, ring4);
-  if (rem > 1) step(kc + 1, ring1, ring0);
-  if (rem > 2) step(kc + 2, ring2, ring1);
-  if (rem > 3) step(kc + 3, ring3, ring2);
-#else
-#error "FM_GEMM_STAGES must be 4 or 5"
-#endif
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the ring's trailing loads
+  gemm256_mainloop(acc, src, a.d_in / kGK, wv, wm, wn, ring0, ring1, ring2, ring3, ring4);
   // acc[cg][rg][i] (lane l) = Y[tile row 64 wm + 32 rg + l % 32]
   //                            [head column 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]
 

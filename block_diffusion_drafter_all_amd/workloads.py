@@ -38,6 +38,21 @@ class WriteInputs:
 
 
 @dataclass
+class UpstreamInputs:
+    """What the write's rows are made from (fm_context_rows): the window rows'
+    concatenated target hidden states through fc and hidden_norm, the anchors'
+    token embeddings through anchor_proj and anchor_norm."""
+    hidden: torch.Tensor          # (bs * window, n_aux * d_target) bf16
+    w_fc: torch.Tensor            # (dim, n_aux * d_target) bf16
+    hidden_norm_w: torch.Tensor   # (dim,) fp32
+    anchor_ids: torch.Tensor      # (bs,) int32
+    embedding: torch.Tensor       # (vocab, d_target) bf16
+    w_anchor_proj: torch.Tensor   # (dim, d_target) bf16
+    b_anchor_proj: torch.Tensor   # (dim,) bf16
+    anchor_norm_w: torch.Tensor   # (dim,) fp32
+
+
+@dataclass
 class Workload:
     name: str
     workload_id: int
@@ -59,6 +74,7 @@ class Workload:
     self_k_norm_w: list                # L x (Dh,) fp32
     write: WriteInputs | None = None
     n_cand: int = 1                    # candidate blocks per request (tree drafting)
+    upstream: UpstreamInputs | None = None  # the write's rows made by fm_context_rows (write.x receives them)
     kv_scales: list | None = None      # e4m3 pool: (k_scale, v_scale) per layer (None = 1)
     q_scales: list | None = None       # e4m3 pool: fixed query scale per layer (None = per request and head)
     eps: float = EPS
@@ -146,7 +162,7 @@ def _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K, q_scale=1.0):
 
 
 def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_major", scale_down=None,
-                  q_scale=1.0, seed=None, n_cand=1, kv_fp8=False) -> Workload:
+                  q_scale=1.0, seed=None, n_cand=1, kv_fp8=False, upstream=False) -> Workload:
     """The seeded inputs of one workload.
 
     1  tiny fp32 full step: 1 request, ctx 64, 1 layer, 4 x 64, page 16,
@@ -167,6 +183,12 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     ``kv_fp8``: the pools hold e4m3 (the same N(0, 1) draws cast to e4m3;
     bf16 workloads only); the write stores e4m3 at scale 1 and cross-attention
     quantizes its queries (sglang/model.py ``_kv_fp8`` path).
+    ``upstream`` (workload 5): the write's rows are made on the device from
+    the window rows' concatenated target hidden states (``n_aux`` = 5 layers
+    of ``d_target`` = 4096, N(0, 1)) through ``fc`` (N(0, 0.02^2)) and
+    ``hidden_norm``, and from the anchors' token embeddings (vocab 151936,
+    N(0, 1)) through ``anchor_proj`` (N(0, 0.02^2), bias N(0, 0.1^2)) and
+    ``anchor_norm``; ``write.x`` is the buffer that receives them.
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + workload_id if seed is None else seed)
@@ -255,7 +277,22 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
                              torch.arange(bs, device=device)]).to(torch.int32)
         write = WriteInputs(x=x, w_kv=w_kv, k_norm_w=None, row_req=row_req, row_pos=row_pos,
                             commit_lens=commit, window=window)
+        if upstream:
+            n_aux, d_target, vocab = sd.get("n_aux", 5), sd.get("d_target", 4096), sd.get("vocab", 151936)
+            hidden = _randn((bs * window, n_aux * d_target), gen, dtype, device)
+            w_fc = _randn((d_in, n_aux * d_target), gen, dtype, device, std=0.02)
+            anchor_ids = torch.randint(0, vocab, (bs,), generator=gen, device=device, dtype=torch.int32)
+            embedding = _randn((vocab, d_target), gen, dtype, device)
+            w_ap = _randn((d_in, d_target), gen, dtype, device, std=0.02)
+            b_ap = _randn((d_in,), gen, dtype, device, std=0.1)
+            up_norms = _norm_weights(2, d_in, gen, device, weights)
+            upstream_inputs = UpstreamInputs(hidden=hidden, w_fc=w_fc, hidden_norm_w=up_norms[0],
+                                             anchor_ids=anchor_ids, embedding=embedding, w_anchor_proj=w_ap,
+                                             b_anchor_proj=b_ap, anchor_norm_w=up_norms[1])
+            x.fill_(float("nan"))  # filled by fm_context_rows; skipped rows keep the NaN
 
+    if not upstream or workload_id != 5:
+        upstream_inputs = None
     q_norm_w = _norm_weights(L, Dh, gen, device, weights)
     self_q = _norm_weights(L, Dh, gen, device, weights)
     self_k = _norm_weights(L, Dh, gen, device, weights)
@@ -266,5 +303,6 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     return Workload(name=names[workload_id], workload_id=workload_id, bs=bs, K=K, L=L, H=H, Dh=Dh, page_size=ps,
                     dtype=dtype, ctx_lens=ctx.contiguous(), cu_seqlens_q=cu_q, page_table=pt, pools=pools, q=q,
                     qkv=qkv, q_norm_w=q_norm_w, self_q_norm_w=self_q, self_k_norm_w=self_k, write=write,
-                    n_cand=n_cand, meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale,
-                                             kv_fp8=kv_fp8))
+                    n_cand=n_cand, upstream=upstream_inputs,
+                    meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale,
+                              kv_fp8=kv_fp8))

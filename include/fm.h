@@ -4,6 +4,9 @@
  * The draft step of the FlashMap block drafter (flashmap 0.1.0 wheel:
  * sglang/model.py ``forward`` / ``_denoise``, vllm/model.py ``forward`` /
  * ``_dit``, modeling_flashmap.py ``draft``) runs, for every DiT layer:
+ *   0. the rows that write takes: committed target positions through fc and
+ *      hidden_norm, anchors through anchor_proj and anchor_norm
+ *                                             -> fm_context_rows
  *   1. the context/anchor K/V write: one GEMM over every layer's context K/V
  *      weight, RMS k-norm, interleaved-pair RoPE and a paged scatter that skips
  *      uncommitted verify columns            -> fm_write_context_kv
@@ -139,6 +142,51 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
                         int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
                         float eps, float rope_theta, const float* kv_scales, int32_t* out_slots,
                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------- context rows -- */
+
+/* Workspace bytes fm_context_rows needs (0 for invalid sizes). */
+size_t fm_context_rows_workspace_size(int64_t n_hidden, int64_t n_anchor, int32_t d_hidden, int32_t d_target,
+                                      int32_t dim);
+
+/*
+ * The rows fm_write_context_kv projects (sglang/model.py ``_write_context``,
+ * ``_anchor_kv_impl``; vllm/model.py ``combine_hidden_states``,
+ * ``precompute_and_store_context_kv``, ``_prologue``;
+ * modeling_flashmap.py ``fc``, ``hidden_norm``, ``anchor_proj``, ``anchor_norm``):
+ *
+ *   rows[r]            = RMSNorm(W_fc hidden[r]; hidden_norm_w, eps)            r < n_hidden
+ *   rows[n_hidden + a] = RMSNorm(W_ap embedding[anchor_ids[a]] + b_ap; anchor_norm_w, eps)
+ *
+ * fp32 accumulation, each row rounded once to bf16.  Hidden rows the commit
+ * rule skips are neither computed nor written (their rows are left as they
+ * were); it is the rule of fm_write_context_kv, so passing ``rows`` as its x
+ * (with the anchors as its last n_anchor rows) writes the same context.
+ *
+ * hidden       DEVICE bf16 [n_hidden, d_hidden]: the target's hidden states of
+ *              the chosen layers, concatenated per row (d_hidden = n_aux *
+ *              target hidden size), a multiple of 32.
+ * w_fc         DEVICE bf16 [dim, d_hidden] (``fc``, no bias).
+ * hidden_norm_w, anchor_norm_w   DEVICE fp32 [dim].
+ * anchor_ids   DEVICE int32 [n_anchor]: anchor tokens; an id outside [0, vocab)
+ *              reads a clamped row and sets bit 0 of the workspace error word.
+ * embedding    DEVICE bf16 [vocab, d_target] (the target's token embedding).
+ * w_anchor_proj DEVICE bf16 [dim, d_target];  b_anchor_proj DEVICE bf16 [dim].
+ * dim          DiT width, a multiple of 1024 in [1024, 8192].
+ * commit_lens, window, bs  optional verify-window rule, as in
+ *              fm_write_context_kv: rows [0, bs*window) are request-major
+ *              windows and column j of request b is computed only if
+ *              j < commit_lens[b] (NULL: every hidden row).
+ * rows         DEVICE bf16 [n_hidden + n_anchor, dim].
+ * ws           DEVICE workspace of fm_context_rows_workspace_size(...) bytes,
+ *              256-byte aligned.
+ * Every pointer 16-byte aligned.
+ */
+int fm_context_rows(const void* hidden, int64_t n_hidden, int32_t d_hidden, const void* w_fc,
+                    const float* hidden_norm_w, const int32_t* anchor_ids, int64_t n_anchor, const void* embedding,
+                    int64_t vocab, int32_t d_target, const void* w_anchor_proj, const void* b_anchor_proj,
+                    const float* anchor_norm_w, int32_t dim, const int32_t* commit_lens, int32_t window, int32_t bs,
+                    float eps, void* rows, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------ cross-attention -- */
 

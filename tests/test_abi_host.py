@@ -184,3 +184,42 @@ def test_binding_dtype_pairs():
         B._dtype_code(f32, torch.float8_e4m3fn)
     with pytest.raises(TypeError):
         B._dtype_code(bf, torch.float32)
+
+
+def _rows(lib, **over):
+    a = dict(hidden=FAKE, n_hidden=8, d_hidden=512, w_fc=FAKE, hn=FAKE, ids=FAKE, n_anchor=2, emb=FAKE, vocab=100,
+             d_target=256, wap=FAKE, bap=FAKE, an=FAKE, dim=1024, cl=None, win=0, bs=0, eps=1e-6, rows=FAKE, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(over)
+    return lib.fm_context_rows(a["hidden"], a["n_hidden"], a["d_hidden"], a["w_fc"], a["hn"], a["ids"], a["n_anchor"],
+                               a["emb"], a["vocab"], a["d_target"], a["wap"], a["bap"], a["an"], a["dim"], a["cl"],
+                               a["win"], a["bs"], a["eps"], a["rows"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(hidden=None), B.FM_E_INVALID, "hidden-row pointer"),
+    (dict(ids=None), B.FM_E_INVALID, "anchor-row pointer"),
+    (dict(dim=1000), B.FM_E_UNSUPPORTED, "dim"),
+    (dict(dim=9216), B.FM_E_UNSUPPORTED, "dim"),
+    (dict(d_hidden=500), B.FM_E_UNSUPPORTED, "d_hidden"),
+    (dict(d_target=100), B.FM_E_UNSUPPORTED, "d_target"),
+    (dict(vocab=0), B.FM_E_INVALID, "vocab"),
+    (dict(cl=FAKE, win=0, bs=1), B.FM_E_INVALID, "window"),
+    (dict(cl=FAKE, win=5, bs=2), B.FM_E_INVALID, "bs * window"),
+    (dict(rows=FAKE + 8), B.FM_E_INVALID, "aligned"),
+    (dict(ws_bytes=100), B.FM_E_WORKSPACE, "needed"),
+    (dict(eps=-1.0), B.FM_E_INVALID, "eps"),
+    (dict(n_hidden=-1), B.FM_E_INVALID, "n_hidden"),
+])
+def test_context_rows_rejects(lib, over, status, needle):
+    assert _rows(lib, **over) == status
+    assert needle in B.fm_last_error()
+
+
+def test_context_rows_empty_and_workspace(lib):
+    assert _rows(lib, n_hidden=0, n_anchor=0, hidden=None, ids=None) == B.FM_OK
+    # the partials of the contraction ranges dominate: more rows, more bytes
+    small = lib.fm_context_rows_workspace_size(64, 64, 20480, 4096, 4096)
+    big = lib.fm_context_rows_workspace_size(1088, 64, 20480, 4096, 4096)
+    assert 0 < small < big and big >= 1088 * 4096 * 4
+    assert lib.fm_context_rows_workspace_size(-1, 0, 64, 64, 1024) == 0

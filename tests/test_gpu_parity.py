@@ -436,3 +436,111 @@ def test_fp8_pool_static_q_scale_saturates():
     S.run_step(w, buf)
     torch.cuda.synchronize()
     _check_attention(w, buf, list(range(w.bs)))
+
+
+# ------------------------------------------------- rows of the K/V write
+# sglang/model.py ``_write_context`` (fc, hidden_norm) and ``_anchor_kv_impl``
+# (embedding, anchor_proj, anchor_norm).  The rows buffer is bf16: the write
+# reads it as its x, so each stage is checked against the oracle from its own
+# inputs.
+
+
+def _oracle_rows(w, rows_idx=None, anchors=None):
+    """Oracle rows for the given committed window rows and anchors."""
+    up = w.upstream
+    out = {}
+    if rows_idx:
+        out["hidden"] = O.context_input_rows(to_np(up.hidden[torch.as_tensor(rows_idx, device=up.hidden.device)]),
+                                             to_np(up.w_fc), to_np(up.hidden_norm_w), w.eps)
+    if anchors:
+        ids = up.anchor_ids.cpu().numpy()[anchors]
+        uniq, inv = np.unique(ids, return_inverse=True)
+        emb = to_np(up.embedding[torch.as_tensor(uniq, device=up.embedding.device, dtype=torch.long)])
+        out["anchor"] = O.anchor_input_rows(inv, emb, to_np(up.w_anchor_proj), to_np(up.b_anchor_proj),
+                                            to_np(up.anchor_norm_w), w.eps)
+    return out
+
+
+def _committed_rows(w):
+    wr = w.write
+    cl = wr.commit_lens.cpu().numpy()
+    return [b * wr.window + j for b in range(w.bs) for j in range(int(cl[b]))]
+
+
+def test_context_rows_small_step():
+    log("rows of the write: fc + hidden_norm, anchor_proj + anchor_norm, then the step")
+    w = make_workload(5, weights="random", upstream=True,
+                      scale_down=dict(bs=6, ctx=(20, 90), L=2, H=4, d_in=1024, n_aux=2, d_target=256, vocab=1000))
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    wr = w.write
+    live = _committed_rows(w)
+    n_win = w.bs * wr.window
+    ref = _oracle_rows(w, live, list(range(w.bs)))
+    compare(wr.x[torch.as_tensor(live, device=wr.x.device)], ref["hidden"], "rows: fc + hidden_norm")
+    compare(wr.x[n_win:], ref["anchor"], "rows: anchor_proj + anchor_norm")
+    skipped = sorted(set(range(n_win)) - set(live))
+    assert skipped and torch.isnan(wr.x[torch.as_tensor(skipped, device=wr.x.device)].float()).all(), \
+        "rows the commit rule skips must be left untouched"
+    assert int(buf.rows_ws[4:8].view(torch.int32).item()) == 0
+    slots, keys, values = _write_oracle(w)
+    _check_write(w, buf, before, slots, keys, values)
+    _check_full_step_attention(w, buf, before, slots, keys, values, list(range(w.bs)))
+
+
+def test_context_rows_full_size_sampled():
+    log("rows of the write at full size: 5 x 4096 -> 4096 (fc), vocab 151936 (sampled rows)")
+    w = make_workload(5, upstream=True)
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    wr = w.write
+    live = _committed_rows(w)
+    rng = np.random.default_rng(21)
+    pick = sorted(rng.choice(live, size=48, replace=False).tolist())
+    ref = _oracle_rows(w, pick, list(range(w.bs)))
+    compare(wr.x[torch.as_tensor(pick, device=wr.x.device)], ref["hidden"], "rows: fc + hidden_norm (48 rows)")
+    compare(wr.x[w.bs * wr.window:], ref["anchor"], "rows: anchors (all 64)")
+    slots, keys, values = _write_oracle(w)
+    np.testing.assert_array_equal(buf.out_slots.cpu().numpy(), slots)
+    reqs = _sample(w, 2, 7)
+    _check_full_step_attention(w, buf, before, slots, keys, values, reqs)
+
+
+def test_prefill_in_chunks():
+    # a prefill of 4100 rows (two full chunks of 2048 and a ragged one) of one
+    # request: the pool against the oracle's write of the oracle's rows (rounded
+    # to bf16, the rows buffer's type)
+    log("prefill: 4100 rows in chunks of 2048")
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    n, d_hidden, dim, L, H, Dh, ps = 4100, 512, 1024, 2, 4, 128, 16
+    n_pages = math.ceil(n / ps) + 5
+    hidden = torch.randn((n, d_hidden), generator=gen, device=dev).to(torch.bfloat16)
+    w_fc = (0.05 * torch.randn((dim, d_hidden), generator=gen, device=dev)).to(torch.bfloat16)
+    g_h = 1 + 0.1 * torch.randn(dim, generator=gen, device=dev)
+    w_kv = (0.03 * torch.randn((L * 2 * H * Dh, dim), generator=gen, device=dev)).to(torch.bfloat16)
+    k_norm_w = 1 + 0.1 * torch.randn((L, Dh), generator=gen, device=dev)
+    perm = torch.randperm(n_pages, generator=gen, device=dev).to(torch.int32)
+    page_table = perm[: math.ceil(n / ps)][None, :].contiguous()
+    pools = [B.KVPool(torch.zeros((n_pages, H, ps, Dh), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3),
+                      torch.zeros((n_pages, H, ps, Dh), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3))
+             for _ in range(L)]
+    positions = torch.arange(n, dtype=torch.int32, device=dev)
+    row_req = torch.zeros(n, dtype=torch.int32, device=dev)
+    out_slots = torch.empty(n, dtype=torch.int32, device=dev)
+    S.write_prefill(hidden, positions, row_req, page_table, pools, w_fc, g_h, w_kv, k_norm_w, 1e-6, 1e6,
+                    out_slots=out_slots)
+    torch.cuda.synchronize()
+    rows = O.round_to_bfloat16(O.context_input_rows(to_np(hidden), to_np(w_fc), to_np(g_h), 1e-6))
+    slots, keys, values = O.write_context_kv(rows, to_np(w_kv), to_np(k_norm_w), np.zeros(n, dtype=np.int64),
+                                             np.arange(n), page_table.cpu().numpy(), ps, L, H, Dh, 1e-6, 1e6)
+    np.testing.assert_array_equal(out_slots.cpu().numpy(), slots)
+    for l in range(L):
+        sl = torch.as_tensor(slots, device=dev, dtype=torch.long)
+        compare(pools[l].k[sl // ps, sl % ps], keys[:, l], f"prefill K L{l}")
+        compare(pools[l].v[sl // ps, sl % ps], values[:, l], f"prefill V L{l}")
