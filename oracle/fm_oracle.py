@@ -64,6 +64,10 @@ __all__ = [
     "scatter_into_pool",
     "paged_cross_attention",
     "block_self_attention",
+    "layer_norm",
+    "gelu",
+    "ada_layer_norm",
+    "dit_layer",
 ]
 
 
@@ -380,3 +384,58 @@ def block_self_attention(qkv, q_norm_w, k_norm_w, ctx_lens, scale, theta, eps):
             kh = apply_rope(rms_norm(qkv[b, :, 1, h], k_norm_w, eps), positions, theta)
             out[b, :, h] = attention(qh, kh, qkv[b, :, 2, h], scale)
     return out
+
+
+# ---------------------------------------------------------- the DiT layer --
+
+
+def layer_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """LayerNorm over the last axis without affine parameters
+    (``F.layer_norm(x, (dim,), eps=eps)``)."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + float(eps))
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """GELU with the exact normal CDF (``F.gelu``'s default): x * Phi(x)."""
+    from scipy.special import erf
+
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def ada_layer_norm(h, scale, shift, eps):
+    """A time-modulated LayerNorm: ``layer_norm(h) * scale + shift`` with the
+    step's per-channel ``scale`` (already ``1 + scale``) and ``shift`` (the
+    sglang model's ``_denoise``; modeling_flashmap.py ``FlashMapAdaLayerNorm``)."""
+    return layer_norm(h, eps) * np.asarray(scale, dtype=np.float64) + np.asarray(shift, dtype=np.float64)
+
+
+def dit_layer(h, mod, w, self_attention, cross_attention, eps):
+    """One DiT block of the draft step (the sglang model's ``_denoise`` loop
+    body; modeling_flashmap.py ``FlashMapLayer.forward``), on rows ``h (M,
+    dim)``:
+
+      h += s_gate * o_self(self_attention(qkv(ada_ln(h; s_scale, s_shift))))
+      h += c_gate * o_cross(cross_attention(q(ada_ln(h; c_scale, c_shift))))
+      h += m_gate * fc2(gelu(fc1(ada_ln(h; m_scale, m_shift)) + b1)) + b2)
+
+    ``mod``: the step's per-layer vectors ``s_scale, s_shift, s_gate, c_scale,
+    c_shift, c_gate, m_scale, m_shift, m_gate`` (dim,), scales already ``1 +
+    scale``.  ``w``: ``qkv (3 dim, dim)`` (q, k, v heads), ``o_self``,
+    ``q``, ``o_cross`` (dim, dim), ``fc1 (I, dim)``, ``b1 (I)``, ``fc2 (dim,
+    I)``, ``b2 (dim)``; no bias elsewhere.  ``self_attention(qkv)`` maps the
+    (M, 3 dim) projections to (M, dim) (norms and RoPE inside);
+    ``cross_attention(q)`` maps the raw (M, dim) queries to (M, dim)."""
+    f = lambda k: np.asarray(mod[k], dtype=np.float64)  # noqa: E731
+    W = lambda k: np.asarray(w[k], dtype=np.float64)    # noqa: E731
+    h = np.asarray(h, dtype=np.float64).copy()
+    x = ada_layer_norm(h, f("s_scale"), f("s_shift"), eps)
+    h = h + f("s_gate") * (self_attention(x @ W("qkv").T) @ W("o_self").T)
+    x = ada_layer_norm(h, f("c_scale"), f("c_shift"), eps)
+    h = h + f("c_gate") * (cross_attention(x @ W("q").T) @ W("o_cross").T)
+    x = ada_layer_norm(h, f("m_scale"), f("m_shift"), eps)
+    y = gelu(x @ W("fc1").T + W("b1")) @ W("fc2").T + W("b2")
+    return h + f("m_gate") * y

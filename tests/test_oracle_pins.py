@@ -546,3 +546,60 @@ def test_written_context_is_read_back_by_paged_attention(rng):
         kk = O.round_to_storage(keys[:, 0, h], "f32")
         vv = O.round_to_storage(values[:, 0, h], "f32")
         np.testing.assert_allclose(out[:, h], O.attention(qh, kk, vv, 0.25), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------- the DiT layer
+
+
+def test_layer_norm_and_gelu_against_torch(rng):
+    x = rng.standard_normal((5, 64)) * 3 + 1.5
+    np.testing.assert_allclose(O.layer_norm(x, 1e-6), F.layer_norm(torch.from_numpy(x), (64,), eps=1e-6).numpy(),
+                               rtol=1e-12, atol=1e-13)
+    y = O.layer_norm(x, 0.0)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, rtol=1e-12)
+    g = rng.standard_normal(1000) * 4
+    np.testing.assert_allclose(O.gelu(g), F.gelu(torch.from_numpy(g)).numpy(), rtol=1e-12, atol=1e-15)
+    # closed forms: Phi(0) = 1/2, Phi(1) = (1 + erf(1/sqrt 2)) / 2 = 0.841344746068543
+    np.testing.assert_allclose(O.gelu(np.array([0.0, 1.0, -1.0])), [0.0, 0.841344746068543, -0.158655253931457],
+                               rtol=1e-14, atol=1e-15)
+
+
+def _dit_case(rng, M=6, dim=16, inter=40):
+    w = {"qkv": rng.standard_normal((3 * dim, dim)) * 0.3, "o_self": rng.standard_normal((dim, dim)) * 0.3,
+         "q": rng.standard_normal((dim, dim)) * 0.3, "o_cross": rng.standard_normal((dim, dim)) * 0.3,
+         "fc1": rng.standard_normal((inter, dim)) * 0.3, "b1": rng.standard_normal(inter) * 0.1,
+         "fc2": rng.standard_normal((dim, inter)) * 0.3, "b2": rng.standard_normal(dim) * 0.1}
+    mod = {k: (1.0 + 0.2 * rng.standard_normal(dim)) if k.endswith("scale") else 0.3 * rng.standard_normal(dim)
+           for k in ("s_scale", "s_shift", "s_gate", "c_scale", "c_shift", "c_gate", "m_scale", "m_shift", "m_gate")}
+    h = rng.standard_normal((M, dim)) * 2
+    return h, mod, w
+
+
+def test_dit_layer_against_a_torch_composition(rng):
+    h, mod, w = _dit_case(rng)
+    ctx = rng.standard_normal((9, 16))
+    sa = lambda qkv: np.tanh(qkv[:, :16] + qkv[:, 32:])       # stand-ins: any fixed maps  # noqa: E731
+    ca = lambda q: q @ ctx.T @ ctx / 9.0                        # noqa: E731
+    got = O.dit_layer(h, mod, w, sa, ca, 1e-6)
+    t = {k: torch.from_numpy(np.asarray(v)) for k, v in {**w, **mod}.items()}
+    x = torch.from_numpy(h)
+    ln = lambda v, a, b: F.layer_norm(v, (16,), eps=1e-6) * t[a] + t[b]  # noqa: E731
+    x = x + t["s_gate"] * F.linear(torch.from_numpy(sa(F.linear(ln(x, "s_scale", "s_shift"), t["qkv"]).numpy())),
+                                   t["o_self"])
+    x = x + t["c_gate"] * F.linear(torch.from_numpy(ca(F.linear(ln(x, "c_scale", "c_shift"), t["q"]).numpy())),
+                                   t["o_cross"])
+    x = x + t["m_gate"] * F.linear(F.gelu(F.linear(ln(x, "m_scale", "m_shift"), t["fc1"], t["b1"])), t["fc2"], t["b2"])
+    np.testing.assert_allclose(got, x.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_dit_layer_gates_and_zero_branches(rng):
+    h, mod, w = _dit_case(rng)
+    sa = lambda qkv: qkv[:, :16] * 2.0                          # noqa: E731
+    ca = lambda q: q - 1.0                                      # noqa: E731
+    closed = dict(mod, s_gate=np.zeros(16), c_gate=np.zeros(16), m_gate=np.zeros(16))
+    np.testing.assert_array_equal(O.dit_layer(h, closed, w, sa, ca, 1e-6), h)   # every gate shut: identity
+    # only the MLP open, with fc2 = 0: the residual gains m_gate * b2 exactly
+    only = dict(closed, m_gate=mod["m_gate"])
+    got = O.dit_layer(h, only, dict(w, fc2=np.zeros_like(w["fc2"])), sa, ca, 1e-6)
+    np.testing.assert_allclose(got, h + mod["m_gate"] * w["b2"], rtol=1e-15, atol=1e-15)
