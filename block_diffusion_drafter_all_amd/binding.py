@@ -24,6 +24,10 @@ FM_E_HIP = -4
 FM_F32 = 0
 FM_BF16 = 1
 FM_BF16_E4M3 = 2
+FM_LINEAR_BF16 = 0
+FM_LINEAR_GELU_BF16 = 1
+FM_LINEAR_RESIDUAL = 2
+FM_LINEAR_ASSIGN_F32 = 3
 
 SYMBOLS = (
     "fm_last_error",
@@ -32,6 +36,9 @@ SYMBOLS = (
     "fm_write_context_kv",
     "fm_context_rows_workspace_size",
     "fm_context_rows",
+    "fm_ada_layer_norm",
+    "fm_linear_workspace_size",
+    "fm_linear",
     "fm_cross_attention_workspace_size",
     "fm_plan_cross_attention",
     "fm_paged_cross_attention",
@@ -88,6 +95,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         vp, c_i64, c_i32, vp, vp, vp, c_i64, vp, c_i64, c_i32, vp, vp, vp, c_i32, vp, c_i32, c_i32, f32, vp, vp,
         c_sz, vp,
     ]
+    lib.fm_ada_layer_norm.restype = ctypes.c_int
+    lib.fm_ada_layer_norm.argtypes = [vp, c_i64, c_i32, vp, vp, f32, vp, vp]
+    lib.fm_linear_workspace_size.restype = c_sz
+    lib.fm_linear_workspace_size.argtypes = [c_i64, c_i32, c_i32]
+    lib.fm_linear.restype = ctypes.c_int
+    lib.fm_linear.argtypes = [vp, c_i64, c_i32, vp, c_i32, vp, ctypes.c_int, vp, vp, vp, c_sz, vp]
     lib.fm_cross_attention_workspace_size.restype = c_sz
     lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]
     lib.fm_plan_cross_attention.restype = ctypes.c_int
@@ -283,6 +296,52 @@ def fm_context_rows(hidden, w_fc, hidden_norm_w, anchor_ids, embedding, w_anchor
         _ptr(b_anchor_proj), _ptr(anchor_norm_w), dim, _ptr(commit_lens), window, 0 if bs is None else bs, eps,
         _ptr(rows), _ptr(ws), ws.numel(), _stream()))
     return rows
+
+
+def fm_ada_layer_norm(h, scale, shift, eps, out=None):
+    """``LayerNorm(h) * scale + shift`` of the fp32 residual stream ``h (rows,
+    dim)`` into bf16 ``out``."""
+    _need(h, "h", torch.float32)
+    _need(scale, "scale", torch.float32)
+    _need(shift, "shift", torch.float32)
+    rows, dim = h.shape
+    if out is None:
+        out = torch.empty((rows, dim), dtype=torch.bfloat16, device=h.device)
+    _need(out, "out", torch.bfloat16)
+    _check(load_library().fm_ada_layer_norm(_ptr(h), rows, dim, _ptr(scale), _ptr(shift), eps, _ptr(out), _stream()))
+    return out
+
+
+def fm_linear_workspace_size(M: int, N: int, K: int) -> int:
+    return load_library().fm_linear_workspace_size(M, N, K)
+
+
+def fm_linear(x, w, bias=None, epilogue=FM_LINEAR_BF16, gate=None, out=None, ws=None):
+    """``y = x w^T + bias`` with an epilogue: bf16 out, GELU bf16 out, the
+    gated residual ``out += gate * y`` into an fp32 ``out``, or fp32 ``out = y``."""
+    lib = load_library()
+    _need(x, "x", torch.bfloat16)
+    _need(w, "w", torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape != (N, K):
+        raise ValueError("w must be (N, K) for x (M, K)")
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16)
+    if gate is not None:
+        _need(gate, "gate", torch.float32)
+    f32_out = epilogue in (FM_LINEAR_RESIDUAL, FM_LINEAR_ASSIGN_F32)
+    if out is None:
+        if epilogue == FM_LINEAR_RESIDUAL:
+            raise ValueError("the residual epilogue updates an existing out")
+        out = torch.empty((M, N), dtype=torch.float32 if f32_out else torch.bfloat16, device=x.device)
+    _need(out, "out", torch.float32 if f32_out else torch.bfloat16)
+    need = lib.fm_linear_workspace_size(M, N, K)
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib.fm_linear(_ptr(x), M, K, _ptr(w), N, _ptr(bias), epilogue, _ptr(gate), _ptr(out), _ptr(ws),
+                         0 if ws is None else ws.numel(), _stream()))
+    return out
 
 
 def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16,

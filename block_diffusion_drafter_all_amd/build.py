@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_DIR = os.path.join(PKG_DIR, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfm.so")
-SOURCES = ("abi.cpp", "context_rows.hip", "cross_attention.hip", "self_attention.hip", "write_kv.hip")
+SOURCES = ("abi.cpp", "context_rows.hip", "cross_attention.hip", "dit.hip", "self_attention.hip", "write_kv.hip")
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled: the compiler must not form

@@ -272,6 +272,62 @@ int fm_context_rows(const void* hidden, int64_t n_hidden, int32_t d_hidden, cons
   return from_hip(fm::launch_context_rows(a, stream), fn);
 }
 
+int fm_ada_layer_norm(const float* h, int64_t rows, int32_t dim, const float* scale, const float* shift, float eps,
+                      void* out, hipStream_t stream) {
+  const char* fn = "fm_ada_layer_norm";
+  if (rows < 0) return fail(FM_E_INVALID, "%s: rows %lld < 0", fn, (long long)rows);
+  if (rows == 0) return ok();
+  if (!h || !scale || !shift || !out) return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
+  if (dim < 1024 || dim % 1024 || dim > 8192)
+    return fail(FM_E_UNSUPPORTED, "%s: dim %d must be a multiple of 1024 in [1024, 8192]", fn, dim);
+  if (!aligned16(h) || !aligned16(scale) || !aligned16(shift) || !aligned16(out))
+    return fail(FM_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FM_E_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (rows > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: rows above 2^31-1", fn);
+  fm::AdaLnArgs a{h, rows, dim, scale, shift, eps, out};
+  return from_hip(fm::launch_ada_layer_norm(a, stream), fn);
+}
+
+size_t fm_linear_workspace_size(int64_t M, int32_t N, int32_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  const int splits = fm::linear_splits(M, N, K);
+  return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0;
+}
+
+int fm_linear(const void* x, int64_t M, int32_t K, const void* w, int32_t N, const void* bias,
+              fm_linear_epilogue epilogue, const float* gate, void* out, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  const char* fn = "fm_linear";
+  if (M < 0) return fail(FM_E_INVALID, "%s: M %lld < 0", fn, (long long)M);
+  if (M == 0) return ok();
+  if (!x || !w || !out) return fail(FM_E_INVALID, "%s: x, w and out are required", fn);
+  if ((int)epilogue < 0 || (int)epilogue > 3) return fail(FM_E_UNSUPPORTED, "%s: epilogue %d", fn, (int)epilogue);
+  if (epilogue == FM_LINEAR_RESIDUAL && !gate) return fail(FM_E_INVALID, "%s: the residual epilogue needs gate", fn);
+  if (K < 32 || K % 32) return fail(FM_E_UNSUPPORTED, "%s: K %d must be a positive multiple of 32", fn, K);
+  if (N < 1024 || N % 1024) return fail(FM_E_UNSUPPORTED, "%s: N %d must be a positive multiple of 1024", fn, N);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (bias && !aligned16(bias)) || (gate && !aligned16(gate)))
+    return fail(FM_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  if (M > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: M above 2^31-1", fn);
+  const int splits = fm::linear_splits(M, N, K);
+  const size_t need = fm_linear_workspace_size(M, N, K);
+  if (need > 0) {
+    if (int s = check_ws(fn, ws, ws_bytes, need)) return s;
+  }
+  fm::LinearArgs a{};
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.gate = gate;
+  a.out = out;
+  a.part = static_cast<float*>(ws);
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.splits = splits;
+  a.epilogue = (int)epilogue;
+  return from_hip(fm::launch_linear(a, stream), fn);
+}
+
 size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt) {
   const int nqf = fm::q_frags(max_q);
   if (bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || nqf == 0) return 0;

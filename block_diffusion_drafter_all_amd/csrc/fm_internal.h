@@ -274,6 +274,37 @@ struct CtxRowsArgs {
   CtxRowsLayout lay;
 };
 
+// -------------------------------------------------------------- DiT layer --
+
+struct AdaLnArgs {
+  const float* h;      // fp32 [rows, dim]
+  int64_t rows;
+  int32_t dim;
+  const float* scale;  // [dim], already 1 + scale
+  const float* shift;  // [dim]
+  float eps;
+  void* out;           // bf16 [rows, dim]
+};
+
+// Epilogues of fm_linear (the values of fm_linear_epilogue in fm.h).
+constexpr int kLinBf16 = 0, kLinGeluBf16 = 1, kLinResidual = 2, kLinAssignF32 = 3;
+
+struct LinearArgs {
+  const void* x;       // bf16 [M, K]
+  const void* w;       // bf16 [N, K]
+  const void* bias;    // bf16 [N] or null
+  const float* gate;   // [N] (residual epilogue)
+  void* out;           // bf16 [M, N], or the fp32 stream [M, N]
+  float* part;         // fp32 [splits][M][N] when splits > 1
+  int64_t M, K, N;
+  int32_t splits, epilogue;
+};
+
+// Contraction ranges of a projection: enough to give the chip ~256 workgroups.
+inline int linear_splits(int64_t M, int64_t N, int64_t K) {
+  return proj_splits((M + 255) / 256, N / 256, K);
+}
+
 // -------------------------------------------------------------- launchers --
 // Each returns hipSuccess or the launch error.  dtype: 0 = fp32, 1 = bf16,
 // 2 = bf16 activations over an e4m3 pool (write and cross-attention only).
@@ -284,5 +315,7 @@ hipError_t launch_self_attention(const SelfArgs& a, int dtype, int Dh, hipStream
 hipError_t launch_write(const WritePrepArgs& p, const WriteGemmArgs& g, int dtype, int Dh,
                         int64_t n_rows, hipStream_t s);
 hipError_t launch_context_rows(const CtxRowsArgs& a, hipStream_t s);
+hipError_t launch_ada_layer_norm(const AdaLnArgs& a, hipStream_t s);
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
 }  // namespace fm

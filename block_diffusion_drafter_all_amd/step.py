@@ -29,6 +29,7 @@ class StepBuffers:
     self_out: list
     out_slots: torch.Tensor | None
     rows_ws: torch.Tensor | None = None
+    dit: dict | None = None               # the DiT blocks' activations and workspace
 
 
 def allocate(w: Workload) -> StepBuffers:
@@ -48,7 +49,19 @@ def allocate(w: Workload) -> StepBuffers:
         rows_ws = torch.empty(B.fm_context_rows_workspace_size(up.hidden.shape[0], up.anchor_ids.shape[0],
                                                                up.hidden.shape[1], up.embedding.shape[1],
                                                                up.w_fc.shape[0]), dtype=torch.uint8, device=dev)
-    return StepBuffers(cross_ws, write_ws, cross_out, self_out, out_slots, rows_ws)
+    dit = None
+    if w.dit is not None:
+        rows, dim = w.dit.embedded.shape[0], w.H * w.Dh
+        inter = w.dit.layers[0]["fc1"].shape[0]
+        f32, bf = dict(dtype=torch.float32, device=dev), dict(dtype=torch.bfloat16, device=dev)
+        shapes = [(rows, 3 * dim, dim), (rows, dim, dim), (rows, inter, dim), (rows, dim, inter),
+                  (rows, dim, w.dit.w_xe.shape[1])]
+        dit = dict(h=torch.empty((rows, dim), **f32), xn=torch.empty((rows, dim), **bf),
+                   qkv=torch.empty((rows, 3 * dim), **bf), q=torch.empty((rows, dim), **bf),
+                   mlp=torch.empty((rows, inter), **bf), out=torch.empty((rows, dim), **bf),
+                   ws=torch.empty(max(B.fm_linear_workspace_size(*s) for s in shapes) + 256, dtype=torch.uint8,
+                                  device=dev))
+    return StepBuffers(cross_ws, write_ws, cross_out, self_out, out_slots, rows_ws, dit)
 
 
 def context_rows(w: Workload, buf: StepBuffers) -> None:
@@ -88,12 +101,55 @@ def layer(w: Workload, buf: StepBuffers, l: int) -> None:
 
 
 def run_step(w: Workload, buf: StepBuffers) -> None:
-    """Write (if the workload has one), plan, then every layer."""
+    """Write (if the workload has one), plan, then every layer: the two
+    attentions alone, or the whole DiT block around them."""
     if w.write is not None:
         write_context(w, buf)
     plan(w, buf)
+    if w.dit is not None:
+        dit_embed(w, buf)
+        for l in range(w.L):
+            dit_layer(w, buf, l)
+        dit_final(w, buf)
+        return
     for l in range(w.L):
         layer(w, buf, l)
+
+
+def dit_embed(w: Workload, buf: StepBuffers) -> None:
+    """The block's residual stream: x_embed of the jump's input rows."""
+    d = w.dit
+    B.fm_linear(d.embedded, d.w_xe, d.b_xe, B.FM_LINEAR_ASSIGN_F32, out=buf.dit["h"], ws=buf.dit["ws"])
+
+
+def dit_layer(w: Workload, buf: StepBuffers, l: int) -> None:
+    """One DiT block (sglang/model.py ``_denoise``): self-attention, then
+    cross-attention, then the MLP, each behind a modulated LayerNorm and a
+    gated residual into the fp32 stream ``h``."""
+    d, a, lw, m = w.dit, buf.dit, w.dit.layers[l], w.dit.mods[l]
+    h, xn, ws = a["h"], a["xn"], a["ws"]
+    rows = h.shape[0]
+    B.fm_ada_layer_norm(h, m["s_scale"], m["s_shift"], w.eps, out=xn)
+    B.fm_linear(xn, lw["qkv"], out=a["qkv"], ws=ws)
+    sa = buf.self_out[l]
+    B.fm_block_self_attention(a["qkv"].view(w.bs * w.n_cand, w.K, 3, w.H, w.Dh), w.self_q_norm_w[l],
+                              w.self_k_norm_w[l], w.block_ctx_lens, w.softmax_scale, w.theta, w.eps, out=sa)
+    B.fm_linear(sa.view(rows, -1), lw["o_self"], epilogue=B.FM_LINEAR_RESIDUAL, gate=m["s_gate"], out=h, ws=ws)
+    B.fm_ada_layer_norm(h, m["c_scale"], m["c_shift"], w.eps, out=xn)
+    B.fm_linear(xn, lw["q"], out=a["q"], ws=ws)
+    ca = buf.cross_out[l]
+    B.fm_paged_cross_attention(a["q"].view(rows, w.H, w.Dh), w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens,
+                               w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=ca,
+                               max_q=w.max_q, fp8_scales=w.fp8_scales(l))
+    B.fm_linear(ca.view(rows, -1), lw["o_cross"], epilogue=B.FM_LINEAR_RESIDUAL, gate=m["c_gate"], out=h, ws=ws)
+    B.fm_ada_layer_norm(h, m["m_scale"], m["m_shift"], w.eps, out=xn)
+    B.fm_linear(xn, lw["fc1"], lw["b1"], B.FM_LINEAR_GELU_BF16, out=a["mlp"], ws=ws)
+    B.fm_linear(a["mlp"], lw["fc2"], lw["b2"], B.FM_LINEAR_RESIDUAL, gate=m["m_gate"], out=h, ws=ws)
+
+
+def dit_final(w: Workload, buf: StepBuffers) -> None:
+    """The final modulated LayerNorm of the block's rows."""
+    B.fm_ada_layer_norm(buf.dit["h"], w.dit.final_scale, w.dit.final_shift, w.eps, out=buf.dit["out"])
 
 
 PREFILL_CHUNK = 2048  # rows per write call in a prefill (sglang/model.py ``_WRITE_CHUNK``)

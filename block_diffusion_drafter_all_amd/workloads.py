@@ -53,6 +53,20 @@ class UpstreamInputs:
 
 
 @dataclass
+class DitInputs:
+    """The rest of the DiT blocks (fm_ada_layer_norm, fm_linear): the jump's
+    input rows through x_embed, per layer the projections, the MLP and the
+    step's modulation vectors, and the final modulation."""
+    embedded: torch.Tensor        # (rows, d_target) bf16: the block's embedded state
+    w_xe: torch.Tensor            # (dim, d_target) bf16
+    b_xe: torch.Tensor            # (dim,) bf16
+    layers: list                  # per layer: qkv, o_self, q, o_cross, fc1, b1, fc2, b2 (bf16)
+    mods: list                    # per layer: s/c/m _scale (1 + scale), _shift, _gate (dim,) fp32
+    final_scale: torch.Tensor     # (dim,) fp32, 1 + scale
+    final_shift: torch.Tensor     # (dim,) fp32
+
+
+@dataclass
 class Workload:
     name: str
     workload_id: int
@@ -75,6 +89,7 @@ class Workload:
     write: WriteInputs | None = None
     n_cand: int = 1                    # candidate blocks per request (tree drafting)
     upstream: UpstreamInputs | None = None  # the write's rows made by fm_context_rows (write.x receives them)
+    dit: DitInputs | None = None       # the rest of the DiT blocks around the two attentions
     kv_scales: list | None = None      # e4m3 pool: (k_scale, v_scale) per layer (None = 1)
     q_scales: list | None = None       # e4m3 pool: fixed query scale per layer (None = per request and head)
     eps: float = EPS
@@ -162,7 +177,7 @@ def _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K, q_scale=1.0):
 
 
 def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_major", scale_down=None,
-                  q_scale=1.0, seed=None, n_cand=1, kv_fp8=False, upstream=False) -> Workload:
+                  q_scale=1.0, seed=None, n_cand=1, kv_fp8=False, upstream=False, dit=False) -> Workload:
     """The seeded inputs of one workload.
 
     1  tiny fp32 full step: 1 request, ctx 64, 1 layer, 4 x 64, page 16,
@@ -189,6 +204,12 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     ``hidden_norm``, and from the anchors' token embeddings (vocab 151936,
     N(0, 1)) through ``anchor_proj`` (N(0, 0.02^2), bias N(0, 0.1^2)) and
     ``anchor_norm``; ``write.x`` is the buffer that receives them.
+    ``dit``: the rest of every DiT block around the attentions (the sglang
+    model's ``_denoise``): the block's rows start as ``x_embed`` of N(0, 1)
+    embedded states (``d_target`` wide), each layer's projections are
+    N(0, 0.02^2) (MLP width 4 dim, biases N(0, 0.1^2)), its modulations
+    1 + 0.1 N(0, 1) (scales), 0.1 N(0, 1) (shifts) and 0.3 N(0, 1) (gates);
+    the attentions take the projections' outputs instead of ``q``/``qkv``.
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + workload_id if seed is None else seed)
@@ -293,6 +314,28 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
 
     if not upstream or workload_id != 5:
         upstream_inputs = None
+    dit_inputs = None
+    if dit:
+        dim, inter, d_target = H * Dh, 4 * H * Dh, sd.get("d_target", 4096)
+        rows = bs * n_cand * K
+        lw = []
+        for _ in range(L):
+            lw.append(dict(qkv=_randn((3 * dim, dim), gen, dtype, device, std=0.02),
+                           o_self=_randn((dim, dim), gen, dtype, device, std=0.02),
+                           q=_randn((dim, dim), gen, dtype, device, std=0.02),
+                           o_cross=_randn((dim, dim), gen, dtype, device, std=0.02),
+                           fc1=_randn((inter, dim), gen, dtype, device, std=0.02),
+                           b1=_randn((inter,), gen, dtype, device, std=0.1),
+                           fc2=_randn((dim, inter), gen, dtype, device, std=0.02),
+                           b2=_randn((dim,), gen, dtype, device, std=0.1)))
+        def mvec(kind):
+            z = torch.randn(dim, generator=gen, device=device)
+            return (1.0 + 0.1 * z) if kind == "scale" else (0.1 * z if kind == "shift" else 0.3 * z)
+        mods = [{f"{b}_{k}": mvec(k) for b in ("s", "c", "m") for k in ("scale", "shift", "gate")} for _ in range(L)]
+        dit_inputs = DitInputs(embedded=_randn((rows, d_target), gen, dtype, device),
+                               w_xe=_randn((dim, d_target), gen, dtype, device, std=0.02),
+                               b_xe=_randn((dim,), gen, dtype, device, std=0.1), layers=lw, mods=mods,
+                               final_scale=mvec("scale"), final_shift=mvec("shift"))
     q_norm_w = _norm_weights(L, Dh, gen, device, weights)
     self_q = _norm_weights(L, Dh, gen, device, weights)
     self_k = _norm_weights(L, Dh, gen, device, weights)
@@ -303,6 +346,6 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     return Workload(name=names[workload_id], workload_id=workload_id, bs=bs, K=K, L=L, H=H, Dh=Dh, page_size=ps,
                     dtype=dtype, ctx_lens=ctx.contiguous(), cu_seqlens_q=cu_q, page_table=pt, pools=pools, q=q,
                     qkv=qkv, q_norm_w=q_norm_w, self_q_norm_w=self_q, self_k_norm_w=self_k, write=write,
-                    n_cand=n_cand, upstream=upstream_inputs,
+                    n_cand=n_cand, upstream=upstream_inputs, dit=dit_inputs,
                     meta=dict(layout=layout, weights=weights, n_pages=n_pages, scale_down=sd, q_scale=q_scale,
                               kv_fp8=kv_fp8))

@@ -15,6 +15,9 @@
  *      per step) + fm_paged_cross_attention (once per layer)
  *   3. bidirectional self-attention within each draft block
  *                                             -> fm_block_self_attention
+ *   around them, the rest of each DiT block: time-modulated LayerNorms,
+ *   projections with gated residuals, the GELU MLP
+ *                                             -> fm_ada_layer_norm, fm_linear
  *
  * Conventions shared by every entry point
  *   - Pointers named as DEVICE pointers are device memory owned by the caller;
@@ -187,6 +190,47 @@ int fm_context_rows(const void* hidden, int64_t n_hidden, int32_t d_hidden, cons
                     int64_t vocab, int32_t d_target, const void* w_anchor_proj, const void* b_anchor_proj,
                     const float* anchor_norm_w, int32_t dim, const int32_t* commit_lens, int32_t window, int32_t bs,
                     float eps, void* rows, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------- the DiT layer -- */
+
+/*
+ * The time-modulated LayerNorm of a DiT block (sglang/model.py ``_denoise``;
+ * modeling_flashmap.py ``FlashMapAdaLayerNorm``):
+ *   out[r] = LayerNorm(h[r]) * scale + shift      (no affine LayerNorm, eps)
+ * h      DEVICE fp32 [rows, dim]: the residual stream.
+ * scale  DEVICE fp32 [dim]: the step's 1 + scale;  shift  DEVICE fp32 [dim].
+ * out    DEVICE bf16 [rows, dim]: the next projection's operand (rounded once).
+ * dim    a multiple of 1024 in [1024, 8192].  Pointers 16-byte aligned.
+ */
+int fm_ada_layer_norm(const float* h, int64_t rows, int32_t dim, const float* scale, const float* shift, float eps,
+                      void* out, hipStream_t stream);
+
+/* Epilogues of fm_linear (y = x W^T + bias, fp32 accumulate). */
+typedef enum fm_linear_epilogue {
+  FM_LINEAR_BF16 = 0,        /* out bf16 [M, N] = y                           (qkv, q projections) */
+  FM_LINEAR_GELU_BF16 = 1,   /* out bf16 [M, N] = gelu(y), exact erf GELU     (fc1) */
+  FM_LINEAR_RESIDUAL = 2,    /* out fp32 [M, N] += gate * y                   (o_proj, fc2: gated residual) */
+  FM_LINEAR_ASSIGN_F32 = 3   /* out fp32 [M, N] = y                           (x_embed) */
+} fm_linear_epilogue;
+
+/* Workspace bytes fm_linear needs for these sizes (0: none). */
+size_t fm_linear_workspace_size(int64_t M, int32_t N, int32_t K);
+
+/*
+ * A projection of the DiT block (sglang/model.py ``_denoise``: qkv, self and
+ * cross ``o_proj``, cross ``q_proj``, ``fc1`` + GELU, ``fc2``; ``x_embed``),
+ * y = x W^T + bias with the gated residual of ``hidden = hidden + gate * y``
+ * folded in.  The contraction may be split into ranges whose fp32 partials
+ * are summed in a fixed order (the result does not depend on scheduling).
+ * x     DEVICE bf16 [M, K] row-major;  w  DEVICE bf16 [N, K] (nn.Linear layout).
+ * bias  DEVICE bf16 [N] or NULL;  gate  DEVICE fp32 [N] (FM_LINEAR_RESIDUAL).
+ * K a multiple of 32; N a multiple of 1024.  Pointers 16-byte aligned.
+ * ws    DEVICE, fm_linear_workspace_size(M, N, K) bytes, 256-byte aligned (may
+ *       be NULL when that is 0).
+ */
+int fm_linear(const void* x, int64_t M, int32_t K, const void* w, int32_t N, const void* bias,
+              fm_linear_epilogue epilogue, const float* gate, void* out, void* ws, size_t ws_bytes,
+              hipStream_t stream);
 
 /* ------------------------------------------------------ cross-attention -- */
 

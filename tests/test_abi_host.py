@@ -223,3 +223,25 @@ def test_context_rows_empty_and_workspace(lib):
     big = lib.fm_context_rows_workspace_size(1088, 64, 20480, 4096, 4096)
     assert 0 < small < big and big >= 1088 * 4096 * 4
     assert lib.fm_context_rows_workspace_size(-1, 0, 64, 64, 1024) == 0
+
+
+def test_dit_entry_points_reject(lib):
+    f = lib.fm_ada_layer_norm
+    assert f(FAKE, 4, 1000, FAKE, FAKE, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED and "dim" in B.fm_last_error()
+    assert f(None, 4, 1024, FAKE, FAKE, 1e-6, FAKE, None) == B.FM_E_INVALID
+    assert f(FAKE, 4, 1024, FAKE, FAKE, -1.0, FAKE, None) == B.FM_E_INVALID and "eps" in B.fm_last_error()
+    assert f(None, 0, 1024, None, None, 1e-6, None, None) == B.FM_OK
+    g = lib.fm_linear
+    assert g(FAKE, 8, 512, FAKE, 2000, None, 0, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert "N 2000" in B.fm_last_error()
+    assert g(FAKE, 8, 500, FAKE, 2048, None, 0, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert g(FAKE, 8, 512, FAKE, 2048, None, B.FM_LINEAR_RESIDUAL, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert "gate" in B.fm_last_error()
+    assert g(FAKE, 8, 512, FAKE, 2048, None, 7, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert g(None, 8, 512, FAKE, 2048, None, 0, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_INVALID
+    assert g(None, 0, 512, None, 2048, None, 0, None, None, None, 0, None) == B.FM_OK
+    # a contraction split into ranges needs its partials' workspace
+    need = lib.fm_linear_workspace_size(256, 1024, 4096)
+    assert need >= 2 * 256 * 1024 * 4
+    assert g(FAKE, 256, 4096, FAKE, 1024, None, 0, None, FAKE, FAKE, need - 1, None) == B.FM_E_WORKSPACE
+    assert lib.fm_linear_workspace_size(1024, 16384, 4096) == 0   # 256 output tiles: no split

@@ -544,3 +544,136 @@ def test_prefill_in_chunks():
         sl = torch.as_tensor(slots, device=dev, dtype=torch.long)
         compare(pools[l].k[sl // ps, sl % ps], keys[:, l], f"prefill K L{l}")
         compare(pools[l].v[sl // ps, sl % ps], values[:, l], f"prefill V L{l}")
+
+
+
+# ------------------------------------------------------- the DiT blocks
+# sglang/model.py ``_denoise``: modulated LayerNorms, the projections with
+# gated residuals, the GELU MLP, around the two attentions.
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 512, 2048), (1024, 1024, 16384), (37, 4096, 1024)])
+def test_linear_epilogues(M, K, N):
+    log(f"fm_linear M={M} K={K} N={N} (ranges: {B.fm_linear_workspace_size(M, N, K) > 0})")
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(M + K + N)
+    x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=gen, device=dev) / math.sqrt(K)).to(torch.bfloat16)
+    b = (0.1 * torch.randn(N, generator=gen, device=dev)).to(torch.bfloat16)
+    gate = 0.3 * torch.randn(N, generator=gen, device=dev)
+    h0 = torch.randn((M, N), generator=gen, device=dev)
+    y = B.fm_linear(x, w)
+    yg = B.fm_linear(x, w, b, B.FM_LINEAR_GELU_BF16)
+    ya = B.fm_linear(x, w, b, B.FM_LINEAR_ASSIGN_F32)
+    h = h0.clone()
+    B.fm_linear(x, w, b, B.FM_LINEAR_RESIDUAL, gate=gate, out=h)
+    torch.cuda.synchronize()
+    ref = to_np(x) @ to_np(w).T
+    compare(y, ref, "linear bf16")
+    compare(yg, O.gelu(ref + to_np(b)), "linear + bias + gelu")
+    compare(ya, ref + to_np(b), "linear + bias (fp32)", max_abs=1e-3, mean_abs=1e-4)
+    compare(h, to_np(h0) + to_np(gate) * (ref + to_np(b)), "gated residual (fp32)", max_abs=1e-3, mean_abs=1e-4)
+
+
+def test_ada_layer_norm():
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    for dim in (1024, 4096):
+        h = 2 * torch.randn((77, dim), generator=gen, device=dev) + 5.0   # a large mean: the two-pass variance
+        sc = 1 + 0.1 * torch.randn(dim, generator=gen, device=dev)
+        sh = 0.1 * torch.randn(dim, generator=gen, device=dev)
+        out = B.fm_ada_layer_norm(h, sc, sh, 1e-6)
+        torch.cuda.synchronize()
+        compare(out, O.ada_layer_norm(to_np(h), to_np(sc), to_np(sh), 1e-6), f"ada layer norm dim {dim}")
+
+
+def _oracle_dit_layer(w, buf, l, h_in, reqs):
+    """Oracle DiT block on the rows of requests ``reqs`` from the GPU's own
+    residual stream, with the attentions reading the GPU-written pools."""
+    K, H, Dh, nc = w.K, w.H, w.Dh, w.n_cand
+    rows = np.concatenate([np.arange(b * nc * K, (b + 1) * nc * K) for b in reqs])
+    blocks = [b * nc + i for b in reqs for i in range(nc)]
+    pk, pv, pt_rows = compact_context(w, l, reqs)
+    ctx = w.ctx_lens.cpu().numpy()
+    bctx = w.block_ctx_lens.cpu().numpy()[blocks]
+    width = max([len(r) for r in pt_rows] + [1])
+    pt = np.zeros((len(reqs), width), dtype=np.int64)
+    for i, r in enumerate(pt_rows):
+        pt[i, :len(r)] = r
+    cu = np.arange(len(reqs) + 1) * nc * K
+    fp8 = w.fp8_scales(l)
+    sc = {} if fp8 is None else dict(q_scale=fp8[0] or None, k_scale=fp8[1], v_scale=fp8[2])
+
+    def self_attention(qkv):
+        o = O.block_self_attention(qkv.reshape(len(blocks), K, 3, H, Dh), to_np(w.self_q_norm_w[l]),
+                                   to_np(w.self_k_norm_w[l]), bctx, w.softmax_scale, w.theta, w.eps)
+        return o.reshape(len(rows), H * Dh)
+
+    def cross_attention(q):
+        o = O.paged_cross_attention(q.reshape(len(rows), H, Dh), to_np(w.q_norm_w[l]), pk, pv, pt, ctx[reqs], cu,
+                                    w.page_size, w.softmax_scale, w.theta, w.eps,
+                                    kv_e4m3=w.pool_dtype == torch.float8_e4m3fn, **sc)
+        return o.reshape(len(rows), H * Dh)
+
+    lw = {k: to_np(v) for k, v in w.dit.layers[l].items()}
+    mod = {k: to_np(v) for k, v in w.dit.mods[l].items()}
+    return rows, O.dit_layer(h_in[rows], mod, lw, self_attention, cross_attention, w.eps)
+
+
+def _compare_stream(gpu, ref, what):
+    """The fp32 residual stream against the oracle.  Its error is the bf16
+    rounding of the operands fed to each projection, relative to the values
+    carried, so the bar scales with the stream's RMS (at least 1)."""
+    s = max(1.0, float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2))))
+    log(f"  {what}: stream RMS {s:.2f}")
+    compare(gpu, ref, what, max_abs=2e-2 * s, mean_abs=2e-3 * s)
+
+
+def _run_dit_stagewise(w, buf):
+    """The step with the residual stream captured around every block."""
+    if w.write is not None:
+        S.write_context(w, buf)
+    S.plan(w, buf)
+    S.dit_embed(w, buf)
+    hs = [buf.dit["h"].clone()]
+    for l in range(w.L):
+        S.dit_layer(w, buf, l)
+        hs.append(buf.dit["h"].clone())
+    S.dit_final(w, buf)
+    torch.cuda.synchronize()
+    return [to_np(h) for h in hs]
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_dit_step_small(kv_fp8):
+    log(f"DiT blocks around the attentions, small step (e4m3 pool: {kv_fp8})")
+    w = make_workload(5, weights="random", dit=True, kv_fp8=kv_fp8,
+                      scale_down=dict(bs=4, ctx=(20, 300), L=2, H=8, d_in=1024, d_target=512))
+    buf = S.allocate(w)
+    hs = _run_dit_stagewise(w, buf)
+    d = w.dit
+    ref0 = to_np(d.embedded) @ to_np(d.w_xe).T + to_np(d.b_xe)
+    compare(hs[0], ref0, "x_embed (fp32)", max_abs=1e-3, mean_abs=1e-4)
+    reqs = list(range(w.bs))
+    for l in range(w.L):
+        rows, ref = _oracle_dit_layer(w, buf, l, hs[l], reqs)
+        _compare_stream(hs[l + 1][rows], ref, f"DiT block {l}: residual stream")
+    compare(buf.dit["out"], O.ada_layer_norm(hs[-1], to_np(d.final_scale), to_np(d.final_shift), w.eps),
+            "final modulated LayerNorm")
+    assert ws_error_word(buf.cross_ws) == 0
+
+
+def test_dit_step_full_size_sampled():
+    log("DiT blocks at full size (64 requests, 5 layers, dim 4096, MLP 16384): block 0 on sampled requests")
+    w = make_workload(5, dit=True)
+    buf = S.allocate(w)
+    hs = _run_dit_stagewise(w, buf)
+    reqs = _sample(w, 2, 8)
+    log(f"  sampled requests {reqs}")
+    rows, ref = _oracle_dit_layer(w, buf, 0, hs[0], reqs)
+    _compare_stream(hs[1][rows], ref, "DiT block 0: residual stream (sampled)")
+    d = w.dit
+    compare(buf.dit["out"][torch.as_tensor(rows, device=buf.dit["out"].device)],
+            O.ada_layer_norm(hs[-1][rows], to_np(d.final_scale), to_np(d.final_shift), w.eps), "final LayerNorm")
