@@ -64,6 +64,9 @@ def parse():
                     help="candidate blocks per request (tree drafting): 16 query rows each, one context read")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="e4m3 KV pool (written at scale 1; queries quantized per request and head)")
+    ap.add_argument("--dit", action="store_true",
+                    help="the whole one-jump draft step: x_embed, every DiT block (modulated LayerNorms, "
+                         "projections, gated residuals, GELU MLP) around the two attentions, the final norm")
     ap.add_argument("--upstream", action="store_true",
                     help="config 5: make the write's rows on the device from the target hidden states (fc + "
                          "hidden_norm) and the anchor tokens (embedding + anchor_proj + anchor_norm) in the step")
@@ -106,7 +109,8 @@ def _kib_per_dispatch(rows, match):
 def workload_key(args) -> str:
     """Names the workload a traffic record was measured on."""
     return (f"config={args.config},layout={args.layout},candidates={args.candidates},"
-            f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}" + (",upstream" if args.upstream else ""))
+            f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}" + (",upstream" if args.upstream else "")
+            + (",dit" if args.dit else ""))
 
 
 def _traffic_records() -> dict:
@@ -231,6 +235,18 @@ def context_rows_flops(w) -> int:
     return 2 * live * up.hidden.shape[1] * dim + 2 * up.anchor_ids.shape[0] * up.embedding.shape[1] * dim
 
 
+def dit_linear_flops(w) -> int:
+    """MFMA flops of one step's DiT projections (x_embed and, per layer,
+    qkv, q, the two o_proj, fc1, fc2)."""
+    d = w.dit
+    if d is None:
+        return 0
+    rows, dim = d.embedded.shape[0], w.H * w.Dh
+    inter = d.layers[0]["fc1"].shape[0]
+    per_layer = 2 * rows * dim * (3 * dim + 3 * dim + 2 * inter)
+    return w.L * per_layer + 2 * rows * d.embedded.shape[1] * dim
+
+
 def describe(w) -> dict:
     ctx = w.ctx_lens.cpu().tolist()
     d = {
@@ -248,6 +264,9 @@ def describe(w) -> dict:
     if w.write is not None:
         d["write_rows"] = int(w.write.x.shape[0])
         d["write_d_in"] = int(w.write.x.shape[1])
+    if w.dit is not None:
+        d["dit"] = {"dim": w.H * w.Dh, "mlp": int(w.dit.layers[0]["fc1"].shape[0]),
+                    "x_embed_in": int(w.dit.embedded.shape[1])}
     if w.upstream is not None:
         d["upstream"] = {"hidden_width": int(w.upstream.hidden.shape[1]), "vocab": int(w.upstream.embedding.shape[0]),
                          "dim": int(w.upstream.w_fc.shape[0])}
@@ -347,8 +366,10 @@ def main():
         return
     if args.upstream and args.config != 5:
         raise SystemExit("--upstream applies to config 5 (the full draft step)")
+    if args.dit and args.config != 5:
+        raise SystemExit("--dit applies to config 5 (the full draft step)")
     w = make_workload(args.config, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8,
-                      upstream=args.upstream)
+                      upstream=args.upstream, dit=args.dit)
     buf = S.allocate(w)
     torch.cuda.synchronize()
 
@@ -366,6 +387,21 @@ def main():
             if events is not None:
                 events["write"][1].record()
         S.plan(w, buf)
+        if w.dit is not None:
+            def timed(kind, call):
+                if events is None:
+                    call()
+                    return
+                e0, e1 = E()
+                e0.record()
+                call()
+                e1.record()
+                events.setdefault(kind, []).append((e0, e1))
+            timed("linear", lambda: S.dit_embed(w, buf))
+            for l in range(w.L):
+                S.dit_layer(w, buf, l, timed)
+            timed("norm", lambda: S.dit_final(w, buf))
+            return
         for l in range(w.L):
             if events is not None:
                 events["self"][l][0].record()
@@ -388,7 +424,8 @@ def main():
     # Timed region: exactly --steps steps.  Events bracket each cross-attention
     # call on the stream it is launched on (torch's current stream).
     E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
-    per_step = [dict(rows=E(), write=E(), self=[E() for _ in range(w.L)], cross=[E() for _ in range(w.L)])
+    n_pre = 0 if w.dit is not None else w.L   # the DiT step appends its own events per call
+    per_step = [dict(rows=E(), write=E(), self=[E() for _ in range(n_pre)], cross=[E() for _ in range(n_pre)])
                 for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -442,6 +479,13 @@ def main():
         out["write"] = {"avg_ms": avg_w, "flops": wf, "tflops": wf / (avg_w * 1e-3) / 1e12,
                         "mfma_frac_of_bf16_peak": wf / (avg_w * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                         "algorithmic_bytes": wb}
+    if w.dit is not None:
+        lin_ms = sum(ev[0].elapsed_time(ev[1]) for st in per_step for ev in st.get("linear", [])) / args.steps
+        norm_ms = sum(ev[0].elapsed_time(ev[1]) for st in per_step for ev in st.get("norm", [])) / args.steps
+        lf = dit_linear_flops(w)
+        out["dit"] = {"linear_ms_per_step": lin_ms, "norm_ms_per_step": norm_ms, "linear_flops_per_step": lf,
+                      "linear_tflops": lf / (lin_ms * 1e-3) / 1e12,
+                      "mfma_frac_of_bf16_peak": lf / (lin_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
     if rows_ms:
         rf = context_rows_flops(w)
         avg_r = sum(rows_ms) / len(rows_ms)

@@ -122,29 +122,38 @@ def dit_embed(w: Workload, buf: StepBuffers) -> None:
     B.fm_linear(d.embedded, d.w_xe, d.b_xe, B.FM_LINEAR_ASSIGN_F32, out=buf.dit["h"], ws=buf.dit["ws"])
 
 
-def dit_layer(w: Workload, buf: StepBuffers, l: int) -> None:
+def _untimed(kind, call):
+    call()
+
+
+def dit_layer(w: Workload, buf: StepBuffers, l: int, timed=_untimed) -> None:
     """One DiT block (sglang/model.py ``_denoise``): self-attention, then
     cross-attention, then the MLP, each behind a modulated LayerNorm and a
-    gated residual into the fp32 stream ``h``."""
-    d, a, lw, m = w.dit, buf.dit, w.dit.layers[l], w.dit.mods[l]
+    gated residual into the fp32 stream ``h``.  ``timed(kind, call)`` runs
+    each library call (kind: "norm", "linear", "self", "cross"), so a caller
+    can bracket it with events."""
+    a, lw, m = buf.dit, w.dit.layers[l], w.dit.mods[l]
     h, xn, ws = a["h"], a["xn"], a["ws"]
     rows = h.shape[0]
-    B.fm_ada_layer_norm(h, m["s_scale"], m["s_shift"], w.eps, out=xn)
-    B.fm_linear(xn, lw["qkv"], out=a["qkv"], ws=ws)
-    sa = buf.self_out[l]
-    B.fm_block_self_attention(a["qkv"].view(w.bs * w.n_cand, w.K, 3, w.H, w.Dh), w.self_q_norm_w[l],
-                              w.self_k_norm_w[l], w.block_ctx_lens, w.softmax_scale, w.theta, w.eps, out=sa)
-    B.fm_linear(sa.view(rows, -1), lw["o_self"], epilogue=B.FM_LINEAR_RESIDUAL, gate=m["s_gate"], out=h, ws=ws)
-    B.fm_ada_layer_norm(h, m["c_scale"], m["c_shift"], w.eps, out=xn)
-    B.fm_linear(xn, lw["q"], out=a["q"], ws=ws)
-    ca = buf.cross_out[l]
-    B.fm_paged_cross_attention(a["q"].view(rows, w.H, w.Dh), w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens,
-                               w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=ca,
-                               max_q=w.max_q, fp8_scales=w.fp8_scales(l))
-    B.fm_linear(ca.view(rows, -1), lw["o_cross"], epilogue=B.FM_LINEAR_RESIDUAL, gate=m["c_gate"], out=h, ws=ws)
-    B.fm_ada_layer_norm(h, m["m_scale"], m["m_shift"], w.eps, out=xn)
-    B.fm_linear(xn, lw["fc1"], lw["b1"], B.FM_LINEAR_GELU_BF16, out=a["mlp"], ws=ws)
-    B.fm_linear(a["mlp"], lw["fc2"], lw["b2"], B.FM_LINEAR_RESIDUAL, gate=m["m_gate"], out=h, ws=ws)
+    sa, ca = buf.self_out[l], buf.cross_out[l]
+    timed("norm", lambda: B.fm_ada_layer_norm(h, m["s_scale"], m["s_shift"], w.eps, out=xn))
+    timed("linear", lambda: B.fm_linear(xn, lw["qkv"], out=a["qkv"], ws=ws))
+    timed("self", lambda: B.fm_block_self_attention(
+        a["qkv"].view(w.bs * w.n_cand, w.K, 3, w.H, w.Dh), w.self_q_norm_w[l], w.self_k_norm_w[l], w.block_ctx_lens,
+        w.softmax_scale, w.theta, w.eps, out=sa))
+    timed("linear", lambda: B.fm_linear(sa.view(rows, -1), lw["o_self"], epilogue=B.FM_LINEAR_RESIDUAL,
+                                        gate=m["s_gate"], out=h, ws=ws))
+    timed("norm", lambda: B.fm_ada_layer_norm(h, m["c_scale"], m["c_shift"], w.eps, out=xn))
+    timed("linear", lambda: B.fm_linear(xn, lw["q"], out=a["q"], ws=ws))
+    timed("cross", lambda: B.fm_paged_cross_attention(
+        a["q"].view(rows, w.H, w.Dh), w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens, w.cu_seqlens_q,
+        w.softmax_scale, w.theta, w.eps, buf.cross_ws, out=ca, max_q=w.max_q, fp8_scales=w.fp8_scales(l)))
+    timed("linear", lambda: B.fm_linear(ca.view(rows, -1), lw["o_cross"], epilogue=B.FM_LINEAR_RESIDUAL,
+                                        gate=m["c_gate"], out=h, ws=ws))
+    timed("norm", lambda: B.fm_ada_layer_norm(h, m["m_scale"], m["m_shift"], w.eps, out=xn))
+    timed("linear", lambda: B.fm_linear(xn, lw["fc1"], lw["b1"], B.FM_LINEAR_GELU_BF16, out=a["mlp"], ws=ws))
+    timed("linear", lambda: B.fm_linear(a["mlp"], lw["fc2"], lw["b2"], B.FM_LINEAR_RESIDUAL, gate=m["m_gate"],
+                                        out=h, ws=ws))
 
 
 def dit_final(w: Workload, buf: StepBuffers) -> None:

@@ -40,7 +40,8 @@ def test_traffic_record_is_per_workload(tmp_path, monkeypatch):
     import types
 
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "t.json"))
-    args = types.SimpleNamespace(config=5, layout="head_major", candidates=1, kv_fp8=False, upstream=False)
+    args = types.SimpleNamespace(config=5, layout="head_major", candidates=1, kv_fp8=False, upstream=False,
+                                 dit=False)
     key = bench.workload_key(args)
     rec = {"workload": key, "sources_sha256": bench.kernel_sources_hash(), "traffic_bytes_per_launch": 123.0}
     json.dump({"records": {key: rec}}, open(tmp_path / "t.json", "w"))
