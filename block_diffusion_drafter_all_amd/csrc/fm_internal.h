@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -227,9 +228,11 @@ struct CtxRowsLayout {
   int s_fc, s_anchor;  // contraction splits of the two projections
 };
 
-// Contraction splits of a projection with m_tiles x n_tiles output tiles and
-// a k-wide contraction: enough (1..8, a power of two dividing k / 32) to give
-// the chip about 256 workgroups.
+// Contraction splits of the two projections that share one launch of the
+// context rows (m_tiles x n_tiles output tiles of 256 x 256, a k-wide
+// contraction): enough (1..8, a power of two dividing k / 32, at least four
+// 32-wide slices per range) to give the chip about 256 workgroups, so the two
+// together fill it.
 inline int proj_splits(int64_t m_tiles, int64_t n_tiles, int64_t k) {
   const int64_t tiles = m_tiles * n_tiles > 0 ? m_tiles * n_tiles : 1;
   int s = 1;
@@ -301,8 +304,28 @@ struct LinearArgs {
 };
 
 // Contraction ranges of a projection: enough to give the chip ~256 workgroups.
+// Contraction splits of one projection launch (M x N outputs in 256 x 256
+// tiles, a K-wide contraction): the s in {1, 2, 4, 8} (dividing K / 32, at
+// least four 32-wide slices per range) with the least modelled time, the
+// smallest on a tie.  One workgroup fills a CU, so the tiles run in rounds of
+// kGemmCUs; a range of K / 32 / s slices takes about a microsecond per slice
+// when the chip is full; with s > 1 the partials (s fp32 outputs) are written,
+// then read back with the output by a row kernel at about 5 TB/s.  A split that
+// only adds a round (192 tiles in two ranges: 384 workgroups, two rounds of half
+// the work) gains nothing and pays the partials, so it is not taken.
+constexpr int64_t kGemmCUs = 256;
 inline int linear_splits(int64_t M, int64_t N, int64_t K) {
-  return proj_splits((M + 255) / 256, N / 256, K);
+  const int64_t tiles = std::max<int64_t>(((M + 255) / 256) * (N / 256), 1);
+  const double out_bytes = (double)tiles * 256.0 * 256.0 * 4.0;
+  int best = 1;
+  double best_us = 0.0;
+  for (int s = 1; s <= 8; s *= 2) {
+    if ((K / 32) % s != 0 || (s > 1 && K / 32 / s < 4)) break;
+    const int64_t rounds = (tiles * s + kGemmCUs - 1) / kGemmCUs;
+    const double us = (double)rounds * (double)(K / 32 / s) + (s > 1 ? (s + 1) * out_bytes / 5.0e6 : 0.0);
+    if (s == 1 || us < best_us) best = s, best_us = us;
+  }
+  return best;
 }
 
 // -------------------------------------------------------------- launchers --
