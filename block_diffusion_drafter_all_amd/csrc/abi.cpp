@@ -32,6 +32,8 @@ int ok() {
 
 int from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
+  if (e == hipErrorInvalidConfiguration)  // a launcher's own grid check, before anything was enqueued
+    return fail(FM_E_UNSUPPORTED, "%s: the sizes need a launch grid of 2^32 or more work-items", what);
   return fail(FM_E_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
 }
 
@@ -291,7 +293,9 @@ int fm_ada_layer_norm(const float* h, int64_t rows, int32_t dim, const float* sc
 size_t fm_linear_workspace_size(int64_t M, int32_t N, int32_t K) {
   if (M < 1 || N < 1 || K < 1) return 0;
   const int splits = fm::linear_splits(M, N, K);
-  return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * 4 : 0;
+  if (splits == 1) return 0;
+  if ((double)splits * (double)M * (double)N * 4.0 > 0x1p62) return SIZE_MAX;  // no such buffer exists
+  return (size_t)splits * (size_t)M * (size_t)N * 4;
 }
 
 int fm_linear(const void* x, int64_t M, int32_t K, const void* w, int32_t N, const void* bias,

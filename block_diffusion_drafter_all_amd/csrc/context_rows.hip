@@ -202,23 +202,27 @@ __global__ __launch_bounds__(256) void rows_norm_kernel(CtxRowsArgs a) {
 }  // namespace
 
 hipError_t launch_context_rows(const CtxRowsArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(ctx_prep_kernel, dim3(1), dim3(1024), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int n_tiles = a.dim / kGN;
-  auto grid_of = [&](int64_t rows, int splits) {
+  auto grid_of = [&](int64_t rows, int splits, int64_t* wgs) {
     ProjGrid g{};
+    *wgs = 0;
     if (rows == 0) return g;
     g.m_tiles = (int)((rows + kGM - 1) / kGM);
     g.splits = splits;
-    g.wgs = (int)((((int64_t)n_tiles * splits + 7) / 8) * 8 * g.m_tiles);
+    *wgs = (((int64_t)n_tiles * splits + 7) / 8) * 8 * g.m_tiles;
+    g.wgs = (int)std::min<int64_t>(*wgs, INT32_MAX);
     return g;
   };
-  const ProjGrid hid = grid_of(a.n_hidden, a.lay.s_fc), anc = grid_of(a.n_anchor, a.lay.s_anchor);
-  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)(hid.wgs + anc.wgs)), dim3(64 * kGemmWaves), 0, s, a, n_tiles,
+  int64_t hid_wgs, anc_wgs;
+  const ProjGrid hid = grid_of(a.n_hidden, a.lay.s_fc, &hid_wgs), anc = grid_of(a.n_anchor, a.lay.s_anchor, &anc_wgs);
+  const int64_t rows = a.n_hidden + a.n_anchor;
+  if (!grid_fits(hid_wgs + anc_wgs, 64 * kGemmWaves) || !grid_fits(rows, 256)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(ctx_prep_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)(hid_wgs + anc_wgs)), dim3(64 * kGemmWaves), 0, s, a, n_tiles,
                      hid, anc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t rows = a.n_hidden + a.n_anchor;
   hipLaunchKernelGGL(rows_norm_kernel, dim3((unsigned)rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }

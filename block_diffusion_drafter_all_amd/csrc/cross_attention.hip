@@ -767,6 +767,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
 template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF, int OCC>
 hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.bs * a.H;
+  if (!grid_fits((pairs + 3) / 4, 256) || !grid_fits((a.lay.n_waves + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((q_prologue_kernel<T, PT, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinearArgs a, int sp
 }  // namespace
 
 hipError_t launch_ada_layer_norm(const AdaLnArgs& a, hipStream_t s) {
+  if (!grid_fits(a.rows, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(ada_ln_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -179,6 +180,8 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   const int n_tiles = (int)(a.N / kGN), m_tiles = (int)((a.M + kGM - 1) / kGM);
   const int splits = a.splits;
   const int64_t groups = ((int64_t)n_tiles * splits + 7) / 8;
+  if (!grid_fits(groups * 8 * m_tiles, 64 * kGemmWaves) || (splits > 1 && !grid_fits(a.M, 256)))
+    return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(linear_gemm_kernel, dim3((unsigned)(groups * 8 * m_tiles)), dim3(64 * kGemmWaves), 0, s, a,
                      n_tiles, m_tiles, splits);
   hipError_t e = hipGetLastError();

@@ -39,6 +39,13 @@ constexpr int32_t kCtxMagic = 0x464d4358;    // "FMCX"
 constexpr int cross_occupancy(int dtype) { return dtype == 2 ? FM_CROSS_OCC_FP8 : (dtype == 1 ? FM_CROSS_OCC_BF16 : 1); }
 constexpr int kMaxPlanWaves = 4096;  // most attention waves one plan describes
 
+// One dispatch holds fewer than 2^32 work-items per grid dimension.  The
+// launchers check every grid of a call before its first launch and return
+// hipErrorInvalidConfiguration (nothing enqueued) when one does not fit.
+inline bool grid_fits(int64_t workgroups, int threads) {
+  return workgroups >= 0 && workgroups <= (((int64_t)1 << 32) - 1) / threads;
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------ pool descriptor

@@ -104,6 +104,7 @@ template <class T, int D>
 hipError_t launch_self_typed(const SelfArgs& a, hipStream_t s) {
   const int64_t units = (int64_t)a.n_blocks * a.H;
   if (units <= 0) return hipSuccess;
+  if (!grid_fits((units + 3) / 4, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((self_attn_kernel<T, D>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -263,19 +263,21 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
 
 template <class T, class PT, int D>
 hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, int64_t n_rows, hipStream_t s) {
+  const int n_tiles = g.L * 2 * g.H;
+  const bool tiled = sizeof(typename T::storage) == 2 && D == kDhGemm;
+  const int64_t m_tiles = tiled ? (n_rows + kGM - 1) / kGM : (n_rows + 63) / 64;
+  const int64_t groups = (n_tiles / 2 + 7) / 8;  // 256-row tiles of W: two heads each
+  if (tiled ? !grid_fits(groups * 8 * m_tiles, 64 * kGemmWaves) : (!grid_fits(n_tiles, 256) || m_tiles > INT32_MAX))
+    return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(write_prep_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_tiles = g.L * 2 * g.H;
-  if (sizeof(typename T::storage) == 2 && D == kDhGemm) {
-    const int m_tiles = (int)((n_rows + kGM - 1) / kGM);
-    const int64_t groups = (n_tiles / 2 + 7) / 8;  // 256-row tiles of W: two heads each
+  if (tiled) {
     hipLaunchKernelGGL(write_gemm_bf16_kernel<PT>, dim3((unsigned)(groups * 8 * m_tiles)), dim3(64 * kGemmWaves), 0,
-                       s, g, n_tiles / 2, m_tiles);
+                       s, g, n_tiles / 2, (int)m_tiles);
     return hipGetLastError();
   }
-  const unsigned m_tiles = (unsigned)((n_rows + 63) / 64);
-  hipLaunchKernelGGL((write_gemm_kernel<T, PT, D>), dim3((unsigned)n_tiles, m_tiles), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((write_gemm_kernel<T, PT, D>), dim3((unsigned)n_tiles, (unsigned)m_tiles), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

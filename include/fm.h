@@ -54,7 +54,8 @@ extern "C" {
 typedef enum fm_status {
   FM_OK = 0,
   FM_E_INVALID = -1,     /* a null required pointer, a negative size, inconsistent sizes */
-  FM_E_UNSUPPORTED = -2, /* a shape or type this build does not implement */
+  FM_E_UNSUPPORTED = -2, /* a shape or type this build does not implement, or sizes whose launch grid
+                            would reach 2^32 work-items */
   FM_E_WORKSPACE = -3,   /* workspace null, misaligned or smaller than required */
   FM_E_HIP = -4          /* a HIP launch failed */
 } fm_status;
@@ -213,7 +214,8 @@ typedef enum fm_linear_epilogue {
   FM_LINEAR_ASSIGN_F32 = 3   /* out fp32 [M, N] = y                           (x_embed) */
 } fm_linear_epilogue;
 
-/* Workspace bytes fm_linear needs for these sizes (0: none). */
+/* Workspace bytes fm_linear needs for these sizes (0: none; SIZE_MAX: sizes
+ * no buffer can serve, which fm_linear rejects). */
 size_t fm_linear_workspace_size(int64_t M, int32_t N, int32_t K);
 
 /*

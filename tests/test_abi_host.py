@@ -175,6 +175,24 @@ def test_self_attention_rejects(lib):
     assert "FM_BF16" in B.fm_last_error()
 
 
+def test_launch_grid_limit(lib):
+    """Sizes whose launch grid would reach 2^32 work-items are refused before
+    anything is enqueued (the check runs ahead of every launch of the call)."""
+    # 2^25 rows x 256 threads
+    assert lib.fm_ada_layer_norm(FAKE, 1 << 25, 1024, FAKE, FAKE, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
+    assert "2^32" in B.fm_last_error()
+    # 2^24 rows x 2^20 outputs: 2^16 x 2^12 tiles of 512 threads
+    assert lib.fm_linear(FAKE, 1 << 24, 512, FAKE, 1 << 20, None, 0, None, FAKE, FAKE, 1 << 30, None) \
+        == B.FM_E_UNSUPPORTED
+    assert "2^32" in B.fm_last_error()
+    # 2^25 blocks x 4 heads, one wave each
+    assert lib.fm_block_self_attention(FAKE, B.FM_BF16, 1 << 25, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE,
+                                       None) == B.FM_E_UNSUPPORTED
+    assert "2^32" in B.fm_last_error()
+    # the largest sizes the checks still pass are well inside the limit
+    assert lib.fm_linear_workspace_size(1 << 24, 1 << 20, 512) == 0
+
+
 def test_binding_dtype_pairs():
     bf, f32 = torch.zeros(1, dtype=torch.bfloat16), torch.zeros(1)
     assert B._dtype_code(bf) == B.FM_BF16 and B._dtype_code(f32) == B.FM_F32
