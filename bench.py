@@ -352,7 +352,7 @@ def main():
         write_traffic(args.write_traffic, args.traffic_command, workload_key(args))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1",
                           "requested_gpus": args.gpus}))
         sys.exit(2)
     import torch

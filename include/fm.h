@@ -54,7 +54,7 @@ extern "C" {
 typedef enum fm_status {
   FM_OK = 0,
   FM_E_INVALID = -1,     /* a null required pointer, a negative size, inconsistent sizes */
-  FM_E_UNSUPPORTED = -2, /* a shape or type this build does not implement, or sizes whose launch grid
+  FM_E_UNSUPPORTED = -2, /* a shape or type the library does not implement, or sizes whose launch grid
                             would reach 2^32 work-items */
   FM_E_WORKSPACE = -3,   /* workspace null, misaligned or smaller than required */
   FM_E_HIP = -4          /* a HIP launch failed */
