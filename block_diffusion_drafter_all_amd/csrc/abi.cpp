@@ -229,8 +229,8 @@ int fm_context_rows(const void* hidden, int64_t n_hidden, int32_t d_hidden, cons
   if (!aligned16(rows)) return fail(FM_E_INVALID, "%s: rows must be 16-byte aligned", fn);
   if (n_hidden > 0) {
     if (!hidden || !w_fc || !hidden_norm_w) return fail(FM_E_INVALID, "%s: a hidden-row pointer is null", fn);
-    if (d_hidden < 32 || d_hidden % 32)
-      return fail(FM_E_UNSUPPORTED, "%s: d_hidden %d must be a positive multiple of 32", fn, d_hidden);
+    if (d_hidden < 64 || d_hidden % 64)
+      return fail(FM_E_UNSUPPORTED, "%s: d_hidden %d must be a positive multiple of 64", fn, d_hidden);
     if (!aligned16(hidden) || !aligned16(w_fc) || !aligned16(hidden_norm_w))
       return fail(FM_E_INVALID, "%s: hidden, w_fc and hidden_norm_w must be 16-byte aligned", fn);
     if (commit_lens != nullptr && (window < 1 || bs < 1 || (int64_t)bs * window > n_hidden))
@@ -239,8 +239,8 @@ int fm_context_rows(const void* hidden, int64_t n_hidden, int32_t d_hidden, cons
   if (n_anchor > 0) {
     if (!anchor_ids || !embedding || !w_anchor_proj || !b_anchor_proj || !anchor_norm_w)
       return fail(FM_E_INVALID, "%s: an anchor-row pointer is null", fn);
-    if (d_target < 32 || d_target % 32)
-      return fail(FM_E_UNSUPPORTED, "%s: d_target %d must be a positive multiple of 32", fn, d_target);
+    if (d_target < 64 || d_target % 64)
+      return fail(FM_E_UNSUPPORTED, "%s: d_target %d must be a positive multiple of 64", fn, d_target);
     if (vocab < 1) return fail(FM_E_INVALID, "%s: vocab %lld < 1", fn, (long long)vocab);
     if (!aligned16(embedding) || !aligned16(w_anchor_proj) || !aligned16(b_anchor_proj) || !aligned16(anchor_norm_w))
       return fail(FM_E_INVALID, "%s: embedding, w_anchor_proj, b_anchor_proj, anchor_norm_w must be 16-byte aligned",
@@ -307,7 +307,7 @@ int fm_linear(const void* x, int64_t M, int32_t K, const void* w, int32_t N, con
   if (!x || !w || !out) return fail(FM_E_INVALID, "%s: x, w and out are required", fn);
   if ((int)epilogue < 0 || (int)epilogue > 3) return fail(FM_E_UNSUPPORTED, "%s: epilogue %d", fn, (int)epilogue);
   if (epilogue == FM_LINEAR_RESIDUAL && !gate) return fail(FM_E_INVALID, "%s: the residual epilogue needs gate", fn);
-  if (K < 32 || K % 32) return fail(FM_E_UNSUPPORTED, "%s: K %d must be a positive multiple of 32", fn, K);
+  if (K < 64 || K % 64) return fail(FM_E_UNSUPPORTED, "%s: K %d must be a positive multiple of 64", fn, K);
   if (N < 1024 || N % 1024) return fail(FM_E_UNSUPPORTED, "%s: N %d must be a positive multiple of 1024", fn, N);
   if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (bias && !aligned16(bias)) || (gate && !aligned16(gate)))
     return fail(FM_E_INVALID, "%s: pointers must be 16-byte aligned", fn);

@@ -237,13 +237,13 @@ struct CtxRowsLayout {
 
 // Contraction splits of the two projections that share one launch of the
 // context rows (m_tiles x n_tiles output tiles of 256 x 256, a k-wide
-// contraction): enough (1..8, a power of two dividing k / 32, at least four
-// 32-wide slices per range) to give the chip about 256 workgroups, so the two
+// contraction): enough (1..8, a power of two dividing k / 64, at least two
+// 64-wide stages per range) to give the chip about 256 workgroups, so the two
 // together fill it.
 inline int proj_splits(int64_t m_tiles, int64_t n_tiles, int64_t k) {
   const int64_t tiles = m_tiles * n_tiles > 0 ? m_tiles * n_tiles : 1;
   int s = 1;
-  while (s < 8 && tiles * s < 256 && (k / 32) % (2 * s) == 0 && k / 32 / (2 * s) >= 4) s *= 2;
+  while (s < 8 && tiles * s < 256 && (k / 64) % (2 * s) == 0 && k / 64 / (2 * s) >= 2) s *= 2;
   return s;
 }
 
@@ -312,11 +312,11 @@ struct LinearArgs {
 
 // Contraction ranges of a projection: enough to give the chip ~256 workgroups.
 // Contraction splits of one projection launch (M x N outputs in 256 x 256
-// tiles, a K-wide contraction): the s in {1, 2, 4, 8} (dividing K / 32, at
-// least four 32-wide slices per range) with the least modelled time, the
+// tiles, a K-wide contraction): the s in {1, 2, 4, 8} (dividing K / 64, at
+// least two 64-wide stages per range) with the least modelled time, the
 // smallest on a tie.  One workgroup fills a CU, so the tiles run in rounds of
-// kGemmCUs; a range of K / 32 / s slices takes about a microsecond per slice
-// when the chip is full; with s > 1 the partials (s fp32 outputs) are written,
+// kGemmCUs; a range takes about a microsecond per 32 of its K / s when the
+// chip is full; with s > 1 the partials (s fp32 outputs) are written,
 // then read back with the output by a row kernel at about 5 TB/s.  A split that
 // only adds a round (192 tiles in two ranges: 384 workgroups, two rounds of half
 // the work) gains nothing and pays the partials, so it is not taken.
@@ -327,7 +327,7 @@ inline int linear_splits(int64_t M, int64_t N, int64_t K) {
   int best = 1;
   double best_us = 0.0;
   for (int s = 1; s <= 8; s *= 2) {
-    if ((K / 32) % s != 0 || (s > 1 && K / 32 / s < 4)) break;
+    if ((K / 64) % s != 0 || (s > 1 && K / 64 / s < 2)) break;
     const int64_t rounds = (tiles * s + kGemmCUs - 1) / kGemmCUs;
     const double us = (double)rounds * (double)(K / 32 / s) + (s > 1 ? (s + 1) * out_bytes / 5.0e6 : 0.0);
     if (s == 1 || us < best_us) best = s, best_us = us;

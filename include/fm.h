@@ -169,7 +169,7 @@ size_t fm_context_rows_workspace_size(int64_t n_hidden, int64_t n_anchor, int32_
  *
  * hidden       DEVICE bf16 [n_hidden, d_hidden]: the target's hidden states of
  *              the chosen layers, concatenated per row (d_hidden = n_aux *
- *              target hidden size), a multiple of 32.
+ *              target hidden size), a multiple of 64.
  * w_fc         DEVICE bf16 [dim, d_hidden] (``fc``, no bias).
  * hidden_norm_w, anchor_norm_w   DEVICE fp32 [dim].
  * anchor_ids   DEVICE int32 [n_anchor]: anchor tokens; an id outside [0, vocab)
@@ -226,7 +226,7 @@ size_t fm_linear_workspace_size(int64_t M, int32_t N, int32_t K);
  * are summed in a fixed order (the result does not depend on scheduling).
  * x     DEVICE bf16 [M, K] row-major;  w  DEVICE bf16 [N, K] (nn.Linear layout).
  * bias  DEVICE bf16 [N] or NULL;  gate  DEVICE fp32 [N] (FM_LINEAR_RESIDUAL).
- * K a multiple of 32; N a multiple of 1024.  Pointers 16-byte aligned.
+ * K a multiple of 64; N a multiple of 1024.  Pointers 16-byte aligned.
  * ws    DEVICE, fm_linear_workspace_size(M, N, K) bytes, 256-byte aligned (may
  *       be NULL when that is 0).
  */

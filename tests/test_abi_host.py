@@ -220,6 +220,7 @@ def _rows(lib, **over):
     (dict(dim=1000), B.FM_E_UNSUPPORTED, "dim"),
     (dict(dim=9216), B.FM_E_UNSUPPORTED, "dim"),
     (dict(d_hidden=500), B.FM_E_UNSUPPORTED, "d_hidden"),
+    (dict(d_hidden=96), B.FM_E_UNSUPPORTED, "multiple of 64"),
     (dict(d_target=100), B.FM_E_UNSUPPORTED, "d_target"),
     (dict(vocab=0), B.FM_E_INVALID, "vocab"),
     (dict(cl=FAKE, win=0, bs=1), B.FM_E_INVALID, "window"),
@@ -253,6 +254,9 @@ def test_dit_entry_points_reject(lib):
     assert g(FAKE, 8, 512, FAKE, 2000, None, 0, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
     assert "N 2000" in B.fm_last_error()
     assert g(FAKE, 8, 500, FAKE, 2048, None, 0, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    # the tile streams the contraction in 64-wide stages
+    assert g(FAKE, 8, 96, FAKE, 2048, None, 0, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
+    assert "multiple of 64" in B.fm_last_error()
     assert g(FAKE, 8, 512, FAKE, 2048, None, B.FM_LINEAR_RESIDUAL, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_INVALID
     assert "gate" in B.fm_last_error()
     assert g(FAKE, 8, 512, FAKE, 2048, None, 7, None, FAKE, FAKE, 1 << 30, None) == B.FM_E_UNSUPPORTED
