@@ -507,49 +507,64 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     const int last_page = min(tb + 15, lctx - 1) >> a.log2ps;
     return wreq == lb && first_page >= wbase && last_page - wbase < kWin;
   };
-  // Page id of the next tile, read from the window one tile ahead so the read
-  // has completed by the time that tile's loads are issued.
+  // Page id of the next tile, read one tile ahead so the read has completed
+  // by the time that tile's loads are issued: from the window (per lane), or
+  // with one page per tile straight from the page table through the scalar
+  // cache (an index past the row reads as -1, a bad page).
   int pg_next = 0;
   bool pg_have = false;
   auto prefetch_page = [&]() {
     pg_have = false;
     if (exhausted || lk >= lT) return;
     const int tb = lk << 4;
-    if (!window_covers(tb)) return;
-    pg_next = win[((min(tb + c, lctx - 1) >> a.log2ps) - wbase) & (kWin - 1)];
-    pg_have = true;
+    if constexpr (UNIFORM_PAGE) {
+      const int idx = tb >> a.log2ps;
+      pg_next = idx < a.pt_stride ? sload_i32(a.page_table + (int64_t)lb * a.pt_stride + idx) : -1;
+      pg_have = true;
+    } else {
+      if (!window_covers(tb)) return;
+      pg_next = win[((min(tb + c, lctx - 1) >> a.log2ps) - wbase) & (kWin - 1)];
+      pg_have = true;
+    }
   };
 
   auto load_slot = [&](StreamSlot<PT, D, kQIn>& s, int j) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
     uint32_t flags = 0;
+    uint32_t keys = 0;  // UNIFORM_PAGE: the tile's valid keys, in scalar registers
     if (j < n_tiles && !exhausted) {
       const bool last_of_pair = lk == lT - 1;
       flags = (lk == 0 || j == 0) ? kStart : 0;
       if (last_of_pair || j == n_tiles - 1)
         flags |= kEnd | ((seg_from0 && last_of_pair) ? kWhole : 0) | (seg_first ? 0 : kPart1);
       const int tb = lk << 4;
-      const int tok = tb + c;
-      const int tok_c = min(tok, lctx - 1);
-      int page;
-      if (pg_have) {
-        page = pg_next;
-      } else {
-        if (!window_covers(tb))
-          // the whole request's page row when it fits (every head's pair reuses it)
-          fill_window(lb, ((lctx - 1) >> a.log2ps) < kWin ? 0 : (tb >> a.log2ps));
-        page = win[((tok_c >> a.log2ps) - wbase) & (kWin - 1)];
-      }
-      if (UNIFORM_PAGE) {
+      if constexpr (UNIFORM_PAGE) {
         // one page per tile: scalar tile base; the lanes' slots c are in the page
-        const int pu = __builtin_amdgcn_readfirstlane(page);
+        int pu;
+        if (pg_have) {
+          pu = pg_next;
+        } else {
+          const int idx = tb >> a.log2ps;
+          pu = idx < a.pt_stride ? sload_i32(a.page_table + (int64_t)lb * a.pt_stride + idx) : -1;
+        }
         const bool page_ok = pu >= 0 && (int64_t)pu < a.pool.num_pages;
-        ok = tok < lctx && page_ok;
-        bad = tok < lctx && !page_ok;
+        keys = page_ok ? (kKeyMask >> (16 - min(16, lctx - tb))) : 0u;  // tb < lctx: at least one key
+        bad_page |= !page_ok;
         tile_base = (int64_t)lh * a.pool.head_stride +
                     (page_ok ? (int64_t)pu * a.pool.page_stride + (int64_t)(tb & ps_mask) * a.pool.slot_stride : 0);
       } else {
+        const int tok = tb + c;
+        const int tok_c = min(tok, lctx - 1);
+        int page;
+        if (pg_have) {
+          page = pg_next;
+        } else {
+          if (!window_covers(tb))
+            // the whole request's page row when it fits (every head's pair reuses it)
+            fill_window(lb, ((lctx - 1) >> a.log2ps) < kWin ? 0 : (tb >> a.log2ps));
+          page = win[((tok_c >> a.log2ps) - wbase) & (kWin - 1)];
+        }
         const bool page_ok = page >= 0 && (int64_t)page < a.pool.num_pages;
         ok = tok < lctx && page_ok;
         bad = tok < lctx && !page_ok;
@@ -584,8 +599,12 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
         s.v[ch] = load16_stream(vpool + off + ch * 4 * EPC + g * EPC);
       }
     }
-    s.mf = flags | (uint32_t)(__ballot(ok) & 0xffffull);
-    bad_page |= __ballot(bad) != 0;
+    if constexpr (UNIFORM_PAGE) {
+      s.mf = flags | keys;
+    } else {
+      s.mf = flags | (uint32_t)(__ballot(ok) & 0xffffull);
+      bad_page |= __ballot(bad) != 0;
+    }
   };
 
   // ---- compute state (per query fragment f) ----
