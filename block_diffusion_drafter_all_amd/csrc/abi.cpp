@@ -210,7 +210,9 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 
 size_t fm_context_rows_workspace_size(int64_t n_hidden, int64_t n_anchor, int32_t d_hidden, int32_t d_target,
                                       int32_t dim) {
-  if (n_hidden < 0 || n_anchor < 0 || d_hidden < 1 || d_target < 1 || dim < 1) return 0;
+  // each width matters only when its rows exist (anchors alone pass d_hidden = 0)
+  if (n_hidden < 0 || n_anchor < 0 || dim < 1 || (n_hidden == 0 && n_anchor == 0)) return 0;
+  if ((n_hidden > 0 && d_hidden < 1) || (n_anchor > 0 && d_target < 1)) return 0;
   return fm::ctx_rows_layout(n_hidden, n_anchor, d_hidden, d_target, dim).total;
 }
 

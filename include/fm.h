@@ -149,7 +149,8 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
 
 /* ------------------------------------------------------- context rows -- */
 
-/* Workspace bytes fm_context_rows needs (0 for invalid sizes). */
+/* Workspace bytes fm_context_rows needs (0 for invalid sizes or no rows).  A
+ * width counts only when its rows exist: anchors alone pass d_hidden = 0. */
 size_t fm_context_rows_workspace_size(int64_t n_hidden, int64_t n_anchor, int32_t d_hidden, int32_t d_target,
                                       int32_t dim);
 

@@ -242,6 +242,9 @@ def test_context_rows_empty_and_workspace(lib):
     big = lib.fm_context_rows_workspace_size(1088, 64, 20480, 4096, 4096)
     assert 0 < small < big and big >= 1088 * 4096 * 4
     assert lib.fm_context_rows_workspace_size(-1, 0, 64, 64, 1024) == 0
+    # anchors alone need a workspace though they pass no hidden width (and hidden rows alone no target width)
+    assert lib.fm_context_rows_workspace_size(0, 3, 0, 128, 1024) > 0
+    assert lib.fm_context_rows_workspace_size(5, 0, 128, 0, 1024) > 0
 
 
 def test_dit_entry_points_reject(lib):

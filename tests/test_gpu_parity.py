@@ -510,6 +510,50 @@ def test_context_rows_full_size_sampled():
     _check_full_step_attention(w, buf, before, slots, keys, values, reqs)
 
 
+def test_context_rows_edge_cases():
+    # Nothing committed (the hidden rows are left as they were, the anchors
+    # still computed), anchors only, and anchor ids outside [0, vocab) (read as
+    # the clamped row, error bit 0 set).
+    log("rows of the write: nothing committed; anchors only; out-of-vocabulary anchor ids")
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(41)
+    bs, window, d_hidden, d_target, dim, vocab = 3, 16, 256, 128, 1024, 97
+    hidden = torch.randn((bs * window, d_hidden), generator=gen, device=dev).to(torch.bfloat16)
+    w_fc = (0.05 * torch.randn((dim, d_hidden), generator=gen, device=dev)).to(torch.bfloat16)
+    g_h = 1 + 0.1 * torch.randn(dim, generator=gen, device=dev)
+    emb = torch.randn((vocab, d_target), generator=gen, device=dev).to(torch.bfloat16)
+    w_ap = (0.05 * torch.randn((dim, d_target), generator=gen, device=dev)).to(torch.bfloat16)
+    b_ap = (0.1 * torch.randn(dim, generator=gen, device=dev)).to(torch.bfloat16)
+    g_a = 1 + 0.1 * torch.randn(dim, generator=gen, device=dev)
+    ids = torch.tensor([5, vocab - 1, 0], dtype=torch.int32, device=dev)
+    ref = O.anchor_input_rows(ids.cpu().numpy(), to_np(emb), to_np(w_ap), to_np(b_ap), to_np(g_a), 1e-6)
+
+    commit = torch.zeros(bs, dtype=torch.int32, device=dev)
+    rows = torch.full((bs * window + bs, dim), float("nan"), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B.fm_context_rows_workspace_size(bs * window, bs, d_hidden, d_target, dim), dtype=torch.uint8,
+                     device=dev)
+    B.fm_context_rows(hidden, w_fc, g_h, ids, emb, w_ap, b_ap, g_a, 1e-6, commit_lens=commit, window=window,
+                      rows=rows, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(rows[: bs * window].float()).all(), "no committed column: no hidden row is written"
+    compare(rows[bs * window:], ref, "anchors, nothing committed")
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+
+    only = B.fm_context_rows(None, None, None, ids, emb, w_ap, b_ap, g_a, 1e-6)
+    torch.cuda.synchronize()
+    compare(only, ref, "anchors only")
+
+    bad = torch.tensor([5, vocab + 3, -2], dtype=torch.int32, device=dev)
+    ws3 = torch.zeros(B.fm_context_rows_workspace_size(0, 3, 0, d_target, dim), dtype=torch.uint8, device=dev)
+    out = B.fm_context_rows(None, None, None, bad, emb, w_ap, b_ap, g_a, 1e-6, ws=ws3)
+    torch.cuda.synchronize()
+    assert int(ws3[4:8].view(torch.int32).item()) & 1, "an id outside the vocabulary sets error bit 0"
+    clamped = np.clip(bad.cpu().numpy(), 0, vocab - 1)
+    compare(out, O.anchor_input_rows(clamped, to_np(emb), to_np(w_ap), to_np(b_ap), to_np(g_a), 1e-6),
+            "out-of-range ids read the clamped rows")
+
+
 def test_prefill_in_chunks():
     # a prefill of 4100 rows (two full chunks of 2048 and a ragged one) of one
     # request: the pool against the oracle's write of the oracle's rows (rounded
@@ -552,7 +596,8 @@ def test_prefill_in_chunks():
 # gated residuals, the GELU MLP, around the two attentions.
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 512, 2048), (1024, 1024, 16384), (37, 4096, 1024)])
+@pytest.mark.parametrize("M,K,N", [(300, 512, 2048), (1024, 1024, 16384), (37, 4096, 1024), (1, 64, 1024),
+                                   (257, 512, 1024)])
 def test_linear_epilogues(M, K, N):
     log(f"fm_linear M={M} K={K} N={N} (ranges: {B.fm_linear_workspace_size(M, N, K) > 0})")
     dev = torch.device("cuda")
