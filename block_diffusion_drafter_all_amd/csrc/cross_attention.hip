@@ -16,15 +16,17 @@
 // restarts its load pipeline at a pair boundary: the loader walks on to the
 // next pair and carries that pair's query rows along with its first tile.
 //   - K/V tiles are read straight from the pages into MFMA operand layout
-//     (16-byte loads; page ids come from a per-wave LDS window, so waiting for
-//     one never waits for K/V loads in flight);
+//     (16-byte loads).  Page ids are read one tile ahead: with pages of at
+//     least 16 tokens (one page per tile) as one scalar load of the page-table
+//     entry, else from a per-wave LDS window of the request's page row; either
+//     way waiting for one never waits for K/V loads in flight;
 //   - S^T = K Q^T leaves each lane one query row and four keys, which is the
 //     B-operand layout of O^T = V^T P^T, so the online softmax and its rescale
 //     stay in registers; V is moved to column layout by an MFMA against a 0/1
 //     selection matrix;
 //   - a pair that lies inside one wave's range is written final; a pair cut by
-//     range boundaries leaves (m, l, O) partials that the merge kernel adds up
-//     in wave order (deterministic).
+//     range boundaries leaves (m, l, O) partials, and the last of its waves to
+//     finish adds them up in wave order in the kernel's tail (deterministic).
 
 #include <type_traits>
 

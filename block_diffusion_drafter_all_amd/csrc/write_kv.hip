@@ -106,7 +106,6 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
   f32x4_t acc[NDT];
 #pragma unroll
   for (int ct = 0; ct < NDT; ++ct) acc[ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
   for (int k0 = 0; k0 < a.d_in; k0 += KC) {
     const u32x4_t xb = load16(xrow + k0);
     u32x4_t wa[NDT];
