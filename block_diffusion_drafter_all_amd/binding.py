@@ -155,13 +155,16 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, contiguous=True) -> None:
+def _need(t: torch.Tensor, name: str, dtype=None, contiguous=True, shape=None) -> None:
+    """The C ABI takes bare pointers, so every extent it will touch is checked here."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 @dataclass
@@ -281,6 +284,10 @@ def fm_context_rows(hidden, w_fc, hidden_norm_w, anchor_ids, embedding, w_anchor
     if commit_lens is not None:
         _need(commit_lens, "commit_lens", torch.int32)
         bs = commit_lens.shape[0] if bs is None else bs
+        if commit_lens.shape[0] < bs:
+            raise ValueError("commit_lens needs an entry for each of the bs requests")
+    if ws is not None:
+        _need(ws, "ws", torch.uint8)
     dev = (hidden if hidden is not None else anchor_ids).device
     if rows is None:
         rows = torch.empty((n_hidden + n_anchor, dim), dtype=torch.bfloat16, device=dev)
@@ -302,12 +309,12 @@ def fm_ada_layer_norm(h, scale, shift, eps, out=None):
     """``LayerNorm(h) * scale + shift`` of the fp32 residual stream ``h (rows,
     dim)`` into bf16 ``out``."""
     _need(h, "h", torch.float32)
-    _need(scale, "scale", torch.float32)
-    _need(shift, "shift", torch.float32)
     rows, dim = h.shape
+    _need(scale, "scale", torch.float32, shape=(dim,))
+    _need(shift, "shift", torch.float32, shape=(dim,))
     if out is None:
         out = torch.empty((rows, dim), dtype=torch.bfloat16, device=h.device)
-    _need(out, "out", torch.bfloat16)
+    _need(out, "out", torch.bfloat16, shape=(rows, dim))
     _check(load_library().fm_ada_layer_norm(_ptr(h), rows, dim, _ptr(scale), _ptr(shift), eps, _ptr(out), _stream()))
     return out
 
@@ -327,15 +334,17 @@ def fm_linear(x, w, bias=None, epilogue=FM_LINEAR_BF16, gate=None, out=None, ws=
     if w.shape != (N, K):
         raise ValueError("w must be (N, K) for x (M, K)")
     if bias is not None:
-        _need(bias, "bias", torch.bfloat16)
+        _need(bias, "bias", torch.bfloat16, shape=(N,))
     if gate is not None:
-        _need(gate, "gate", torch.float32)
+        _need(gate, "gate", torch.float32, shape=(N,))
     f32_out = epilogue in (FM_LINEAR_RESIDUAL, FM_LINEAR_ASSIGN_F32)
     if out is None:
         if epilogue == FM_LINEAR_RESIDUAL:
             raise ValueError("the residual epilogue updates an existing out")
         out = torch.empty((M, N), dtype=torch.float32 if f32_out else torch.bfloat16, device=x.device)
-    _need(out, "out", torch.float32 if f32_out else torch.bfloat16)
+    _need(out, "out", torch.float32 if f32_out else torch.bfloat16, shape=(M, N))
+    if ws is not None:
+        _need(ws, "ws", torch.uint8)
     need = lib.fm_linear_workspace_size(M, N, K)
     if need and (ws is None or ws.numel() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -376,8 +385,12 @@ def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     if out is None:
         out = torch.empty_like(q)
-    _need(out, "out", q.dtype)
+    _need(out, "out", q.dtype, shape=q.shape)
+    _need(ws, "ws", torch.uint8)
     total_q, H, Dh = q.shape
+    _need(q_norm_w, "q_norm_w", torch.float32, shape=(Dh,))
+    if tuple(pool.k.shape[2:]) != (H, Dh):
+        raise ValueError(f"the pool holds {tuple(pool.k.shape[2:])} (H, Dh) per slot, q {(H, Dh)}")
     if page_table.shape[0] < ctx_lens.shape[0] or cu_seqlens_q.shape[0] != ctx_lens.shape[0] + 1:
         raise ValueError("page_table needs a row per request and cu_seqlens_q bs + 1 entries")
     desc = pool.descriptor()
@@ -398,9 +411,12 @@ def fm_block_self_attention(qkv, q_norm_w, k_norm_w, ctx_lens, softmax_scale, ro
     n_blocks, K, three, H, Dh = qkv.shape
     if three != 3:
         raise ValueError("qkv must be (n_blocks, K, 3, H, Dh)")
+    _need(q_norm_w, "q_norm_w", torch.float32, shape=(Dh,))
+    _need(k_norm_w, "k_norm_w", torch.float32, shape=(Dh,))
+    _need(ctx_lens, "ctx_lens", torch.int32, shape=(n_blocks,))
     if out is None:
         out = torch.empty((n_blocks, K, H, Dh), dtype=qkv.dtype, device=qkv.device)
-    _need(out, "out", qkv.dtype)
+    _need(out, "out", qkv.dtype, shape=(n_blocks, K, H, Dh))
     _check(lib.fm_block_self_attention(
         _ptr(qkv), _dtype_code(qkv), n_blocks, K, _ptr(q_norm_w), _ptr(k_norm_w), _ptr(ctx_lens), H, Dh,
         softmax_scale, rope_theta, eps, _ptr(out), _stream()))

@@ -722,3 +722,30 @@ def test_dit_step_full_size_sampled():
     d = w.dit
     compare(buf.dit["out"][torch.as_tensor(rows, device=buf.dit["out"].device)],
             O.ada_layer_norm(hs[-1][rows], to_np(d.final_scale), to_np(d.final_shift), w.eps), "final LayerNorm")
+
+
+def test_binding_refuses_mismatched_extents():
+    # The C ABI takes bare pointers; the binding checks every extent it passes
+    # (nothing is launched for these calls).
+    dev = torch.device("cuda")
+    x = torch.zeros((8, 64), dtype=torch.bfloat16, device=dev)
+    w = torch.zeros((1024, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="out must have shape"):
+        B.fm_linear(x, w, out=torch.empty((4, 1024), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError, match="bias must have shape"):
+        B.fm_linear(x, w, torch.zeros(512, dtype=torch.bfloat16, device=dev))
+    h = torch.zeros((3, 1024), device=dev)
+    with pytest.raises(ValueError, match="scale must have shape"):
+        B.fm_ada_layer_norm(h, torch.ones(512, device=dev), torch.zeros(1024, device=dev), 1e-6)
+    q = torch.zeros((16, 4, 64), dtype=torch.bfloat16, device=dev)
+    pool = B.KVPool(torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device=dev),
+                    torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device=dev))
+    one = torch.ones(1, dtype=torch.int32, device=dev)
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(1, 4, 64), dtype=torch.uint8, device=dev)
+    with pytest.raises(ValueError, match="pool holds"):
+        B.fm_paged_cross_attention(q, torch.ones(64, device=dev), pool, torch.zeros((1, 4), dtype=torch.int32,
+                                   device=dev), one, torch.tensor([0, 16], dtype=torch.int32, device=dev),
+                                   0.125, 1e6, 1e-6, ws)
+    qkv = torch.zeros((2, 16, 3, 4, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError, match="ctx_lens must have shape"):
+        B.fm_block_self_attention(qkv, torch.ones(64, device=dev), torch.ones(64, device=dev), one, 0.125, 1e6, 1e-6)
