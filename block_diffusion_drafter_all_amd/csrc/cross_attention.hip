@@ -259,9 +259,9 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
       uint8_t* dst = (uint8_t*)(a.ws + a.lay.q_hat) + (((int64_t)b * kQRows * NQF + k) * a.H + h) * D;
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {  // EPC (8) consecutive columns -> 8 codes
-        u32x2_t w = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < EPC; ++j) w[j >> 2] |= f32_to_e4m3_bits(qf[f][ch * EPC + j] * r) << (8 * (j & 3));
+        const float* x = &qf[f][ch * EPC];
+        const u32x2_t w = {f32x4_to_e4m3(x[0] * r, x[1] * r, x[2] * r, x[3] * r),
+                           f32x4_to_e4m3(x[4] * r, x[5] * r, x[6] * r, x[7] * r)};
         *(u32x2_t*)(dst + ch * 4 * EPC + g * EPC) = w;
       }
     }

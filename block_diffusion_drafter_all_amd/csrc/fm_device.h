@@ -55,22 +55,17 @@ __device__ __forceinline__ float round_bf16(float f) {
   return bf16_bits_to_f32(f32_to_bf16_bits(f));
 }
 
-// fp32 -> e4m3 code: nearest, ties to even, magnitudes past 448 saturating to
-// 448 (the pool must stay finite).  Normal results (>= 2^-6) round the fp32
-// significand to 3 bits in place and rebias the exponent (127 -> 7); below
-// 2^-6 the grid step is 2^-9, so the code is the rounded multiple of it (a
-// result of 8 is the code of 2^-6 as well).
-__device__ __forceinline__ uint32_t f32_to_e4m3_bits(float f) {
-  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
-  const float a = fminf(fabsf(f), 448.0f);
-  uint32_t code;
-  if (a >= 0.015625f) {
-    const uint32_t u = __float_as_uint(a);
-    code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  } else {
-    code = (uint32_t)rintf(a * 512.0f);
-  }
-  return sign | code;
+// Four fp32 values -> four OCP e4m3 codes (the first in the low byte):
+// nearest, ties to even, magnitudes past 448 saturating to 448 (the pool must
+// stay finite).  Clamped first, then converted by gfx950's packed fp8
+// conversion; over every multiple of 2^-13 below 520 (both signs), every
+// midpoint of the e4m3 grid and 2M random values of 2^-14..2^9 it gives the
+// same codes as rounding the significand to 3 bits (2^-9 steps below 2^-6).
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  auto sat = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
 }
 
 template <class T>
@@ -405,8 +400,7 @@ __device__ __forceinline__ void store4<F32>(float* p, const f32x4_t& v, float sc
 
 template <>
 __device__ __forceinline__ void store4<E4m3>(uint8_t* p, const f32x4_t& v, float scale) {
-  *(uint32_t*)p = f32_to_e4m3_bits(v[0] * scale) | (f32_to_e4m3_bits(v[1] * scale) << 8) |
-                  (f32_to_e4m3_bits(v[2] * scale) << 16) | (f32_to_e4m3_bits(v[3] * scale) << 24);
+  *(uint32_t*)p = f32x4_to_e4m3(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
 }
 
 // Exclusive prefix sum over a 1024-thread block; returns the block total in *total.
