@@ -749,3 +749,86 @@ def test_binding_refuses_mismatched_extents():
     qkv = torch.zeros((2, 16, 3, 4, 64), dtype=torch.bfloat16, device=dev)
     with pytest.raises(ValueError, match="ctx_lens must have shape"):
         B.fm_block_self_attention(qkv, torch.ones(64, device=dev), torch.ones(64, device=dev), one, 0.125, 1e6, 1e-6)
+
+
+@pytest.mark.parametrize("ps", [16, 4])
+def test_bad_page_ids_are_skipped_and_flagged(ps):
+    # Page-table entries outside [0, num_pages) (too large or negative): the
+    # tokens of that page are skipped and bit 0 of the workspace error word is
+    # set (the C ABI's device-side index checks); every other token and
+    # request is computed as usual.  Page size 16 reads page ids through the
+    # scalar cache, 4 through the per-wave window.
+    log(f"page-table entries outside the pool, page size {ps}: tokens skipped, error bit set")
+    ctx = [40, 70, 33, 90]
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=1, H=2, Dh=128, ps=ps))
+    dev = w.ctx_lens.device
+    n_pages = w.pools[0].k.shape[0]
+    bad = {1: (2, n_pages + 7), 2: (0, -3)}  # request -> (logical page, out-of-range id)
+    pt = w.page_table.clone()
+    for b, (j, v) in bad.items():
+        pt[b, j] = v
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    out = torch.full_like(w.q[0], float("nan"))
+    B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], pt, w.ctx_lens, w.cu_seqlens_q, w.softmax_scale,
+                               w.theta, w.eps, ws, out=out)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) & 1, "an out-of-range page id sets error bit 0"
+    # expected: each request's context without the bad page's tokens (oracle steps)
+    q, qnw = to_np(w.q[0]), to_np(w.q_norm_w[0])
+    pk, pv = to_np(w.pools[0].k), to_np(w.pools[0].v)
+    good_pt = w.page_table.cpu().numpy()
+    cu = w.cu_seqlens_q.cpu().numpy()
+    ref = np.zeros(q.shape)
+    for b, n in enumerate(ctx):
+        pages = good_pt[b][: -(-n // ps)]
+        kb = pk[pages].reshape(-1, w.H, w.Dh)[:n]
+        vb = pv[pages].reshape(-1, w.H, w.Dh)[:n]
+        keep = np.ones(n, dtype=bool)
+        if b in bad:
+            j = bad[b][0]
+            keep[j * ps:(j + 1) * ps] = False
+        r0, r1 = cu[b], cu[b + 1]
+        positions = n + np.arange(r1 - r0) % 16
+        for h in range(w.H):
+            qh = O.apply_rope(O.rms_norm(q[r0:r1, h], qnw, w.eps), positions, w.theta)
+            ref[r0:r1, h] = O.attention(qh, kb[keep, h], vb[keep, h], w.softmax_scale)
+    compare(out, ref, f"cross-attention with bad page ids, ps {ps}")
+
+
+def test_write_skips_rows_of_bad_pages():
+    # A row whose page-table entry lies outside the pool is not written (its
+    # slot reads -1) and sets error bit 0; the other rows land as usual.
+    log("write: rows on an out-of-range page are skipped and flagged")
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(51)
+    L, H, Dh, ps, d_in, n_pages = 1, 2, 128, 16, 256, 6
+    n = 40  # positions 0..39 of one request: pages 0, 1, 2 of its row
+    x = torch.randn((n, d_in), generator=gen, device=dev).to(torch.bfloat16)
+    w_kv = (0.05 * torch.randn((L * 2 * H * Dh, d_in), generator=gen, device=dev)).to(torch.bfloat16)
+    knw = 1 + 0.1 * torch.randn((L, Dh), generator=gen, device=dev)
+    pt = torch.tensor([[3, n_pages + 2, 1]], dtype=torch.int32, device=dev)  # logical page 1 is outside the pool
+    sentinel = -7.0
+    pools = [B.KVPool(torch.full((n_pages, ps, H, Dh), sentinel, dtype=torch.bfloat16, device=dev),
+                      torch.full((n_pages, ps, H, Dh), sentinel, dtype=torch.bfloat16, device=dev))]
+    row_req = torch.zeros(n, dtype=torch.int32, device=dev)
+    row_pos = torch.arange(n, dtype=torch.int32, device=dev)
+    slots = torch.empty(n, dtype=torch.int32, device=dev)
+    ws = torch.zeros(B.fm_write_context_kv_workspace_size(n), dtype=torch.uint8, device=dev)
+    B.fm_write_context_kv(x, w_kv, knw, row_req, row_pos, pt, pools, 1e-6, 1e6, out_slots=slots, ws=ws)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) & 1, "a row on an out-of-range page sets error bit 0"
+    got = slots.cpu().numpy()
+    want = np.array([3 * ps + p if p < 16 else (-1 if p < 32 else 1 * ps + p - 32) for p in range(n)])
+    np.testing.assert_array_equal(got, want)
+    live = np.nonzero(want >= 0)[0]
+    s_, keys, values = O.write_context_kv(to_np(x)[live], to_np(w_kv), to_np(knw), np.zeros(len(live), np.int64),
+                                          live, np.array([[3, 0, 1]]), ps, L, H, Dh, 1e-6, 1e6)
+    kk = pools[0].k.reshape(-1, H, Dh)
+    vv = pools[0].v.reshape(-1, H, Dh)
+    sl = torch.as_tensor(want[live], device=dev, dtype=torch.long)
+    compare(kk[sl], keys[:, 0], "keys of the rows on valid pages")
+    compare(vv[sl], values[:, 0], "values of the rows on valid pages")
+    untouched = np.setdiff1d(np.arange(n_pages * ps), want[live])
+    assert (kk[torch.as_tensor(untouched, device=dev)].float() == sentinel).all(), "no other slot is written"
