@@ -443,7 +443,11 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   const WaveRec rec = ((const WaveRec*)(ws + a.lay.wave_rec))[w];
   const bool plan_ok =
       (ph.magic == kPlanMagic) & (ph.bs == a.bs) & (ph.H == a.H) & (ph.n_waves == a.lay.n_waves) & (ph.nqf == NQF);
-  const int n_tiles = plan_ok ? rec.count : 0;
+  if (!plan_ok) {  // no plan for these sizes: nothing is computed, and the error word says so
+    if (w == 0 && lane_id() == 0) atomicOr(&hdr->error, 4);
+    return;
+  }
+  const int n_tiles = rec.count;
   if (n_tiles <= 0) return;
 
   // Per-wave LDS window of page ids.

@@ -296,16 +296,17 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  * page_table  DEVICE int32 [bs, pt_stride].
  * ctx_lens, bs, H  as given to fm_plan_cross_attention, whose plan ``ws``
  *             must hold (same stream, earlier; lengths unchanged since).  A
- *             plan made for other shapes or another pool type leaves ``out``
- *             untouched.  If the
+ *             plan made for other shapes or another pool type computes
+ *             nothing (only the zero rows of empty contexts are written) and
+ *             sets bit 2 of the error word.  If the
  *             lengths changed after the plan, the outputs are unspecified, no
  *             access leaves the buffers, and bit 1 of the error word is set
  *             when a wave's share runs past the last tile; plan again.
  * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
  *             [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most max_q of them.
  * max_q       host bound on query rows per request (<= 64), the value the plan
- *             in ``ws`` was made with (a plan made with another value leaves
- *             ``out`` untouched); rows past it are not computed.
+ *             in ``ws`` was made with (a plan made with another value is a
+ *             plan for other shapes, above); rows past it are not computed.
  * Dh in {64, 128}; page_size a power of two in [1, 4096].
  */
 int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,

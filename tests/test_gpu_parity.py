@@ -832,3 +832,36 @@ def test_write_skips_rows_of_bad_pages():
     compare(vv[sl], values[:, 0], "values of the rows on valid pages")
     untouched = np.setdiff1d(np.arange(n_pages * ps), want[live])
     assert (kk[torch.as_tensor(untouched, device=dev)].float() == sentinel).all(), "no other slot is written"
+
+
+def test_cross_attention_with_a_plan_for_other_sizes():
+    # A plan made with another max_q (or other shapes) computes nothing but the
+    # zero rows of empty contexts and sets bit 2 of the error word.
+    log("cross-attention called with a plan made for another max_q")
+    ctx = [40, 0, 70]
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=1, H=2, Dh=128, ps=16))
+    dev = w.ctx_lens.device
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 32), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=16)
+    out = torch.full_like(w.q[0], float("nan"))
+    B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, w.cu_seqlens_q,
+                               w.softmax_scale, w.theta, w.eps, ws, out=out, max_q=32)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) & 4, "a plan for other sizes sets error bit 2"
+    cu = w.cu_seqlens_q.cpu().numpy()
+    for b, n in enumerate(ctx):
+        rows = out[cu[b]:cu[b + 1]].float()
+        if n == 0:
+            assert (rows == 0).all(), "empty contexts still get their zero rows"
+        else:
+            assert torch.isnan(rows).all(), "nothing else is written"
+    # planned again with the call's max_q, the same call computes and clears nothing else
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=32)
+    B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, w.cu_seqlens_q,
+                               w.softmax_scale, w.theta, w.eps, ws, out=out, max_q=32)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) == 0
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows)
+    compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross-attention after planning again")
