@@ -301,7 +301,9 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  *             sets bit 2 of the error word.  If the
  *             lengths changed after the plan, the outputs are unspecified, no
  *             access leaves the buffers, and bit 1 of the error word is set
- *             when a wave's share runs past the last tile; plan again.
+ *             when a wave's share runs past the last tile (not every change
+ *             does that, so the bit is no proof that nothing changed); plan
+ *             again.
  * cu_seqlens_q  DEVICE int32 [bs+1]: query rows of request b are
  *             [cu_seqlens_q[b], cu_seqlens_q[b+1]), at most max_q of them.
  * max_q       host bound on query rows per request (<= 64), the value the plan

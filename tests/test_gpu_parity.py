@@ -865,3 +865,35 @@ def test_cross_attention_with_a_plan_for_other_sizes():
     pk, pv, rows = compact_context(w, 0, reqs)
     ref = oracle_cross(w, 0, reqs, pk, pv, rows)
     compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross-attention after planning again")
+
+
+def test_cross_attention_after_lengths_shrank_flags_bit1():
+    # Lengths shortened after the plan so that a wave's planned share runs past
+    # the last tile: every request after the first emptied, so the waves that
+    # cross out of request 0 find no tiles left.  The outputs are unspecified,
+    # nothing outside the buffers is touched, and bit 1 of the error word is
+    # set; planning again gives the right result.  (Many more tiles than
+    # waves, so that shares cross from one request into the next.)
+    log("cross-attention with lengths shortened after the plan")
+    ctx = [1500, 1200, 1800, 1500, 900, 1650, 1400, 1100]
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=1, H=32, Dh=128, ps=16))
+    dev = w.ctx_lens.device
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    shorter = torch.zeros_like(w.ctx_lens)
+    shorter[0] = w.ctx_lens[0]
+    out = torch.empty_like(w.q[0])
+    B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, shorter, w.cu_seqlens_q,
+                               w.softmax_scale, w.theta, w.eps, ws, out=out)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) & 2, "a share running past the last tile sets error bit 1"
+    w.ctx_lens = shorter
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, w.cu_seqlens_q,
+                               w.softmax_scale, w.theta, w.eps, ws, out=out)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) == 0
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows)
+    compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross-attention after planning again")
