@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--upstream", action="store_true",
                     help="config 5: make the write's rows on the device from the target hidden states (fc + "
                          "hidden_norm) and the anchor tokens (embedding + anchor_proj + anchor_norm) in the step")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="before each timed step, stream a 1 GiB scratch buffer (untimed) so the step starts with "
+                         "a cold MALL; ms_per_step is then the mean of the per-step events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
@@ -162,6 +165,36 @@ def measured_traffic(key: str):
     if rec is None or rec.get("sources_sha256") != kernel_sources_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def hbm_ceilings() -> dict:
+    """Context for the HBM figures: torch's plain 1 GiB device-to-device copy,
+    bytes read + written per second, best of 5 after one warm-up."""
+    import torch
+
+    src = torch.ones((COPY_BYTES // 2,), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    return {"torch_copy_GBps": 2 * COPY_BYTES / (min(t) * 1e-3) / 1e9, "copy_bytes": COPY_BYTES}
 
 
 def copy_calibration() -> None:
@@ -343,7 +376,7 @@ def cpu_baseline(w, n_req: int):
             "sample": (f"{len(reqs)} of {w.bs} requests (ids {reqs}): their write rows and, for all {w.L} layers, "
                        f"their self-attention blocks and cross-attention rows; {dt:.1f} s wall; numpy fp64, "
                        f"BLAS threads {blas}"),
-            "seconds": dt}
+            "seconds": dt, "cpu_model": cpu_model()}
 
 
 def main():
@@ -425,19 +458,28 @@ def main():
     # call on the stream it is launched on (torch's current stream).
     E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
     n_pre = 0 if w.dit is not None else w.L   # the DiT step appends its own events per call
-    per_step = [dict(rows=E(), write=E(), self=[E() for _ in range(n_pre)], cross=[E() for _ in range(n_pre)])
-                for _ in range(args.steps)]
+    per_step = [dict(step=E(), rows=E(), write=E(), self=[E() for _ in range(n_pre)],
+                     cross=[E() for _ in range(n_pre)]) for _ in range(args.steps)]
+    flush = torch.empty((COPY_BYTES // 4,), dtype=torch.float32, device="cuda").zero_() if args.flush_mall else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
+        if flush is not None:
+            flush.add_(1.0)  # 1 GiB read and written: the MALL (256 MB) holds none of the step's data
+        per_step[s]["step"][0].record()
         one_step(per_step[s])
+        per_step[s]["step"][1].record()
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
+    step_ms = sorted(st["step"][0].elapsed_time(st["step"][1]) for st in per_step)
+    ms_step = sum(step_ms) / len(step_ms) if flush is not None else ms_total / args.steps
+
+    def pct(p):
+        return step_ms[min(len(step_ms) - 1, int(round(p / 100 * (len(step_ms) - 1))))]
 
     cross_ms = [ev[0].elapsed_time(ev[1]) for st in per_step for ev in st["cross"]]
     self_ms = [ev[0].elapsed_time(ev[1]) for st in per_step for ev in st["self"]]
@@ -467,6 +509,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(workload_key(args)), "bytes_per_launch": cb,
                      "avg_launch_ms": avg_cross},
+        "step_ms": {"p10": pct(10), "p50": pct(50), "p90": pct(90), "mall": "flushed" if flush is not None else "warm"},
         "kv_read_GBps": achieved,
         "kv_read_pct_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "attention_rows_per_s": rows / (sum(cross_ms + self_ms) / args.steps * 1e-3),
@@ -491,6 +534,9 @@ def main():
         avg_r = sum(rows_ms) / len(rows_ms)
         out["context_rows"] = {"avg_ms": avg_r, "flops": rf, "tflops": rf / (avg_r * 1e-3) / 1e12,
                                "mfma_frac_of_bf16_peak": rf / (avg_r * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    props = torch.cuda.get_device_properties(0)
+    out["context"] = {"device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                      "rocm_hip": torch.version.hip, "torch": torch.__version__, **hbm_ceilings()}
     if not args.no_cpu_baseline:
         n_req = args.cpu_sample_requests or max(1, min(w.bs, 24))
         out["cpu_baseline"] = cpu_baseline(w, n_req)
