@@ -59,7 +59,10 @@ __device__ __forceinline__ GemmLoad gemm_load_of(int wv, int lane, int i) {
 // acc += the tile's product over ns stages.  src[i]: the start of this lane's
 // load i at stage 0 (row start + 8 chunk elements); stage s reads src[i] +
 // 64 s.  Afterwards acc[cg][rg][i] (lane l) = Y[X row 64 wm + 32 rg + l % 32]
-// [W row 128 wn + 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4].
+// [W row 128 wn + 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4].  With MMA false
+// the wave only issues its share of the loads and meets every barrier (the
+// same sequence of both), reads no fragments and leaves acc untouched.
+template <bool MMA = true>
 __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const uint16_t* const (&src)[kLoadsPerWave],
                                                  int ns, int wv, int wm, int wn, uint8_t* buf0, uint8_t* buf1) {
   const int lane = lane_id();
@@ -80,6 +83,7 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
     bf16x8_t A[4], B[2];  // W, X
   };
   auto read = [&](const uint8_t* b, int t, Frags& f) {
+    if constexpr (!MMA) return;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       f.A[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(b + off[t] + (4 * wn + q) * 4096));
@@ -88,6 +92,7 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
       f.B[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(b + 32768 + off[t] + (2 * wm + q) * 4096));
   };
   auto mma = [&](const Frags& f) {
+    if constexpr (!MMA) return;
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
@@ -96,6 +101,7 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
   };
   // the order of issue in a k step: each fragment read (then each load) behind one MFMA
   auto interleave = [&](bool loads) {
+    if constexpr (!MMA) return;
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -144,6 +150,20 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
   }
   if (s < ns) stage(s, buf0, buf1);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & kWaitLgkm0);  // drain the trailing loads and reads
+}
+
+// The mainloop for a wave whose 64 X rows are live or not (wave-uniform): a
+// wave whose rows all lie past the end of the tile's rows (the padding of a
+// partial last tile) still moves its share of each stage through LDS but
+// skips the fragment reads and MFMAs, leaving the matrix core of its SIMD to
+// the other wave there.
+__device__ __forceinline__ void gemm256_mainloop_rows(f32x16_t (&acc)[4][2],
+                                                      const uint16_t* const (&src)[kLoadsPerWave], int ns, int wv,
+                                                      int wm, int wn, uint8_t* buf0, uint8_t* buf1, bool rows_live) {
+  if (rows_live)
+    gemm256_mainloop<true>(acc, src, ns, wv, wm, wn, buf0, buf1);
+  else
+    gemm256_mainloop<false>(acc, src, ns, wv, wm, wn, buf0, buf1);
 }
 
 // Declares the two LDS stages of a GEMM kernel.
