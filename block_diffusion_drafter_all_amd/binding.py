@@ -159,6 +159,9 @@ def _need(t: torch.Tensor, name: str, dtype=None, contiguous=True, shape=None) -
     """The C ABI takes bare pointers, so every extent it will touch is checked here."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the kernels run on the current device "
+                         f"(cuda:{torch.cuda.current_device()})")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if contiguous and not t.is_contiguous():
@@ -178,6 +181,8 @@ class KVPool:
 
     def descriptor(self) -> fm_kv_pool:
         k, v = self.k, self.v
+        _need(k, "pool k", contiguous=False)
+        _need(v, "pool v", contiguous=False)
         if k.dim() != 4 or v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
             raise ValueError("k and v must be (pages, page_size, H, Dh) views of one shape, stride and dtype")
         if k.stride(3) != 1:
@@ -234,6 +239,8 @@ def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, 
         raise ValueError("kv_scales needs one (k_scale, v_scale) pair per layer")
     code = _dtype_code(x, pools[0].k.dtype)
     n_rows, d_in = x.shape
+    if ws is not None:
+        _need(ws, "ws", torch.uint8)
     if ws is None:
         ws = torch.empty(lib.fm_write_context_kv_workspace_size(n_rows), dtype=torch.uint8, device=x.device)
     _check(lib.fm_write_context_kv(

@@ -270,3 +270,35 @@ def test_dit_entry_points_reject(lib):
     assert need >= 2 * 256 * 1024 * 4
     assert g(FAKE, 256, 4096, FAKE, 1024, None, 0, None, FAKE, FAKE, need - 1, None) == B.FM_E_WORKSPACE
     assert lib.fm_linear_workspace_size(1024, 16384, 4096) == 0   # 256 output tiles: no split
+
+
+def test_binding_refuses_host_tensors(lib):
+    # The C ABI takes bare device pointers: a host tensor reaching a kernel
+    # would be a GPU memory fault, so the binding refuses it before any call.
+    bf = dict(dtype=torch.bfloat16)
+    i32 = dict(dtype=torch.int32)
+    pool = B.KVPool(torch.zeros((4, 16, 2, 64), **bf), torch.zeros((4, 16, 2, 64), **bf))
+    calls = {
+        "fm_linear": lambda: B.fm_linear(torch.zeros((8, 64), **bf), torch.zeros((256, 64), **bf)),
+        "fm_ada_layer_norm": lambda: B.fm_ada_layer_norm(torch.zeros((2, 256)), torch.ones(256), torch.zeros(256),
+                                                         1e-6),
+        "fm_plan_cross_attention": lambda: B.fm_plan_cross_attention(torch.ones(1, **i32), 2, 64,
+                                                                     torch.zeros(4096, dtype=torch.uint8)),
+        "fm_paged_cross_attention": lambda: B.fm_paged_cross_attention(
+            torch.zeros((16, 2, 64), **bf), torch.ones(64), pool, torch.zeros((1, 4), **i32), torch.ones(1, **i32),
+            torch.tensor([0, 16], **i32), 0.125, 1e6, 1e-6, torch.zeros(4096, dtype=torch.uint8)),
+        "fm_block_self_attention": lambda: B.fm_block_self_attention(
+            torch.zeros((1, 16, 3, 2, 64), **bf), torch.ones(64), torch.ones(64), torch.ones(1, **i32), 0.125, 1e6,
+            1e-6),
+        "fm_write_context_kv": lambda: B.fm_write_context_kv(
+            torch.zeros((2, 64), **bf), torch.zeros((256, 64), **bf), torch.ones((1, 64)), torch.zeros(2, **i32),
+            torch.zeros(2, **i32), torch.zeros((1, 4), **i32), [pool], 1e-6, 1e6),
+        "fm_context_rows": lambda: B.fm_context_rows(
+            torch.zeros((2, 64), **bf), torch.zeros((256, 64), **bf), torch.ones(256), None, None, None, None, None,
+            1e-6),
+    }
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="must be a GPU tensor"):
+            call()
+    with pytest.raises(ValueError, match="pool k must be a GPU tensor"):
+        pool.descriptor()
