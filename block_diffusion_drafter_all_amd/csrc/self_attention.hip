@@ -17,6 +17,47 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// RMSNorm of a slot's q and k fragments (weights wq, wk), then the
+// interleaved-pair rotation of both at the slot's position.  q and k turn by
+// the same angles, so each sine and cosine is evaluated once for the two;
+// every element sees the same operations as one row through norm_rope_row.
+template <class T, int D>
+__device__ __forceinline__ void norm_rope_qk(float (&q)[D / 4], float (&k)[D / 4], const float* __restrict__ wq,
+                                             const float* __restrict__ wk, float eps, int pos, const RopeFreqs& rf,
+                                             int g) {
+  constexpr int EPC = T::EPC;
+  constexpr int NCH = D / (4 * EPC);
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i) {
+    sq += q[i] * q[i];
+    sk += k[i] * k[i];
+  }
+  sq = wave_sum_groups(sq);
+  sk = wave_sum_groups(sk);
+  const float rq = 1.0f / sqrtf(sq / (float)D + eps);
+  const float rk = 1.0f / sqrtf(sk / (float)D + eps);
+  const float fpos = (float)pos;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int j = 0; j < EPC; j += 2) {
+      const int col = ch * 4 * EPC + g * EPC + j;
+      const int f0 = ch * 2 * EPC + j / 2;  // frequency index col / 2, by lane group
+      const float inv = sel4(g, rf.inv[f0], rf.inv[f0 + EPC / 2], rf.inv[f0 + EPC], rf.inv[f0 + 3 * EPC / 2]);
+      float sn, cs;
+      angle_sincos(fpos * inv, &sn, &cs);
+      const int e = ch * EPC + j;
+      const float q0 = q[e] * rq * wq[col], q1 = q[e + 1] * rq * wq[col + 1];
+      const float k0 = k[e] * rk * wk[col], k1 = k[e + 1] * rk * wk[col + 1];
+      q[e] = q0 * cs - q1 * sn;
+      q[e + 1] = q1 * cs + q0 * sn;
+      k[e] = k0 * cs - k1 * sn;
+      k[e + 1] = k1 * cs + k0 * sn;
+    }
+  }
+}
+
 // --------------------------------------------------------- self-attention --
 
 template <class T, int D>
@@ -55,8 +96,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfArgs a) {
       kf[ch * EPC + j] = chunk_elem<T>(vk, j);
     }
   }
-  norm_rope_row<T, D>(qf, a.q_norm_w, a.eps, ctx + c, a.rope, g);
-  norm_rope_row<T, D>(kf, a.k_norm_w, a.eps, ctx + c, a.rope, g);
+  norm_rope_qk<T, D>(qf, kf, a.q_norm_w, a.k_norm_w, a.eps, ctx + c, a.rope, g);
   u32x4_t qop[NCH], kop[NCH];
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
