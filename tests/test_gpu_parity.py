@@ -897,3 +897,31 @@ def test_cross_attention_after_lengths_shrank_flags_bit1():
     pk, pv, rows = compact_context(w, 0, reqs)
     ref = oracle_cross(w, 0, reqs, pk, pv, rows)
     compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross-attention after planning again")
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_seeded_sweep_of_shapes(case):
+    # Seeded draws over the combinations the parametrized tests above take one
+    # at a time: page size, head dim, heads, layout, candidate blocks, pool
+    # type, and a request mix of empty, sub-tile, tile-edge and long contexts.
+    rng = np.random.default_rng(500 + case)
+    ps = int(rng.choice([1, 4, 8, 16, 32, 64]))
+    Dh = int(rng.choice([64, 128]))
+    H = int(rng.choice([1, 2, 3, 5, 8]))
+    n_cand = int(rng.choice([1, 2, 4]))
+    fp8 = bool(rng.integers(2))
+    layout = str(rng.choice(["head_major", "token_major"]))
+    bs = int(rng.integers(1, 10))
+    ctx = [int(rng.choice([0, 1, 15, 16, 17, 63, 64, 65])) if rng.random() < 0.4 else int(rng.integers(1, 3000))
+           for _ in range(bs)]
+    log(f"sweep {case}: ps {ps} Dh {Dh} H {H} candidates {n_cand} e4m3 {fp8} {layout} ctx {ctx}")
+    w = make_workload(3, weights="random", layout=layout, n_cand=n_cand, kv_fp8=fp8,
+                      scale_down=dict(ctx_list=ctx, L=1, H=H, Dh=Dh, ps=ps), seed=900 + case)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    _check_attention(w, buf, list(range(w.bs)), self_blocks=range(w.bs * n_cand))
+    rows = w.cu_seqlens_q.cpu().numpy()
+    for b in range(w.bs):  # an empty context gives exactly zero
+        if ctx[b] == 0:
+            assert torch.count_nonzero(buf.cross_out[0][int(rows[b]):int(rows[b + 1])]) == 0
