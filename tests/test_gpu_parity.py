@@ -925,3 +925,28 @@ def test_seeded_sweep_of_shapes(case):
     for b in range(w.bs):  # an empty context gives exactly zero
         if ctx[b] == 0:
             assert torch.count_nonzero(buf.cross_out[0][int(rows[b]):int(rows[b + 1])]) == 0
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_seeded_sweep_of_writes(case):
+    # Seeded draws of the write's shape: request count and commits (so the
+    # live rows end anywhere inside a 256-row tile and its 64-row waves),
+    # layers, heads, d_in and pool type; then the step's attention on the
+    # written pool.
+    rng = np.random.default_rng(700 + case)
+    bs = int(rng.integers(1, 40))
+    L = int(rng.integers(1, 4))
+    H = int(rng.choice([1, 2, 3, 4]))
+    d_in = int(rng.choice([64, 192, 256, 512]))
+    fp8 = bool(rng.integers(2))
+    log(f"write sweep {case}: bs {bs} L {L} H {H} d_in {d_in} e4m3 {fp8}")
+    w = make_workload(5, weights="random", kv_fp8=fp8, seed=1700 + case,
+                      scale_down=dict(bs=bs, ctx=(20, 400), L=L, H=H, d_in=d_in))
+    buf = S.allocate(w)
+    before = _snapshot(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    slots, keys, values = _write_oracle(w)
+    log(f"  live rows {int((slots >= 0).sum())} of {slots.shape[0]}")
+    _check_write(w, buf, before, slots, keys, values)
+    _check_full_step_attention(w, buf, before, slots, keys, values, list(range(w.bs)))
