@@ -599,6 +599,19 @@ def test_prefill_in_chunks():
 @pytest.mark.parametrize("M,K,N", [(300, 512, 2048), (1024, 1024, 16384), (37, 4096, 1024), (1, 64, 1024),
                                    (257, 512, 1024)])
 def test_linear_epilogues(M, K, N):
+    _check_linear(M, K, N)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_linear_seeded_shapes(case):
+    # Seeded shapes: any row count (partial last tiles, waves of padding rows),
+    # contractions that split into ranges or not, and widths 1024..4096 (the
+    # entry point takes N in multiples of 1024).
+    rng = np.random.default_rng(300 + case)
+    _check_linear(int(rng.integers(1, 700)), 64 * int(rng.integers(1, 33)), 1024 * int(rng.integers(1, 5)))
+
+
+def _check_linear(M, K, N):
     log(f"fm_linear M={M} K={K} N={N} (ranges: {B.fm_linear_workspace_size(M, N, K) > 0})")
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
