@@ -51,3 +51,17 @@ def test_traffic_record_is_per_workload(tmp_path, monkeypatch):
     rec["sources_sha256"] = "0" * 64
     json.dump({"records": {key: rec}}, open(tmp_path / "t.json", "w"))
     assert bench.measured_traffic(key) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # The path runs on one GPU: --gpus above 1 ends with a message and status 2,
+    # before torch or the GPU is touched.
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["requested_gpus"] == 2 and "one GPU" in line["error"]
