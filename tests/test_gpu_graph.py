@@ -105,3 +105,45 @@ def test_graph_replay_matches_eager(case):
             assert torch.equal(_bits(got), _bits(want)), f"replay {replay}: output {i} differs from the eager step"
         assert ws_error_word(buf.cross_ws) == 0
     del graph
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_graph_replay_reads_new_inputs(kv_fp8):
+    # A serving loop captures once and updates the inputs in place: new query
+    # rows and shorter context lengths (the plan is rebuilt on the device from
+    # the lengths at every replay).  Each replay must equal an eager step on
+    # the same inputs, bit for bit.
+    log(f"graph replay over inputs updated in place (e4m3 pool: {kv_fp8})")
+    w = make_workload(5, weights="random", scale_down=SMALL, kv_fp8=kv_fp8)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        S.run_step(w, buf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        S.run_step(w, buf)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda")
+    for replay in range(3):
+        gen.manual_seed(40 + replay)
+        for q in w.q:
+            q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype))
+        shrink = torch.randint(0, 9, w.ctx_lens.shape, generator=gen, device="cuda", dtype=torch.int32)
+        w.ctx_lens.copy_(torch.clamp(w.ctx_lens - shrink, min=0))
+        torch.cuda.synchronize()
+        S.run_step(w, buf)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in buf.cross_out]
+        for t in buf.cross_out:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for l, (got, want) in enumerate(zip(buf.cross_out, ref)):
+            assert torch.equal(_bits(got), _bits(want)), f"replay {replay}: layer {l} differs from the eager step"
+        assert ws_error_word(buf.cross_ws) == 0
+    del graph
