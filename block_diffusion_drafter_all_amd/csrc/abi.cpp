@@ -361,6 +361,8 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
   a.ctx_lens = ctx_lens;
   a.bs = bs;
   a.H = H;
+  a.Dh = Dh;
+  a.dtype = (int32_t)dt;
   a.ws = static_cast<uint8_t*>(ws);
   a.lay = lay;
   return from_hip(fm::launch_plan(a, stream), fn);
@@ -436,12 +438,13 @@ int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int3
   if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
   if (dt == FM_BF16_E4M3)
     return fail(FM_E_UNSUPPORTED, "%s: the block's own q, k, v are activations: use FM_BF16", fn);
-  if (K < 1 || K > 16) return fail(FM_E_UNSUPPORTED, "%s: block size %d not in [1, 16]", fn, K);
+  if (K < 1 || K > 64) return fail(FM_E_UNSUPPORTED, "%s: block size %d not in [1, 64]", fn, K);
   if (!qkv || !q_norm_w || !k_norm_w || !ctx_lens || !out)
     return fail(FM_E_INVALID, "%s: a required pointer is null", fn);
   if (!aligned16(qkv) || !aligned16(out)) return fail(FM_E_INVALID, "%s: qkv and out must be 16-byte aligned", fn);
   if (!std::isfinite(softmax_scale)) return fail(FM_E_INVALID, "%s: softmax_scale must be finite", fn);
-  if ((int64_t)n_blocks * H > INT32_MAX) return fail(FM_E_UNSUPPORTED, "%s: n_blocks * H too large", fn);
+  if ((int64_t)n_blocks * H * ((K + 15) / 16) > INT32_MAX)
+    return fail(FM_E_UNSUPPORTED, "%s: n_blocks * H * query tiles too large", fn);
   fm::SelfArgs a{};
   a.qkv = qkv;
   a.out = out;

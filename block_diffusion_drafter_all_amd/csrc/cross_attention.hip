@@ -183,7 +183,25 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     hdr->H = a.H;
     hdr->nqf = a.lay.nqf;
     hdr->total_tiles = G;
+    hdr->Dh = a.Dh;
+    hdr->dtype = a.dtype;
   }
+}
+
+// Pool type code of a kernel instantiation (the fm_dtype value of the call).
+template <class T, class PT>
+__device__ constexpr int pool_type_code() {
+  return std::is_same<PT, E4m3>::value ? 2 : (std::is_same<T, Bf16>::value ? 1 : 0);
+}
+
+// Whether the plan in the workspace was made for this call's sizes and pool
+// type.  The layout past the header depends on all of them, so a call with any
+// other value must neither read the plan's records nor write its own queries
+// over them.
+template <class T, class PT, int D, int NQF>
+__device__ __forceinline__ bool plan_matches(const PlanHeader& ph, const CrossArgs& a) {
+  return (ph.magic == kPlanMagic) & (ph.bs == a.bs) & (ph.H == a.H) & (ph.n_waves == a.lay.n_waves) &
+         (ph.nqf == NQF) & (ph.Dh == D) & (ph.dtype == pool_type_code<T, PT>());
 }
 
 // ----------------------------------------------------------- query rows --
@@ -211,6 +229,8 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   const int ctx0 = max(0, a.ctx_lens[b]);
   const int r0 = max(0, a.cu_q[b]);
   const int nq = max(0, min(min(a.cu_q[b + 1], a.total_q) - r0, kQRows * NQF));
+  // A plan for other sizes keeps its records: no query row is written over them.
+  const bool plan_ok = plan_matches<T, PT, D, NQF>(*(const PlanHeader*)a.ws, a);
   if constexpr (std::is_same<PT, E4m3>::value) {
     if (ctx0 == 0) {  // empty context: the output rows are zero
 #pragma unroll
@@ -224,6 +244,7 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
       }
       return;
     }
+    if (!plan_ok) return;
     float qf[NQF][D / 4];
     float amax = 0.f;
 #pragma unroll
@@ -279,6 +300,7 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
       }
       continue;
     }
+    if (!plan_ok) continue;
     float qf[D / 4];
     const st* qrow = (const st*)a.q + ((int64_t)(has ? r0 + k : 0) * a.H + h) * D;
 #pragma unroll
@@ -441,8 +463,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   // together and a mismatched plan simply leaves the wave no tiles.)
   const PlanHeader ph = *(const PlanHeader*)hdr;
   const WaveRec rec = ((const WaveRec*)(ws + a.lay.wave_rec))[w];
-  const bool plan_ok =
-      (ph.magic == kPlanMagic) & (ph.bs == a.bs) & (ph.H == a.H) & (ph.n_waves == a.lay.n_waves) & (ph.nqf == NQF);
+  const bool plan_ok = plan_matches<T, PT, D, NQF>(ph, a);
   if (!plan_ok) {  // no plan for these sizes: nothing is computed, and the error word says so
     if (w == 0 && lane_id() == 0) atomicOr(&hdr->error, 4);
     return;

@@ -76,6 +76,8 @@ struct PlanHeader {
   int32_t H;
   int32_t nqf;        // query fragments per request
   int64_t total_tiles;
+  int32_t Dh;         // head dim: the workspace layout past the header depends on it
+  int32_t dtype;      // pool type (0 fp32, 1 bf16, 2 e4m3) the plan was cut for
 };
 
 // One wave's range: it starts at tile ``k`` of pair (b, h), which is tile
@@ -128,6 +130,7 @@ inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves, int nqf) {
 struct PlanArgs {
   const int32_t* ctx_lens;
   int32_t bs, H;
+  int32_t Dh, dtype;  // recorded in the header: a call checks them against its own
   uint8_t* ws;
   PlanLayout lay;
 };

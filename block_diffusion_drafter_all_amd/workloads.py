@@ -169,9 +169,9 @@ def _norm_weights(L, Dh, gen, device, kind):
     return [1.0 + 0.1 * torch.randn(Dh, generator=gen, device=device) for _ in range(L)]
 
 
-def _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K, q_scale=1.0):
+def _attention_inputs(bs, L, H, Dh, dtype, device, gen, cu_q, K):
     total_q = int(cu_q[-1].item())
-    q = [_randn((total_q, H, Dh), gen, dtype, device, std=q_scale) for _ in range(L)]
+    q = [_randn((total_q, H, Dh), gen, dtype, device) for _ in range(L)]
     qkv = [_randn((bs, K, 3, H, Dh), gen, dtype, device) for _ in range(L)]
     return q, qkv
 
@@ -190,8 +190,11 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
        c ~ U{1..17} verify columns at p-c .. p-1 plus its anchor at p; one GEMM
        from 4096 to 5 x 2 x 32 x 128 (W ~ N(0, 0.02^2)), then 5 layers.
 
-    ``scale_down`` (dict) overrides bs / length bounds for small parity runs;
-    ``q_scale`` multiplies the queries (a "peaky" softmax variant).
+    ``scale_down`` (dict) overrides bs / length bounds for small parity runs
+    (and, for workloads 2 and 3, the activation and pool type: ``dtype``);
+    ``q_scale`` multiplies the cross-attention query norm weight (a "peaky"
+    softmax variant: the norm would cancel a scale on the raw queries, so the
+    weight carries it and the scores' spread grows by that factor).
     ``n_cand`` candidate blocks per request (tree drafting): each request's
     cross-attention query holds ``n_cand * K`` rows, candidate-major, and the
     self-attention runs over ``bs * n_cand`` blocks.
@@ -226,7 +229,7 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
         bs = sd.get("bs", 8 if workload_id == 2 else 64)
         lo, hi = sd.get("ctx", (512, 2048) if workload_id == 2 else (1024, 8192))
         L = sd.get("L", 1 if workload_id == 2 else 5)
-        H, Dh, ps, dtype = sd.get("H", 32), sd.get("Dh", 128), sd.get("ps", 16), torch.bfloat16
+        H, Dh, ps, dtype = sd.get("H", 32), sd.get("Dh", 128), sd.get("ps", 16), sd.get("dtype", torch.bfloat16)
         ctx = torch.randint(lo, hi + 1, (bs,), generator=gen, device=device, dtype=torch.int32)
         if "ctx_list" in sd:                 # explicit lengths (edge cases)
             ctx = torch.tensor(sd["ctx_list"], dtype=torch.int32, device=device)
@@ -279,7 +282,7 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
     pool_dtype = torch.float8_e4m3fn if kv_fp8 else dtype
     pools = [_pool_tensors(n_pages, ps, H, Dh, pool_dtype, device, gen, layout) for _ in range(L)]
     cu_q = torch.arange(0, (bs + 1) * K * n_cand, K * n_cand, dtype=torch.int32, device=device)
-    q, qkv = _attention_inputs(bs * n_cand, L, H, Dh, dtype, device, gen, cu_q, K, q_scale)
+    q, qkv = _attention_inputs(bs * n_cand, L, H, Dh, dtype, device, gen, cu_q, K)
 
     if workload_id == 1:
         # the write fills the whole context 0..63: x = [k | v] with W = I
@@ -336,7 +339,7 @@ def make_workload(workload_id: int, device="cuda", weights="ones", layout="head_
                                w_xe=_randn((dim, d_target), gen, dtype, device, std=0.02),
                                b_xe=_randn((dim,), gen, dtype, device, std=0.1), layers=lw, mods=mods,
                                final_scale=mvec("scale"), final_shift=mvec("shift"))
-    q_norm_w = _norm_weights(L, Dh, gen, device, weights)
+    q_norm_w = [w * q_scale for w in _norm_weights(L, Dh, gen, device, weights)]
     self_q = _norm_weights(L, Dh, gen, device, weights)
     self_k = _norm_weights(L, Dh, gen, device, weights)
     if write is not None:

@@ -296,9 +296,10 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
  * page_table  DEVICE int32 [bs, pt_stride].
  * ctx_lens, bs, H  as given to fm_plan_cross_attention, whose plan ``ws``
  *             must hold (same stream, earlier; lengths unchanged since).  A
- *             plan made for other shapes or another pool type computes
- *             nothing (only the zero rows of empty contexts are written) and
- *             sets bit 2 of the error word.  If the
+ *             plan made for another bs, H, Dh, max_q fragment count or pool
+ *             type (the plan header records each) computes nothing: only the
+ *             zero rows of empty contexts are written, the plan's records are
+ *             left as they were, and bit 2 of the error word is set.  If the
  *             lengths changed after the plan, the outputs are unspecified, no
  *             access leaves the buffers, and bit 1 of the error word is set
  *             when a wave's share runs past the last tile (not every change
@@ -333,7 +334,8 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
  * q_norm_w, k_norm_w  DEVICE fp32 [Dh].
  * ctx_lens  DEVICE int32 [n_blocks].
  * out   DEVICE [n_blocks, K, H, Dh] contiguous, dtype dt.
- * 1 <= K <= 16; Dh in {64, 128}.
+ * 1 <= K <= 64 (a draft block is 16 slots; larger blocks run one wavefront
+ * per 16-slot query tile, each scoring all K keys); Dh in {64, 128}.
  */
 int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int32_t K,
                             const float* q_norm_w, const float* k_norm_w, const int32_t* ctx_lens,

@@ -166,7 +166,8 @@ def test_write_zero_rows_is_noop(lib):
 
 def test_self_attention_rejects(lib):
     f = lib.fm_block_self_attention
-    assert f(FAKE, B.FM_BF16, 4, 17, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
+    assert f(FAKE, B.FM_BF16, 4, 65, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
+    assert "block size 65" in B.fm_last_error()
     assert f(FAKE, B.FM_BF16, 4, 0, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
     assert f(None, B.FM_BF16, 4, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_INVALID
     assert f(None, B.FM_BF16, 0, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_OK
@@ -189,6 +190,12 @@ def test_launch_grid_limit(lib):
     assert lib.fm_block_self_attention(FAKE, B.FM_BF16, 1 << 25, 16, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE,
                                        None) == B.FM_E_UNSUPPORTED
     assert "2^32" in B.fm_last_error()
+    # blocks of 32 and 64 slots pass the size checks (one wave per 16-slot query
+    # tile): 2^24 blocks x 4 heads x 2 or 4 tiles reach the grid limit instead
+    for K in (32, 64):
+        assert lib.fm_block_self_attention(FAKE, B.FM_BF16, 1 << 24, K, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6,
+                                           FAKE, None) == B.FM_E_UNSUPPORTED
+        assert "2^32" in B.fm_last_error()
     # the largest sizes the checks still pass are well inside the limit
     assert lib.fm_linear_workspace_size(1 << 24, 1 << 20, 512) == 0
 

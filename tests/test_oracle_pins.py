@@ -68,6 +68,34 @@ def test_rope_identity_norm_and_pair_locality(rng):
         assert set(np.nonzero(changed)[0]) == {2 * i, 2 * i + 1}
 
 
+def test_rope_angle_is_one_float32_product(rng):
+    # The angle is the float32 product rope_tables forms (modeling_flashmap.py:
+    # positions.float() * inv_freq): torch's own float32 multiply of the
+    # positions and the inverse frequencies gives the same bits, at every
+    # position up to the long request's last draft slot (131072 + 16).  The
+    # rotation uses exactly that angle: at positions past 2^17 a rotation by the
+    # exact float64 angle pos * theta^(-2i/D) differs from it by far more than
+    # float64 rounding, so an oracle that formed the angle in float64 fails here.
+    d, theta = 128, 1e6
+    inv = O.rope_inv_freq(d, theta)
+    pos = np.arange(0, 131072 + 17)
+    want = torch.arange(0, 131072 + 17).float()[:, None] * torch.from_numpy(inv)[None, :]
+    got = O.rope_angles(pos, inv)
+    assert got.dtype == np.float32
+    np.testing.assert_array_equal(got.view(np.uint32), want.numpy().view(np.uint32))
+
+    far = np.array([131072, 131075, 131087, 131088])
+    x = rng.standard_normal((len(far), d))
+    ang32 = (torch.from_numpy(far).float()[:, None] * torch.from_numpy(inv)[None, :]).double().numpy()
+    z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * ang32)
+    y = O.apply_rope(x, far, theta)
+    np.testing.assert_allclose(y[:, 0::2], z.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y[:, 1::2], z.imag, rtol=0, atol=1e-12)
+    ang64 = far[:, None].astype(np.float64) * np.array([theta ** (-2.0 * i / d) for i in range(d // 2)])[None, :]
+    z64 = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * ang64)
+    assert np.max(np.abs(y[:, 0::2] - z64.real)) > 1e-4, "the angle must carry float32 rounding"
+
+
 def test_rope_relative_position(rng):
     # <R_m q, R_n k> depends only on m - n (up to the float32 rounding of angles).
     d, theta = 64, 1e6
