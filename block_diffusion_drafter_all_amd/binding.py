@@ -34,6 +34,7 @@ SYMBOLS = (
     "fm_version",
     "fm_write_context_kv_workspace_size",
     "fm_write_context_kv",
+    "fm_write_context_kv_noalloc",
     "fm_context_rows_workspace_size",
     "fm_context_rows",
     "fm_ada_layer_norm",
@@ -87,6 +88,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_write_context_kv.argtypes = [
         vp, c_i64, c_i32, ctypes.c_int, vp, vp, vp, vp, vp, c_i32, vp, c_i64, c_i32, c_i32,
         ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp,
+    ]
+    lib.fm_write_context_kv_noalloc.restype = ctypes.c_int
+    lib.fm_write_context_kv_noalloc.argtypes = [
+        vp, c_i64, c_i32, ctypes.c_int, vp, vp, vp, vp, vp, c_i32, vp, c_i64, c_i32, c_i32,
+        ctypes.POINTER(fm_kv_pool), c_i32, c_i32, c_i32, f32, f32, ctypes.POINTER(f32), vp, vp,
     ]
     lib.fm_context_rows_workspace_size.restype = c_sz
     lib.fm_context_rows_workspace_size.argtypes = [c_i64, c_i64, c_i32, c_i32, c_i32]
@@ -206,13 +212,12 @@ def _floats(values):
     return (ctypes.c_float * len(flat))(*flat)
 
 
-def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta,
-                        commit_lens=None, window=0, out_slots=None, ws=None, kv_scales=None):
-    """Project, k-norm, rotate and scatter every layer's context K/V rows into
-    ``pools`` (a list of KVPool, one per layer).  Returns ``out_slots`` if given.
-    ``kv_scales``: e4m3 pools only, one (k_scale, v_scale) per layer (the pool
-    receives k / k_scale and v / v_scale); None = 1."""
-    lib = load_library()
+FM_WRITE_NOALLOC_MAX_ROWS = 65536
+
+
+def _write_args(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta, commit_lens, window,
+                out_slots, kv_scales):
+    """Checked C-ABI arguments of the write, up to out_slots."""
     _need(x, "x")
     _need(w_kv, "w_kv", x.dtype)
     _need(k_norm_w, "k_norm_w", torch.float32)
@@ -239,15 +244,36 @@ def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, 
         raise ValueError("kv_scales needs one (k_scale, v_scale) pair per layer")
     code = _dtype_code(x, pools[0].k.dtype)
     n_rows, d_in = x.shape
+    return (_ptr(x), n_rows, d_in, code, _ptr(w_kv), _ptr(k_norm_w), _ptr(row_req), _ptr(row_pos),
+            _ptr(commit_lens), window, _ptr(page_table), page_table.stride(0), pools[0].page_size,
+            page_table.shape[0], descs, L, H, Dh, eps, rope_theta, _floats(kv_scales), _ptr(out_slots))
+
+
+def fm_write_context_kv(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta,
+                        commit_lens=None, window=0, out_slots=None, ws=None, kv_scales=None):
+    """Project, k-norm, rotate and scatter every layer's context K/V rows into
+    ``pools`` (a list of KVPool, one per layer).  Returns ``out_slots`` if given.
+    ``kv_scales``: e4m3 pools only, one (k_scale, v_scale) per layer (the pool
+    receives k / k_scale and v / v_scale); None = 1."""
+    lib = load_library()
+    args = _write_args(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta, commit_lens,
+                       window, out_slots, kv_scales)
     if ws is not None:
         _need(ws, "ws", torch.uint8)
     if ws is None:
-        ws = torch.empty(lib.fm_write_context_kv_workspace_size(n_rows), dtype=torch.uint8, device=x.device)
-    _check(lib.fm_write_context_kv(
-        _ptr(x), n_rows, d_in, code, _ptr(w_kv), _ptr(k_norm_w), _ptr(row_req), _ptr(row_pos),
-        _ptr(commit_lens), window, _ptr(page_table), page_table.stride(0), pools[0].page_size,
-        page_table.shape[0], descs, L, H, Dh, eps, rope_theta, _floats(kv_scales), _ptr(out_slots), _ptr(ws),
-        ws.numel(), _stream()))
+        ws = torch.empty(lib.fm_write_context_kv_workspace_size(x.shape[0]), dtype=torch.uint8, device=x.device)
+    _check(lib.fm_write_context_kv(*args, _ptr(ws), ws.numel(), _stream()))
+    return out_slots
+
+
+def fm_write_context_kv_noalloc(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta,
+                                commit_lens=None, window=0, out_slots=None, kv_scales=None):
+    """fm_write_context_kv with the library's static per-GPU workspace (at most
+    FM_WRITE_NOALLOC_MAX_ROWS rows; calls on one GPU must not overlap)."""
+    lib = load_library()
+    args = _write_args(x, w_kv, k_norm_w, row_req, row_pos, page_table, pools, eps, rope_theta, commit_lens,
+                       window, out_slots, kv_scales)
+    _check(lib.fm_write_context_kv_noalloc(*args, _stream()))
     return out_slots
 
 

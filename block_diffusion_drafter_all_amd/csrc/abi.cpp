@@ -137,14 +137,22 @@ const char* fm_version(void) { return "fm 0.1.0 (gfx950)"; }
 
 size_t fm_write_context_kv_workspace_size(int64_t n_rows) { return fm::write_layout(n_rows).total; }
 
-int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt, const void* w_kv,
-                        const float* k_norm_w, const int32_t* row_req, const int32_t* row_pos,
-                        const int32_t* commit_lens, int32_t window, const int32_t* page_table, int64_t pt_stride,
-                        int32_t page_size, int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
-                        float eps, float rope_theta, const float* kv_scales, int32_t* out_slots, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "fm_write_context_kv";
+}  // extern "C"
+
+namespace {
+
+// The write of fm_write_context_kv and fm_write_context_kv_noalloc: with
+// ``use_scratch`` the workspace is the static per-device array (ws ignored).
+int write_context_kv(const char* fn, bool use_scratch, const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt,
+                     const void* w_kv, const float* k_norm_w, const int32_t* row_req, const int32_t* row_pos,
+                     const int32_t* commit_lens, int32_t window, const int32_t* page_table, int64_t pt_stride,
+                     int32_t page_size, int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
+                     float eps, float rope_theta, const float* kv_scales, int32_t* out_slots, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
   if (n_rows < 0) return fail(FM_E_INVALID, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (use_scratch && n_rows > fm::kWriteScratchRows)
+    return fail(FM_E_UNSUPPORTED, "%s: n_rows %lld above the %lld rows its static workspace serves", fn,
+                (long long)n_rows, (long long)fm::kWriteScratchRows);
   if (n_rows == 0) return ok();
   if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
   if (!x || !w_kv || !k_norm_w || !row_req || !row_pos || !page_table || !pools)
@@ -172,6 +180,15 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
     for (int i = 0; i < 2 * L; ++i)
       if (!(kv_scales[i] > 0.f) || !std::isfinite(kv_scales[i]) || !std::isfinite(1.0 / kv_scales[i]))
         return fail(FM_E_INVALID, "%s: kv_scales[%d] must be finite and > 0", fn, i);
+  }
+  if (use_scratch) {
+    uint8_t* sp = nullptr;
+    size_t sb = 0;
+    const hipError_t e = fm::write_scratch(&sp, &sb);
+    if (e != hipSuccess)
+      return fail(FM_E_HIP, "%s: no device address for the static workspace: %s", fn, hipGetErrorString(e));
+    ws = sp;
+    ws_bytes = sb;
   }
   if (int s = check_ws(fn, ws, ws_bytes, fm::write_layout(n_rows).total)) return s;
 
@@ -206,6 +223,34 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
   }
   g.rope = rope_freqs(rope_theta, Dh);
   return from_hip(fm::launch_write(p, g, (int)dt, Dh, n_rows, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt, const void* w_kv,
+                        const float* k_norm_w, const int32_t* row_req, const int32_t* row_pos,
+                        const int32_t* commit_lens, int32_t window, const int32_t* page_table, int64_t pt_stride,
+                        int32_t page_size, int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
+                        float eps, float rope_theta, const float* kv_scales, int32_t* out_slots, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  return write_context_kv("fm_write_context_kv", false, x, n_rows, d_in, dt, w_kv, k_norm_w, row_req, row_pos,
+                          commit_lens, window, page_table, pt_stride, page_size, bs, pools, L, H, Dh, eps,
+                          rope_theta, kv_scales, out_slots, ws, ws_bytes, stream);
+}
+
+static_assert(FM_WRITE_NOALLOC_MAX_ROWS == fm::kWriteScratchRows, "fm.h states the static workspace's row limit");
+
+int fm_write_context_kv_noalloc(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt, const void* w_kv,
+                                const float* k_norm_w, const int32_t* row_req, const int32_t* row_pos,
+                                const int32_t* commit_lens, int32_t window, const int32_t* page_table,
+                                int64_t pt_stride, int32_t page_size, int32_t bs, const fm_kv_pool* pools, int32_t L,
+                                int32_t H, int32_t Dh, float eps, float rope_theta, const float* kv_scales,
+                                int32_t* out_slots, hipStream_t stream) {
+  return write_context_kv("fm_write_context_kv_noalloc", true, x, n_rows, d_in, dt, w_kv, k_norm_w, row_req,
+                          row_pos, commit_lens, window, page_table, pt_stride, page_size, bs, pools, L, H, Dh, eps,
+                          rope_theta, kv_scales, out_slots, nullptr, 0, stream);
 }
 
 size_t fm_context_rows_workspace_size(int64_t n_hidden, int64_t n_anchor, int32_t d_hidden, int32_t d_target,

@@ -46,7 +46,7 @@ inline bool grid_fits(int64_t workgroups, int threads) {
   return workgroups >= 0 && workgroups <= (((int64_t)1 << 32) - 1) / threads;
 }
 
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------ pool descriptor
 
@@ -182,8 +182,8 @@ struct WriteLayout {
   size_t live_row, live_pos, live_page, live_off, total;
 };
 
-inline WriteLayout write_layout(int64_t n_rows) {
-  WriteLayout w;
+constexpr WriteLayout write_layout(int64_t n_rows) {
+  WriteLayout w{};
   size_t off = 256;
   size_t n = (size_t)(n_rows > 0 ? n_rows : 0);
   w.live_row = off;  off = align256(off + n * 4);
@@ -193,6 +193,16 @@ inline WriteLayout write_layout(int64_t n_rows) {
   w.total = off;
   return w;
 }
+
+// Rows the no-allocation write (fm_write_context_kv_noalloc) serves: its
+// workspace is a static device array of write_layout(kWriteScratchRows).total
+// bytes (about 1 MB), one copy per GPU.
+constexpr int64_t kWriteScratchRows = 65536;
+constexpr size_t kWriteScratchBytes = write_layout(kWriteScratchRows).total;
+
+// Device address of the current device's copy of that array (looked up once
+// per device, then cached); ``bytes`` receives its size.
+hipError_t write_scratch(uint8_t** ptr, size_t* bytes);
 
 struct WritePrepArgs {
   const int32_t* row_req;

@@ -14,7 +14,15 @@
 //      e4m3 pool is written with scale 1: sglang/model.py ``_kv_write`` with
 //      ``kv_norm_rope_write_fp8``).
 
+#include <mutex>
+
 #include "gemm_core.h"
+
+// Workspace of the no-allocation write: one static array per GPU, held until
+// the process ends.  Host code must not pass this name to a kernel (on the
+// host it is a stand-in, not a device address): fm::write_scratch looks up
+// each device's address once and every launch takes that address.
+static __device__ __align__(256) uint8_t scratch[fm::kWriteScratchBytes];
 
 namespace fm {
 
@@ -281,6 +289,26 @@ hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, in
 }
 
 }  // namespace
+
+hipError_t write_scratch(uint8_t** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // with this device current: its own copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<uint8_t*>(p);
+  }
+  *ptr = addr[dev];
+  *bytes = kWriteScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t launch_write(const WritePrepArgs& p, const WriteGemmArgs& g, int dtype, int Dh, int64_t n_rows,
                         hipStream_t s) {

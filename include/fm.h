@@ -147,6 +147,33 @@ int fm_write_context_kv(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt
                         float eps, float rope_theta, const float* kv_scales, int32_t* out_slots,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Rows fm_write_context_kv_noalloc serves (its static workspace's size). */
+#define FM_WRITE_NOALLOC_MAX_ROWS 65536
+
+/*
+ * fm_write_context_kv without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, computation and results
+ * as fm_write_context_kv (the same kernels); the workspace is instead a static
+ * device array of about 1 MB that the library holds on every GPU it runs on
+ * until the process ends.  The entry point allocates and frees nothing.
+ *
+ * n_rows must not exceed FM_WRITE_NOALLOC_MAX_ROWS (FM_E_UNSUPPORTED
+ * otherwise, nothing enqueued).  The array's device address is looked up on a
+ * device's first call (FM_E_HIP if that fails).  Every call on one GPU shares
+ * that GPU's array: calls that may overlap on one GPU (different streams, or
+ * host threads without ordering) race and must be serialized by the caller.
+ * The array needs no initialisation: each call rewrites what it reads.
+ */
+int fm_write_context_kv_noalloc(const void* x, int64_t n_rows, int32_t d_in, fm_dtype dt,
+                                const void* w_kv, const float* k_norm_w,
+                                const int32_t* row_req, const int32_t* row_pos,
+                                const int32_t* commit_lens, int32_t window,
+                                const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                                int32_t bs, const fm_kv_pool* pools, int32_t L, int32_t H, int32_t Dh,
+                                float eps, float rope_theta, const float* kv_scales, int32_t* out_slots,
+                                hipStream_t stream);
+
 /* ------------------------------------------------------- context rows -- */
 
 /* Workspace bytes fm_context_rows needs (0 for invalid sizes or no rows).  A

@@ -164,6 +164,32 @@ def test_write_zero_rows_is_noop(lib):
     assert _write(lib, n_rows=0, x=None) == B.FM_OK
 
 
+def _write_noalloc(lib, **over):
+    pools = (B.fm_kv_pool * 2)(_pool(), _pool())
+    a = dict(x=FAKE, n_rows=8, d_in=512, dt=B.FM_BF16, w=FAKE, kn=FAKE, rr=FAKE, rp=FAKE, cl=None, win=0, pt=FAKE,
+             pt_stride=4, ps=16, bs=1, pools=pools, L=2, H=4, Dh=64, eps=1e-6, theta=1e6, slots=None)
+    a.update(over)
+    return lib.fm_write_context_kv_noalloc(a["x"], a["n_rows"], a["d_in"], a["dt"], a["w"], a["kn"], a["rr"],
+                                           a["rp"], a["cl"], a["win"], a["pt"], a["pt_stride"], a["ps"], a["bs"],
+                                           a["pools"], a["L"], a["H"], a["Dh"], a["eps"], a["theta"], None,
+                                           a["slots"], None)
+
+
+def test_noalloc_write_limits_and_validation(lib):
+    """The no-allocation write refuses more rows than its static workspace
+    serves, and validates like fm_write_context_kv, before any GPU call."""
+    assert B.FM_WRITE_NOALLOC_MAX_ROWS == 65536
+    assert _write_noalloc(lib, n_rows=65537) == B.FM_E_UNSUPPORTED
+    assert "65536 rows its static workspace" in B.fm_last_error()
+    assert _write_noalloc(lib, n_rows=0, x=None) == B.FM_OK
+    assert _write_noalloc(lib, n_rows=-1) == B.FM_E_INVALID
+    assert _write_noalloc(lib, Dh=96) == B.FM_E_UNSUPPORTED
+    assert _write_noalloc(lib, x=None) == B.FM_E_INVALID
+    assert _write_noalloc(lib, L=17) == B.FM_E_UNSUPPORTED
+    # the static workspace covers the write layout of its largest call
+    assert lib.fm_write_context_kv_workspace_size(65536) <= (1 << 20) + 1024
+
+
 def test_self_attention_rejects(lib):
     f = lib.fm_block_self_attention
     assert f(FAKE, B.FM_BF16, 4, 65, FAKE, FAKE, FAKE, 4, 64, 0.1, 1e6, 1e-6, FAKE, None) == B.FM_E_UNSUPPORTED
