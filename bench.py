@@ -82,6 +82,13 @@ def parse():
                          "graph and --steps replays of it give value; the eager pass (first) still gives the "
                          "per-call events of the roofline and is reported under \"eager\"")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the sweep that also times the cross-attention of workloads 2 (warm and with the MALL "
+                         "flushed), 3 and 4 in the same run (reported under \"configs\")")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps of each workload of the sweep (after 3 untimed ones)")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="also time the oracle on a sample of each workload of the sweep")
     ap.add_argument("--cpu-sample-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = 24, about 10-20 s of CPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +192,35 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def host_cpu() -> dict:
+    """The host's processor as lscpu describes it, and the cores this process
+    may run on."""
+    info = {"model_name": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count()}
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        keep = ("Model name", "Vendor ID", "CPU family", "Model", "Stepping", "Socket(s)", "Core(s) per socket",
+                "Thread(s) per core", "CPU(s)", "CPU max MHz")
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in keep:
+                info["lscpu " + k.strip()] = v.strip()
+    except (OSError, ValueError):
+        pass
+    return info
+
+
+def oracle_threads() -> int:
+    """Threads for the oracle's BLAS: every core this process may run on,
+    within the CPU share the environment sets (OMP_NUM_THREADS)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return min(cores, share) if share > 0 else cores
+
+
 def hbm_ceilings() -> dict:
     """Context for the HBM figures: torch's plain 1 GiB device-to-device copy,
     bytes read + written per second, best of 5 after one warm-up."""
@@ -203,6 +239,105 @@ def hbm_ceilings() -> dict:
         torch.cuda.synchronize()
         t.append(e0.elapsed_time(e1))
     return {"torch_copy_GBps": 2 * COPY_BYTES / (min(t) * 1e-3) / 1e9, "copy_bytes": COPY_BYTES}
+
+
+def _probe_lib():
+    import ctypes
+
+    from block_diffusion_drafter_all_amd.build import PROBE_LIB_PATH
+
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise SystemExit(f"{PROBE_LIB_PATH} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.fm_probe_stream_read.restype = ctypes.c_int
+    lib.fm_probe_stream_read.argtypes = [vp, sz, ctypes.c_int32, vp, ctypes.POINTER(sz), vp]
+    lib.fm_probe_tile_gather.restype = ctypes.c_int
+    lib.fm_probe_tile_gather.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    return lib
+
+
+def _best_rate(launch, nbytes: float, reps: int = 5) -> float:
+    """GB/s of the fastest of ``reps`` timed launches (one untimed first)."""
+    import torch
+
+    launch()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return nbytes / (best * 1e-3) / 1e9
+
+
+def tile_offsets(w, layer: int):
+    """Byte offsets (int64, on the device) of the K/V tiles one cross-attention
+    call of ``w`` reads, in the plan's order: (request, head) pairs, then
+    16-token tiles in position order.  None unless a tile is one contiguous run
+    (pages of at least 16 tokens in the head-major layout)."""
+    import torch
+
+    k = w.pools[layer].k
+    s = k.element_size()
+    if w.page_size < 16 or k.stride(1) * s != w.Dh * s:
+        return None
+    page_b, slot_b, head_b = k.stride(0) * s, k.stride(1) * s, k.stride(2) * s
+    pt = w.page_table.to(torch.int64)
+    out = []
+    for b, c in enumerate(w.ctx_lens.cpu().tolist()):
+        n = (c + 15) // 16
+        if n == 0:
+            continue
+        t = torch.arange(n, device=pt.device) * 16
+        base = pt[b, t // w.page_size] * page_b + (t % w.page_size) * slot_b
+        out.append((torch.arange(w.H, device=pt.device)[:, None] * head_b + base[None, :]).reshape(-1))
+    return torch.cat(out)
+
+
+def probe_ceilings(w, n_waves: int) -> dict:
+    """What the memory system delivers on this machine: a streaming read of 4 GiB,
+    and the tiles one cross-attention call of ``w`` reads, gathered in the
+    plan's order over the plan's number of waves with no arithmetic (layer 0's
+    pool).  Both best of 5."""
+    import ctypes
+
+    import torch
+
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    buf = torch.ones((1 << 32) // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(4096 * 64, dtype=torch.int32, device="cuda")
+    nread = ctypes.c_size_t(0)
+
+    def read():
+        if lib.fm_probe_stream_read(buf.data_ptr(), buf.numel() * 4, 2048, sink.data_ptr(), ctypes.byref(nread),
+                                    stream) != 0:
+            raise RuntimeError("fm_probe_stream_read failed")
+
+    read()
+    out["stream_read_GBps"] = _best_rate(read, float(nread.value))
+    out["stream_read_bytes"] = int(nread.value)
+    del buf
+    off = tile_offsets(w, 0)
+    if off is not None:
+        tb = 16 * w.Dh * w.pools[0].k.element_size()
+        pk, pv = w.pools[0].k, w.pools[0].v
+
+        def gather():
+            if lib.fm_probe_tile_gather(pk.data_ptr(), pv.data_ptr(), off.data_ptr(), off.numel(), tb, n_waves,
+                                        sink.data_ptr(), stream) != 0:
+                raise RuntimeError("fm_probe_tile_gather failed")
+
+        out["tile_gather_GBps"] = _best_rate(gather, float(off.numel()) * 2 * tb)
+        out["tile_gather"] = (f"{off.numel()} K/V tile pairs of {tb} B (layer 0's call), {n_waves} waves, "
+                              f"plan order, no arithmetic")
+    return out
 
 
 def copy_calibration() -> None:
@@ -327,7 +462,7 @@ def cpu_baseline(w, n_req: int):
     def host(t):
         return t.detach().to(torch.float64).cpu().numpy()
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = oracle_threads()
     rng = np.random.default_rng(0)
     reqs = sorted(rng.choice(w.bs, size=min(n_req, w.bs), replace=False).tolist())
     ps = w.page_size
@@ -384,7 +519,113 @@ def cpu_baseline(w, n_req: int):
             "sample": (f"{len(reqs)} of {w.bs} requests (ids {reqs}): their write rows and, for all {w.L} layers, "
                        f"their self-attention blocks and cross-attention rows; {dt:.1f} s wall; numpy fp64, "
                        f"BLAS threads {blas}"),
-            "seconds": dt, "cpu_model": cpu_model()}
+            "seconds": dt, "cpu_model": cpu_model(), "host": host_cpu()}
+
+
+def plan_waves(pool_dtype) -> int:
+    """Resident cross-attention waves the plan cuts for (CUs x 4 SIMDs x the
+    pool type's waves per SIMD, at most 4096)."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return min(cus * 4 * (2 if pool_dtype == torch.float8_e4m3fn else 1), 4096)
+
+
+def time_attention(w, steps: int, warmup: int, flush_mall: bool) -> dict:
+    """The attention step of ``w`` (plan, then per layer self- and
+    cross-attention), ``steps`` timed steps with events around every step and
+    every cross-attention call; with ``flush_mall`` a 1 GiB buffer is streamed
+    (untimed, between the events) before each step."""
+    import torch
+
+    from block_diffusion_drafter_all_amd import binding as B
+    from block_diffusion_drafter_all_amd import step as S
+
+    buf = S.allocate(w)
+    flush = torch.zeros((COPY_BYTES // 4,), dtype=torch.float32, device="cuda") if flush_mall else None
+    E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
+
+    def step(ev=None):
+        S.plan(w, buf)
+        for l in range(w.L):
+            B.fm_block_self_attention(w.qkv[l], w.self_q_norm_w[l], w.self_k_norm_w[l], w.block_ctx_lens,
+                                      w.softmax_scale, w.theta, w.eps, out=buf.self_out[l])
+            if ev is not None:
+                ev["cross"][l][0].record()
+            B.fm_paged_cross_attention(w.q[l], w.q_norm_w[l], w.pools[l], w.page_table, w.ctx_lens,
+                                       w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws,
+                                       out=buf.cross_out[l], max_q=w.max_q, fp8_scales=w.fp8_scales(l))
+            if ev is not None:
+                ev["cross"][l][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [dict(step=E(), cross=[E() for _ in range(w.L)]) for _ in range(steps)]
+    for s in range(steps):
+        if flush is not None:
+            flush.add_(1.0)
+        evs[s]["step"][0].record()
+        step(evs[s])
+        evs[s]["step"][1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(e["step"][0].elapsed_time(e["step"][1]) for e in evs)
+    cross_ms = [c[0].elapsed_time(c[1]) for e in evs for c in e["cross"]]
+    first_ms = [e["cross"][0][0].elapsed_time(e["cross"][0][1]) for e in evs]
+    avg_cross = sum(cross_ms) / len(cross_ms)
+    nbytes = cross_bytes(w)
+    rows = w.total_q * w.L
+    mean_step = sum(step_ms) / len(step_ms)
+    res = {"steps": steps, "step_ms_mean": mean_step, "step_ms_p50": step_ms[len(step_ms) // 2],
+           "rows_per_s": rows / (mean_step * 1e-3), "cross_avg_ms": avg_cross,
+           "cross_first_layer_avg_ms": sum(first_ms) / len(first_ms), "bytes_per_launch": nbytes,
+           "mall": "flushed before each step" if flush_mall else "warm (data left by the previous step)"}
+    per_call = avg_cross
+    if not flush_mall:
+        # Calls whose kernels take less than the host needs to launch them leave
+        # launch gaps inside per-call events; calls enqueued back to back give
+        # the device's own time per call (the last layer's call, its plan kept).
+        n = 20
+        e0, e1 = E()
+        e0.record()
+        for _ in range(n):
+            B.fm_paged_cross_attention(w.q[-1], w.q_norm_w[-1], w.pools[-1], w.page_table, w.ctx_lens,
+                                       w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, buf.cross_ws,
+                                       out=buf.cross_out[-1], max_q=w.max_q, fp8_scales=w.fp8_scales(w.L - 1))
+        e1.record()
+        torch.cuda.synchronize()
+        res["cross_back_to_back_ms"] = e0.elapsed_time(e1) / n
+        per_call = min(per_call, res["cross_back_to_back_ms"])
+    res["kv_read_GBps"] = nbytes / (per_call * 1e-3) / 1e9
+    res["frac"] = res["kv_read_GBps"] / HBM_PEAK_GBPS
+    res["frac_basis"] = ("per-call events (each call after a MALL flush)" if flush_mall else
+                         "the shorter of per-call events and back-to-back calls")
+    return res
+
+
+def sweep_configs(args) -> dict:
+    """The cross-attention of workloads 2 (warm and MALL-flushed), 3 and 4,
+    timed in this run with the main workload's pool options."""
+    import torch
+
+    from block_diffusion_drafter_all_amd.workloads import make_workload
+
+    res = {}
+    for name, cid, flush in (("2_warm", 2, False), ("2_flushed", 2, True), ("3", 3, False), ("4", 4, False)):
+        print(f"[bench] timing workload {name}", file=sys.stderr, flush=True)
+        w = make_workload(cid, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8)
+        torch.cuda.synchronize()
+        r = {"workload": describe(w)}
+        r.update(time_attention(w, args.config_steps, 3, flush))
+        key = (f"config={cid},layout={args.layout},candidates={args.candidates},"
+               f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}")
+        r["traffic"] = measured_traffic(key)
+        if args.cpu_configs:
+            r["cpu_baseline"] = cpu_baseline(w, min(w.bs, args.cpu_sample_requests or 24))
+        res[name] = r
+        del w
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -575,10 +816,18 @@ def main():
         out["timing"] = "eager launches"
     props = torch.cuda.get_device_properties(0)
     out["context"] = {"device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
-                      "rocm_hip": torch.version.hip, "torch": torch.__version__, **hbm_ceilings()}
+                      "rocm_hip": torch.version.hip, "torch": torch.__version__, **hbm_ceilings(),
+                      **probe_ceilings(w, plan_waves(w.pool_dtype))}
+    for k in ("stream_read_GBps", "tile_gather_GBps"):
+        if k in out["context"]:
+            out["roofline"]["frac_of_" + k[:-5]] = achieved / out["context"][k]
     if not args.no_cpu_baseline:
         n_req = args.cpu_sample_requests or max(1, min(w.bs, 24))
         out["cpu_baseline"] = cpu_baseline(w, n_req)
+    if not args.no_configs:
+        del w, buf
+        torch.cuda.empty_cache()
+        out["configs"] = sweep_configs(args)
     print(json.dumps(out), flush=True)
 
 

@@ -19,6 +19,9 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_DIR = os.path.join(PKG_DIR, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libfm.so")
 SOURCES = ("abi.cpp", "context_rows.hip", "cross_attention.hip", "dit.hip", "self_attention.hip", "write_kv.hip")
+# The benchmark's memory-system probes (include/fm_probe.h), a library of their own.
+PROBE_LIB_PATH = os.path.join(LIB_DIR, "libfm_probe.so")
+PROBE_SOURCES = ("probe.hip",)
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled: the compiler must not form
@@ -50,22 +53,29 @@ def _compile(hipcc: str, src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source and link libfm.so; returns its path.  Always rebuilds."""
-    hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    extra = list(extra_flags or [])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s, extra), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(hipcc: str, objs: list[str], path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile every source and link libfm.so and libfm_probe.so; returns
+    libfm.so's path.  Always rebuilds."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    extra = list(extra_flags or [])
+    every = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(every)) as ex:
+        objs = dict(zip(every, ex.map(lambda s: _compile(hipcc, s, extra), every)))
+    _link(hipcc, [objs[s] for s in SOURCES], LIB_PATH)
+    _link(hipcc, [objs[s] for s in PROBE_SOURCES], PROBE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
     return LIB_PATH
 
 

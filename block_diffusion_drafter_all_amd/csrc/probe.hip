@@ -1,0 +1,106 @@
+// Memory-system probes for the benchmark (include/fm_probe.h): a streaming
+// read and a gather of exactly the tiles a paged cross-attention call reads.
+// They fold what they read into a sink and compute nothing else.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fm_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4_t* gptr_u32x4;
+
+constexpr int kDepth = 4;       // 8 KB blocks (or tile pairs) in flight per wave
+constexpr int kBlock = 8192;    // bytes of one streaming-read block: eight 1 KB loads
+
+__device__ __forceinline__ u32x4_t ld(const uint8_t* p) { return *(gptr_u32x4)(p); }
+
+__device__ __forceinline__ void finish(uint32_t* sink, int64_t w, int lane, const u32x4_t& acc) {
+  sink[w * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Wave w reads blocks [w * per_wave, (w + 1) * per_wave) of 8 KB.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* buf, int64_t per_wave, uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint8_t* base = buf + w * per_wave * kBlock + lane * 16;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (int64_t i = 0; i < per_wave; i += kDepth) {
+    u32x4_t r[kDepth][8];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int64_t blk = i + d < per_wave ? i + d : per_wave - 1;  // past the share: re-read its last block
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) r[d][ch] = ld(base + blk * kBlock + ch * 1024);
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) acc ^= r[d][ch];
+  }
+  finish(sink, w, lane, acc);
+}
+
+// Wave w reads tiles [n w / W, n (w + 1) / W) of the list, K and V of each.
+__global__ __launch_bounds__(256) void tile_gather_kernel(const uint8_t* k, const uint8_t* v, const int64_t* off,
+                                                          int64_t n_tiles, int chunks, int n_waves, uint32_t* sink) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= n_waves) return;
+  const int64_t t0 = n_tiles * w / n_waves, t1 = n_tiles * (w + 1) / n_waves;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (int64_t t = t0; t < t1; t += kDepth) {
+    u32x4_t r[kDepth][16];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int64_t tt = t + d < t1 ? t + d : t1 - 1;
+      const int64_t o = off[tt];  // wave-uniform
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) {
+        if (ch < chunks) {
+          r[d][ch] = ld(k + o + ch * 1024 + lane * 16);
+          r[d][8 + ch] = ld(v + o + ch * 1024 + lane * 16);
+        } else {
+          r[d][ch] = r[d][8 + ch] = (u32x4_t){0u, 0u, 0u, 0u};
+        }
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+      for (int ch = 0; ch < 16; ++ch) acc ^= r[d][ch];
+  }
+  finish(sink, w, lane, acc);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
+
+}  // namespace
+
+extern "C" {
+
+int fm_probe_stream_read(const void* buf, size_t bytes, int32_t n_waves, uint32_t* sink, size_t* bytes_read,
+                         hipStream_t stream) {
+  if (!buf || !sink || !bytes_read || n_waves < 4 || n_waves % 4 || ((uintptr_t)buf & 15)) return -1;
+  const int64_t per_wave = (int64_t)(bytes / (size_t)n_waves / kBlock);
+  if (per_wave < 1) return -1;
+  *bytes_read = (size_t)per_wave * kBlock * (size_t)n_waves;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)(n_waves / 4)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(buf), per_wave, sink);
+  return status_of(hipGetLastError());
+}
+
+int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles, int32_t tile_bytes,
+                         int32_t n_waves, uint32_t* sink, hipStream_t stream) {
+  if (!k || !v || !tile_off || !sink || n_tiles < 1 || n_waves < 4 || n_waves % 4) return -1;
+  if (tile_bytes < 1024 || tile_bytes > 8192 || tile_bytes % 1024) return -2;
+  if (((uintptr_t)k & 15) || ((uintptr_t)v & 15)) return -1;
+  hipLaunchKernelGGL(tile_gather_kernel, dim3((unsigned)(n_waves / 4)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), tile_off, n_tiles,
+                     tile_bytes / 1024, n_waves, sink);
+  return status_of(hipGetLastError());
+}
+
+}  // extern "C"

@@ -335,3 +335,26 @@ def test_binding_refuses_host_tensors(lib):
             call()
     with pytest.raises(ValueError, match="pool k must be a GPU tensor"):
         pool.descriptor()
+
+
+def test_probe_library_exports_and_validation():
+    """The benchmark's probe library exports what include/fm_probe.h declares
+    and refuses bad arguments before launching anything."""
+    from block_diffusion_drafter_all_amd.build import PROBE_LIB_PATH
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(REPO_DIR, "include", "fm_probe.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(fm_probe_[a-z_0-9]+)\s*\(", text)))
+    assert declared == ["fm_probe_stream_read", "fm_probe_tile_gather"]
+    plib = ctypes.CDLL(PROBE_LIB_PATH)
+    for name in declared:
+        assert hasattr(plib, name), name
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    plib.fm_probe_stream_read.argtypes = [vp, sz, ctypes.c_int32, vp, ctypes.POINTER(sz), vp]
+    plib.fm_probe_tile_gather.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    n = ctypes.c_size_t(0)
+    assert plib.fm_probe_stream_read(FAKE, 1 << 20, 6, FAKE, ctypes.byref(n), None) == -1      # waves not 4k
+    assert plib.fm_probe_stream_read(FAKE, 4096, 4, FAKE, ctypes.byref(n), None) == -1         # under one block each
+    assert plib.fm_probe_stream_read(None, 1 << 30, 4, FAKE, ctypes.byref(n), None) == -1
+    assert plib.fm_probe_tile_gather(FAKE, FAKE, FAKE, 10, 3000, 8, FAKE, None) == -2          # tile not k KB
+    assert plib.fm_probe_tile_gather(FAKE, FAKE, FAKE, 0, 4096, 8, FAKE, None) == -1           # no tiles
+    assert plib.fm_probe_tile_gather(FAKE, FAKE + 8, FAKE, 10, 4096, 8, FAKE, None) == -1      # misaligned
