@@ -730,11 +730,14 @@ def _oracle_dit_layer(w, buf, l, h_in, reqs):
 
 
 def _compare_stream(gpu, ref, what):
-    """The fp32 residual stream against the oracle, at the same fixed bar as
-    every other floating output."""
-    s = float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2)))
+    """The fp32 residual stream against the oracle.  Every operand a
+    projection takes is rounded once to bf16 (relative error up to 2^-9), and
+    fc2 contracts 16384 such GELU outputs, so the stream's error scales with
+    the magnitude of the values carried: the bar is the bf16 bar times the
+    stream's RMS (at least 1)."""
+    s = max(1.0, float(np.sqrt(np.mean(np.asarray(ref, dtype=np.float64) ** 2))))
     log(f"  {what}: stream RMS {s:.2f}")
-    compare(gpu, ref, what)
+    compare(gpu, ref, what, max_abs=2e-2 * s, mean_abs=2e-3 * s)
 
 
 def _run_dit_stagewise(w, buf):
