@@ -83,8 +83,8 @@ def parse():
                          "per-call events of the roofline and is reported under \"eager\"")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the sweep that also times the cross-attention of workloads 2 (warm and with the MALL "
-                         "flushed), 3 and 4 in the same run (reported under \"configs\")")
+                    help="skip the sweep that also times the cross-attention of workloads 1, 2 (warm and with the "
+                         "MALL flushed), 3 and 4 in the same run (reported under \"configs\")")
     ap.add_argument("--config-steps", type=int, default=10,
                     help="timed steps of each workload of the sweep (after 3 untimed ones)")
     ap.add_argument("--cpu-configs", action="store_true",
@@ -449,25 +449,23 @@ def describe(w) -> dict:
     return d
 
 
-def cpu_baseline(w, n_req: int):
-    """Time the oracle (as it stands) on a bounded sample of the same step:
-    for ``n_req`` requests, their write rows, then for every layer their
-    self-attention block and their cross-attention rows."""
+def cpu_baseline_inputs(w, n_req: int) -> dict:
+    """Host copies (float32, exact for the bf16 / e4m3 / fp32 values) of what
+    the oracle needs for a bounded sample of ``w``'s step: ``n_req`` requests'
+    write rows, and per layer their self-attention blocks, query rows and
+    context pages."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
 
     def host(t):
-        return t.detach().to(torch.float64).cpu().numpy()
+        return t.detach().to(torch.float32).cpu().numpy()
 
-    cores = oracle_threads()
     rng = np.random.default_rng(0)
     reqs = sorted(rng.choice(w.bs, size=min(n_req, w.bs), replace=False).tolist())
     ps = w.page_size
-    # host copies (not timed): pages of the sampled requests, their inputs
-    inputs = []
+    pages = []
     for l in range(w.L):
         ids, rows, at = [], [], 0
         for b in reqs:
@@ -476,49 +474,59 @@ def cpu_baseline(w, n_req: int):
             rows.append(np.arange(at, at + n))
             at += n
         idx = torch.cat(ids)
-        inputs.append((host(w.pools[l].k[idx]), host(w.pools[l].v[idx]), rows))
-    cu = w.cu_seqlens_q.cpu().numpy()
-    ctx = w.ctx_lens.cpu().numpy()
+        pages.append((host(w.pools[l].k[idx]), host(w.pools[l].v[idx]), rows))
     wr_in = None
     if w.write is not None:
         wr = w.write
         row_req = wr.row_req.cpu().numpy()
-        mask = np.isin(row_req, reqs)
-        sel = np.nonzero(mask)[0]
+        sel = np.nonzero(np.isin(row_req, reqs))[0]
         cl = None if wr.commit_lens is None else wr.commit_lens.cpu().numpy()
-        # keep the window structure: re-index the sampled requests' windows
-        wr_in = dict(x=host(wr.x[torch.as_tensor(sel, device=wr.x.device)]), w=host(wr.w_kv), kn=host(wr.k_norm_w),
-                     pos=wr.row_pos.cpu().numpy()[sel], req=row_req[sel], pt=w.page_table.cpu().numpy(),
-                     commit=cl, sel=sel)
-    q = [host(w.q[l]) for l in range(w.L)]
+        live = O.live_rows(len(wr.row_pos), wr.row_pos.cpu().numpy(), cl, wr.window)[sel]
+        keep = sel[np.nonzero(live)[0]]
+        wr_in = dict(x=host(wr.x[torch.as_tensor(keep, device=wr.x.device)]), w=host(wr.w_kv), kn=host(wr.k_norm_w),
+                     pos=wr.row_pos.cpu().numpy()[keep], req=row_req[keep], pt=w.page_table.cpu().numpy())
     blocks = [b * w.n_cand + i for b in reqs for i in range(w.n_cand)]   # candidate blocks of the sample
-    qkv = [host(w.qkv[l][torch.as_tensor(blocks, device=w.qkv[l].device)]) for l in range(w.L)]
-    block_ctx = w.block_ctx_lens.cpu().numpy()[blocks]
+    return dict(
+        reqs=reqs, bs=w.bs, L=w.L, H=w.H, Dh=w.Dh, ps=ps, eps=w.eps, theta=w.theta, scale=w.softmax_scale,
+        e4m3=w.pool_dtype.itemsize == 1, pages=pages, write=wr_in, cu=w.cu_seqlens_q.cpu().numpy(),
+        ctx=w.ctx_lens.cpu().numpy(), q=[host(w.q[l]) for l in range(w.L)],
+        q_norm=[host(w.q_norm_w[l]) for l in range(w.L)],
+        qkv=[host(w.qkv[l][torch.as_tensor(blocks, device=w.qkv[l].device)]) for l in range(w.L)],
+        self_q=[host(w.self_q_norm_w[l]) for l in range(w.L)], self_k=[host(w.self_k_norm_w[l]) for l in range(w.L)],
+        block_ctx=w.block_ctx_lens.cpu().numpy()[blocks])
+
+
+def cpu_baseline_run(smp: dict) -> dict:
+    """Time the oracle (as it stands) on a sample from cpu_baseline_inputs:
+    the sampled requests' write rows, then for every layer their
+    self-attention blocks and their cross-attention rows."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle as O
+
+    cores = oracle_threads()
+    reqs, cu, ctx = smp["reqs"], smp["cu"], smp["ctx"]
     with threadpool_limits(limits=cores):
         blas = [i.get("num_threads") for i in threadpool_info()]
         t0 = time.perf_counter()
-        if wr_in is not None:
-            # live rows of the sampled requests (commit rule applied the oracle's way)
-            live = O.live_rows(len(w.write.row_pos), w.write.row_pos.cpu().numpy(), wr_in["commit"],
-                               w.write.window)[wr_in["sel"]]
-            keep = np.nonzero(live)[0]
-            O.write_context_kv(wr_in["x"][keep], wr_in["w"], wr_in["kn"], wr_in["req"][keep], wr_in["pos"][keep],
-                               wr_in["pt"], ps, w.L, w.H, w.Dh, w.eps, w.theta)
-        for l in range(w.L):
-            O.block_self_attention(qkv[l], host(w.self_q_norm_w[l]), host(w.self_k_norm_w[l]), block_ctx,
-                                   w.softmax_scale, w.theta, w.eps)
-            pk, pv, rows = inputs[l]
+        wr = smp["write"]
+        if wr is not None:
+            O.write_context_kv(wr["x"], wr["w"], wr["kn"], wr["req"], wr["pos"], wr["pt"], smp["ps"], smp["L"],
+                               smp["H"], smp["Dh"], smp["eps"], smp["theta"])
+        for l in range(smp["L"]):
+            O.block_self_attention(smp["qkv"][l], smp["self_q"][l], smp["self_k"][l], smp["block_ctx"], smp["scale"],
+                                   smp["theta"], smp["eps"])
+            pk, pv, rows = smp["pages"][l]
             for i, b in enumerate(reqs):
-                pt = rows[i][None, :]
-                O.paged_cross_attention(q[l][cu[b]:cu[b + 1]], host(w.q_norm_w[l]), pk, pv, pt, [ctx[b]],
-                                        [0, cu[b + 1] - cu[b]], ps, w.softmax_scale, w.theta, w.eps,
-                                        kv_e4m3=w.pool_dtype.itemsize == 1)
+                O.paged_cross_attention(smp["q"][l][cu[b]:cu[b + 1]], smp["q_norm"][l], pk, pv, rows[i][None, :],
+                                        [ctx[b]], [0, cu[b + 1] - cu[b]], smp["ps"], smp["scale"], smp["theta"],
+                                        smp["eps"], kv_e4m3=smp["e4m3"])
         dt = time.perf_counter() - t0
-    rows = sum(int(cu[b + 1] - cu[b]) for b in reqs) * w.L
+    rows = sum(int(cu[b + 1] - cu[b]) for b in reqs) * smp["L"]
     return {"value": rows / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{len(reqs)} of {w.bs} requests (ids {reqs}): their write rows and, for all {w.L} layers, "
-                       f"their self-attention blocks and cross-attention rows; {dt:.1f} s wall; numpy fp64, "
-                       f"BLAS threads {blas}"),
+            "sample": (f"{len(reqs)} of {smp['bs']} requests (ids {reqs}): their written rows and, for all "
+                       f"{smp['L']} layers, their self-attention blocks and cross-attention rows; {dt:.1f} s wall; "
+                       f"numpy fp64, BLAS threads {blas}"),
             "seconds": dt, "cpu_model": cpu_model(), "host": host_cpu()}
 
 
@@ -531,11 +539,13 @@ def plan_waves(pool_dtype) -> int:
     return min(cus * 4 * (2 if pool_dtype == torch.float8_e4m3fn else 1), 4096)
 
 
-def time_attention(w, steps: int, warmup: int, flush_mall: bool) -> dict:
+def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: float = 0.3) -> dict:
     """The attention step of ``w`` (plan, then per layer self- and
     cross-attention), ``steps`` timed steps with events around every step and
     every cross-attention call; with ``flush_mall`` a 1 GiB buffer is streamed
-    (untimed, between the events) before each step."""
+    (untimed, between the events) before each step.  Untimed steps run first,
+    at least ``warmup`` of them and at least ``warm_seconds`` of them, so the
+    timed ones do not see clocks still ramping after an idle stretch."""
     import torch
 
     from block_diffusion_drafter_all_amd import binding as B
@@ -558,8 +568,13 @@ def time_attention(w, steps: int, warmup: int, flush_mall: bool) -> dict:
             if ev is not None:
                 ev["cross"][l][1].record()
 
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < warm_seconds:
         step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [dict(step=E(), cross=[E() for _ in range(w.L)]) for _ in range(steps)]
     for s in range(steps):
@@ -604,14 +619,17 @@ def time_attention(w, steps: int, warmup: int, flush_mall: bool) -> dict:
 
 
 def sweep_configs(args) -> dict:
-    """The cross-attention of workloads 2 (warm and MALL-flushed), 3 and 4,
+    """The cross-attention of workloads 1, 2 (warm and MALL-flushed), 3 and 4,
     timed in this run with the main workload's pool options."""
     import torch
 
     from block_diffusion_drafter_all_amd.workloads import make_workload
 
-    res = {}
-    for name, cid, flush in (("2_warm", 2, False), ("2_flushed", 2, True), ("3", 3, False), ("4", 4, False)):
+    res, samples = {}, {}
+    for name, cid, flush in (("1", 1, False), ("2_warm", 2, False), ("2_flushed", 2, True), ("3", 3, False),
+                             ("4", 4, False)):
+        if cid == 1 and (args.kv_fp8 or args.candidates != 1):
+            continue  # the tiny workload is fp32, one block per request
         print(f"[bench] timing workload {name}", file=sys.stderr, flush=True)
         w = make_workload(cid, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8)
         torch.cuda.synchronize()
@@ -620,11 +638,13 @@ def sweep_configs(args) -> dict:
         key = (f"config={cid},layout={args.layout},candidates={args.candidates},"
                f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}")
         r["traffic"] = measured_traffic(key)
-        if args.cpu_configs:
-            r["cpu_baseline"] = cpu_baseline(w, min(w.bs, args.cpu_sample_requests or 24))
+        if args.cpu_configs and not flush:
+            samples[name] = cpu_baseline_inputs(w, min(w.bs, args.cpu_sample_requests or 24))
         res[name] = r
         del w
         torch.cuda.empty_cache()
+    for name, smp in samples.items():  # the oracle after all of the sweep's GPU timing
+        res[name]["cpu_baseline"] = cpu_baseline_run(smp)
     return res
 
 
@@ -821,13 +841,17 @@ def main():
     for k in ("stream_read_GBps", "tile_gather_GBps"):
         if k in out["context"]:
             out["roofline"]["frac_of_" + k[:-5]] = achieved / out["context"][k]
+    # The oracle (CPU only) runs last: every GPU figure is taken with the GPU busy.
+    cpu_sample = None
     if not args.no_cpu_baseline:
         n_req = args.cpu_sample_requests or max(1, min(w.bs, 24))
-        out["cpu_baseline"] = cpu_baseline(w, n_req)
+        cpu_sample = cpu_baseline_inputs(w, n_req)
     if not args.no_configs:
         del w, buf
         torch.cuda.empty_cache()
         out["configs"] = sweep_configs(args)
+    if cpu_sample is not None:
+        out["cpu_baseline"] = cpu_baseline_run(cpu_sample)
     print(json.dumps(out), flush=True)
 
 

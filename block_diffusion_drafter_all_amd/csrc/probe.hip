@@ -35,6 +35,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* buf, in
 #pragma unroll
       for (int ch = 0; ch < 8; ++ch) r[d][ch] = ld(base + blk * kBlock + ch * 1024);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the group issued before the first use
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
 #pragma unroll
@@ -43,34 +44,34 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* buf, in
   finish(sink, w, lane, acc);
 }
 
-// Wave w reads tiles [n w / W, n (w + 1) / W) of the list, K and V of each.
+// Wave w reads tiles [n w / W, n (w + 1) / W) of the list, K and V of each
+// (CH loads of 1 KB per operand and tile, so the registers held in flight
+// match the tile size and two waves per SIMD fit).
+template <int CH>
 __global__ __launch_bounds__(256) void tile_gather_kernel(const uint8_t* k, const uint8_t* v, const int64_t* off,
-                                                          int64_t n_tiles, int chunks, int n_waves, uint32_t* sink) {
+                                                          int64_t n_tiles, int n_waves, uint32_t* sink) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= n_waves) return;
   const int64_t t0 = n_tiles * w / n_waves, t1 = n_tiles * (w + 1) / n_waves;
   u32x4_t acc = {0u, 0u, 0u, 0u};
   for (int64_t t = t0; t < t1; t += kDepth) {
-    u32x4_t r[kDepth][16];
+    u32x4_t r[kDepth][2 * CH];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int64_t tt = t + d < t1 ? t + d : t1 - 1;
       const int64_t o = off[tt];  // wave-uniform
 #pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        if (ch < chunks) {
-          r[d][ch] = ld(k + o + ch * 1024 + lane * 16);
-          r[d][8 + ch] = ld(v + o + ch * 1024 + lane * 16);
-        } else {
-          r[d][ch] = r[d][8 + ch] = (u32x4_t){0u, 0u, 0u, 0u};
-        }
+      for (int ch = 0; ch < CH; ++ch) {
+        r[d][ch] = ld(k + o + ch * 1024 + lane * 16);
+        r[d][CH + ch] = ld(v + o + ch * 1024 + lane * 16);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the group issued before the first use
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
 #pragma unroll
-      for (int ch = 0; ch < 16; ++ch) acc ^= r[d][ch];
+      for (int ch = 0; ch < 2 * CH; ++ch) acc ^= r[d][ch];
   }
   finish(sink, w, lane, acc);
 }
@@ -97,9 +98,16 @@ int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, 
   if (!k || !v || !tile_off || !sink || n_tiles < 1 || n_waves < 4 || n_waves % 4) return -1;
   if (tile_bytes < 1024 || tile_bytes > 8192 || tile_bytes % 1024) return -2;
   if (((uintptr_t)k & 15) || ((uintptr_t)v & 15)) return -1;
-  hipLaunchKernelGGL(tile_gather_kernel, dim3((unsigned)(n_waves / 4)), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), tile_off, n_tiles,
-                     tile_bytes / 1024, n_waves, sink);
+  const uint8_t* kb = static_cast<const uint8_t*>(k);
+  const uint8_t* vb = static_cast<const uint8_t*>(v);
+  const dim3 grid((unsigned)(n_waves / 4)), block(256);
+  switch (tile_bytes / 1024) {
+    case 1: hipLaunchKernelGGL(tile_gather_kernel<1>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
+    case 2: hipLaunchKernelGGL(tile_gather_kernel<2>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
+    case 4: hipLaunchKernelGGL(tile_gather_kernel<4>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
+    case 8: hipLaunchKernelGGL(tile_gather_kernel<8>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
+    default: return -2;  // 3, 5, 6, 7 KB tiles: not a tile size of a pool
+  }
   return status_of(hipGetLastError());
 }
 

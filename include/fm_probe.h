@@ -38,8 +38,8 @@ int fm_probe_stream_read(const void* buf, size_t bytes, int32_t n_waves, uint32_
 
 /* Gather of n_tiles K/V tile pairs: tile i is tile_bytes contiguous bytes at
  * k + tile_off[i] and as many at v + tile_off[i] (tile_off DEVICE int64
- * [n_tiles], byte offsets, 16-byte aligned; tile_bytes a multiple of 1024 up to
- * 8192).  The tiles are cut into n_waves equal contiguous ranges, one per
+ * [n_tiles], byte offsets, 16-byte aligned; tile_bytes 1024, 2048, 4096 or
+ * 8192, -2 otherwise).  The tiles are cut into n_waves equal contiguous ranges, one per
  * wavefront (the attention plan's equal shares), each read in order with four
  * tiles in flight, 1 KB per load instruction.  sink DEVICE uint32[n_waves * 64].
  * n_waves a positive multiple of 4. */
