@@ -454,10 +454,17 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   a.q = q;
   a.out = out;
   a.q_norm_w = q_norm_w;
+  if (pool->page_stride > UINT32_MAX || pool->slot_stride > UINT32_MAX || pool->head_stride > UINT32_MAX)
+    return fail(FM_E_UNSUPPORTED, "%s: pool strides must be below 2^32 elements", fn);
   a.pool = to_desc(*pool);
   a.page_table = page_table;
   a.pt_stride = pt_stride;
   a.log2ps = log2_exact(page_size);
+  a.page_stride32 = (uint32_t)pool->page_stride;
+  a.slot_stride32 = (uint32_t)pool->slot_stride;
+  a.head_stride32 = (uint32_t)pool->head_stride;
+  a.num_pages32 = (int32_t)std::min<int64_t>(pool->num_pages, INT32_MAX);  // page ids are int32
+  a.pt_stride32 = (int32_t)std::min<int64_t>(pt_stride, INT32_MAX);
   a.ctx_lens = ctx_lens;
   a.cu_q = cu_seqlens_q;
   a.bs = bs;

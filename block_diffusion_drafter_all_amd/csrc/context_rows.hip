@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void proj_gemm_kernel(CtxRowsAr
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cg][rg][i] = 0.f;
-  gemm256_mainloop_rows(acc, src, (int)(Ks / kGK), wv, wm, wn, buf0, buf1, m0 + 64 * wm < M);
+  gemm256_mainloop_rows(acc, src, (int)(Ks / kGK), wv, wm, wn, buf0, buf1, M - (m0 + 64 * wm));
 
   // acc[cg][rg][i] (lane l) = Y[row m0 + 64 wm + 32 rg + l % 32]
   //                            [column 256 n + 128 wn + 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]

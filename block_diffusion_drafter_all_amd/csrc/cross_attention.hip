@@ -528,7 +528,11 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   };
 
   int64_t kv_last = 0;  // per-lane element offset of the last real tile (a safe re-read)
-  int64_t tile_base = 0;  // UNIFORM_PAGE: wave-uniform element offset of the tile (kept for re-reads)
+  uint64_t tile_base = 0;  // UNIFORM_PAGE: wave-uniform element offset of the tile (kept for re-reads)
+  // Wave-uniform per-request and per-pair parts of the addresses: the
+  // request's page-table row and the head's offset in the pool.
+  const int32_t* prow = a.page_table + (int64_t)lb * a.pt_stride;
+  uint64_t hoff = (uint64_t)(uint32_t)lh * a.head_stride32;
   // UNIFORM_PAGE: this lane's constant offset inside a tile (slot c, column group g)
   const uint32_t lane_off_b = (uint32_t)(((int64_t)c * a.pool.slot_stride + g * EPC) * (int64_t)sizeof(pst));
   bool bad_page = false;
@@ -551,7 +555,9 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
         lctx = max(0, sload_i32(a.ctx_lens + lb));
         lT = tiles_of(lctx);
       } while (lT == 0);
+      prow = a.page_table + (int64_t)lb * a.pt_stride;
     }
+    hoff = (uint64_t)(uint32_t)lh * a.head_stride32;
     exhausted = exhausted || lT == 0;
   };
   auto window_covers = [&](int tb) -> bool {
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     const int tb = lk << 4;
     if constexpr (UNIFORM_PAGE) {
       const int idx = tb >> a.log2ps;
-      pg_next = idx < a.pt_stride ? sload_i32(a.page_table + (int64_t)lb * a.pt_stride + idx) : -1;
+      pg_next = idx < a.pt_stride32 ? sload_i32(prow + idx) : -1;
       pg_have = true;
     } else {
       if (!window_covers(tb)) return;
@@ -598,13 +604,14 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
           pu = pg_next;
         } else {
           const int idx = tb >> a.log2ps;
-          pu = idx < a.pt_stride ? sload_i32(a.page_table + (int64_t)lb * a.pt_stride + idx) : -1;
+          pu = idx < a.pt_stride32 ? sload_i32(prow + idx) : -1;
         }
-        const bool page_ok = pu >= 0 && (int64_t)pu < a.pool.num_pages;
+        const bool page_ok = (uint32_t)pu < (uint32_t)a.num_pages32;  // also rules out pu < 0
         keys = page_ok ? (kKeyMask >> (16 - min(16, lctx - tb))) : 0u;  // tb < lctx: at least one key
         bad_page |= !page_ok;
-        tile_base = (int64_t)lh * a.pool.head_stride +
-                    (page_ok ? (int64_t)pu * a.pool.page_stride + (int64_t)(tb & ps_mask) * a.pool.slot_stride : 0);
+        tile_base = hoff + (page_ok ? (uint64_t)(uint32_t)pu * a.page_stride32 +
+                                          (uint64_t)(uint32_t)(tb & ps_mask) * a.slot_stride32
+                                    : 0);
       } else {
         const int tok = tb + c;
         const int tok_c = min(tok, lctx - 1);

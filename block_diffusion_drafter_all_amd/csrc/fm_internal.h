@@ -143,6 +143,11 @@ struct CrossArgs {
   const int32_t* page_table;
   int64_t pt_stride;
   int32_t log2ps;
+  // The pool's strides (elements, each below 2^32), its page count and the
+  // page-table row length clamped to 2^31 - 1, as 32-bit scalars for the
+  // loader's per-tile arithmetic.
+  uint32_t page_stride32, slot_stride32, head_stride32;
+  int32_t num_pages32, pt_stride32;
   const int32_t* ctx_lens;
   const int32_t* cu_q;
   int32_t bs, H;

@@ -59,12 +59,14 @@ __device__ __forceinline__ GemmLoad gemm_load_of(int wv, int lane, int i) {
 // acc += the tile's product over ns stages.  src[i]: the start of this lane's
 // load i at stage 0 (row start + 8 chunk elements); stage s reads src[i] +
 // 64 s.  Afterwards acc[cg][rg][i] (lane l) = Y[X row 64 wm + 32 rg + l % 32]
-// [W row 128 wn + 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4].  With MMA false
-// the wave only issues its share of the loads and meets every barrier (the
-// same sequence of both), reads no fragments and leaves acc untouched.
-template <bool MMA = true>
+// [W row 128 wn + 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4], for the wave's
+// first RG blocks of 32 X rows (rg < RG; the others are left untouched).
+// With RG = 0 the wave only issues its share of the loads and meets every
+// barrier (the same sequence in every case) and reads no fragments.
+template <int RG = 2>
 __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const uint16_t* const (&src)[kLoadsPerWave],
                                                  int ns, int wv, int wm, int wn, uint8_t* buf0, uint8_t* buf1) {
+  constexpr bool MMA = RG > 0;
   const int lane = lane_id();
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto issue = [&](int s, uint8_t* b) {  // stage s into a buffer
@@ -88,7 +90,7 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
     for (int q = 0; q < 4; ++q)
       f.A[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(b + off[t] + (4 * wn + q) * 4096));
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < RG; ++q)
       f.B[q] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(b + 32768 + off[t] + (2 * wm + q) * 4096));
   };
   auto mma = [&](const Frags& f) {
@@ -96,25 +98,32 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg)
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg)
+      for (int rg = 0; rg < RG; ++rg)
         acc[cg][rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.A[cg], f.B[rg], acc[cg][rg], 0, 0, 0);
   };
   // the order of issue in a k step: each fragment read (then each load) behind one MFMA
+  // (4 RG MFMAs and 4 + RG reads a step: with one block the fifth read follows the fourth)
   auto interleave = [&](bool loads) {
     if constexpr (!MMA) return;
+    constexpr int kPairs = RG == 2 ? 6 : 4;
 #pragma unroll
-    for (int j = 0; j < 6; ++j) {
+    for (int j = 0; j < kPairs; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
-    if (loads) {
+    if constexpr (RG == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the fifth read
+    if constexpr (RG == 2) {
+      if (loads) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerWave / 2, 0);  // global->LDS loads
+        for (int j = 0; j < 2; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerWave / 2, 0);  // global->LDS loads
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    } else if (loads) {
+      __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerWave, 0);  // global->LDS loads
     }
   };
   Frags fa, fb;
@@ -152,18 +161,20 @@ __device__ __forceinline__ void gemm256_mainloop(f32x16_t (&acc)[4][2], const ui
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & kWaitLgkm0);  // drain the trailing loads and reads
 }
 
-// The mainloop for a wave whose 64 X rows are live or not (wave-uniform): a
-// wave whose rows all lie past the end of the tile's rows (the padding of a
-// partial last tile) still moves its share of each stage through LDS but
-// skips the fragment reads and MFMAs, leaving the matrix core of its SIMD to
-// the other wave there.
+// The mainloop for a wave with ``rows`` live X rows (wave-uniform, clamped to
+// 0..64): the 32-row MFMA blocks past them (the padding of a partial tile)
+// are not multiplied, and a wave with none still moves its share of each
+// stage through LDS but reads no fragments, leaving the matrix core of its
+// SIMD to the other wave there.
 __device__ __forceinline__ void gemm256_mainloop_rows(f32x16_t (&acc)[4][2],
                                                       const uint16_t* const (&src)[kLoadsPerWave], int ns, int wv,
-                                                      int wm, int wn, uint8_t* buf0, uint8_t* buf1, bool rows_live) {
-  if (rows_live)
-    gemm256_mainloop<true>(acc, src, ns, wv, wm, wn, buf0, buf1);
+                                                      int wm, int wn, uint8_t* buf0, uint8_t* buf1, int64_t rows) {
+  if (rows > 32)
+    gemm256_mainloop<2>(acc, src, ns, wv, wm, wn, buf0, buf1);
+  else if (rows > 0)
+    gemm256_mainloop<1>(acc, src, ns, wv, wm, wn, buf0, buf1);
   else
-    gemm256_mainloop<false>(acc, src, ns, wv, wm, wn, buf0, buf1);
+    gemm256_mainloop<0>(acc, src, ns, wv, wm, wn, buf0, buf1);
 }
 
 // Declares the two LDS stages of a GEMM kernel.

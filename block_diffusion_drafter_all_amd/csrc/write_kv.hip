@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cg][rg][i] = 0.f;
-  gemm256_mainloop_rows(acc, src, a.d_in / kGK, wv, wm, wn, buf0, buf1, m0 + 64 * wm < live);
+  gemm256_mainloop_rows(acc, src, a.d_in / kGK, wv, wm, wn, buf0, buf1, live - (m0 + 64 * wm));
   // acc[cg][rg][i] (lane l) = Y[tile row 64 wm + 32 rg + l % 32]
   //                            [head column 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]
 

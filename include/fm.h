@@ -75,7 +75,9 @@ typedef enum fm_dtype { FM_F32 = 0, FM_BF16 = 1, FM_BF16_E4M3 = 2 } fm_dtype;
  * s*slot_stride + h*head_stride, head_dim contiguous elements; the value is at
  * the same offset from v.  Element type = the call's pool type (fp32, bf16 or
  * e4m3 for FM_F32, FM_BF16, FM_BF16_E4M3); strides count elements.
- * All strides and the byte addresses of k and v must be multiples of 16 bytes. */
+ * All strides and the byte addresses of k and v must be multiples of 16 bytes;
+ * fm_paged_cross_attention also takes each stride below 2^32 elements
+ * (FM_E_UNSUPPORTED otherwise). */
 typedef struct fm_kv_pool {
   void* k;               /* DEVICE */
   void* v;               /* DEVICE */

@@ -105,6 +105,7 @@ def _cross(lib, **over):
     (dict(theta=0.0), B.FM_E_INVALID, "rope_theta"),
     (dict(scale=float("inf")), B.FM_E_INVALID, "softmax_scale"),
     (dict(pt_stride=0), B.FM_E_INVALID, "pt_stride"),
+    (dict(pool=B.fm_kv_pool(FAKE, FAKE, 4, 1 << 32, 256, 64)), B.FM_E_UNSUPPORTED, "below 2^32"),
 ])
 def test_cross_attention_rejects(lib, over, status, needle):
     assert _cross(lib, **over) == status
