@@ -75,7 +75,7 @@ def parse():
                     help="config 5: make the write's rows on the device from the target hidden states (fc + "
                          "hidden_norm) and the anchor tokens (embedding + anchor_proj + anchor_norm) in the step")
     ap.add_argument("--flush-mall", action="store_true",
-                    help="before each timed step, stream a 1 GiB scratch buffer (untimed) so the step starts with "
+                    help="before each timed step, read a 1 GiB scratch buffer (untimed) so the step starts with "
                          "a cold MALL; ms_per_step is then the mean of the per-step events")
     ap.add_argument("--no-graph", action="store_true",
                     help="report the eager launches' time as value.  By default one step is also captured in a HIP "
@@ -255,6 +255,33 @@ def _probe_lib():
     lib.fm_probe_tile_gather.restype = ctypes.c_int
     lib.fm_probe_tile_gather.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
     return lib
+
+
+class MallFlush:
+    """Evicts the step's data from the MALL (256 MB) before a timed step: one
+    streaming read of a 1 GiB buffer (the probe library's read kernel).  The
+    flush only reads, so it leaves clean lines behind: a flush that also wrote
+    its buffer would leave up to 256 MB of dirty lines, whose write-back to
+    HBM would then share the bandwidth with the timed step's reads."""
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        self._lib = _probe_lib()
+        self._buf = torch.ones((COPY_BYTES // 4,), dtype=torch.int32, device="cuda")
+        self._sink = torch.empty(2048 * 64, dtype=torch.int32, device="cuda")
+        self._n = ctypes.c_size_t(0)
+
+    def __call__(self):
+        import ctypes
+
+        import torch
+
+        if self._lib.fm_probe_stream_read(self._buf.data_ptr(), self._buf.numel() * 4, 2048, self._sink.data_ptr(),
+                                          ctypes.byref(self._n), torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("fm_probe_stream_read failed")
 
 
 def _best_rate(launch, nbytes: float, reps: int = 5) -> float:
@@ -542,7 +569,7 @@ def plan_waves(pool_dtype) -> int:
 def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: float = 0.3) -> dict:
     """The attention step of ``w`` (plan, then per layer self- and
     cross-attention), ``steps`` timed steps with events around every step and
-    every cross-attention call; with ``flush_mall`` a 1 GiB buffer is streamed
+    every cross-attention call; with ``flush_mall`` a 1 GiB buffer is read
     (untimed, between the events) before each step.  Untimed steps run first,
     at least ``warmup`` of them and at least ``warm_seconds`` of them, so the
     timed ones do not see clocks still ramping after an idle stretch."""
@@ -552,7 +579,7 @@ def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: f
     from block_diffusion_drafter_all_amd import step as S
 
     buf = S.allocate(w)
-    flush = torch.zeros((COPY_BYTES // 4,), dtype=torch.float32, device="cuda") if flush_mall else None
+    flush = MallFlush() if flush_mall else None
     E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
 
     def step(ev=None):
@@ -579,7 +606,7 @@ def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: f
     evs = [dict(step=E(), cross=[E() for _ in range(w.L)]) for _ in range(steps)]
     for s in range(steps):
         if flush is not None:
-            flush.add_(1.0)
+            flush()
         evs[s]["step"][0].record()
         step(evs[s])
         evs[s]["step"][1].record()
@@ -729,14 +756,14 @@ def main():
     n_pre = 0 if w.dit is not None else w.L   # the DiT step appends its own events per call
     per_step = [dict(step=E(), rows=E(), write=E(), self=[E() for _ in range(n_pre)],
                      cross=[E() for _ in range(n_pre)]) for _ in range(args.steps)]
-    flush = torch.empty((COPY_BYTES // 4,), dtype=torch.float32, device="cuda").zero_() if args.flush_mall else None
+    flush = MallFlush() if args.flush_mall else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
         if flush is not None:
-            flush.add_(1.0)  # 1 GiB read and written: the MALL (256 MB) holds none of the step's data
+            flush()  # 1 GiB read: the MALL (256 MB) holds none of the step's data
         per_step[s]["step"][0].record()
         one_step(per_step[s])
         per_step[s]["step"][1].record()

@@ -196,6 +196,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
       const int64_t P = pair_off[b] + (int64_t)h * T;
       pr.w0 = wave_of(P);
       pr.w1 = wave_of(P + T - 1);
+      pr.slot0 = starts[pr.w0] < P ? 1 : 0;
       for (int u = pr.w0; u <= pr.w1; ++u) pr.parts += starts[u + 1] > starts[u] ? 1 : 0;
     }
     prec[i] = pr;
@@ -366,57 +367,44 @@ struct PvType<E4m3> {
   typedef Bf16 type;
 };
 
-// Where the cut pair (b, h) lies in the tile stream: its first tile P, the
-// waves w0..w1 holding its tiles, how many of them hold a part, and its counter.
-struct CutPair {
-  int64_t P;
-  int w0, w1, parts;
-  int32_t* cnt;
-};
-
-__device__ __forceinline__ CutPair cut_pair(const CrossArgs& a, int b, int h) {
-  const int nt = tiles_of(sload_i32(a.ctx_lens + b));
-  const PairRec pr = ((const PairRec*)(a.ws + a.lay.pair_rec))[(int64_t)b * a.H + h];
-  CutPair p;
-  p.P = ((const int64_t*)(a.ws + a.lay.pair_off))[b] + (int64_t)h * nt;
-  p.w0 = pr.w0;
-  p.w1 = pr.w1;
-  p.parts = pr.parts;
-  p.cnt = (int32_t*)(a.ws + a.lay.merge_cnt) + p.w0;
-  return p;
+// The plan's record of the cut pair (b, h): its waves w0..w1, how many of
+// them hold a part, and the partial slot of w0.
+__device__ __forceinline__ PairRec pair_rec_of(const CrossArgs& a, int b, int h) {
+  return ((const PairRec*)(a.ws + a.lay.pair_rec))[(int64_t)b * a.H + h];
 }
 
-// Counts this wave's partial of the cut pair (b, h) in (its stores must be
-// acknowledged already) and tells whether it was the pair's last part.
-__device__ __forceinline__ bool count_in(const CrossArgs& a, int b, int h) {
-  const CutPair p = cut_pair(a, b, h);
+// Counts this wave's partial of a cut pair in on the pair's counter (indexed
+// by its first wave; this wave's partial stores must be acknowledged
+// already) and returns the parts counted before it: the pair's last part
+// sees pr.parts - 1.
+__device__ __forceinline__ int count_in(const CrossArgs& a, const PairRec& pr) {
   int before = 0;
-  if (lane_id() == 0) before = __hip_atomic_fetch_add(p.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __shfl(before, 0) == p.parts - 1;
+  if (lane_id() == 0)
+    before = __hip_atomic_fetch_add((int32_t*)(a.ws + a.lay.merge_cnt) + pr.w0, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  return __shfl(before, 0);
 }
 
 // Combines the partials of the cut pair (b, h) in wave order, fragment by
 // fragment,
 //   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,   M = max_w m_w,
-// (accumulated online, two parts per round of loads), writes the output rows
-// and re-arms the pair's counter for the next call.  Called by the wave that
-// counted the last part in: every other part was acknowledged before it was
-// counted.  Lanes hold the same fragment of the rows as in the attention loop.
+// writes the output rows and re-arms the pair's counter for the next call.
+// The parts are read kMergeBatch at a time: one round of loads (the waves'
+// records with them) and one rescale per batch, so a pair cut over up to
+// kMergeBatch waves costs one round trip.  Called by the wave that counted the
+// last part in: every other part was acknowledged before it was counted.
+// Lanes hold the same fragment of the rows as in the attention loop.
+constexpr int kMergeBatch = 4;
+
 template <class T, class PT, int D, int NQF>
-__device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
+__device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, const PairRec& pr) {
   typedef typename T::storage st;
   constexpr int NDT = D / 16;
   const int lane = lane_id(), g = lane >> 4, c = lane & 15;
-  const CutPair cp = cut_pair(a, b, h);
-  const int64_t P = cp.P;
-  const int w0 = cp.w0, w1 = cp.w1;
-  int32_t* cnt = cp.cnt;
+  const int w0 = pr.w0, w1 = pr.w1;
   const WaveRec* rec = (const WaveRec*)(a.ws + a.lay.wave_rec);
   const __amdgpu_buffer_rsrc_t prs = partials_rsrc(a);
   const uint32_t o_base = (uint32_t)(a.lay.partial_o - a.lay.partial_ml);
-  auto part_of = [&](int wv) -> uint32_t {  // the wave's partial slot holding this pair
-    return (uint32_t)(wv * 2 + ((wv == w0 && rec[w0].start < P) ? 1 : 0));
-  };
   const int r0 = max(0, sload_i32(a.cu_q + b));
   const int nq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - r0, kQRows * NQF));
   for (int f = 0; f < NQF; ++f) {
@@ -424,32 +412,39 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
     f32x4_t acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    auto combine = [&](bool ok, u32x2_t ml, const u32x4_t* ow) {
-      const float m_w = __uint_as_float(ml[0]), l_w = __uint_as_float(ml[1]);
-      const float m_new = fmaxf(m_acc, m_w);
-      const bool live = ok && m_new != kNegInf;
-      const float sa = (live && m_acc != kNegInf) ? exp2f(m_acc - m_new) : (live ? 0.f : 1.f);
-      const float sw = (live && m_w != kNegInf) ? exp2f(m_w - m_new) : 0.f;
-      l_acc = l_acc * sa + l_w * sw;
+    for (int base = w0; base <= w1; base += kMergeBatch) {
+      bool ok[kMergeBatch];
+      u32x2_t ml[kMergeBatch];
+      u32x4_t ov[kMergeBatch][NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] = acc[dt] * sa + __builtin_bit_cast(f32x4_t, ow[dt]) * sw;
-      m_acc = live ? m_new : m_acc;
-    };
-    for (int wv = w0; wv <= w1; wv += 2) {
-      const int wb = min(wv + 1, w1);
-      const bool ok_a = rec[wv].count > 0;
-      const bool ok_b = wv + 1 <= w1 && rec[wb].count > 0;
-      const uint32_t pa = part_of(wv) * NQF + f, pb = part_of(wb) * NQF + f;
-      u32x4_t oa[NDT], ob[NDT];
-      const u32x2_t mla = __builtin_amdgcn_raw_buffer_load_b64(prs, (pa * 64 + lane) * 8, 0, kDeviceScope);
-      const u32x2_t mlb = __builtin_amdgcn_raw_buffer_load_b64(prs, (pb * 64 + lane) * 8, 0, kDeviceScope);
+      for (int j = 0; j < kMergeBatch; ++j) {  // past w1: a re-read of w1's part, not counted
+        const int wv = min(base + j, w1);
+        ok[j] = base + j <= w1 && rec[wv].count > 0;
+        const uint32_t part = (uint32_t)((wv * 2 + (wv == w0 ? pr.slot0 : 0)) * NQF + f);
+        ml[j] = __builtin_amdgcn_raw_buffer_load_b64(prs, (part * 64 + lane) * 8, 0, kDeviceScope);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        oa[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pa * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
-        ob[dt] = __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((pb * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
+        for (int dt = 0; dt < NDT; ++dt)
+          ov[j][dt] =
+              __builtin_amdgcn_raw_buffer_load_b128(prs, o_base + ((part * NDT + dt) * 64 + lane) * 16, 0, kDeviceScope);
       }
-      combine(ok_a, mla, oa);
-      combine(ok_b, mlb, ob);
+      float m_new = m_acc;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (ok[j]) m_new = fmaxf(m_new, __uint_as_float(ml[j][0]));
+      if (m_new == kNegInf) continue;  // nothing counted yet
+      const float sa = m_acc == kNegInf ? 0.f : exp2_hw(m_acc - m_new);
+      l_acc *= sa;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= sa;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float m_w = __uint_as_float(ml[j][0]);
+        const float sw = (ok[j] && m_w != kNegInf) ? exp2_hw(m_w - m_new) : 0.f;
+        l_acc += __uint_as_float(ml[j][1]) * sw;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] += __builtin_bit_cast(f32x4_t, ov[j][dt]) * sw;
+      }
+      m_acc = m_new;
     }
     const float inv = l_acc > 0.f ? 1.0f / l_acc : 0.f;
     const int k = kQRows * f + c;
@@ -459,7 +454,8 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h) {
       for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), acc[dt], inv * a.v_descale);
     }
   }
-  if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0)
+    __hip_atomic_store((int32_t*)(a.ws + a.lay.merge_cnt) + w0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // UNIFORM_PAGE: page_size >= 16, so the 16 keys of a tile share one page and
@@ -830,15 +826,20 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   const int err = (bad_page ? 1 : 0) | (exhausted ? 2 : 0);
   if (err && lane == 0) atomicOr(&hdr->error, err);
   // The pairs this wave cut: the last of each pair's waves to get here merges it.
+  // (The pairs' records are read while the partial stores are acknowledged.)
   if (cut_b[0] >= 0 || cut_b[1] >= 0) {
+    PairRec pr[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (cut_b[k] >= 0) pr[k] = pair_rec_of(a, cut_b[k], cut_h[k]);
     wait_stores_acknowledged();  // this wave's partials before their counts
-    int last[2] = {0, 0};
+    int before[2] = {-1, -1};
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (cut_b[k] >= 0) last[k] = count_in(a, cut_b[k], cut_h[k]);
+      if (cut_b[k] >= 0) before[k] = count_in(a, pr[k]);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (last[k]) merge_pair<T, PT, D, NQF>(a, cut_b[k], cut_h[k]);
+      if (cut_b[k] >= 0 && before[k] == pr[k].parts - 1) merge_pair<T, PT, D, NQF>(a, cut_b[k], cut_h[k], pr[k]);
   }
 }
 

@@ -90,9 +90,12 @@ struct WaveRec {
 };
 
 // Where a pair's tiles lie among the wave ranges: the first and last wave
-// holding them and how many waves hold a part (1: the pair is whole).
+// holding them, how many waves hold a part (1: the pair is whole), and the
+// partial slot of its first wave (1 when that wave's range starts in an
+// earlier pair, whose partial takes slot 0; every later wave starts inside
+// the pair and uses slot 0).
 struct PairRec {
-  int32_t w0, w1, parts, pad;
+  int32_t w0, w1, parts, slot0;
 };
 
 struct PlanLayout {
