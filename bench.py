@@ -82,6 +82,9 @@ def parse():
                          "graph and --steps replays of it give value; the eager pass (first) still gives the "
                          "per-call events of the roofline and is reported under \"eager\"")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-xcd-calibration", action="store_true",
+                    help="plan with the library's default XCD weights instead of weights measured on this box by "
+                         "the tile-gather probe (timed waves, equal shares) before the timed steps")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the sweep that also times the cross-attention of workloads 1, 2 (warm and with the "
                          "MALL flushed), 3 and 4 in the same run (reported under \"configs\")")
@@ -254,6 +257,9 @@ def _probe_lib():
     lib.fm_probe_stream_read.argtypes = [vp, sz, ctypes.c_int32, vp, ctypes.POINTER(sz), vp]
     lib.fm_probe_tile_gather.restype = ctypes.c_int
     lib.fm_probe_tile_gather.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.fm_probe_tile_gather_timed.restype = ctypes.c_int
+    lib.fm_probe_tile_gather_timed.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                               vp]
     return lib
 
 
@@ -365,6 +371,47 @@ def probe_ceilings(w, n_waves: int) -> dict:
         out["tile_gather"] = (f"{off.numel()} K/V tile pairs of {tb} B (layer 0's call), {n_waves} waves, "
                               f"plan order, no arithmetic")
     return out
+
+
+def xcd_calibration(w, n_waves: int, reps: int = 3) -> dict | None:
+    """Weights of the plan's wave shares by XCD for this box: the tile-gather
+    probe reads layer 0's tiles in equal shares over the plan's waves, timing
+    every wave; an XCD's weight is proportional to its rate (tiles per unit
+    time, averaged over its waves and ``reps`` runs), normalised to a mean of
+    1000 and clamped to [850, 1150].  None when the pool's tiles are not
+    contiguous runs (the probe needs them)."""
+    import torch
+
+    off = tile_offsets(w, 0)
+    if off is None:
+        return None
+    lib = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    tb = 16 * w.Dh * w.pools[0].k.element_size()
+    pk, pv = w.pools[0].k, w.pools[0].v
+    sink = torch.empty(n_waves * 64, dtype=torch.int32, device="cuda")
+    rec = torch.zeros(n_waves * 4, dtype=torch.int64, device="cuda")
+    per_tile = [[] for _ in range(8)]
+    for rep in range(reps + 1):
+        if lib.fm_probe_tile_gather_timed(pk.data_ptr(), pv.data_ptr(), off.data_ptr(), off.numel(), tb, n_waves,
+                                          sink.data_ptr(), rec.data_ptr(), stream) != 0:
+            raise RuntimeError("fm_probe_tile_gather_timed failed")
+        torch.cuda.synchronize()
+        if rep == 0:
+            continue  # untimed first run
+        r = rec.view(n_waves, 4).cpu().tolist()
+        for t0, t1, xcd, tiles in r:
+            if tiles > 0:
+                per_tile[int(xcd) % 8].append((t1 - t0) / tiles)
+    if any(not v for v in per_tile):
+        return None
+    t = [sum(v) / len(v) for v in per_tile]
+    rate = [1.0 / x for x in t]
+    mean_rate = sum(rate) / 8
+    weights = [int(round(min(1150.0, max(850.0, 1000.0 * r / mean_rate)))) for r in rate]
+    return {"xcd_weights": weights, "xcd_us_per_tile": [round(x * 0.01, 4) for x in t],
+            "xcd_calibration": (f"tile-gather probe over layer 0's {off.numel()} tile pairs, {n_waves} waves in "
+                                f"equal shares, {reps} timed runs")}
 
 
 def copy_calibration() -> None:
@@ -566,7 +613,8 @@ def plan_waves(pool_dtype) -> int:
     return min(cus * 4 * (2 if pool_dtype == torch.float8_e4m3fn else 1), 4096)
 
 
-def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: float = 0.3) -> dict:
+def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: float = 0.3,
+                   xcd_weights=None) -> dict:
     """The attention step of ``w`` (plan, then per layer self- and
     cross-attention), ``steps`` timed steps with events around every step and
     every cross-attention call; with ``flush_mall`` a 1 GiB buffer is read
@@ -579,6 +627,7 @@ def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: f
     from block_diffusion_drafter_all_amd import step as S
 
     buf = S.allocate(w)
+    buf.xcd_weights = xcd_weights
     flush = MallFlush() if flush_mall else None
     E = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa: E731
 
@@ -645,9 +694,10 @@ def time_attention(w, steps: int, warmup: int, flush_mall: bool, warm_seconds: f
     return res
 
 
-def sweep_configs(args) -> dict:
+def sweep_configs(args, xcd_weights=None) -> dict:
     """The cross-attention of workloads 1, 2 (warm and MALL-flushed), 3 and 4,
-    timed in this run with the main workload's pool options."""
+    timed in this run with the main workload's pool options (and its plan
+    weights: the XCDs' rates are the box's, not the workload's)."""
     import torch
 
     from block_diffusion_drafter_all_amd.workloads import make_workload
@@ -661,7 +711,7 @@ def sweep_configs(args) -> dict:
         w = make_workload(cid, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8)
         torch.cuda.synchronize()
         r = {"workload": describe(w)}
-        r.update(time_attention(w, args.config_steps, 3, flush))
+        r.update(time_attention(w, args.config_steps, 3, flush, xcd_weights=xcd_weights))
         key = (f"config={cid},layout={args.layout},candidates={args.candidates},"
                f"kv={'e4m3' if args.kv_fp8 else 'activation-type'}")
         r["traffic"] = measured_traffic(key)
@@ -700,6 +750,12 @@ def main():
     w = make_workload(args.config, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8,
                       upstream=args.upstream, dit=args.dit)
     buf = S.allocate(w)
+    # The e4m3 kernel (two waves per SIMD) is bound by its instruction issue, not by the XCDs' memory rates:
+    # weighted shares only slow it, so it keeps the library's equal shares.
+    calib = (None if args.no_xcd_calibration or w.pool_dtype == torch.float8_e4m3fn else
+             xcd_calibration(w, plan_waves(w.pool_dtype)))
+    if calib is not None:
+        buf.xcd_weights = calib["xcd_weights"]
     torch.cuda.synchronize()
 
     def one_step(events=None):
@@ -865,6 +921,11 @@ def main():
     out["context"] = {"device": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                       "rocm_hip": torch.version.hip, "torch": torch.__version__, **hbm_ceilings(),
                       **probe_ceilings(w, plan_waves(w.pool_dtype))}
+    if calib is not None:
+        out["context"].update(calib)
+    else:
+        out["context"]["xcd_weights"] = ("library default" + (" (equal shares over an e4m3 pool)"
+                                                              if w.pool_dtype == torch.float8_e4m3fn else ""))
     for k in ("stream_read_GBps", "tile_gather_GBps"):
         if k in out["context"]:
             out["roofline"]["frac_of_" + k[:-5]] = achieved / out["context"][k]
@@ -876,7 +937,7 @@ def main():
     if not args.no_configs:
         del w, buf
         torch.cuda.empty_cache()
-        out["configs"] = sweep_configs(args)
+        out["configs"] = sweep_configs(args, buf.xcd_weights)
     if cpu_sample is not None:
         out["cpu_baseline"] = cpu_baseline_run(cpu_sample)
     print(json.dumps(out), flush=True)

@@ -42,6 +42,7 @@ SYMBOLS = (
     "fm_linear",
     "fm_cross_attention_workspace_size",
     "fm_plan_cross_attention",
+    "fm_plan_cross_attention_weighted",
     "fm_paged_cross_attention",
     "fm_block_self_attention",
 )
@@ -111,6 +112,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_cross_attention_workspace_size.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.c_int]
     lib.fm_plan_cross_attention.restype = ctypes.c_int
     lib.fm_plan_cross_attention.argtypes = [vp, c_i32, c_i32, c_i32, c_i32, ctypes.c_int, vp, c_sz, vp]
+    lib.fm_plan_cross_attention_weighted.restype = ctypes.c_int
+    lib.fm_plan_cross_attention_weighted.argtypes = [vp, c_i32, c_i32, c_i32, c_i32, ctypes.c_int,
+                                                     ctypes.POINTER(c_i32), vp, c_sz, vp]
     lib.fm_paged_cross_attention.restype = ctypes.c_int
     lib.fm_paged_cross_attention.argtypes = [
         vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
@@ -391,14 +395,27 @@ def fm_cross_attention_workspace_size(bs: int, H: int, Dh: int, max_q: int = 16,
     return load_library().fm_cross_attention_workspace_size(bs, H, Dh, max_q, _pool_code(pool_dtype))
 
 
-def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16, pool_dtype=torch.bfloat16):
+XCDS = 8
+
+
+def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16, pool_dtype=torch.bfloat16, xcd_weights=None):
     """Build the per-step tile schedule into ``ws`` (every layer reuses it) for
-    calls over pools of ``pool_dtype``."""
+    calls over pools of ``pool_dtype``; ``xcd_weights`` (8 ints in [500,
+    2000]) weight the wave shares by XCD instead of the library's default."""
+    if xcd_weights is not None:
+        weights = [int(x) for x in xcd_weights]
+        if len(weights) != XCDS:
+            raise ValueError(f"xcd_weights needs {XCDS} values, got {len(weights)}")
     lib = load_library()
     _need(ctx_lens, "ctx_lens", torch.int32)
     _need(ws, "ws", torch.uint8)
-    _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), ctx_lens.shape[0], H, Dh, max_q, _pool_code(pool_dtype),
-                                       _ptr(ws), ws.numel(), _stream()))
+    if xcd_weights is None:
+        _check(lib.fm_plan_cross_attention(_ptr(ctx_lens), ctx_lens.shape[0], H, Dh, max_q, _pool_code(pool_dtype),
+                                           _ptr(ws), ws.numel(), _stream()))
+        return
+    arr = (ctypes.c_int32 * XCDS)(*weights)
+    _check(lib.fm_plan_cross_attention_weighted(_ptr(ctx_lens), ctx_lens.shape[0], H, Dh, max_q,
+                                                _pool_code(pool_dtype), arr, _ptr(ws), ws.numel(), _stream()))
 
 
 def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,

@@ -386,9 +386,20 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
   return fm::plan_layout(bs, H, Dh, plan_waves(dt), nqf).total;
 }
 
-int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "fm_plan_cross_attention";
+}  // extern "C"
+
+namespace {
+
+// Streaming the same bytes at one wave per SIMD, waves on odd XCDs take 3-5%
+// longer than waves on even ones on most MI355X parts measured (per-wave
+// clocks over one call), so the default plan for the pools that run one wave
+// per SIMD (bf16, fp32) weights the shares 1021 : 979 for even : odd XCDs
+// (1.2% off a call of workload 3).  The e4m3 kernel, two waves per SIMD, ran
+// slower with that skew and keeps equal shares.
+constexpr int32_t kXcdSkew = 21;
+
+int plan_cross_attention(const char* fn, const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
+                         fm_dtype dt, const int32_t* xcd_weights, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (dt != FM_F32 && dt != FM_BF16 && dt != FM_BF16_E4M3)
     return fail(FM_E_UNSUPPORTED, "%s: dtype %d is not FM_F32, FM_BF16 or FM_BF16_E4M3", fn, (int)dt);
   if (bs < 0) return fail(FM_E_INVALID, "%s: bs %d < 0", fn, bs);
@@ -408,9 +419,37 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
   a.H = H;
   a.Dh = Dh;
   a.dtype = (int32_t)dt;
+  for (int x = 0; x < fm::kXcds; ++x) {
+    if (xcd_weights == nullptr) {
+      a.xcd_w[x] = dt == FM_BF16_E4M3 ? 1000 : (x % 2 == 0 ? 1000 + kXcdSkew : 1000 - kXcdSkew);
+    } else {
+      if (xcd_weights[x] < fm::kXcdWeightMin || xcd_weights[x] > fm::kXcdWeightMax)
+        return fail(FM_E_INVALID, "%s: xcd_weights[%d] = %d outside [%d, %d]", fn, x, xcd_weights[x],
+                    fm::kXcdWeightMin, fm::kXcdWeightMax);
+      a.xcd_w[x] = xcd_weights[x];
+    }
+  }
   a.ws = static_cast<uint8_t*>(ws);
   a.lay = lay;
   return from_hip(fm::launch_plan(a, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q, fm_dtype dt,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  return plan_cross_attention("fm_plan_cross_attention", ctx_lens, bs, H, Dh, max_q, dt, nullptr, ws, ws_bytes,
+                              stream);
+}
+
+int fm_plan_cross_attention_weighted(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
+                                     fm_dtype dt, const int32_t* xcd_weights, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  const char* fn = "fm_plan_cross_attention_weighted";
+  if (!xcd_weights) return fail(FM_E_INVALID, "%s: xcd_weights is null", fn);
+  return plan_cross_attention(fn, ctx_lens, bs, H, Dh, max_q, dt, xcd_weights, ws, ws_bytes, stream);
 }
 
 int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,

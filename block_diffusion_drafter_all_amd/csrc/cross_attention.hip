@@ -104,26 +104,22 @@ __device__ __forceinline__ void wait_stores_acknowledged() { asm volatile("s_wai
 
 // ------------------------------------------------------------------- plan --
 
-// Workgroups go round-robin over the 8 XCDs, so wave w (4 per workgroup) runs
-// on XCD (w / 4) mod 8.  Streaming the same bytes at one wave per SIMD, waves
-// on odd XCDs take 3-5% longer than waves on even ones (measured per wave over
-// one call on MI355X: 865-885 us against 824-851 us for equal shares), so for
-// the pools that run one wave per SIMD (bf16, fp32) the shares are weighted
-// (1000 + FM_CROSS_XCD_SKEW) : (1000 - FM_CROSS_XCD_SKEW) for even : odd XCDs
-// (1.2% off a call of workload 3).  The e4m3 kernel, two waves per SIMD, runs
-// slower with any skew and keeps equal shares.  The weights are constants:
-// the cut depends only on the lengths, and so do the results.
-#ifndef FM_CROSS_XCD_SKEW
-#define FM_CROSS_XCD_SKEW 21
-#endif
-
-// First tile of wave w's share of G tiles over NW waves (share_start(G, NW, NW, s) = G).
-__device__ __forceinline__ int64_t share_start(int64_t G, int w, int NW, int skew) {
-  const int64_t kEven = 1000 + skew, kOdd = 1000 - skew;
+// First tile of wave w's share of G tiles over NW waves, shares weighted by
+// the XCD each wave runs on (share_start(G, NW, NW, W) = G).  Workgroups go
+// round-robin over the 8 XCDs, so wave w (4 per workgroup) runs on XCD
+// (w / 4) mod 8.  The weights are inputs: the cut depends only on them and
+// on the lengths, and so do the results.
+__device__ __forceinline__ int64_t share_start(int64_t G, int w, int NW, const int32_t* W) {
+  int64_t sum8 = 0;
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x) sum8 += W[x];
   auto weight_before = [&](int v) -> int64_t {  // total weight of waves 0 .. v-1
-    const int64_t blk = v >> 2, part = v & 3;   // whole workgroups before v, and v's own waves before it
-    const int64_t even_blk = (blk + 1) >> 1, odd_blk = blk >> 1;
-    return 4 * (even_blk * kEven + odd_blk * kOdd) + part * ((blk & 1) ? kOdd : kEven);
+    const int64_t blk = v >> 2, part = v & 3;    // whole workgroups before v, and v's own waves before it
+    const int64_t turns = blk / kXcds, rem = blk % kXcds;
+    int64_t acc = 4 * turns * sum8;
+#pragma unroll
+    for (int x = 0; x < kXcds; ++x) acc += x < rem ? 4 * (int64_t)W[x] : 0;
+    return acc + part * W[rem];
   };
   return G * weight_before(w) / weight_before(NW);
 }
@@ -149,8 +145,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   if (tid == 0) pair_off[a.bs] = carry;
   const int64_t G = carry;
   const int NW = a.lay.n_waves;
-  const int skew = a.dtype == 2 ? 0 : FM_CROSS_XCD_SKEW;
-  for (int w = tid; w <= NW; w += 1024) starts[w] = share_start(G, w, NW, skew);
+  for (int w = tid; w <= NW; w += 1024) starts[w] = share_start(G, w, NW, a.xcd_w);
   __syncthreads();
   for (int w = tid; w < NW; w += 1024) {
     const int64_t g0 = starts[w], g1 = starts[w + 1];

@@ -130,10 +130,17 @@ inline PlanLayout plan_layout(int bs, int H, int Dh, int n_waves, int nqf) {
   return p;
 }
 
+// The weights of the plan's wave shares by XCD: workgroups go round-robin
+// over the 8 XCDs, so wave w (4 per workgroup) runs on XCD (w / 4) mod 8 and
+// its share of the tile stream is proportional to xcd_w[(w / 4) mod 8].
+constexpr int kXcds = 8;
+constexpr int32_t kXcdWeightMin = 500, kXcdWeightMax = 2000;
+
 struct PlanArgs {
   const int32_t* ctx_lens;
   int32_t bs, H;
   int32_t Dh, dtype;  // recorded in the header: a call checks them against its own
+  int32_t xcd_w[kXcds];
   uint8_t* ws;
   PlanLayout lay;
 };

@@ -46,13 +46,16 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* buf, in
 
 // Wave w reads tiles [n w / W, n (w + 1) / W) of the list, K and V of each
 // (CH loads of 1 KB per operand and tile, so the registers held in flight
-// match the tile size and two waves per SIMD fit).
+// match the tile size and two waves per SIMD fit).  With rec, lane 0 of each
+// wave records its start and end on the constant 100 MHz clock, its XCD and
+// its tile count.
 template <int CH>
 __global__ __launch_bounds__(256) void tile_gather_kernel(const uint8_t* k, const uint8_t* v, const int64_t* off,
-                                                          int64_t n_tiles, int n_waves, uint32_t* sink) {
+                                                          int64_t n_tiles, int n_waves, uint32_t* sink, uint64_t* rec) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= n_waves) return;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int64_t t0 = n_tiles * w / n_waves, t1 = n_tiles * (w + 1) / n_waves;
   u32x4_t acc = {0u, 0u, 0u, 0u};
   for (int64_t t = t0; t < t1; t += kDepth) {
@@ -74,6 +77,15 @@ __global__ __launch_bounds__(256) void tile_gather_kernel(const uint8_t* k, cons
       for (int ch = 0; ch < 2 * CH; ++ch) acc ^= r[d][ch];
   }
   finish(sink, w, lane, acc);
+  if (rec != nullptr && lane == 0) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    rec[4 * w] = t_start;
+    rec[4 * w + 1] = t_end;
+    rec[4 * w + 2] = xcc & 0xF;
+    rec[4 * w + 3] = (uint64_t)(t1 - t0);
+  }
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? 0 : -4; }
@@ -93,8 +105,12 @@ int fm_probe_stream_read(const void* buf, size_t bytes, int32_t n_waves, uint32_
   return status_of(hipGetLastError());
 }
 
-int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles, int32_t tile_bytes,
-                         int32_t n_waves, uint32_t* sink, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int tile_gather(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles, int32_t tile_bytes,
+                int32_t n_waves, uint32_t* sink, uint64_t* rec, hipStream_t stream) {
   if (!k || !v || !tile_off || !sink || n_tiles < 1 || n_waves < 4 || n_waves % 4) return -1;
   if (tile_bytes < 1024 || tile_bytes > 8192 || tile_bytes % 1024) return -2;
   if (((uintptr_t)k & 15) || ((uintptr_t)v & 15)) return -1;
@@ -102,13 +118,29 @@ int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, 
   const uint8_t* vb = static_cast<const uint8_t*>(v);
   const dim3 grid((unsigned)(n_waves / 4)), block(256);
   switch (tile_bytes / 1024) {
-    case 1: hipLaunchKernelGGL(tile_gather_kernel<1>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
-    case 2: hipLaunchKernelGGL(tile_gather_kernel<2>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
-    case 4: hipLaunchKernelGGL(tile_gather_kernel<4>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
-    case 8: hipLaunchKernelGGL(tile_gather_kernel<8>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink); break;
+    case 1: hipLaunchKernelGGL(tile_gather_kernel<1>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink, rec); break;
+    case 2: hipLaunchKernelGGL(tile_gather_kernel<2>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink, rec); break;
+    case 4: hipLaunchKernelGGL(tile_gather_kernel<4>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink, rec); break;
+    case 8: hipLaunchKernelGGL(tile_gather_kernel<8>, grid, block, 0, stream, kb, vb, tile_off, n_tiles, n_waves, sink, rec); break;
     default: return -2;  // 3, 5, 6, 7 KB tiles: not a tile size of a pool
   }
   return status_of(hipGetLastError());
+}
+
+}  // namespace
+
+extern "C" {
+
+int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles, int32_t tile_bytes,
+                         int32_t n_waves, uint32_t* sink, hipStream_t stream) {
+  return tile_gather(k, v, tile_off, n_tiles, tile_bytes, n_waves, sink, nullptr, stream);
+}
+
+int fm_probe_tile_gather_timed(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles,
+                               int32_t tile_bytes, int32_t n_waves, uint32_t* sink, uint64_t* wave_rec,
+                               hipStream_t stream) {
+  if (!wave_rec) return -1;
+  return tile_gather(k, v, tile_off, n_tiles, tile_bytes, n_waves, sink, wave_rec, stream);
 }
 
 }  // extern "C"

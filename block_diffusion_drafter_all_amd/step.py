@@ -30,6 +30,7 @@ class StepBuffers:
     out_slots: torch.Tensor | None
     rows_ws: torch.Tensor | None = None
     dit: dict | None = None               # the DiT blocks' activations and workspace
+    xcd_weights: list | None = None       # the plan's per-XCD share weights (None: the library's default)
 
 
 def allocate(w: Workload) -> StepBuffers:
@@ -89,7 +90,8 @@ def write_kv(w: Workload, buf: StepBuffers) -> None:
 
 
 def plan(w: Workload, buf: StepBuffers) -> None:
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.max_q, pool_dtype=w.pool_dtype)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, buf.cross_ws, max_q=w.max_q, pool_dtype=w.pool_dtype,
+                              xcd_weights=buf.xcd_weights)
 
 
 def layer(w: Workload, buf: StepBuffers, l: int) -> None:

@@ -278,9 +278,14 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
  * ``_cross_attention_schedule``: it depends only on shapes and lengths).
  *
  * The work of a call is the stream of 16-key tiles of every (request, head)
- * pair; the plan cuts it into equal contiguous ranges, one per resident
- * wavefront of the attention kernel, so every wave moves the same number of
- * K/V bytes whatever the mix of context lengths.
+ * pair; the plan cuts it into contiguous ranges, one per resident wavefront
+ * of the attention kernel, whatever the mix of context lengths.  Workgroups
+ * run round-robin on the part's 8 XCDs (wave w on XCD (w / 4) mod 8), and a
+ * range's length is proportional to its XCD's weight: by default 1021 for
+ * even and 979 for odd XCDs over bf16 and fp32 pools (waves on odd XCDs
+ * stream ~4% slower on most parts measured), equal over an e4m3 pool.
+ * fm_plan_cross_attention_weighted takes the 8 weights instead.  The cut, and
+ * so every result bit, depends only on the lengths and the weights.
  * ctx_lens  DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
  * max_q     host bound on query rows per request: one draft block (16) or up
  *           to four candidate blocks side by side (<= 64), checked here.
@@ -292,6 +297,18 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
  */
 int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
                             fm_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* fm_plan_cross_attention with the XCD weights given: xcd_weights HOST int32
+ * [8], weight of the waves on XCD x (read during the call; each in
+ * [500, 2000], FM_E_INVALID otherwise).  For parts whose XCDs stream at rates
+ * other than the default's: over bf16 and fp32 pools (one wave per SIMD, bound
+ * by the XCDs' memory rates), weights proportional to each XCD's measured rate
+ * (fm_probe_tile_gather_timed of fm_probe.h measures it) let every wave finish
+ * at the same time.  The e4m3 kernel is bound by instruction issue instead and
+ * runs fastest on equal shares. */
+int fm_plan_cross_attention_weighted(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
+                                     fm_dtype dt, const int32_t* xcd_weights, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /*
  * Paged cross-attention (sglang/model.py ``_paged_cross_attention`` +

@@ -46,6 +46,15 @@ int fm_probe_stream_read(const void* buf, size_t bytes, int32_t n_waves, uint32_
 int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles, int32_t tile_bytes,
                          int32_t n_waves, uint32_t* sink, hipStream_t stream);
 
+/* fm_probe_tile_gather that also times every wave: wave_rec DEVICE uint64
+ * [n_waves][4] receives, for wave w, its start and end on the GPU's constant
+ * 100 MHz clock (s_memrealtime), the XCD it ran on (0-7) and the tiles it
+ * read.  The XCDs' rates (tiles per unit time) give the weights of
+ * fm_plan_cross_attention_weighted (fm.h).  -1 if wave_rec is null. */
+int fm_probe_tile_gather_timed(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles,
+                               int32_t tile_bytes, int32_t n_waves, uint32_t* sink, uint64_t* wave_rec,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,6 +129,27 @@ def test_plan_rejects(lib):
     assert "dtype" in B.fm_last_error()
 
 
+def test_weighted_plan_rejects(lib):
+    """The XCD weights are checked on the host before anything is enqueued."""
+    good = (ctypes.c_int32 * 8)(*([1000] * 8))
+    assert lib.fm_plan_cross_attention_weighted(FAKE, 4, 32, 128, 16, B.FM_BF16, None, FAKE, 1 << 30,
+                                                None) == B.FM_E_INVALID
+    assert "xcd_weights is null" in B.fm_last_error()
+    for bad in (499, 2001, 0, -1000):
+        w = (ctypes.c_int32 * 8)(*([1000] * 7 + [bad]))
+        assert lib.fm_plan_cross_attention_weighted(FAKE, 4, 32, 128, 16, B.FM_BF16, w, FAKE, 1 << 30,
+                                                    None) == B.FM_E_INVALID
+        assert "xcd_weights[7]" in B.fm_last_error()
+    # the shape checks are the unweighted call's
+    assert lib.fm_plan_cross_attention_weighted(FAKE, 4, 32, 96, 16, B.FM_BF16, good, FAKE, 1 << 30,
+                                                None) == B.FM_E_UNSUPPORTED
+    assert lib.fm_plan_cross_attention_weighted(FAKE, 4, 32, 128, 16, B.FM_BF16, good, FAKE, 10,
+                                                None) == B.FM_E_WORKSPACE
+    with pytest.raises(ValueError):
+        B.fm_plan_cross_attention(torch.ones(1, dtype=torch.int32), 2, 64, torch.ones(1, dtype=torch.uint8),
+                                  xcd_weights=[1000] * 7)
+
+
 def _write(lib, **over):
     pools = (B.fm_kv_pool * 2)(_pool(), _pool())
     a = dict(x=FAKE, n_rows=8, d_in=512, dt=B.FM_BF16, w=FAKE, kn=FAKE, rr=FAKE, rp=FAKE, cl=None, win=0, pt=FAKE,
@@ -345,7 +366,7 @@ def test_probe_library_exports_and_validation():
 
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(REPO_DIR, "include", "fm_probe.h")).read(), flags=re.S)
     declared = sorted(set(re.findall(r"\b(fm_probe_[a-z_0-9]+)\s*\(", text)))
-    assert declared == ["fm_probe_stream_read", "fm_probe_tile_gather"]
+    assert declared == ["fm_probe_stream_read", "fm_probe_tile_gather", "fm_probe_tile_gather_timed"]
     plib = ctypes.CDLL(PROBE_LIB_PATH)
     for name in declared:
         assert hasattr(plib, name), name
@@ -359,3 +380,7 @@ def test_probe_library_exports_and_validation():
     assert plib.fm_probe_tile_gather(FAKE, FAKE, FAKE, 10, 3000, 8, FAKE, None) == -2          # tile not k KB
     assert plib.fm_probe_tile_gather(FAKE, FAKE, FAKE, 0, 4096, 8, FAKE, None) == -1           # no tiles
     assert plib.fm_probe_tile_gather(FAKE, FAKE + 8, FAKE, 10, 4096, 8, FAKE, None) == -1      # misaligned
+    plib.fm_probe_tile_gather_timed.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                                vp]
+    assert plib.fm_probe_tile_gather_timed(FAKE, FAKE, FAKE, 10, 4096, 8, FAKE, None, None) == -1  # no records
+    assert plib.fm_probe_tile_gather_timed(FAKE, FAKE, FAKE, 10, 3000, 8, FAKE, FAKE, None) == -2

@@ -975,6 +975,34 @@ def test_plan_records_head_dim_and_pool_type():
     assert torch.isnan(out1).all(), "nothing is computed"
 
 
+def test_plan_xcd_weights():
+    # The plan's per-XCD weights move the cut points and nothing else: the
+    # default weights given explicitly reproduce the default plan bit for bit;
+    # skewed weights give the oracle's result, and the same bits on every call.
+    log("cross-attention planned with explicit XCD weights")
+    w = make_workload(2, weights="random")  # 8 requests: most pairs are cut between waves
+    dev = w.ctx_lens.device
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
+
+    def call():
+        return B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens,
+                                          w.cu_seqlens_q, w.softmax_scale, w.theta, w.eps, ws).clone()
+
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    base = call()
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, xcd_weights=[1021, 979] * 4)
+    assert torch.equal(call(), base), "the default weights, given explicitly, are the default plan"
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, xcd_weights=[700, 1300, 900, 1100, 1000, 1000, 1500, 500])
+    a, b = call(), call()
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) == 0
+    assert torch.equal(a, b), "one plan, one result"
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows)
+    compare(rows_of(w, reqs, a), np.concatenate([ref[b] for b in reqs]), "cross-attention, skewed XCD weights")
+
+
 def test_cross_attention_after_lengths_shrank_flags_bit1():
     # Lengths shortened after the plan so that a wave's planned share runs past
     # the last tile: every request after the first emptied, so the waves that
