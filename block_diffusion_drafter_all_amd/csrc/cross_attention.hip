@@ -124,6 +124,13 @@ __device__ __forceinline__ int64_t share_start(int64_t G, int w, int NW, const i
   return G * weight_before(w) / weight_before(NW);
 }
 
+// Batches up to this many requests keep each request's length and first
+// tile in LDS, so the plan's searches and lookups never wait on memory.
+constexpr int kPlanLdsRequests = 2048;
+
+// One workgroup.  kLds: bs <= kPlanLdsRequests (else the request tables are
+// read back from the workspace).
+template <bool kLds>
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   uint8_t* ws = a.ws;
   PlanHeader* hdr = (PlanHeader*)ws;
@@ -132,17 +139,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   PairRec* prec = (PairRec*)(ws + a.lay.pair_rec);
   int32_t* cnt = (int32_t*)(ws + a.lay.merge_cnt);
   __shared__ int64_t starts[kMaxPlanWaves + 1];
+  __shared__ int64_t lds_off[kLds ? kPlanLdsRequests + 1 : 1];
+  __shared__ int32_t lds_ctx[kLds ? kPlanLdsRequests : 1];
+  const int64_t* off = kLds ? lds_off : pair_off;  // first tile of request b's pairs in the stream
+  auto ctx_of = [&](int b) -> int { return kLds ? lds_ctx[b] : max(0, a.ctx_lens[b]); };
   const int tid = threadIdx.x;
   int64_t carry = 0;
   for (int base = 0; base < a.bs; base += 1024) {
     const int b = base + tid;
-    const int64_t v = b < a.bs ? (int64_t)tiles_of(a.ctx_lens[b]) * a.H : 0;
+    const int ctx = b < a.bs ? max(0, a.ctx_lens[b]) : 0;
     int64_t tot;
-    const int64_t ex = block_exclusive_scan_i64(v, &tot);
-    if (b < a.bs) pair_off[b] = carry + ex;
+    const int64_t ex = block_exclusive_scan_i64((int64_t)tiles_of(ctx) * a.H, &tot);
+    if (b < a.bs) {
+      pair_off[b] = carry + ex;
+      if constexpr (kLds) {
+        lds_off[b] = carry + ex;
+        lds_ctx[b] = ctx;
+      }
+    }
     carry += tot;
   }
-  if (tid == 0) pair_off[a.bs] = carry;
+  if (tid == 0) {
+    pair_off[a.bs] = carry;
+    if constexpr (kLds) lds_off[a.bs] = carry;
+  }
   const int64_t G = carry;
   const int NW = a.lay.n_waves;
   for (int w = tid; w <= NW; w += 1024) starts[w] = share_start(G, w, NW, a.xcd_w);
@@ -152,16 +172,16 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     WaveRec r{};
     r.start = g0;
     if (g1 > g0) {
-      // the request whose pairs hold tile g0: the largest b with pair_off[b] <= g0
+      // the request whose pairs hold tile g0: the largest b with off[b] <= g0
       int lo = 0, hi = a.bs - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (pair_off[mid] <= g0) lo = mid;
+        if (off[mid] <= g0) lo = mid;
         else hi = mid - 1;
       }
-      const int ctx = max(0, a.ctx_lens[lo]);
+      const int ctx = ctx_of(lo);
       const int T = tiles_of(ctx);
-      const int64_t rel = g0 - pair_off[lo];
+      const int64_t rel = g0 - off[lo];
       r.b = lo;
       r.h = (int)(rel / T);
       r.k = (int)(rel % T);
@@ -185,10 +205,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   const int64_t pairs = (int64_t)a.bs * a.H;
   for (int64_t i = tid; i < pairs; i += 1024) {
     const int b = (int)(i / a.H), h = (int)(i % a.H);
-    const int T = tiles_of(a.ctx_lens[b]);
+    const int T = tiles_of(ctx_of(b));
     PairRec pr{};
     if (T > 0) {
-      const int64_t P = pair_off[b] + (int64_t)h * T;
+      const int64_t P = off[b] + (int64_t)h * T;
       pr.w0 = wave_of(P);
       pr.w1 = wave_of(P + T - 1);
       pr.slot0 = starts[pr.w0] < P ? 1 : 0;
@@ -899,7 +919,10 @@ hipError_t launch_cross_dh(const CrossArgs& a, int dtype, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  if (a.bs <= kPlanLdsRequests)
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(1024), 0, s, a);
+  else
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1063,6 +1063,23 @@ def test_seeded_sweep_of_shapes(case):
             assert torch.count_nonzero(buf.cross_out[0][int(rows[b]):int(rows[b + 1])]) == 0
 
 
+@pytest.mark.parametrize("bs", [2048, 2100])
+def test_plan_many_requests(bs):
+    # The plan keeps per-request tables in LDS up to 2048 requests and reads
+    # them back from the workspace beyond: both sides of that line, with
+    # short, empty and tile-edge contexts, on sampled requests.
+    rng = np.random.default_rng(bs)
+    ctx = [int(rng.choice([0, 1, 16, 17])) if rng.random() < 0.2 else int(rng.integers(1, 120)) for _ in range(bs)]
+    log(f"plan over {bs} requests")
+    w = make_workload(3, weights="random", scale_down=dict(ctx_list=ctx, L=1, H=2, Dh=64, ps=16), seed=bs)
+    buf = S.allocate(w)
+    S.run_step(w, buf)
+    torch.cuda.synchronize()
+    assert ws_error_word(buf.cross_ws) == 0
+    reqs = sorted(set([0, 1, bs // 2, bs - 2, bs - 1] + [int(x) for x in rng.choice(bs, 40, replace=False)]))
+    _check_attention(w, buf, reqs, self_blocks=reqs)
+
+
 @pytest.mark.parametrize("case", range(8))
 def test_seeded_sweep_of_writes(case):
     # Seeded draws of the write's shape: request count and commits (so the
