@@ -46,6 +46,20 @@ constexpr int kWin = 512;  // page ids cached per wave
 #ifndef FM_CROSS_DEPTH_F32
 #define FM_CROSS_DEPTH_F32 2
 #endif
+#ifndef FM_CROSS_LDS_KV
+#define FM_CROSS_LDS_KV 1  // pages of >= 16 tokens: K/V tiles stream through LDS (whole-line, nontemporal loads)
+#endif
+#ifndef FM_CROSS_LDS_KV_MAXQF
+#define FM_CROSS_LDS_KV_MAXQF 2  // ... for kernels of at most this many query fragments (four: compute-bound,
+                                  // the LDS reads cost more than the loads gain)
+#endif
+#ifndef FM_CROSS_DEPTH_LDS
+#define FM_CROSS_DEPTH_LDS 2  // tiles in flight per wave through LDS (the loads hold no registers)
+#endif
+
+// s_waitcnt with vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+constexpr int wait_vm_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+constexpr int kLoadNT = 2;  // nt in the buffer instructions' cache-policy operand: streamed once, not kept
 
 // Slot flags.
 // Tile flags, kept above the 16 key-mask bits of a stream slot's word.
@@ -473,6 +487,21 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, con
     __hip_atomic_store((int32_t*)(a.ws + a.lay.merge_cnt) + w0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One K/V tile pair into this wave's LDS slot: NDMA direct-to-LDS loads of
+// 1 KB per operand, lane offsets dma_off (the tile's row and chunk order),
+// nontemporal; K at dst, V at dst + TILE_B.  The tile bases are wave-uniform.
+template <int NDMA, int TILE_B>
+__device__ __forceinline__ void tile_to_lds(const void* k, const void* v, uint8_t* dst, const uint32_t* dma_off) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)k, 0, 0x7fffffff, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)v, 0, 0x7fffffff, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(dst + i * 1024), 16, dma_off[i], 0, 0, kLoadNT);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(dst + TILE_B + i * 1024), 16, dma_off[i], 0, 0, kLoadNT);
+  }
+}
+
 // UNIFORM_PAGE: page_size >= 16, so the 16 keys of a tile share one page and
 // the tile's base address is wave-uniform (scalar), with a per-lane offset that
 // never changes.
@@ -510,6 +539,45 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   // Per-wave LDS window of page ids.
   __shared__ int32_t win_all[4][kWin];
   int32_t* win = win_all[wv];
+
+  // K/V through LDS (pages of >= 16 tokens).  Each operand's tile is 16 rows of
+  // kRowB contiguous bytes.  It arrives in kDma direct-to-LDS loads of 1 KB,
+  // each reading whole rows (whole 128-byte lines, with the nontemporal hint):
+  // lane l of load i fetches 16-byte chunk x ^ key(r) of row r, where
+  // r, x = divmod(64 i + l, kCpr), into LDS chunk x of row r.  The MFMA
+  // operand layout then reads chunk q = 4 ch + g of row c from LDS chunk
+  // q ^ key(c): for each 16 lanes of one g the key spreads the 16 reads over
+  // all 64 banks.  A ring of DEPTH slots per wave; loads hold no registers.
+  constexpr bool LDS_KV = UNIFORM_PAGE && FM_CROSS_LDS_KV != 0 && NQF <= FM_CROSS_LDS_KV_MAXQF;
+  constexpr int kRowB = D * (int)sizeof(pst);
+  constexpr int kTileB = 16 * kRowB;
+  constexpr int kCpr = kRowB / 16;                       // 16-byte chunks per row
+  constexpr int kDma = kTileB / 1024;                    // loads per operand and tile
+  constexpr int kKeyDiv = kCpr >= 16 ? 1 : 16 / kCpr;    // rows sharing one 256-byte bank window
+  constexpr int kKeyMod = kCpr >= 16 ? 16 : kCpr;
+  static_assert(!LDS_KV || (kTileB % 1024 == 0 && DEPTH >= 1 && DEPTH <= 3), "LDS ring shape");
+  constexpr int kSlotB = LDS_KV ? 4 * 2 * kTileB : 16;   // one ring slot: 4 waves x (K, V)
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_ring0[kSlotB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_ring1[DEPTH > 1 ? kSlotB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_ring2[DEPTH > 2 ? kSlotB : 16];
+  auto ring_of = [&](auto dslot) -> uint8_t* {  // this wave's K tile of slot d (its V tile follows)
+    constexpr int d = decltype(dslot)::value;
+    uint8_t* base = d == 0 ? kv_ring0 : d == 1 ? kv_ring1 : kv_ring2;
+    return base + wv * 2 * kTileB;
+  };
+  auto row_key = [](int r) { return (r / kKeyDiv) % kKeyMod; };
+  uint32_t dma_off[LDS_KV ? kDma : 1];  // per lane, per load: byte offset inside the tile (slot stride aware)
+  uint32_t lds_off[LDS_KV ? NCH : 1];   // per lane, per operand chunk: byte offset of its LDS chunk
+  if constexpr (LDS_KV) {
+    const uint32_t slot_b = a.slot_stride32 * (uint32_t)sizeof(pst);
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+      const int u = 64 * i + lane, r = u / kCpr, x = u % kCpr;
+      dma_off[i] = (uint32_t)r * slot_b + (uint32_t)((x ^ row_key(r)) * 16);
+    }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) lds_off[ch] = (uint32_t)((c * kCpr + ((4 * ch + g) ^ row_key(c))) * 16);
+  }
 
   Selector<PT> sel;
   sel.init(lane);
@@ -597,7 +665,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     }
   };
 
-  auto load_slot = [&](StreamSlot<PT, D, kQIn>& s, int j) {
+  auto load_slot = [&](StreamSlot<PT, D, kQIn>& s, int j, auto dslot) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
     uint32_t flags = 0;
@@ -653,7 +721,9 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
         prefetch_page();
       }
     }
-    if (UNIFORM_PAGE) {
+    if constexpr (LDS_KV) {
+      tile_to_lds<kDma, kTileB>(kpool + tile_base, vpool + tile_base, ring_of(dslot), dma_off);
+    } else if (UNIFORM_PAGE) {
       // scalar tile base + 32-bit per-lane byte offset (the SGPR-base addressing form)
       const char* kt = (const char*)(kpool + tile_base);
       const char* vt = (const char*)(vpool + tile_base);
@@ -712,7 +782,26 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_slot = [&](const StreamSlot<PT, D, kQIn>& s) {
+  auto compute_slot = [&](const StreamSlot<PT, D, kQIn>& s, auto dslot) {
+    // The tile's K and V: from the slot's registers, or from its LDS slot once
+    // its loads have landed (the DEPTH - 1 later tiles' loads may still be in
+    // flight; any later query-row or partial loads only make the wait stricter).
+    u32x4_t kk[NCH], vv[NCH];
+    if constexpr (LDS_KV) {
+      __builtin_amdgcn_s_waitcnt(wait_vm_only((DEPTH - 1) * 2 * kDma));
+      const uint8_t* src = ring_of(dslot);
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        kk[ch] = *(const u32x4_t*)(src + lds_off[ch]);
+        vv[ch] = *(const u32x4_t*)(src + kTileB + lds_off[ch]);
+      }
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        kk[ch] = s.k[ch];
+        vv[ch] = s.v[ch];
+      }
+    }
     const uint32_t sflags = s.mf & ~kKeyMask;
     if (sflags & kStart) {
       if (!c_fresh) c_next_pair();
@@ -745,7 +834,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     for (int f = 0; f < NQF; ++f) {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, s.k[ch], qop[f][ch]);
+      for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, kk[ch], qop[f][ch]);
       float sv[4];
       if (smask == kKeyMask) {  // a full tile (wave-uniform): no key to mask
 #pragma unroll
@@ -787,7 +876,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     // V moved to column layout once per tile, shared by every fragment
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const auto vt = sel.template transpose_tile<NCH>(s.v, dt);
+      const auto vt = sel.template transpose_tile<NCH>(vv, dt);
 #pragma unroll
       for (int f = 0; f < NQF; ++f) mma_pv<PV>(o[f][dt], vt, p[f]);
     }
@@ -829,13 +918,28 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   // re-read the last tile, a cache hit, and are fully masked with no flags),
   // so the loop body is straight-line and DEPTH-1 tiles stay in flight.
   StreamSlot<PT, D, kQIn> buf[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d) load_slot(buf[d], d);
+  typedef std::integral_constant<int, 0> S0;
+  typedef std::integral_constant<int, 1> S1;
+  typedef std::integral_constant<int, 2> S2;
+  static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
+  if constexpr (DEPTH >= 2) load_slot(buf[0], 0, S0());
+  if constexpr (DEPTH == 3) load_slot(buf[1], 1, S1());
   for (int it = 0; it < n_tiles; it += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      load_slot(buf[(d + DEPTH - 1) % DEPTH], it + d + DEPTH - 1);
-      compute_slot(buf[d]);
+    if constexpr (DEPTH == 1) {
+      load_slot(buf[0], it, S0());
+      compute_slot(buf[0], S0());
+    } else if constexpr (DEPTH == 3) {
+      load_slot(buf[2], it + 2, S2());
+      compute_slot(buf[0], S0());
+      load_slot(buf[0], it + 3, S0());
+      compute_slot(buf[1], S1());
+      load_slot(buf[1], it + 4, S1());
+      compute_slot(buf[2], S2());
+    } else {
+      load_slot(buf[1], it + 1, S1());
+      compute_slot(buf[0], S0());
+      load_slot(buf[0], it + 2, S0());
+      compute_slot(buf[1], S1());
     }
   }
   const int err = (bad_page ? 1 : 0) | (exhausted ? 2 : 0);
@@ -872,8 +976,10 @@ hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
 
 template <class T, class PT, int D, int DEPTH, int NQF, int OCC>
 hipError_t launch_cross_typed(const CrossArgs& a, hipStream_t s) {
-  // page_size >= 16 keeps each 16-key tile inside one page
-  if (a.log2ps >= 4) return launch_cross_paged<T, PT, D, DEPTH, true, NQF, OCC>(a, s);
+  // page_size >= 16 keeps each 16-key tile inside one page; there the K/V
+  // tiles of kernels with few query fragments stream through LDS
+  constexpr bool kLds = FM_CROSS_LDS_KV != 0 && NQF <= FM_CROSS_LDS_KV_MAXQF;
+  if (a.log2ps >= 4) return launch_cross_paged<T, PT, D, kLds ? FM_CROSS_DEPTH_LDS : DEPTH, true, NQF, OCC>(a, s);
   return launch_cross_paged<T, PT, D, DEPTH, false, NQF, OCC>(a, s);
 }
 
