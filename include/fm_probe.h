@@ -8,7 +8,9 @@
  *       order and with the same split over resident wavefronts, with no
  *       arithmetic,
  * so that an HBM-bound kernel can be placed against what the memory system
- * delivers on the same box, next to the published 8 TB/s.
+ * delivers on the same box, next to the published 8 TB/s.  Every load is a
+ * whole-line 16-byte-per-lane load with the nontemporal hint (the kind the
+ * attention kernel issues). 
  *
  * Conventions: DEVICE pointers are caller-owned device memory; calls are
  * asynchronous on ``stream`` and return 0 (or a negative fm_status value of
