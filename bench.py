@@ -83,8 +83,8 @@ def parse():
                          "per-call events of the roofline and is reported under \"eager\"")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-xcd-calibration", action="store_true",
-                    help="plan with the library's default XCD weights instead of weights measured on this box by "
-                         "the tile-gather probe (timed waves, equal shares) before the timed steps")
+                    help="plan with the library's default XCD weights instead of weights measured on this box on "
+                         "the attention kernel itself (its waves timed) before the timed steps")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the sweep that also times the cross-attention of workloads 1, 2 (warm and with the "
                          "MALL flushed), 3 and 4 in the same run (reported under \"configs\")")
@@ -373,45 +373,48 @@ def probe_ceilings(w, n_waves: int) -> dict:
     return out
 
 
-def xcd_calibration(w, n_waves: int, reps: int = 3) -> dict | None:
-    """Weights of the plan's wave shares by XCD for this box: the tile-gather
-    probe reads layer 0's tiles in equal shares over the plan's waves, timing
-    every wave; an XCD's weight is proportional to its rate (tiles per unit
-    time, averaged over its waves and ``reps`` runs), normalised to a mean of
-    1000 and clamped to [850, 1150].  None when the pool's tiles are not
-    contiguous runs (the probe needs them)."""
+def xcd_calibration(w, reps: int = 3, rounds: int = 2) -> dict | None:
+    """Weights of the plan's wave shares by XCD for this box, measured on the
+    attention kernel itself: layer 0's cross-attention call is run timed
+    (fm_paged_cross_attention_timed), every wave's loop time per tile is
+    averaged by XCD, and an XCD's weight is proportional to its rate (tiles per
+    unit time), normalised to a mean of 1000 and clamped to [800, 1200].  The
+    first round plans with the library's default weights, the next with the
+    weights measured so far; the per-tile times of all rounds are averaged."""
     import torch
 
-    off = tile_offsets(w, 0)
-    if off is None:
-        return None
-    lib = _probe_lib()
-    stream = torch.cuda.current_stream().cuda_stream
-    tb = 16 * w.Dh * w.pools[0].k.element_size()
-    pk, pv = w.pools[0].k, w.pools[0].v
-    sink = torch.empty(n_waves * 64, dtype=torch.int32, device="cuda")
-    rec = torch.zeros(n_waves * 4, dtype=torch.int64, device="cuda")
+    from block_diffusion_drafter_all_amd import binding as B
+
+    nw = plan_waves(w.pool_dtype)
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.max_q, w.pool_dtype), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(w.q[0])
+    clock = torch.zeros((nw, 4), dtype=torch.int64, device="cuda")
     per_tile = [[] for _ in range(8)]
-    for rep in range(reps + 1):
-        if lib.fm_probe_tile_gather_timed(pk.data_ptr(), pv.data_ptr(), off.data_ptr(), off.numel(), tb, n_waves,
-                                          sink.data_ptr(), rec.data_ptr(), stream) != 0:
-            raise RuntimeError("fm_probe_tile_gather_timed failed")
-        torch.cuda.synchronize()
-        if rep == 0:
-            continue  # untimed first run
-        r = rec.view(n_waves, 4).cpu().tolist()
-        for t0, t1, xcd, tiles in r:
-            if tiles > 0:
-                per_tile[int(xcd) % 8].append((t1 - t0) / tiles)
-    if any(not v for v in per_tile):
-        return None
-    t = [sum(v) / len(v) for v in per_tile]
-    rate = [1.0 / x for x in t]
-    mean_rate = sum(rate) / 8
-    weights = [int(round(min(1150.0, max(850.0, 1000.0 * r / mean_rate)))) for r in rate]
+    weights = None
+    for _ in range(rounds):
+        B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=w.max_q, pool_dtype=w.pool_dtype,
+                                  xcd_weights=weights)
+        for rep in range(reps + 1):
+            clock.zero_()
+            B.fm_paged_cross_attention(w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, w.cu_seqlens_q,
+                                       w.softmax_scale, w.theta, w.eps, ws, out=out, max_q=w.max_q,
+                                       fp8_scales=w.fp8_scales(0), wave_clock=clock)
+            torch.cuda.synchronize()
+            if rep == 0:
+                continue  # untimed first run
+            for t0, t1, xcd, tiles in clock.cpu().tolist():
+                if tiles > 0:
+                    per_tile[int(xcd) % 8].append((t1 - t0) / tiles)
+        if any(not v for v in per_tile):
+            return None
+        t = [sum(v) / len(v) for v in per_tile]
+        rate = [1.0 / x for x in t]
+        mean_rate = sum(rate) / 8
+        weights = [int(round(min(1200.0, max(800.0, 1000.0 * r / mean_rate)))) for r in rate]
     return {"xcd_weights": weights, "xcd_us_per_tile": [round(x * 0.01, 4) for x in t],
-            "xcd_calibration": (f"tile-gather probe over layer 0's {off.numel()} tile pairs, {n_waves} waves in "
-                                f"equal shares, {reps} timed runs")}
+            "xcd_calibration": (f"layer 0's cross-attention call timed per wave ({nw} waves), {rounds} rounds of "
+                                f"{reps} timed calls")}
 
 
 def copy_calibration() -> None:
@@ -750,12 +753,9 @@ def main():
     w = make_workload(args.config, layout=args.layout, n_cand=args.candidates, kv_fp8=args.kv_fp8,
                       upstream=args.upstream, dit=args.dit)
     buf = S.allocate(w)
-    # The e4m3 kernel (two waves per SIMD) is bound by its instruction issue, not by the XCDs' memory rates:
-    # weighted shares only slow it, so it keeps the library's equal shares.
-    calib = (None if args.no_xcd_calibration or w.pool_dtype == torch.float8_e4m3fn else
-             xcd_calibration(w, plan_waves(w.pool_dtype)))
-    if calib is not None:
-        buf.xcd_weights = calib["xcd_weights"]
+    calib = None if args.no_xcd_calibration else xcd_calibration(w)
+    xcd_weights = None if calib is None else calib["xcd_weights"]
+    buf.xcd_weights = xcd_weights
     torch.cuda.synchronize()
 
     def one_step(events=None):
@@ -924,8 +924,7 @@ def main():
     if calib is not None:
         out["context"].update(calib)
     else:
-        out["context"]["xcd_weights"] = ("library default" + (" (equal shares over an e4m3 pool)"
-                                                              if w.pool_dtype == torch.float8_e4m3fn else ""))
+        out["context"]["xcd_weights"] = "library default"
     for k in ("stream_read_GBps", "tile_gather_GBps"):
         if k in out["context"]:
             out["roofline"]["frac_of_" + k[:-5]] = achieved / out["context"][k]
@@ -937,7 +936,7 @@ def main():
     if not args.no_configs:
         del w, buf
         torch.cuda.empty_cache()
-        out["configs"] = sweep_configs(args, buf.xcd_weights)
+        out["configs"] = sweep_configs(args, xcd_weights)
     if cpu_sample is not None:
         out["cpu_baseline"] = cpu_baseline_run(cpu_sample)
     print(json.dumps(out), flush=True)

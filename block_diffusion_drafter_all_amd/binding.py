@@ -44,6 +44,7 @@ SYMBOLS = (
     "fm_plan_cross_attention",
     "fm_plan_cross_attention_weighted",
     "fm_paged_cross_attention",
+    "fm_paged_cross_attention_timed",
     "fm_block_self_attention",
 )
 
@@ -119,6 +120,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fm_paged_cross_attention.argtypes = [
         vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
         c_i32, f32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp,
+    ]
+    lib.fm_paged_cross_attention_timed.restype = ctypes.c_int
+    lib.fm_paged_cross_attention_timed.argtypes = [
+        vp, ctypes.c_int, c_i64, vp, ctypes.POINTER(fm_kv_pool), vp, c_i64, c_i32, vp, vp, c_i32, c_i32, c_i32,
+        c_i32, f32, f32, f32, ctypes.POINTER(f32), vp, vp, c_sz, vp, c_i64, vp,
     ]
     lib.fm_block_self_attention.restype = ctypes.c_int
     lib.fm_block_self_attention.argtypes = [
@@ -419,12 +425,14 @@ def fm_plan_cross_attention(ctx_lens, H, Dh, ws, max_q=16, pool_dtype=torch.bflo
 
 
 def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu_seqlens_q, softmax_scale,
-                             rope_theta, eps, ws, out=None, max_q=16, fp8_scales=None):
+                             rope_theta, eps, ws, out=None, max_q=16, fp8_scales=None, wave_clock=None):
     """Paged cross-attention of ``q (total_q, H, Dh)`` onto ``pool``; the plan
     in ``ws`` must come from fm_plan_cross_attention with the same lengths and
     ``max_q`` (query rows per request: 16 per draft block, up to 4 blocks).
     ``fp8_scales``: e4m3 pools only, (q_scale, k_scale, v_scale): a fixed
-    query scale (0 = per request and head) and the key/value descales."""
+    query scale (0 = per request and head) and the key/value descales.
+    ``wave_clock`` (int64 device tensor of shape (waves, 4)): also time every
+    wave (fm_paged_cross_attention_timed)."""
     lib = load_library()
     _need(q, "q")
     _need(q_norm_w, "q_norm_w", torch.float32)
@@ -444,10 +452,16 @@ def fm_paged_cross_attention(q, q_norm_w, pool: KVPool, page_table, ctx_lens, cu
     if page_table.shape[0] < ctx_lens.shape[0] or cu_seqlens_q.shape[0] != ctx_lens.shape[0] + 1:
         raise ValueError("page_table needs a row per request and cu_seqlens_q bs + 1 entries")
     desc = pool.descriptor()
-    _check(lib.fm_paged_cross_attention(
-        _ptr(q), _dtype_code(q, pool.k.dtype), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
-        page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), max_q, ctx_lens.shape[0], H, Dh,
-        softmax_scale, rope_theta, eps, _floats(fp8_scales), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    args = (_ptr(q), _dtype_code(q, pool.k.dtype), total_q, _ptr(q_norm_w), ctypes.byref(desc), _ptr(page_table),
+            page_table.stride(0), pool.page_size, _ptr(ctx_lens), _ptr(cu_seqlens_q), max_q, ctx_lens.shape[0], H, Dh,
+            softmax_scale, rope_theta, eps, _floats(fp8_scales), _ptr(out), _ptr(ws), ws.numel())
+    if wave_clock is None:
+        _check(lib.fm_paged_cross_attention(*args, _stream()))
+    else:
+        _need(wave_clock, "wave_clock", torch.int64)
+        if wave_clock.dim() != 2 or wave_clock.shape[1] != 4:
+            raise ValueError("wave_clock needs shape (waves, 4)")
+        _check(lib.fm_paged_cross_attention_timed(*args, _ptr(wave_clock), wave_clock.shape[0], _stream()))
     return out
 
 

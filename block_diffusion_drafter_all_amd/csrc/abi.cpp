@@ -390,13 +390,11 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
 
 namespace {
 
-// Streaming the same bytes at one wave per SIMD, waves on odd XCDs take 3-5%
-// longer than waves on even ones on most MI355X parts measured (per-wave
-// clocks over one call), so the default plan for the pools that run one wave
-// per SIMD (bf16, fp32) weights the shares 1021 : 979 for even : odd XCDs
-// (1.2% off a call of workload 3).  The e4m3 kernel, two waves per SIMD, ran
-// slower with that skew and keeps equal shares.
-constexpr int32_t kXcdSkew = 21;
+// Waves on odd XCDs take ~10% longer per tile than waves on even ones on the
+// MI355X parts measured (per-wave clocks over one call, K/V through LDS), so
+// the default plan weights the shares 1045 : 955 for even : odd XCDs, over
+// every pool type.  fm_plan_cross_attention_weighted takes measured weights.
+constexpr int32_t kXcdSkew = 45;
 
 int plan_cross_attention(const char* fn, const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
                          fm_dtype dt, const int32_t* xcd_weights, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -421,7 +419,7 @@ int plan_cross_attention(const char* fn, const int32_t* ctx_lens, int32_t bs, in
   a.dtype = (int32_t)dt;
   for (int x = 0; x < fm::kXcds; ++x) {
     if (xcd_weights == nullptr) {
-      a.xcd_w[x] = dt == FM_BF16_E4M3 ? 1000 : (x % 2 == 0 ? 1000 + kXcdSkew : 1000 - kXcdSkew);
+      a.xcd_w[x] = x % 2 == 0 ? 1000 + kXcdSkew : 1000 - kXcdSkew;
     } else {
       if (xcd_weights[x] < fm::kXcdWeightMin || xcd_weights[x] > fm::kXcdWeightMax)
         return fail(FM_E_INVALID, "%s: xcd_weights[%d] = %d outside [%d, %d]", fn, x, xcd_weights[x],
@@ -452,12 +450,18 @@ int fm_plan_cross_attention_weighted(const int32_t* ctx_lens, int32_t bs, int32_
   return plan_cross_attention(fn, ctx_lens, bs, H, Dh, max_q, dt, xcd_weights, ws, ws_bytes, stream);
 }
 
-int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
-                             const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
-                             const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs,
-                             int32_t H, int32_t Dh, float softmax_scale, float rope_theta, float eps,
-                             const float* fp8_scales, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "fm_paged_cross_attention";
+}  // extern "C"
+
+namespace {
+
+// The call of fm_paged_cross_attention and fm_paged_cross_attention_timed
+// (wave_clock: null, or wave_clock_len records of 4 words).
+int paged_cross_attention(const char* fn, const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
+                          const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                          const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs, int32_t H,
+                          int32_t Dh, float softmax_scale, float rope_theta, float eps, const float* fp8_scales,
+                          void* out, void* ws, size_t ws_bytes, uint64_t* wave_clock, int64_t wave_clock_len,
+                          hipStream_t stream) {
   if (total_q < 0 || bs < 0) return fail(FM_E_INVALID, "%s: total_q and bs must be >= 0", fn);
   if (total_q == 0 || bs == 0) return ok();
   if (int s = check_common(fn, dt, H, Dh, eps, rope_theta)) return s;
@@ -489,7 +493,10 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   }
   const fm::PlanLayout lay = fm::plan_layout(bs, H, Dh, plan_waves(dt), nqf);
   if (int s = check_ws(fn, ws, ws_bytes, lay.total)) return s;
+  if (wave_clock != nullptr && wave_clock_len < lay.n_waves)
+    return fail(FM_E_INVALID, "%s: %lld wave records for %d waves", fn, (long long)wave_clock_len, lay.n_waves);
   fm::CrossArgs a{};
+  a.wave_clock = wave_clock;
   a.q = q;
   a.out = out;
   a.q_norm_w = q_norm_w;
@@ -518,6 +525,33 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
   a.lay = lay;
   a.rope = rope_freqs(rope_theta, Dh);
   return from_hip(fm::launch_cross_attention(a, (int)dt, Dh, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
+                             const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                             const int32_t* ctx_lens, const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs,
+                             int32_t H, int32_t Dh, float softmax_scale, float rope_theta, float eps,
+                             const float* fp8_scales, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return paged_cross_attention("fm_paged_cross_attention", q, dt, total_q, q_norm_w, pool, page_table, pt_stride,
+                               page_size, ctx_lens, cu_seqlens_q, max_q, bs, H, Dh, softmax_scale, rope_theta, eps,
+                               fp8_scales, out, ws, ws_bytes, nullptr, 0, stream);
+}
+
+int fm_paged_cross_attention_timed(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
+                                   const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride,
+                                   int32_t page_size, const int32_t* ctx_lens, const int32_t* cu_seqlens_q,
+                                   int32_t max_q, int32_t bs, int32_t H, int32_t Dh, float softmax_scale,
+                                   float rope_theta, float eps, const float* fp8_scales, void* out, void* ws,
+                                   size_t ws_bytes, uint64_t* wave_clock, int64_t wave_clock_len, hipStream_t stream) {
+  const char* fn = "fm_paged_cross_attention_timed";
+  if (wave_clock == nullptr) return fail(FM_E_INVALID, "%s: wave_clock is null", fn);
+  return paged_cross_attention(fn, q, dt, total_q, q_norm_w, pool, page_table, pt_stride, page_size, ctx_lens,
+                               cu_seqlens_q, max_q, bs, H, Dh, softmax_scale, rope_theta, eps, fp8_scales, out, ws,
+                               ws_bytes, wave_clock, wave_clock_len, stream);
 }
 
 int fm_block_self_attention(const void* qkv, fm_dtype dt, int32_t n_blocks, int32_t K, const float* q_norm_w,

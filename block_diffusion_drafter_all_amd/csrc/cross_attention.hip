@@ -535,6 +535,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   }
   const int n_tiles = rec.count;
   if (n_tiles <= 0) return;
+  const uint64_t t_start = a.wave_clock != nullptr ? __builtin_amdgcn_s_memrealtime() : 0;
 
   // Per-wave LDS window of page ids.
   __shared__ int32_t win_all[4][kWin];
@@ -940,6 +941,18 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
       compute_slot(buf[0], S0());
       load_slot(buf[0], it + 2, S0());
       compute_slot(buf[1], S1());
+    }
+  }
+  if (a.wave_clock != nullptr) {  // a timed call: this wave's clock over its tile loop
+    const uint64_t t_loop = __builtin_amdgcn_s_memrealtime();
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    if (lane == 0) {
+      uint64_t* r = a.wave_clock + 4 * (int64_t)w;
+      r[0] = t_start;
+      r[1] = t_loop;
+      r[2] = xcc & 0xF;
+      r[3] = (uint64_t)n_tiles;
     }
   }
   const int err = (bad_page ? 1 : 0) | (exhausted ? 2 : 0);

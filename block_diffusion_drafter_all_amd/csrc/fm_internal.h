@@ -170,6 +170,7 @@ struct CrossArgs {
   uint8_t* ws;
   PlanLayout lay;
   RopeFreqs rope;
+  uint64_t* wave_clock;     // or null: per wave, [start, end of its tile loop, XCD, tiles] on the 100 MHz clock
 };
 
 struct SelfArgs {

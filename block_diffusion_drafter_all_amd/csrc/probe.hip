@@ -12,7 +12,8 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4_t* gptr_u32x4;
 
-constexpr int kDepth = 4;       // 8 KB blocks (or tile pairs) in flight per wave
+constexpr int kDepth = 4;       // 8 KB blocks in flight per wave (streaming read)
+constexpr int kNT = 2;          // nt in the buffer instructions' cache-policy operand
 constexpr int kBlock = 8192;    // bytes of one streaming-read block: eight 1 KB loads
 
 // Nontemporal 16-byte load: streamed once, not kept (the hint the attention
@@ -46,38 +47,60 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* buf, in
   finish(sink, w, lane, acc);
 }
 
-// Wave w reads tiles [n w / W, n (w + 1) / W) of the list, K and V of each
-// (CH loads of 1 KB per operand and tile, so the registers held in flight
-// match the tile size and two waves per SIMD fit).  With rec, lane 0 of each
-// wave records its start and end on the constant 100 MHz clock, its XCD and
-// its tile count.
+// Wave w reads tiles [n w / W, n (w + 1) / W) of the list, K and V of each,
+// the way the attention kernel takes them: CH direct-to-LDS loads of 1 KB per
+// operand and tile (whole lines, nontemporal) into a ring of two tiles per
+// wave, each read back from LDS once its loads have landed.  With rec, lane 0
+// of each wave records its start and end on the constant 100 MHz clock, its
+// XCD and its tile count.
+template <int CH>
+__device__ __forceinline__ void gather_tile_to_lds(const uint8_t* k, const uint8_t* v, int64_t o, uint8_t* dst,
+                                                   uint32_t lane_off) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + o), 0, CH * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + o), 0, CH * 1024, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(dst + i * 1024), 16, lane_off + i * 1024, 0, 0, kNT);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(dst + (CH + i) * 1024), 16, lane_off + i * 1024, 0, 0,
+                                             kNT);
+  }
+}
+
 template <int CH>
 __global__ __launch_bounds__(256) void tile_gather_kernel(const uint8_t* k, const uint8_t* v, const int64_t* off,
                                                           int64_t n_tiles, int n_waves, uint32_t* sink, uint64_t* rec) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[4 * 2 * CH * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[4 * 2 * CH * 1024];
   const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int w = blockIdx.x * 4 + wv;
   if (w >= n_waves) return;
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int64_t t0 = n_tiles * w / n_waves, t1 = n_tiles * (w + 1) / n_waves;
+  const int64_t* soff = off;
+  uint8_t* s0 = ring0 + wv * 2 * CH * 1024;
+  uint8_t* s1 = ring1 + wv * 2 * CH * 1024;
+  const uint32_t lane_off = (uint32_t)lane * 16;
+  auto tile = [&](int64_t t) -> int64_t {  // wave-uniform offset of tile t (past the share: its last tile again)
+    return ((const __attribute__((address_space(4))) int64_t*)soff)[t < t1 ? t : t1 - 1];
+  };
+  constexpr int kWait = 2 * CH;  // the next tile's loads may stay in flight
   u32x4_t acc = {0u, 0u, 0u, 0u};
-  for (int64_t t = t0; t < t1; t += kDepth) {
-    u32x4_t r[kDepth][2 * CH];
+  auto drain = [&](const uint8_t* src) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int64_t tt = t + d < t1 ? t + d : t1 - 1;
-      const int64_t o = off[tt];  // wave-uniform
-#pragma unroll
-      for (int ch = 0; ch < CH; ++ch) {
-        r[d][ch] = ld(k + o + ch * 1024 + lane * 16);
-        r[d][CH + ch] = ld(v + o + ch * 1024 + lane * 16);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load of the group issued before the first use
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d)
-#pragma unroll
-      for (int ch = 0; ch < 2 * CH; ++ch) acc ^= r[d][ch];
+    for (int i = 0; i < 2 * CH; ++i) acc ^= *(const u32x4_t*)(src + i * 1024 + lane_off);
+  };
+  if (t1 > t0) gather_tile_to_lds<CH>(k, v, tile(t0), s0, lane_off);
+  for (int64_t t = t0; t < t1; t += 2) {
+    gather_tile_to_lds<CH>(k, v, tile(t + 1), s1, lane_off);
+    __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | 0x0F70);
+    drain(s0);
+    gather_tile_to_lds<CH>(k, v, tile(t + 2), s0, lane_off);
+    __builtin_amdgcn_s_waitcnt((kWait & 15) | ((kWait >> 4) << 14) | 0x0F70);
+    drain(s1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70 & 0xC07F);  // every load landed before the wave ends
   finish(sink, w, lane, acc);
   if (rec != nullptr && lane == 0) {
     const uint64_t t_end = __builtin_amdgcn_s_memrealtime();

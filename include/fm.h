@@ -281,10 +281,10 @@ size_t fm_cross_attention_workspace_size(int32_t bs, int32_t H, int32_t Dh, int3
  * pair; the plan cuts it into contiguous ranges, one per resident wavefront
  * of the attention kernel, whatever the mix of context lengths.  Workgroups
  * run round-robin on the part's 8 XCDs (wave w on XCD (w / 4) mod 8), and a
- * range's length is proportional to its XCD's weight: by default 1021 for
- * even and 979 for odd XCDs over bf16 and fp32 pools (waves on odd XCDs
- * stream ~4% slower on most parts measured), equal over an e4m3 pool.
- * fm_plan_cross_attention_weighted takes the 8 weights instead.  The cut, and
+ * range's length is proportional to its XCD's weight: by default 1045 for
+ * even and 955 for odd XCDs (waves on odd XCDs stream ~10% slower per tile on
+ * the parts measured).  fm_plan_cross_attention_weighted takes the 8 weights
+ * instead.  The cut, and
  * so every result bit, depends only on the lengths and the weights.
  * ctx_lens  DEVICE int32 [bs]: keys per request, p + 1 (0 = empty context).
  * max_q     host bound on query rows per request: one draft block (16) or up
@@ -301,11 +301,9 @@ int fm_plan_cross_attention(const int32_t* ctx_lens, int32_t bs, int32_t H, int3
 /* fm_plan_cross_attention with the XCD weights given: xcd_weights HOST int32
  * [8], weight of the waves on XCD x (read during the call; each in
  * [500, 2000], FM_E_INVALID otherwise).  For parts whose XCDs stream at rates
- * other than the default's: over bf16 and fp32 pools (one wave per SIMD, bound
- * by the XCDs' memory rates), weights proportional to each XCD's measured rate
- * (fm_probe_tile_gather_timed of fm_probe.h measures it) let every wave finish
- * at the same time.  The e4m3 kernel is bound by instruction issue instead and
- * runs fastest on equal shares. */
+ * other than the default's: weights proportional to each XCD's measured rate
+ * (fm_paged_cross_attention_timed measures it) let every wave finish at the
+ * same time. */
 int fm_plan_cross_attention_weighted(const int32_t* ctx_lens, int32_t bs, int32_t H, int32_t Dh, int32_t max_q,
                                      fm_dtype dt, const int32_t* xcd_weights, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
@@ -364,6 +362,23 @@ int fm_paged_cross_attention(const void* q, fm_dtype dt, int64_t total_q, const 
                              const int32_t* cu_seqlens_q, int32_t max_q, int32_t bs, int32_t H, int32_t Dh,
                              float softmax_scale, float rope_theta, float eps, const float* fp8_scales,
                              void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* fm_paged_cross_attention that also times its waves, to measure the XCDs'
+ * rates for fm_plan_cross_attention_weighted on the part at hand: every wave
+ * with tiles writes wave_clock[4 w .. 4 w + 3] (DEVICE uint64) = the start
+ * and the end of its tile loop on the GPU's constant 100 MHz clock
+ * (s_memrealtime), the XCD it ran on (0-7) and its tile count; waves without
+ * tiles write nothing.  wave_clock_len is the number of records the array
+ * holds, at least the plan's wave count (4 per CU, times 2 over an e4m3 pool;
+ * at most 4096), FM_E_INVALID otherwise or if wave_clock is null.  The
+ * results are those of fm_paged_cross_attention, bit for bit. */
+int fm_paged_cross_attention_timed(const void* q, fm_dtype dt, int64_t total_q, const float* q_norm_w,
+                                   const fm_kv_pool* pool, const int32_t* page_table, int64_t pt_stride,
+                                   int32_t page_size, const int32_t* ctx_lens, const int32_t* cu_seqlens_q,
+                                   int32_t max_q, int32_t bs, int32_t H, int32_t Dh, float softmax_scale,
+                                   float rope_theta, float eps, const float* fp8_scales, void* out, void* ws,
+                                   size_t ws_bytes, uint64_t* wave_clock, int64_t wave_clock_len,
+                                   hipStream_t stream);
 
 /* ------------------------------------------------------- self-attention -- */
 

@@ -41,18 +41,20 @@ int fm_probe_stream_read(const void* buf, size_t bytes, int32_t n_waves, uint32_
 /* Gather of n_tiles K/V tile pairs: tile i is tile_bytes contiguous bytes at
  * k + tile_off[i] and as many at v + tile_off[i] (tile_off DEVICE int64
  * [n_tiles], byte offsets, 16-byte aligned; tile_bytes 1024, 2048, 4096 or
- * 8192, -2 otherwise).  The tiles are cut into n_waves equal contiguous ranges, one per
- * wavefront (the attention plan's equal shares), each read in order with four
- * tiles in flight, 1 KB per load instruction.  sink DEVICE uint32[n_waves * 64].
- * n_waves a positive multiple of 4. */
+ * 8192, -2 otherwise).  The tiles are cut into n_waves equal contiguous ranges,
+ * one per wavefront (the attention plan's equal shares), each read in order
+ * the way the attention kernel reads them: direct-to-LDS loads of 1 KB per
+ * instruction, two tile pairs in flight, each read back from LDS.
+ * sink DEVICE uint32[n_waves * 64].  n_waves a positive multiple of 4. */
 int fm_probe_tile_gather(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles, int32_t tile_bytes,
                          int32_t n_waves, uint32_t* sink, hipStream_t stream);
 
 /* fm_probe_tile_gather that also times every wave: wave_rec DEVICE uint64
  * [n_waves][4] receives, for wave w, its start and end on the GPU's constant
  * 100 MHz clock (s_memrealtime), the XCD it ran on (0-7) and the tiles it
- * read.  The XCDs' rates (tiles per unit time) give the weights of
- * fm_plan_cross_attention_weighted (fm.h).  -1 if wave_rec is null. */
+ * read: the XCDs' memory rates with no arithmetic beside them (the attention
+ * kernel's own, which fm_paged_cross_attention_timed of fm.h measures, spread
+ * wider).  -1 if wave_rec is null. */
 int fm_probe_tile_gather_timed(const void* k, const void* v, const int64_t* tile_off, int64_t n_tiles,
                                int32_t tile_bytes, int32_t n_waves, uint32_t* sink, uint64_t* wave_rec,
                                hipStream_t stream);

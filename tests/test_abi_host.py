@@ -112,6 +112,20 @@ def test_cross_attention_rejects(lib, over, status, needle):
     assert needle in B.fm_last_error()
 
 
+def test_timed_cross_attention_rejects(lib):
+    """The timed call takes the untimed call's checks plus its record array."""
+    pool = _pool()
+    args = [FAKE, B.FM_BF16, 16, FAKE, ctypes.byref(pool), FAKE, 4, 16, FAKE, FAKE, 16, 1, 4, 64, 0.125, 1e6, 1e-6,
+            None, FAKE, FAKE, 1 << 30]
+    assert lib.fm_paged_cross_attention_timed(*args, None, 4096, None) == B.FM_E_INVALID
+    assert "wave_clock is null" in B.fm_last_error()
+    assert lib.fm_paged_cross_attention_timed(*args, FAKE, 3, None) == B.FM_E_INVALID
+    assert "wave records" in B.fm_last_error()
+    bad = list(args)
+    bad[13] = 96  # head dim
+    assert lib.fm_paged_cross_attention_timed(*bad, FAKE, 4096, None) == B.FM_E_UNSUPPORTED
+
+
 def test_cross_attention_empty_is_noop(lib):
     assert _cross(lib, total_q=0, q=None) == B.FM_OK
     assert _cross(lib, bs=0) == B.FM_OK

@@ -990,7 +990,7 @@ def test_plan_xcd_weights():
 
     B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
     base = call()
-    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, xcd_weights=[1021, 979] * 4)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, xcd_weights=[1045, 955] * 4)
     assert torch.equal(call(), base), "the default weights, given explicitly, are the default plan"
     B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, xcd_weights=[700, 1300, 900, 1100, 1000, 1000, 1500, 500])
     a, b = call(), call()
@@ -1001,6 +1001,34 @@ def test_plan_xcd_weights():
     pk, pv, rows = compact_context(w, 0, reqs)
     ref = oracle_cross(w, 0, reqs, pk, pv, rows)
     compare(rows_of(w, reqs, a), np.concatenate([ref[b] for b in reqs]), "cross-attention, skewed XCD weights")
+
+
+def test_timed_cross_attention():
+    # The timed call computes the untimed call's bits, and every wave with
+    # tiles records its XCD, its tile count and a loop time that moves forward;
+    # the counts add up to the plan's tile stream.
+    log("cross-attention with its waves timed")
+    w = make_workload(2, weights="random")
+    dev = w.ctx_lens.device
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 16), dtype=torch.uint8, device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws)
+    args = (w.q[0], w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, w.cu_seqlens_q, w.softmax_scale, w.theta,
+            w.eps, ws)
+    base = B.fm_paged_cross_attention(*args).clone()
+    waves = torch.cuda.get_device_properties(0).multi_processor_count * 4
+    clock = torch.zeros((waves, 4), dtype=torch.int64, device=dev)
+    timed = B.fm_paged_cross_attention(*args, wave_clock=clock)
+    torch.cuda.synchronize()
+    assert torch.equal(timed, base)
+    r = clock.cpu().numpy()
+    live = r[:, 3] > 0
+    assert live.sum() > 0
+    assert (r[live, 1] > r[live, 0]).all()
+    assert ((r[live, 2] >= 0) & (r[live, 2] < 8)).all()
+    total = sum((int(c) + 15) // 16 for c in w.ctx_lens.cpu().tolist()) * w.H
+    assert int(r[:, 3].sum()) == total
+    with pytest.raises(B.FmError):
+        B.fm_paged_cross_attention(*args, wave_clock=clock[: waves // 2])
 
 
 def test_cross_attention_after_lengths_shrank_flags_bit1():
