@@ -270,7 +270,9 @@ __device__ __forceinline__ bool plan_matches(const PlanHeader& ph, const CrossAr
 // per-tensor scale when one is given (vllm/model.py ``_dit``), and the stored
 // e4m3 row is q^ / scale, rounded once from fp32; the scale goes to q_scale.
 // A request with an empty context gets its zero output rows here instead.
-// One wavefront per (request, head).
+// One wavefront per (request, head).  Launched for kernels of several query
+// fragments (candidate blocks); the one-fragment kernel does the same work on
+// its own rows (bf16 and fp32 rows: the same bits).
 template <class T, class PT, int D, int NQF>
 __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   typedef typename T::storage st;
@@ -371,17 +373,61 @@ __global__ __launch_bounds__(256) void q_prologue_kernel(CrossArgs a) {
   }
 }
 
+// The output rows of every request with an empty context are zero: wave w
+// writes those of requests w, w + n_waves, ... (the one-fragment kernels, which
+// have no query prologue kernel).
+template <class T, int D>
+__device__ __forceinline__ void zero_empty_rows(const CrossArgs& a, int w) {
+  typedef typename T::storage st;
+  for (int b = w; b < a.bs; b += a.lay.n_waves) {
+    if (sload_i32(a.ctx_lens + b) > 0) continue;
+    const int r0 = max(0, sload_i32(a.cu_q + b));
+    const int nq = max(0, min(min(sload_i32(a.cu_q + b + 1), a.total_q) - r0, kQRows));
+    u32x4_t* o = (u32x4_t*)((st*)a.out + (int64_t)r0 * a.H * D);
+    const int n16 = nq * a.H * D * (int)sizeof(st) / 16;
+    for (int i = lane_id(); i < n16; i += 64) o[i] = (u32x4_t){0u, 0u, 0u, 0u};
+  }
+}
+
+// The e4m3 query scale of one (request, head) whose 16 prepared rows the wave
+// holds (x: this lane's values): the rows' largest magnitude / 448 (at least
+// 1e-12 / 448), or the fixed per-tensor scale when one is given; r = 1 / qs.
+struct QScale {
+  float qs, r;
+};
+template <int N>
+__device__ __forceinline__ QScale query_scale(const CrossArgs& a, const float (&x)[N]) {
+  if (a.q_static > 0.f) return QScale{a.q_static, a.q_static_inv};
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const float am = fmaxf(amax, 1e-12f);
+  return QScale{am / 448.0f, 448.0f / am};
+}
+
+// 16 consecutive columns x[0..15] times r as one chunk of e4m3 codes (nearest
+// even, saturating at 448), column j in byte j.
+__device__ __forceinline__ u32x4_t pack_e4m3_chunk(const float* x, float r) {
+  u32x4_t v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) v[w] = f32x4_to_e4m3(x[4 * w] * r, x[4 * w + 1] * r, x[4 * w + 2] * r, x[4 * w + 3] * r);
+  return v;
+}
+
 // -------------------------------------------------------- cross-attention --
 
-// One K/V tile in the load ring.  With one query fragment, the pair's
-// prepared query rows ride along with its first tile (q); with more, they are
-// read when that tile is computed (q unused).  Which pair a tile belongs to is
+// One K/V tile in the load ring.  With one query fragment, the pair's raw
+// query rows ride along with its first tile (QN 16-byte chunks per lane, q),
+// to be normed and rotated when that tile is computed; with more, the
+// prepared rows are read then (q unused).  Which pair a tile belongs to is
 // not stored: the compute side walks the same pair sequence as the loader.
-template <class T, int D, bool QIN>
+template <class T, int D, int QN>
 struct StreamSlot {
   u32x4_t k[D / (4 * T::EPC)];
   u32x4_t v[D / (4 * T::EPC)];
-  u32x4_t q[QIN ? D / (4 * T::EPC) : 1];
+  u32x4_t q[QN > 0 ? QN : 1];
   uint32_t mf;  // bits 0-15: token t of the tile is a valid key; above: kStart, kEnd, kWhole, kPart1
 };
 
@@ -512,22 +558,34 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   typedef typename PT::storage pst;
   typedef typename PvType<PT>::type PV;
   constexpr bool kFp8 = std::is_same<PT, E4m3>::value;
-  // the pair's query rows ride with its first tile (one fragment), else they are read when it is computed
+  // With one fragment the pair's raw query rows ride with its first tile and
+  // the kernel norms and rotates them itself (q_prologue_kernel's work, fused);
+  // with more, q_prologue_kernel prepares them and they are read when the
+  // pair's first tile is computed.
   constexpr bool kQIn = NQF == 1;
   constexpr int EPC = PT::EPC;
   constexpr int NCH = D / (4 * EPC);
   constexpr int NDT = D / 16;
+  constexpr int kQS = EPC / T::EPC;  // 16-byte chunks of raw query row per operand chunk
+  typedef StreamSlot<PT, D, kQIn ? NCH * kQS : 0> Slot;
   const int lane = lane_id(), g = lane >> 4, c = lane & 15;
   const int wv = wave_in_block();
   uint8_t* ws = a.ws;
   PlanHeader* hdr = (PlanHeader*)ws;
   const int w = blockIdx.x * 4 + wv;
   if (w >= a.lay.n_waves) return;
+  // the query norm weight, issued with the plan loads
+  float qnw_reg[kQIn ? D / 64 : 1];
+  if constexpr (kQIn) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) qnw_reg[i] = load_f32(a.q_norm_w + lane + 64 * i);
+  }
   // The plan header and this wave's record, read together.
   // (No branch on the header before the record is read: the two loads issue
   // together and a mismatched plan simply leaves the wave no tiles.)
   const PlanHeader ph = *(const PlanHeader*)hdr;
   const WaveRec rec = ((const WaveRec*)(ws + a.lay.wave_rec))[w];
+  if constexpr (kQIn) zero_empty_rows<T, D>(a, w);
   const bool plan_ok = plan_matches<T, PT, D, NQF>(ph, a);
   if (!plan_ok) {  // no plan for these sizes: nothing is computed, and the error word says so
     if (w == 0 && lane_id() == 0) atomicOr(&hdr->error, 4);
@@ -540,6 +598,22 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   // Per-wave LDS window of page ids.
   __shared__ int32_t win_all[4][kWin];
   int32_t* win = win_all[wv];
+  // Per-wave LDS copy of the query norm weight (D floats) and the inverse RoPE
+  // frequencies (D / 2), read from LDS so that norming a pair's rows waits on
+  // no vector-memory load behind the tiles in flight and holds no registers.
+  __shared__ float qnw_all[4][kQIn ? D + D / 2 : 1];
+  float* qnw = qnw_all[wv];
+  if constexpr (kQIn) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) qnw[lane + 64 * i] = qnw_reg[i];
+    if (lane == 0) {  // (a per-lane index into the kernel argument would cost scratch)
+#pragma unroll
+      for (int i = 0; i < D / 2; ++i) qnw[D + i] = a.rope.inv[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 
   // K/V through LDS (pages of >= 16 tokens).  Each operand's tile is 16 rows of
   // kRowB contiguous bytes.  It arrives in kDma direct-to-LDS loads of 1 KB,
@@ -666,7 +740,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     }
   };
 
-  auto load_slot = [&](StreamSlot<PT, D, kQIn>& s, int j, auto dslot) {
+  auto load_slot = [&](Slot& s, int j, auto dslot) {
     int64_t off = kv_last;
     bool ok = false, bad = false;
     uint32_t flags = 0;
@@ -711,10 +785,15 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
               (page_ok ? (int64_t)page * a.pool.page_stride + (int64_t)(tok_c & ps_mask) * a.pool.slot_stride : 0);
         kv_last = off;
       }
-      if (kQIn && (flags & kStart)) {  // this pair's prepared query rows ride along with its first tile
-        const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)lb * kQRows + c) * a.H + lh) * D;
+      if (kQIn && (flags & kStart)) {
+        // this pair's raw query rows ride along with its first tile: lane (g, c)
+        // takes row c's columns ch*4*EPC + g*EPC .. +EPC-1 (the operand layout);
+        // a row past the request's count reads row 0 and is zeroed when computed
+        const int r0 = max(0, sload_i32(a.cu_q + lb));
+        const int nq = min(sload_i32(a.cu_q + lb + 1), a.total_q) - r0;
+        const st* qrow = (const st*)a.q + ((int64_t)(c < nq ? r0 + c : 0) * a.H + lh) * D;
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) s.q[ch] = load16(qrow + ch * 4 * EPC + g * EPC);
+        for (int i = 0; i < NCH * kQS; ++i) s.q[i] = load16(qrow + (i / kQS) * 4 * EPC + g * EPC + (i % kQS) * T::EPC);
       }
       ++lk;
       if (j + 1 < n_tiles) {
@@ -783,7 +862,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     for (int dt = 0; dt < NDT; ++dt) o[f][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_slot = [&](const StreamSlot<PT, D, kQIn>& s, auto dslot) {
+  auto compute_slot = [&](const Slot& s, auto dslot) {
     // The tile's K and V: from the slot's registers, or from its LDS slot once
     // its loads have landed (the DEPTH - 1 later tiles' loads may still be in
     // flight; any later query-row or partial loads only make the wait stricter).
@@ -807,11 +886,27 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     if (sflags & kStart) {
       if (!c_fresh) c_next_pair();
       c_fresh = false;
-      if (kFp8) score_scale = a.qscale_log2 * sload_f32((const float*)(ws + a.lay.q_scale) + (int64_t)cb * a.H + chh);
       if constexpr (kQIn) {
+        // q^ = RoPE(RMSNorm(q)) at position ctx_len + c, as q_prologue_kernel
+        // makes it, from the raw rows (zero past the request's rows)
+        float qf[D / 4];
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) qop[0][ch] = s.q[ch];
+        for (int i = 0; i < NCH * kQS; ++i)
+#pragma unroll
+          for (int j = 0; j < T::EPC; ++j) qf[i * T::EPC + j] = c < cnq ? chunk_elem<T>(s.q[i], j) : 0.f;
+        norm_rope_row_lds<PT, D>(qf, qnw, qnw + D, a.eps, max(0, sload_i32(a.ctx_lens + cb)) + c, g);
+        if constexpr (kFp8) {
+          const QScale qsc = query_scale(a, qf);
+          score_scale = a.qscale_log2 * qsc.qs;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) qop[0][ch] = pack_e4m3_chunk(&qf[ch * EPC], qsc.r);
+        } else {
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) qop[0][ch] = pack_chunk<PT>(&qf[ch * EPC]);
+        }
       } else {  // every fragment's prepared rows, read now
+        if (kFp8)
+          score_scale = a.qscale_log2 * sload_f32((const float*)(ws + a.lay.q_scale) + (int64_t)cb * a.H + chh);
         const pst* qrow = (const pst*)(ws + a.lay.q_hat) + (((int64_t)cb * kQRows * NQF + c) * a.H + chh) * D;
 #pragma unroll
         for (int f = 0; f < NQF; ++f)
@@ -918,7 +1013,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   // Every slot index is loaded unconditionally (indices past the range
   // re-read the last tile, a cache hit, and are fully masked with no flags),
   // so the loop body is straight-line and DEPTH-1 tiles stay in flight.
-  StreamSlot<PT, D, kQIn> buf[DEPTH];
+  Slot buf[DEPTH];
   typedef std::integral_constant<int, 0> S0;
   typedef std::integral_constant<int, 1> S1;
   typedef std::integral_constant<int, 2> S2;
@@ -979,9 +1074,11 @@ template <class T, class PT, int D, int DEPTH, bool UNIFORM_PAGE, int NQF, int O
 hipError_t launch_cross_paged(const CrossArgs& a, hipStream_t s) {
   const int64_t pairs = (int64_t)a.bs * a.H;
   if (!grid_fits((pairs + 3) / 4, 256) || !grid_fits((a.lay.n_waves + 3) / 4, 256)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((q_prologue_kernel<T, PT, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if constexpr (NQF > 1) {  // one fragment: the attention kernel prepares its query rows itself
+    hipLaunchKernelGGL((q_prologue_kernel<T, PT, D, NQF>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const unsigned grid = (unsigned)((a.lay.n_waves + 3) / 4);
   hipLaunchKernelGGL((cross_attn_kernel<T, PT, D, DEPTH, UNIFORM_PAGE, NQF, OCC>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();

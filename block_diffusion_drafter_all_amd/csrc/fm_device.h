@@ -382,6 +382,35 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[D / 4], const float* __
   }
 }
 
+// norm_rope_row with the weight and the inverse frequencies (inv[i] for the
+// pair at columns 2i, 2i + 1) read per lane from arrays (LDS copies): the same
+// arithmetic in the same order, so the same bits.
+template <class T, int D>
+__device__ __forceinline__ void norm_rope_row_lds(float (&x)[D / 4], const float* w, const float* inv, float eps,
+                                                  int pos, int g) {
+  constexpr int EPC = T::EPC;
+  constexpr int NCH = D / (4 * EPC);
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 4; ++k) ss += x[k] * x[k];
+  ss = wave_sum_groups(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+  const float fpos = (float)pos;
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int j = 0; j < EPC; j += 2) {
+      const int col = ch * 4 * EPC + g * EPC + j;
+      float sn, cs;
+      angle_sincos(fpos * inv[col >> 1], &sn, &cs);
+      const float y0 = x[ch * EPC + j] * rs * w[col];
+      const float y1 = x[ch * EPC + j + 1] * rs * w[col + 1];
+      x[ch * EPC + j] = y0 * cs - y1 * sn;
+      x[ch * EPC + j + 1] = y1 * cs + y0 * sn;
+    }
+  }
+}
+
 template <class T>
 __device__ __forceinline__ void store4(typename T::storage* p, const f32x4_t& v, float scale);
 

@@ -1063,6 +1063,56 @@ def test_cross_attention_after_lengths_shrank_flags_bit1():
     compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), "cross-attention after planning again")
 
 
+@pytest.mark.parametrize("kind,ps", [("bf16", 16), ("bf16", 4), ("fp32", 16), ("e4m3", 16), ("e4m3", 1)])
+def test_one_fragment_query_rows_and_other_plan(kind, ps):
+    # The one-fragment kernels norm and rotate their query rows themselves and
+    # write the zero rows of empty contexts: ragged row counts (a request with
+    # no rows, one with one), empty and sub-tile contexts; then a plan made for
+    # two fragments, which leaves only those zero rows and sets error bit 2.
+    log(f"one-fragment query rows, {kind} pool, page size {ps}")
+    ctx = [0, 1, 15, 0, 300, 1000, 0]
+    nq = [16, 1, 16, 5, 0, 9, 16]
+    sd = dict(ctx_list=ctx, L=1, H=3, Dh=128, ps=ps)
+    if kind == "fp32":
+        sd["dtype"] = torch.float32
+    w = make_workload(3, weights="random", scale_down=sd, kv_fp8=kind == "e4m3", seed=31)
+    dev = w.ctx_lens.device
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(nq)]), dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    q = torch.randn((int(cu[-1]), w.H, w.Dh), generator=gen, device=dev).to(w.q[0].dtype)
+    w.q[0], w.cu_seqlens_q = q, cu
+    ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, 32, w.pool_dtype), dtype=torch.uint8,
+                     device=dev)
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=16, pool_dtype=w.pool_dtype)
+    out = torch.full_like(q, float("nan"))
+    B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu, w.softmax_scale,
+                               w.theta, w.eps, ws, out=out, max_q=16)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) == 0
+    reqs = list(range(w.bs))
+    pk, pv, rows = compact_context(w, 0, reqs)
+    ref = oracle_cross(w, 0, reqs, pk, pv, rows, q=q)
+    compare(rows_of(w, reqs, out), np.concatenate([ref[b] for b in reqs]), f"one-fragment cross {kind} ps{ps}")
+    cuh = cu.cpu().numpy()
+    for b, n in enumerate(ctx):
+        if n == 0:
+            assert (out[cuh[b]:cuh[b + 1]] == 0).all(), "an empty context must give exactly zero"
+    # a plan for two fragments: the one-fragment call computes nothing else
+    B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=32, pool_dtype=w.pool_dtype)
+    out2 = torch.full_like(q, float("nan"))
+    B.fm_paged_cross_attention(q, w.q_norm_w[0], w.pools[0], w.page_table, w.ctx_lens, cu, w.softmax_scale,
+                               w.theta, w.eps, ws, out=out2, max_q=16)
+    torch.cuda.synchronize()
+    assert ws_error_word(ws) & 4, "a plan for other sizes sets error bit 2"
+    for b, n in enumerate(ctx):
+        r = out2[cuh[b]:cuh[b + 1]].float()
+        if n == 0:
+            assert (r == 0).all(), "empty contexts still get their zero rows"
+        else:
+            assert torch.isnan(r).all(), "nothing else is written"
+
+
 @pytest.mark.parametrize("case", range(16))
 def test_seeded_sweep_of_shapes(case):
     # Seeded draws over the combinations the parametrized tests above take one
@@ -1106,6 +1156,11 @@ def test_plan_many_requests(bs):
     assert ws_error_word(buf.cross_ws) == 0
     reqs = sorted(set([0, 1, bs // 2, bs - 2, bs - 1] + [int(x) for x in rng.choice(bs, 40, replace=False)]))
     _check_attention(w, buf, reqs, self_blocks=reqs)
+    rows = w.cu_seqlens_q.cpu().numpy()
+    empty = [b for b in range(bs) if ctx[b] == 0]
+    assert max(empty) > 1024  # requests past the first wave stride
+    for b in empty:  # every empty context gives exactly zero
+        assert torch.count_nonzero(buf.cross_out[0][int(rows[b]):int(rows[b + 1])]) == 0
 
 
 @pytest.mark.parametrize("case", range(8))
