@@ -857,7 +857,8 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the drafting workload)",
         "config": describe(w),
         "roofline": {"bound": "hbm",
-                     "kernel": "fm_paged_cross_attention (q_prologue_kernel + cross_attn_kernel, one launch)",
+                     "kernel": ("fm_paged_cross_attention (cross_attn_kernel"
+                                + (", after q_prologue_kernel)" if args.candidates > 1 else ")")),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(workload_key(args)), "bytes_per_launch": cb,
                      "avg_launch_ms": avg_cross},
