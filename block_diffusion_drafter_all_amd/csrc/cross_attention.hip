@@ -119,31 +119,53 @@ __device__ __forceinline__ void wait_stores_acknowledged() { asm volatile("s_wai
 // ------------------------------------------------------------------- plan --
 
 // First tile of wave w's share of G tiles over NW waves, shares weighted by
-// the XCD each wave runs on (share_start(G, NW, NW, W) = G).  Workgroups go
+// the XCD each wave runs on (share_start(w = NW) = G).  Workgroups go
 // round-robin over the 8 XCDs, so wave w (4 per workgroup) runs on XCD
 // (w / 4) mod 8.  The weights are inputs: the cut depends only on them and
 // on the lengths, and so do the results.
-__device__ __forceinline__ int64_t share_start(int64_t G, int w, int NW, const int32_t* W) {
+//
+// The share is floor(G wb / wt), wb the weight of waves 0 .. w-1 and wt that
+// of all NW.  With G = Q wt + R it is Q wb + floor(R wb / wt).  Both
+// quotients come from doubles (R wb < wt^2 < 2^46 is exact; G below 2^52),
+// each at most one off its floor, which one product settles: no 64-bit
+// integer division.
+struct ShareSplit {
+  int64_t Q, R, wt;
+};
+
+__device__ __forceinline__ int64_t floor_div_checked(int64_t num, int64_t den) {  // num >= 0, den > 0
+  int64_t f = (int64_t)((double)num / (double)den);
+  if (f * den > num) --f;
+  else if ((f + 1) * den <= num) ++f;
+  return f;
+}
+
+__device__ __forceinline__ int64_t weight_before(int v, const int32_t* W) {  // total weight of waves 0 .. v-1
   int64_t sum8 = 0;
 #pragma unroll
   for (int x = 0; x < kXcds; ++x) sum8 += W[x];
-  auto weight_before = [&](int v) -> int64_t {  // total weight of waves 0 .. v-1
-    const int64_t blk = v >> 2, part = v & 3;    // whole workgroups before v, and v's own waves before it
-    const int64_t turns = blk / kXcds, rem = blk % kXcds;
-    int64_t acc = 4 * turns * sum8;
+  const int64_t blk = v >> 2, part = v & 3;  // whole workgroups before v, and v's own waves before it
+  const int64_t turns = blk / kXcds, rem = blk % kXcds;
+  int64_t acc = 4 * turns * sum8;
 #pragma unroll
-    for (int x = 0; x < kXcds; ++x) acc += x < rem ? 4 * (int64_t)W[x] : 0;
-    return acc + part * W[rem];
-  };
-  return G * weight_before(w) / weight_before(NW);
+  for (int x = 0; x < kXcds; ++x) acc += x < rem ? 4 * (int64_t)W[x] : 0;
+  return acc + part * W[rem];
+}
+
+__device__ __forceinline__ int64_t share_start(const ShareSplit& sp, int w, const int32_t* W) {
+  const int64_t wb = weight_before(w, W);
+  return sp.Q * wb + floor_div_checked(sp.R * wb, sp.wt);
 }
 
 // Batches up to this many requests keep each request's length and first
 // tile in LDS, so the plan's searches and lookups never wait on memory.
 constexpr int kPlanLdsRequests = 2048;
+constexpr int kPlanMaxGroups = 64;
 
-// One workgroup.  kLds: bs <= kPlanLdsRequests (else the request tables are
-// read back from the workspace).
+// kLds: bs <= kPlanLdsRequests.  Then every workgroup of the grid builds the
+// request tables and the wave shares in its own LDS, and the workgroups split
+// the wave and pair records between them.  Otherwise one workgroup, which
+// reads the request tables back from the workspace.
 template <bool kLds>
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   uint8_t* ws = a.ws;
@@ -158,6 +180,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   const int64_t* off = kLds ? lds_off : pair_off;  // first tile of request b's pairs in the stream
   auto ctx_of = [&](int b) -> int { return kLds ? lds_ctx[b] : max(0, a.ctx_lens[b]); };
   const int tid = threadIdx.x;
+  const bool lead = blockIdx.x == 0;  // writes the workspace's request table and header
   int64_t carry = 0;
   for (int base = 0; base < a.bs; base += 1024) {
     const int b = base + tid;
@@ -165,7 +188,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     int64_t tot;
     const int64_t ex = block_exclusive_scan_i64((int64_t)tiles_of(ctx) * a.H, &tot);
     if (b < a.bs) {
-      pair_off[b] = carry + ex;
+      if (lead) pair_off[b] = carry + ex;
       if constexpr (kLds) {
         lds_off[b] = carry + ex;
         lds_ctx[b] = ctx;
@@ -174,14 +197,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     carry += tot;
   }
   if (tid == 0) {
-    pair_off[a.bs] = carry;
+    if (lead) pair_off[a.bs] = carry;
     if constexpr (kLds) lds_off[a.bs] = carry;
   }
   const int64_t G = carry;
   const int NW = a.lay.n_waves;
-  for (int w = tid; w <= NW; w += 1024) starts[w] = share_start(G, w, NW, a.xcd_w);
+  ShareSplit sp;
+  sp.wt = weight_before(NW, a.xcd_w);
+  sp.Q = floor_div_checked(G, sp.wt);
+  sp.R = G - sp.Q * sp.wt;
+  for (int w = tid; w <= NW; w += 1024) starts[w] = share_start(sp, w, a.xcd_w);
   __syncthreads();
-  for (int w = tid; w < NW; w += 1024) {
+  const int first = blockIdx.x * 1024 + tid, stride = gridDim.x * 1024;
+  for (int w = first; w < NW; w += stride) {
     const int64_t g0 = starts[w], g1 = starts[w + 1];
     WaveRec r{};
     r.start = g0;
@@ -195,10 +223,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
       }
       const int ctx = ctx_of(lo);
       const int T = tiles_of(ctx);
-      const int64_t rel = g0 - off[lo];
+      const int64_t rel = g0 - off[lo];  // < H * T
       r.b = lo;
-      r.h = (int)(rel / T);
-      r.k = (int)(rel % T);
+      if (rel <= INT32_MAX) {  // 32-bit division where it fits
+        r.h = (int)rel / T;
+        r.k = (int)rel - r.h * T;
+      } else {
+        r.h = (int)(rel / T);
+        r.k = (int)(rel % T);
+      }
       r.count = (int)(g1 - g0);
       r.ctx = ctx;
     }
@@ -207,8 +240,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
   }
   // Each pair's first and last wave (the last wave whose range starts at or
   // before its first and last tile), and how many waves hold a part of it.
+  // The shares are near-proportional (XCD weights within 1 : 4), so the
+  // proportional guess is a few waves off at most: a short walk from it, and
+  // a bisection of what is left if the walk runs long.
   auto wave_of = [&](int64_t x) -> int {
+    int w = (int)min((int64_t)NW - 1, (int64_t)((double)x * NW / (double)G));
+    for (int step = 0; step < 4; ++step) {
+      if (starts[w] > x) --w;
+      else if (w + 1 < NW && starts[w + 1] <= x) ++w;
+      else return w;
+    }
     int lo = 0, hi = NW - 1;
+    if (starts[w] > x) hi = w - 1;
+    else lo = w;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (starts[mid] <= x) lo = mid;
@@ -216,9 +260,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     }
     return lo;
   };
-  const int64_t pairs = (int64_t)a.bs * a.H;
-  for (int64_t i = tid; i < pairs; i += 1024) {
-    const int b = (int)(i / a.H), h = (int)(i % a.H);
+  const uint32_t pairs = (uint32_t)a.bs * (uint32_t)a.H;  // < 2^31 (checked by the host), so i never wraps
+  for (uint32_t i = first; i < pairs; i += stride) {
+    const int b = (int)(i / (uint32_t)a.H), h = (int)(i - (uint32_t)b * a.H);
     const int T = tiles_of(ctx_of(b));
     PairRec pr{};
     if (T > 0) {
@@ -230,7 +274,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) {
     }
     prec[i] = pr;
   }
-  if (tid == 0) {
+  if (lead && tid == 0) {
     hdr->magic = kPlanMagic;
     hdr->error = 0;
     hdr->n_waves = NW;
@@ -1135,9 +1179,11 @@ hipError_t launch_cross_dh(const CrossArgs& a, int dtype, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  if (a.bs <= kPlanLdsRequests)
-    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(1024), 0, s, a);
-  else
+  if (a.bs <= kPlanLdsRequests) {  // a workgroup per 1024 pairs or waves, at most kPlanMaxGroups
+    const int64_t work = max((int64_t)a.lay.n_waves, (int64_t)a.bs * a.H);
+    const int groups = (int)min((int64_t)kPlanMaxGroups, max((int64_t)1, (work + 1023) / 1024));
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(groups), dim3(1024), 0, s, a);
+  } else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
