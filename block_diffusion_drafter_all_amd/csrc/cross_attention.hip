@@ -50,8 +50,8 @@ constexpr int kWin = 512;  // page ids cached per wave
 #define FM_CROSS_LDS_KV 1  // pages of >= 16 tokens: K/V tiles stream through LDS (whole-line, nontemporal loads)
 #endif
 #ifndef FM_CROSS_LDS_KV_MAXQF
-#define FM_CROSS_LDS_KV_MAXQF 2  // ... for kernels of at most this many query fragments (four: compute-bound,
-                                  // the LDS reads cost more than the loads gain)
+#define FM_CROSS_LDS_KV_MAXQF 4  // ... for kernels of at most this many query fragments (every count: with the
+                                  // bf16 V tile read transposed from LDS, four fragments gain too)
 #endif
 #ifndef FM_CROSS_DEPTH_LDS
 #define FM_CROSS_DEPTH_LDS 2  // tiles in flight per wave through LDS (the loads hold no registers)
@@ -687,6 +687,20 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   auto row_key = [](int r) { return (r / kKeyDiv) % kKeyMod; };
   uint32_t dma_off[LDS_KV ? kDma : 1];  // per lane, per load: byte offset inside the tile (slot stride aware)
   uint32_t lds_off[LDS_KV ? NCH : 1];   // per lane, per operand chunk: byte offset of its LDS chunk
+  // A bf16 V tile is read in column layout by gfx950's transpose read
+  // (ds_read_b64_tr_b16): within each 16 lanes, lane i receives element i % 4
+  // of the 8-byte pieces that lanes 4k + i / 4 (k = 0..3) address.  So for
+  // column tile dt lane (g, c) addresses key 4g + c / 4, columns 16 dt +
+  // 4 (c % 4) .. +3, and receives V[4g .. 4g+3][16 dt + c]: the PV operand,
+  // with no selection product.
+  constexpr bool kVtr = LDS_KV && std::is_same<PT, Bf16>::value;
+  uint32_t vtr_off[kVtr ? NDT : 1];
+  if constexpr (kVtr) {
+    const int r = 4 * g + (c >> 2), q = c & 3;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      vtr_off[dt] = (uint32_t)(kTileB + r * kRowB + (((2 * dt + (q >> 1)) ^ row_key(r)) * 16) + 8 * (q & 1));
+  }
   if constexpr (LDS_KV) {
     const uint32_t slot_b = a.slot_stride32 * (uint32_t)sizeof(pst);
 #pragma unroll
@@ -917,7 +931,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
         kk[ch] = *(const u32x4_t*)(src + lds_off[ch]);
-        vv[ch] = *(const u32x4_t*)(src + kTileB + lds_off[ch]);
+        if constexpr (!kVtr) vv[ch] = *(const u32x4_t*)(src + kTileB + lds_off[ch]);
       }
     } else {
 #pragma unroll
@@ -1014,11 +1028,26 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
       l_lane[f] += psum;
     }
     // V moved to column layout once per tile, shared by every fragment
+    if constexpr (kVtr) {
+      typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4;
+      const uint8_t* src = ring_of(dslot);
+      i16x4_t pb[NQF];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const auto vt = sel.template transpose_tile<NCH>(vv, dt);
+      for (int f = 0; f < NQF; ++f)
+        pb[f] = __builtin_bit_cast(i16x4_t, (u32x2_t){pack_hi16(p[f][0], p[f][1]), pack_hi16(p[f][2], p[f][3])});
 #pragma unroll
-      for (int f = 0; f < NQF; ++f) mma_pv<PV>(o[f][dt], vt, p[f]);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(src + vtr_off[dt]));
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) o[f][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[f], o[f][dt], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const auto vt = sel.template transpose_tile<NCH>(vv, dt);
+#pragma unroll
+        for (int f = 0; f < NQF; ++f) mma_pv<PV>(o[f][dt], vt, p[f]);
+      }
     }
     if (sflags & kEnd) {
       if (sflags & kWhole) {
