@@ -987,8 +987,12 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
 #pragma unroll
     for (int f = 0; f < NQF; ++f) {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kFp8 && NCH == 2) {  // head_dim 128 over e4m3: the whole contraction in one MFMA
+        mma_two_chunks_e4m3(sc, kk[0], kk[1], qop[f][0], qop[f][1]);
+      } else {
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, kk[ch], qop[f][ch]);
+        for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, kk[ch], qop[f][ch]);
+      }
       float sv[4];
       if (smask == kKeyMask) {  // a full tile (wave-uniform): no key to mask
 #pragma unroll

@@ -165,6 +165,19 @@ __device__ __forceinline__ void mma_chunk<E4m3>(f32x4_t& acc, const u32x4_t& a, 
   acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(u64_of(a[2], a[3]), u64_of(b[2], b[3]), acc, 0, 0, 0);
 }
 
+// Two e4m3 chunks of each lane (32 codes) in one gfx950 16x16x128 fp8 MFMA
+// (unit block scales: exponent 127).  The contraction pairs the operands'
+// codes position by position, so any assignment of the 128 contraction
+// indices to (lane group, byte) that A and B share gives the same products;
+// here that of the chunks the lanes already hold.
+__device__ __forceinline__ void mma_two_chunks_e4m3(f32x4_t& acc, const u32x4_t& a0, const u32x4_t& a1,
+                                                    const u32x4_t& b0, const u32x4_t& b1) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8_t b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+}
+
 // Selection operands that move a row fragment into the C layout ("column
 // fragment"): for column tile dt (16 columns), transpose_tile returns, in lane
 // l, M[4*(l/16) + i][16*dt + l%16] for i < 4 -- four consecutive rows of one
