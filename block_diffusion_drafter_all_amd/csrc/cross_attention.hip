@@ -983,50 +983,74 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     }
     const bool start = (sflags & kStart) != 0;
     const uint32_t smask = s.mf & kKeyMask;
+    // The fragments' scores, maxima, rescales and weights run phase by phase
+    // across fragments, with one wave-uniform branch for every rescale, so
+    // their independent MFMA, reduction and exp chains can interleave.
     f32x4_t p[NQF];
+    float sv[NQF][4];
+    {
+      f32x4_t sc[NQF];
 #pragma unroll
-    for (int f = 0; f < NQF; ++f) {
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kFp8 && NCH == 2) {  // head_dim 128 over e4m3: the whole contraction in one MFMA
-        mma_two_chunks_e4m3(sc, kk[0], kk[1], qop[f][0], qop[f][1]);
-      } else {
+      for (int f = 0; f < NQF; ++f) {
+        sc[f] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if constexpr (kFp8 && NCH == 2) {  // head_dim 128 over e4m3: the whole contraction in one MFMA
+          mma_two_chunks_e4m3(sc[f], kk[0], kk[1], qop[f][0], qop[f][1]);
+        } else {
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc, kk[ch], qop[f][ch]);
-      }
-      float sv[4];
-      if (smask == kKeyMask) {  // a full tile (wave-uniform): no key to mask
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = sc[i] * score_scale;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = (smask >> (4 * g + i)) & 1u;
-          sv[i] = valid ? sc[i] * score_scale : kNegInf;
+          for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc[f], kk[ch], qop[f][ch]);
         }
       }
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = wave_max_groups(mx);
-      float psum = 0.f;
-      // Lazy rescale: the reference max moves only when a row's max exceeds
-      // it by more than kRescaleSlack (log2 units), so p <= 2^slack and O, l
-      // (in AGPRs) are rarely rescaled; O / l is the same quotient.  A pair's
-      // first tile always moves it, which also clears O and l (the factor is
-      // 0 while the reference max is -inf).
-      const bool move = start || mx > m_run[f] + kRescaleSlack;
-      if (__ballot(move) != 0) {
-        const float m_new = move ? mx : m_run[f];
+      if (smask == kKeyMask) {  // a full tile (wave-uniform): no key to mask
+#pragma unroll
+        for (int f = 0; f < NQF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[f][i] = sc[f][i] * score_scale;
+      } else {
+#pragma unroll
+        for (int f = 0; f < NQF; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = (smask >> (4 * g + i)) & 1u;
+            sv[f][i] = valid ? sc[f][i] * score_scale : kNegInf;
+          }
+      }
+    }
+    float mx[NQF];
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) mx[f] = fmaxf(fmaxf(sv[f][0], sv[f][1]), fmaxf(sv[f][2], sv[f][3]));
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) mx[f] = wave_max_groups(mx[f]);
+    // Lazy rescale: the reference max moves only when a row's max exceeds it
+    // by more than kRescaleSlack (log2 units), so p <= 2^slack and O, l (in
+    // AGPRs) are rarely rescaled; O / l is the same quotient.  A pair's first
+    // tile always moves it, which also clears O and l (the factor is 0 while
+    // the reference max is -inf).
+    bool move[NQF], any_move = false;
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) {
+      move[f] = start || mx[f] > m_run[f] + kRescaleSlack;
+      any_move |= move[f];
+    }
+    if (__ballot(any_move) != 0) {
+#pragma unroll
+      for (int f = 0; f < NQF; ++f) {
+        const float m_new = move[f] ? mx[f] : m_run[f];
         const float alpha = (m_run[f] == kNegInf) ? 0.f : exp2_hw(m_run[f] - m_new);
-        if (move) {
+        if (move[f]) {
           l_lane[f] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[f][dt] *= alpha;
           m_run[f] = m_new;
         }
       }
+    }
+#pragma unroll
+    for (int f = 0; f < NQF; ++f) {
       const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
+      float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[f][i] = operand_value<PV>(exp2_hw(sv[i] - m_use));
+        p[f][i] = operand_value<PV>(exp2_hw(sv[f][i] - m_use));
         psum += p[f][i];
       }
       l_lane[f] += psum;
