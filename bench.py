@@ -103,10 +103,14 @@ def parse():
 
 
 def kernel_sources_hash() -> str:
+    """SHA-256 of the attention kernel's sources and of the build script that
+    sets their compiler flags."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_diffusion_drafter_all_amd", "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    paths = [os.path.join(ROOT, "block_diffusion_drafter_all_amd", "csrc", n) for n in KERNEL_SOURCES]
+    paths.append(os.path.join(ROOT, "block_diffusion_drafter_all_amd", "build.py"))
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()
 
 

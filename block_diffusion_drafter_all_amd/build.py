@@ -37,6 +37,13 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags.  The attention kernels keep their MFMA accumulators in
+# VGPRs: in the AGPR form the compiler copied every accumulator back to VGPRs
+# on every K/V tile (for the rescale and store paths), 32 to 128 VALU moves a
+# tile; in the VGPR form those copies are gone and nothing spills.
+SOURCE_FLAGS = {"cross_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -46,7 +53,8 @@ def _hipcc() -> str:
 
 def _compile(hipcc: str, src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *extra, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
