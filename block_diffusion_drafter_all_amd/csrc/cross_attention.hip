@@ -1000,20 +1000,15 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
           for (int ch = 0; ch < NCH; ++ch) mma_chunk<PT>(sc[f], kk[ch], qop[f][ch]);
         }
       }
-      if (smask == kKeyMask) {  // a full tile (wave-uniform): no key to mask
+      // scale and key mask in one fma: the bias is 0 for a key of the
+      // context (fma(s, scale, 0) is the rounded product) and -inf past it
+      float bias[4];
 #pragma unroll
-        for (int f = 0; f < NQF; ++f)
+      for (int i = 0; i < 4; ++i) bias[i] = ((smask >> (4 * g + i)) & 1u) ? 0.f : kNegInf;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sv[f][i] = sc[f][i] * score_scale;
-      } else {
+      for (int f = 0; f < NQF; ++f)
 #pragma unroll
-        for (int f = 0; f < NQF; ++f)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = (smask >> (4 * g + i)) & 1u;
-            sv[f][i] = valid ? sc[f][i] * score_scale : kNegInf;
-          }
-      }
+        for (int i = 0; i < 4; ++i) sv[f][i] = fmaf(sc[f][i], score_scale, bias[i]);
     }
     float mx[NQF];
 #pragma unroll
@@ -1044,14 +1039,29 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
         }
       }
     }
+    // bf16 weights: rounded two at a time by one packed conversion, which is
+    // also the PV operand; the sum takes the rounded values in key order
+    constexpr bool kPacked = std::is_same<PV, Bf16>::value;
+    u32x2_t pk[kPacked ? NQF : 1];
 #pragma unroll
     for (int f = 0; f < NQF; ++f) {
       const float m_use = (m_run[f] == kNegInf) ? 0.f : m_run[f];
       float psum = 0.f;
+      if constexpr (kPacked) {
+        float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[f][i] = operand_value<PV>(exp2_hw(sv[f][i] - m_use));
-        psum += p[f][i];
+        for (int i = 0; i < 4; ++i) e[i] = exp2_hw(sv[f][i] - m_use);
+        pk[f] = (u32x2_t){pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3])};
+        const float r[4] = {__uint_as_float(pk[f][0] << 16), __uint_as_float(pk[f][0] & 0xffff0000u),
+                            __uint_as_float(pk[f][1] << 16), __uint_as_float(pk[f][1] & 0xffff0000u)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) psum += r[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[f][i] = operand_value<PV>(exp2_hw(sv[f][i] - m_use));
+          psum += p[f][i];
+        }
       }
       l_lane[f] += psum;
     }
@@ -1059,22 +1069,23 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
     if constexpr (kVtr) {
       typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4;
       const uint8_t* src = ring_of(dslot);
-      i16x4_t pb[NQF];
-#pragma unroll
-      for (int f = 0; f < NQF; ++f)
-        pb[f] = __builtin_bit_cast(i16x4_t, (u32x2_t){pack_hi16(p[f][0], p[f][1]), pack_hi16(p[f][2], p[f][3])});
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const i16x4_t vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(src + vtr_off[dt]));
 #pragma unroll
-        for (int f = 0; f < NQF; ++f) o[f][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[f], o[f][dt], 0, 0, 0);
+        for (int f = 0; f < NQF; ++f)
+          o[f][dt] =
+              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, __builtin_bit_cast(i16x4_t, pk[f]), o[f][dt], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const auto vt = sel.template transpose_tile<NCH>(vv, dt);
 #pragma unroll
-        for (int f = 0; f < NQF; ++f) mma_pv<PV>(o[f][dt], vt, p[f]);
+        for (int f = 0; f < NQF; ++f) {
+          if constexpr (kPacked) mma_pv_packed(o[f][dt], vt, pk[f]);
+          else mma_pv<PV>(o[f][dt], vt, p[f]);
+        }
       }
     }
     if (sflags & kEnd) {

@@ -279,6 +279,22 @@ __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
+// Two fp32 values rounded to bf16 (nearest even) in one v_cvt_pk_bf16_f32:
+// lo in the low half, hi in the high half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// The PV product with the weights already packed as bf16 pairs (pb: keys
+// 4g, 4g+1 | 4g+2, 4g+3 of lane (g, c)); vt as for mma_pv<Bf16>.
+__device__ __forceinline__ void mma_pv_packed(f32x4_t& acc, const f32x4_t& vt, const u32x2_t& pb) {
+  const u32x2_t a = {pack_hi16(vt[0], vt[1]), pack_hi16(vt[2], vt[3])};
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, pb),
+                                                  acc, 0, 0, 0);
+}
+
 // bf16 operands: vt comes from transpose_tile of bf16 or e4m3 data and p from
 // operand_value<Bf16>, so every value is bf16-representable and packing its
 // high half is exact.
