@@ -512,10 +512,11 @@ __device__ __forceinline__ int count_in(const CrossArgs& a, const PairRec& pr) {
 // records with them) and one rescale per batch, so a pair cut over up to
 // kMergeBatch waves costs one round trip.  Called by the wave that counted the
 // last part in: every other part was acknowledged before it was counted.
-// Lanes hold the same fragment of the rows as in the attention loop.
+// Lanes hold the same fragment of the rows as in the attention loop; COLS
+// names the type whose column order (out_col) the fragments follow.
 constexpr int kMergeBatch = 4;
 
-template <class T, class PT, int D, int NQF>
+template <class T, class COLS, int D, int NQF>
 __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, const PairRec& pr) {
   typedef typename T::storage st;
   constexpr int NDT = D / 16;
@@ -570,7 +571,7 @@ __device__ __forceinline__ void merge_pair(const CrossArgs& a, int b, int h, con
     if (k < nq) {
       st* orow = (st*)a.out + ((int64_t)(r0 + k) * a.H + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), acc[dt], inv * a.v_descale);
+      for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<COLS>(dt, g), acc[dt], inv * a.v_descale);
     }
   }
   if (lane == 0)
@@ -687,15 +688,33 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   auto row_key = [](int r) { return (r / kKeyDiv) % kKeyMod; };
   uint32_t dma_off[LDS_KV ? kDma : 1];  // per lane, per load: byte offset inside the tile (slot stride aware)
   uint32_t lds_off[LDS_KV ? NCH : 1];   // per lane, per operand chunk: byte offset of its LDS chunk
-  // A bf16 V tile is read in column layout by gfx950's transpose read
-  // (ds_read_b64_tr_b16): within each 16 lanes, lane i receives element i % 4
-  // of the 8-byte pieces that lanes 4k + i / 4 (k = 0..3) address.  So for
-  // column tile dt lane (g, c) addresses key 4g + c / 4, columns 16 dt +
-  // 4 (c % 4) .. +3, and receives V[4g .. 4g+3][16 dt + c]: the PV operand,
-  // with no selection product.
-  constexpr bool kVtr = LDS_KV && std::is_same<PT, Bf16>::value;
-  uint32_t vtr_off[kVtr ? NDT : 1];
-  if constexpr (kVtr) {
+  // A bf16 or e4m3 V tile is read in column layout by gfx950's transpose
+  // reads, with no selection product.
+  //  - bf16 (ds_read_b64_tr_b16): within each 16 lanes, lane i receives
+  //    element i % 4 of the 8-byte pieces that lanes 4k + i / 4 (k = 0..3)
+  //    address.  For column tile dt lane (g, c) addresses key 4g + c / 4,
+  //    columns 16 dt + 4 (c % 4) .. +3, and receives V[4g .. 4g+3][16 dt + c].
+  //  - e4m3 (ds_read_b64_tr_b8): lane i receives byte i % 8 of the pieces
+  //    that lanes 2k + i / 8 (k = 0..7) address.  Read j serves column tiles
+  //    j and j + NDT/2: lane (g, c) addresses key 4g + (c/2) % 4, columns
+  //    16 dt' + 8 (c % 2) .. +7 with dt' = j for c < 8, else j + NDT/2, and
+  //    receives V[4g .. 4g+3][16 j + c] in bytes 0-3 and the same keys of
+  //    column 16 (j + NDT/2) + c in bytes 4-7.  Tiles NDT/2 apart differ in
+  //    the top bit of the swizzled chunk, so the 32 pieces of a half-wave
+  //    fall on 64 distinct banks.
+  // The output columns then follow the plain order 16 dt + 4 g + i.
+  constexpr bool kVtr = LDS_KV && !std::is_same<PT, F32>::value;
+  typedef std::conditional_t<kVtr, Bf16, PT> OCols;  // the output column order
+  constexpr int kVtrReads = kFp8 ? NDT / 2 : NDT;
+  uint32_t vtr_off[kVtr ? kVtrReads : 1];
+  if constexpr (kVtr && kFp8) {
+    const int k = c >> 1, r = 4 * g + (k & 3);
+#pragma unroll
+    for (int j = 0; j < kVtrReads; ++j) {
+      const int dtp = k < 4 ? j : j + NDT / 2;
+      vtr_off[j] = (uint32_t)(kTileB + r * kRowB + ((dtp ^ row_key(r)) * 16) + 8 * (c & 1));
+    }
+  } else if constexpr (kVtr) {
     const int r = 4 * g + (c >> 2), q = c & 3;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -713,7 +732,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
   }
 
   Selector<PT> sel;
-  sel.init(lane);
+  if constexpr (!kVtr) sel.init(lane);
   const int ps_mask = (1 << a.log2ps) - 1;
   const pst* kpool = (const pst*)a.pool.k;
   const pst* vpool = (const pst*)a.pool.v;
@@ -1066,7 +1085,24 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
       l_lane[f] += psum;
     }
     // V moved to column layout once per tile, shared by every fragment
-    if constexpr (kVtr) {
+    if constexpr (kVtr && kFp8) {
+      typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+      typedef __attribute__((address_space(3))) i32x2_t* lds_i32x2;
+      const uint8_t* src = ring_of(dslot);
+#pragma unroll
+      for (int j = 0; j < kVtrReads; ++j) {
+        const i32x2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2)(src + vtr_off[j]));
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const i16x4_t vt = e4m3x4_to_bf16x4((uint32_t)raw[half]);
+          const int dt = j + half * (NDT / 2);
+#pragma unroll
+          for (int f = 0; f < NQF; ++f)
+            o[f][dt] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, __builtin_bit_cast(i16x4_t, pk[f]), o[f][dt], 0, 0, 0);
+        }
+      }
+    } else if constexpr (kVtr) {
       typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4;
       const uint8_t* src = ring_of(dslot);
 #pragma unroll
@@ -1098,7 +1134,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
           if (k < cnq) {
             st* orow = (st*)a.out + ((int64_t)(cr0 + k) * a.H + chh) * D;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<PT>(dt, g), o[f][dt], inv * a.v_descale);
+            for (int dt = 0; dt < NDT; ++dt) store4<T>(orow + out_col<OCols>(dt, g), o[f][dt], inv * a.v_descale);
           }
         }
       } else {
@@ -1178,7 +1214,7 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
       if (cut_b[k] >= 0) before[k] = count_in(a, pr[k]);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      if (cut_b[k] >= 0 && before[k] == pr[k].parts - 1) merge_pair<T, PT, D, NQF>(a, cut_b[k], cut_h[k], pr[k]);
+      if (cut_b[k] >= 0 && before[k] == pr[k].parts - 1) merge_pair<T, OCols, D, NQF>(a, cut_b[k], cut_h[k], pr[k]);
   }
 }
 

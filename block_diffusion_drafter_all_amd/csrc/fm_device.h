@@ -287,6 +287,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// Four e4m3 codes (byte i = element i) as bf16, exact (bf16 holds every
+// e4m3 value): two packed conversions with a unit scale.
+__device__ __forceinline__ i16x4_t e4m3x4_to_bf16x4(uint32_t codes) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true))};
+  return __builtin_bit_cast(i16x4_t, r);
+}
+
 // The PV product with the weights already packed as bf16 pairs (pb: keys
 // 4g, 4g+1 | 4g+2, 4g+3 of lane (g, c)); vt as for mma_pv<Bf16>.
 __device__ __forceinline__ void mma_pv_packed(f32x4_t& acc, const f32x4_t& vt, const u32x2_t& pb) {
