@@ -164,6 +164,67 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
   }
 }
 
+// The epilogue of the bf16 tile works on 32-column blocks of one head: lane l
+// holds one compacted row (its own) and, in c[i], columns
+// col0 + 8 (i / 4) + 4 (l / 32) + i % 4.  It only reads the accumulators.
+
+// The key head of layer l in acc[0..3][rg] (block cg = columns 32 cg ..):
+// k-normed, rotated and stored to head h of the key pool at (page, slot off)
+// when ``has``.  The sum of squares over the head's 128 columns is 64 in this
+// lane and 64 in lane l ^ 32.  kw: the layer's k-norm weight, inv: the inverse
+// RoPE frequencies (both in LDS).
+template <class PT>
+__device__ __forceinline__ void store_key_head(const WriteGemmArgs& a, const f32x16_t (&acc)[4][2], int rg, int l,
+                                               int h, const float* kw, const float* inv_tab, float fpos, int page,
+                                               int off, bool has) {
+  typedef typename PT::storage pst;
+  const int fchunk = lane_id() >> 5;
+  float ss = 0.f;
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss += acc[cg][rg][i] * acc[cg][rg][i];
+  ss += __shfl_xor(ss, 32);
+  const float rs = 1.0f / sqrtf(ss / (float)kDhGemm + a.eps);
+  const PoolDesc& P = a.pools[l];
+  pst* dst = (pst*)P.k + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride + (int64_t)h * P.head_stride +
+             4 * fchunk;
+  const float sc = a.inv_scale[l][0];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
+#pragma unroll
+      for (int p2 = 0; p2 < 4; p2 += 2) {
+        // columns 32 cg + 8 q + 4 (l/32) + p2, + 1: one interleaved RoPE pair,
+        // frequency index col / 2 = 16 cg + 4 q + 2 (l/32) + p2/2
+        const int col = 32 * cg + 8 * q + 4 * fchunk + p2;
+        float sn, cs;
+        angle_sincos(fpos * inv_tab[16 * cg + 4 * q + p2 / 2 + 2 * fchunk], &sn, &cs);
+        const float y0 = acc[cg][rg][4 * q + p2] * rs * kw[col];
+        const float y1 = acc[cg][rg][4 * q + p2 + 1] * rs * kw[col + 1];
+        v[p2] = y0 * cs - y1 * sn;
+        v[p2 + 1] = y1 * cs + y0 * sn;
+      }
+      if (has) store4<PT>(dst + 32 * cg + 8 * q, (f32x4_t){v[0], v[1], v[2], v[3]}, sc);
+    }
+}
+
+// Stores one block to head h of layer l's {k|v} pool at (page, slot off),
+// rounded once to the pool's type.
+template <class PT>
+__device__ __forceinline__ void store_block(const WriteGemmArgs& a, const f32x16_t& c, int l, int kv, int h, int col0,
+                                            int page, int off) {
+  typedef typename PT::storage pst;
+  const PoolDesc& P = a.pools[l];
+  pst* dst = (pst*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
+             (int64_t)h * P.head_stride + col0 + 4 * (lane_id() >> 5);
+  const float sc = a.inv_scale[l][kv];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store4<PT>(dst + 8 * q, (f32x4_t){c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]}, sc);
+}
+
 // bf16 activations with head_dim 128: the MFMA-tiled GEMM (gemm_core.h), one
 // 256 x 256 tile of Y^T = W X^T per workgroup: two (layer, {k|v}, head) blocks
 // of W against 256 compacted rows, each wave one whole head for 64 rows.  Tiles
@@ -175,8 +236,10 @@ __global__ __launch_bounds__(256) void write_gemm_kernel(WriteGemmArgs a) {
 template <class PT>
 __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(WriteGemmArgs a, int n_tiles,
                                                                               int m_tiles) {
-  typedef typename PT::storage pst;
   FM_GEMM_RING;
+  // per head wn of the tile: the k-norm weight of its layer and the inverse
+  // RoPE frequencies, for the epilogue
+  __shared__ float epi_lds[2][kDhGemm + kDhGemm / 2];
   const int lane = lane_id();
   const int wv = wave_in_block();
   const int wm = wv >> 1, wn = wv & 1;  // rows 64 wm .. +63 of the tile, head wn
@@ -195,7 +258,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
   const int kv = (hn / a.H) & 1;
   const int h = hn - (hn / a.H) * a.H;
   const int32_t* live_row = (const int32_t*)(ws + a.lay.live_row);
-  const int frow = lane & 31, fchunk = lane >> 5;
+  const int frow = lane & 31;
 
   const uint16_t* src[kLoadsPerWave];
 #pragma unroll
@@ -208,6 +271,24 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
       src[i] = (const uint16_t*)a.x + (int64_t)xr * a.d_in + g.chunk * 8;
     }
   }
+  // The epilogue's inputs, fetched while the contraction runs: each row's
+  // page, slot and position, and (key heads) the norm weight, which goes to
+  // LDS with the frequencies once the contraction is done.
+  int page[2], off[2];
+  float fpos[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int li = m0 + 64 * wm + 32 * rg + frow;
+    const int lic = li < live ? li : m0;
+    page[rg] = ((const int32_t*)(ws + a.lay.live_page))[lic];
+    off[rg] = ((const int32_t*)(ws + a.lay.live_off))[lic];
+    fpos[rg] = (float)((const int32_t*)(ws + a.lay.live_pos))[lic];
+  }
+  float kw_reg[2] = {0.f, 0.f};
+  if (kv == 0 && wm == 0) {
+    kw_reg[0] = a.k_norm_w[(int64_t)l * kDhGemm + lane];
+    kw_reg[1] = a.k_norm_w[(int64_t)l * kDhGemm + lane + 64];
+  }
   f32x16_t acc[4][2];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg)
@@ -218,60 +299,33 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void write_gemm_bf16_kernel(Wri
   gemm256_mainloop_rows(acc, src, a.d_in / kGK, wv, wm, wn, buf0, buf1, live - (m0 + 64 * wm));
   // acc[cg][rg][i] (lane l) = Y[tile row 64 wm + 32 rg + l % 32]
   //                            [head column 32 cg + 8 (i / 4) + 4 (l / 32) + i % 4]
-
-  const PoolDesc& P = a.pools[l];
-  const float* kw = a.k_norm_w + (int64_t)l * kDhGemm;
+  float* kw = epi_lds[wn];
+  float* inv_tab = kw + kDhGemm;
+  if (kv == 0 && wm == 0) {
+    kw[lane] = kw_reg[0];
+    kw[lane + 64] = kw_reg[1];
+    if (lane == 0) {  // (a per-lane index into the kernel argument would cost scratch)
+#pragma unroll
+      for (int i = 0; i < kDhGemm / 2; ++i) inv_tab[i] = a.rope.inv[i];
+    }
+  }
+  __syncthreads();
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    float rs = 1.f;
-    if (kv == 0) {  // k-norm over the head's 128 columns: 64 in this lane, 64 in lane l ^ 32
-      float ss = 0.f;
+    const bool has = m0 + 64 * wm + 32 * rg + frow < live;
+    if (kv == 0) {
+      store_key_head<PT>(a, acc, rg, l, h, kw, inv_tab, fpos[rg], page[rg], off[rg], has);
+    } else if (has) {
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ss += acc[cg][rg][i] * acc[cg][rg][i];
-      ss += __shfl_xor(ss, 32);
-      rs = 1.0f / sqrtf(ss / (float)kDhGemm + a.eps);
+      for (int cg = 0; cg < 4; ++cg) store_block<PT>(a, acc[cg][rg], l, 1, h, 32 * cg, page[rg], off[rg]);
     }
-    const int li = m0 + 64 * wm + 32 * rg + frow;
-    const bool has = li < live;
-    const int lic = has ? li : m0;
-    const int page = ((const int32_t*)(ws + a.lay.live_page))[lic];
-    const int off = ((const int32_t*)(ws + a.lay.live_off))[lic];
-    const float fpos = (float)((const int32_t*)(ws + a.lay.live_pos))[lic];
-    pst* dst = (pst*)(kv ? P.v : P.k) + (int64_t)page * P.page_stride + (int64_t)off * P.slot_stride +
-               (int64_t)h * P.head_stride + 4 * fchunk;
-    const float sc = a.inv_scale[l][kv];
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // columns 32 cg + 8 q + 4 (l/32) + 0..3: two interleaved RoPE pairs
-        float v[4] = {acc[cg][rg][4 * q], acc[cg][rg][4 * q + 1], acc[cg][rg][4 * q + 2], acc[cg][rg][4 * q + 3]};
-        if (kv == 0) {
-#pragma unroll
-          for (int p2 = 0; p2 < 4; p2 += 2) {
-            const int col = 32 * cg + 8 * q + 4 * fchunk + p2;
-            // frequency index col / 2 = 16 cg + 4 q + 2 (l/32) + p2/2
-            const int f0 = 16 * cg + 4 * q + p2 / 2;
-            const float inv = fchunk ? a.rope.inv[f0 + 2] : a.rope.inv[f0];
-            float sn, cs;
-            angle_sincos(fpos * inv, &sn, &cs);
-            const float y0 = v[p2] * rs * kw[col];
-            const float y1 = v[p2 + 1] * rs * kw[col + 1];
-            v[p2] = y0 * cs - y1 * sn;
-            v[p2 + 1] = y1 * cs + y0 * sn;
-          }
-        }
-        if (has) store4<PT>(dst + 32 * cg + 8 * q, (f32x4_t){v[0], v[1], v[2], v[3]}, sc);
-      }
   }
 }
 
 template <class T, class PT, int D>
 hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, int64_t n_rows, hipStream_t s) {
   const int n_tiles = g.L * 2 * g.H;
-  const bool tiled = sizeof(typename T::storage) == 2 && D == kDhGemm;
+  constexpr bool tiled = sizeof(typename T::storage) == 2 && D == kDhGemm;
   const int64_t m_tiles = tiled ? (n_rows + kGM - 1) / kGM : (n_rows + 63) / 64;
   const int64_t groups = (n_tiles / 2 + 7) / 8;  // 256-row tiles of W: two heads each
   if (tiled ? !grid_fits(groups * 8 * m_tiles, 64 * kGemmWaves) : (!grid_fits(n_tiles, 256) || m_tiles > INT32_MAX))
@@ -279,7 +333,7 @@ hipError_t launch_write_typed(const WritePrepArgs& p, const WriteGemmArgs& g, in
   hipLaunchKernelGGL(write_prep_kernel, dim3(1), dim3(1024), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (tiled) {
+  if constexpr (tiled) {
     hipLaunchKernelGGL(write_gemm_bf16_kernel<PT>, dim3((unsigned)(groups * 8 * m_tiles)), dim3(64 * kGemmWaves), 0,
                        s, g, n_tiles / 2, (int)m_tiles);
     return hipGetLastError();
