@@ -1029,23 +1029,27 @@ __global__ __launch_bounds__(256, OCC) void cross_attn_kernel(CrossArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[f][i] = fmaf(sc[f][i], score_scale, bias[i]);
     }
+    // Lazy rescale: the reference max moves only when a row's max exceeds it
+    // by more than kRescaleSlack (log2 units), so p <= 2^slack and O, l are
+    // rarely rescaled; O / l is the same quotient.  A pair's first tile always
+    // moves it, which also clears O and l (the factor is 0 while the
+    // reference max is -inf).  A row's max exceeds its reference max exactly
+    // when one of its lanes' own maxima does, so the lanes' maxima and one
+    // ballot decide whether any row moves; the rows' maxima (a reduction over
+    // the four lane groups) are taken only then.
     float mx[NQF];
 #pragma unroll
     for (int f = 0; f < NQF; ++f) mx[f] = fmaxf(fmaxf(sv[f][0], sv[f][1]), fmaxf(sv[f][2], sv[f][3]));
+    bool any_move = start;
 #pragma unroll
-    for (int f = 0; f < NQF; ++f) mx[f] = wave_max_groups(mx[f]);
-    // Lazy rescale: the reference max moves only when a row's max exceeds it
-    // by more than kRescaleSlack (log2 units), so p <= 2^slack and O, l (in
-    // AGPRs) are rarely rescaled; O / l is the same quotient.  A pair's first
-    // tile always moves it, which also clears O and l (the factor is 0 while
-    // the reference max is -inf).
-    bool move[NQF], any_move = false;
-#pragma unroll
-    for (int f = 0; f < NQF; ++f) {
-      move[f] = start || mx[f] > m_run[f] + kRescaleSlack;
-      any_move |= move[f];
-    }
+    for (int f = 0; f < NQF; ++f) any_move |= mx[f] > m_run[f] + kRescaleSlack;
     if (__ballot(any_move) != 0) {
+      bool move[NQF];
+#pragma unroll
+      for (int f = 0; f < NQF; ++f) {
+        mx[f] = wave_max_groups(mx[f]);
+        move[f] = start || mx[f] > m_run[f] + kRescaleSlack;
+      }
 #pragma unroll
       for (int f = 0; f < NQF; ++f) {
         const float m_new = move[f] ? mx[f] : m_run[f];
