@@ -389,13 +389,14 @@ def xcd_calibration(w, reps: int = 3, rounds: int = 2) -> dict | None:
 
     from block_diffusion_drafter_all_amd import binding as B
 
-    nw = plan_waves(w.pool_dtype)
+    nw = 4096  # records for the most waves a plan has; waves without tiles leave theirs at zero
     ws = torch.zeros(B.fm_cross_attention_workspace_size(w.bs, w.H, w.Dh, w.max_q, w.pool_dtype), dtype=torch.uint8,
                      device="cuda")
     out = torch.empty_like(w.q[0])
     clock = torch.zeros((nw, 4), dtype=torch.int64, device="cuda")
     per_tile = [[] for _ in range(8)]
     weights = None
+    n_timed = 0
     for _ in range(rounds):
         B.fm_plan_cross_attention(w.ctx_lens, w.H, w.Dh, ws, max_q=w.max_q, pool_dtype=w.pool_dtype,
                                   xcd_weights=weights)
@@ -407,9 +408,10 @@ def xcd_calibration(w, reps: int = 3, rounds: int = 2) -> dict | None:
             torch.cuda.synchronize()
             if rep == 0:
                 continue  # untimed first run
-            for t0, t1, xcd, tiles in clock.cpu().tolist():
-                if tiles > 0:
-                    per_tile[int(xcd) % 8].append((t1 - t0) / tiles)
+            recs = [r for r in clock.cpu().tolist() if r[3] > 0]
+            n_timed = len(recs)
+            for t0, t1, xcd, tiles in recs:
+                per_tile[int(xcd) % 8].append((t1 - t0) / tiles)
         if any(not v for v in per_tile):
             return None
         t = [sum(v) / len(v) for v in per_tile]
@@ -417,8 +419,8 @@ def xcd_calibration(w, reps: int = 3, rounds: int = 2) -> dict | None:
         mean_rate = sum(rate) / 8
         weights = [int(round(min(1200.0, max(800.0, 1000.0 * r / mean_rate)))) for r in rate]
     return {"xcd_weights": weights, "xcd_us_per_tile": [round(x * 0.01, 4) for x in t],
-            "xcd_calibration": (f"layer 0's cross-attention call timed per wave ({nw} waves), {rounds} rounds of "
-                                f"{reps} timed calls")}
+            "xcd_calibration": (f"layer 0's cross-attention call timed per wave ({n_timed} waves with tiles), "
+                                f"{rounds} rounds of {reps} timed calls")}
 
 
 def copy_calibration() -> None:
