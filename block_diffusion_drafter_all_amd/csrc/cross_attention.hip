@@ -15,15 +15,19 @@
 // wavefront; each wave streams its range with DEPTH tiles in flight and never
 // restarts its load pipeline at a pair boundary: the loader walks on to the
 // next pair and carries that pair's query rows along with its first tile.
-//   - K/V tiles are read straight from the pages into MFMA operand layout
-//     (16-byte loads).  Page ids are read one tile ahead: with pages of at
-//     least 16 tokens (one page per tile) as one scalar load of the page-table
-//     entry, else from a per-wave LDS window of the request's page row; either
-//     way waiting for one never waits for K/V loads in flight;
+//   - with pages of at least 16 tokens (one page per tile) K/V tiles arrive
+//     in a per-wave LDS ring by direct buffer->LDS loads of whole rows
+//     (nontemporal), chunks XOR-swizzled so the operand reads hit every bank;
+//     with smaller pages they are read straight into MFMA operand layout
+//     (16-byte loads into a register ring).  Page ids are read one tile ahead:
+//     one scalar load of the page-table entry for pages of >= 16 tokens, else
+//     from a per-wave LDS window of the request's page row; either way waiting
+//     for one never waits for K/V loads in flight;
 //   - S^T = K Q^T leaves each lane one query row and four keys, which is the
 //     B-operand layout of O^T = V^T P^T, so the online softmax and its rescale
-//     stay in registers; V is moved to column layout by an MFMA against a 0/1
-//     selection matrix;
+//     stay in registers; V reaches column layout through gfx950's LDS
+//     transpose reads (bf16 and e4m3 tiles in LDS) or, in the register ring,
+//     by an MFMA against a 0/1 selection matrix;
 //   - a pair that lies inside one wave's range is written final; a pair cut by
 //     range boundaries leaves (m, l, O) partials, and the last of its waves to
 //     finish adds them up in wave order in the kernel's tail (deterministic).
